@@ -1,0 +1,183 @@
+"""CPU oracle for block-scaled FP8 / MXFP4 quantisation and GEMM (Python side).
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only the test suite, the
+smoke check and the benchmark's CPU-baseline leg may import this package.  It
+shares no code with the HIP library and never imports it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, explicit format tables);
+this module only marshals numpy arrays through ctypes.  Formats are named
+"e4m3", "e5m2", "e2m1", "e8m0" and "mxfp4".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "e8m0": 3, "mxfp4": 2}
+FP8_TILE_ROWS = 128
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.oracle_decode_table.argtypes = [c_int, vp]
+        L.oracle_decode_table.restype = c_int
+        L.oracle_decode.argtypes = [c_int, ctypes.c_uint]
+        L.oracle_decode.restype = ctypes.c_double
+        L.oracle_encode.argtypes = [c_int, ctypes.c_double]
+        L.oracle_encode.restype = ctypes.c_uint
+        L.oracle_encode_array.argtypes = [c_int, vp, i64, vp]
+        L.oracle_encode_array.restype = None
+        L.oracle_mx_exponent.argtypes = [ctypes.c_double]
+        L.oracle_mx_exponent.restype = c_int
+        L.oracle_fp8_quantize.argtypes = [vp, i64, i64, i64, i64, c_int, vp, vp]
+        L.oracle_fp8_quantize.restype = c_int
+        L.oracle_mxfp4_quantize.argtypes = [vp, i64, i64, i64, vp, vp]
+        L.oracle_mxfp4_quantize.restype = c_int
+        L.oracle_gemm_rows.argtypes = [i64, i64, i64, i64, c_int, vp, vp, c_int, vp, vp,
+                                       i64, i64, vp, vp]
+        L.oracle_gemm_rows.restype = c_int
+        L.oracle_gemm_points.argtypes = [i64, i64, i64, i64, c_int, vp, vp, c_int, vp, vp,
+                                         i64, vp, vp, vp, vp]
+        L.oracle_gemm_points.restype = c_int
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = c_int
+        L.oracle_set_threads.argtypes = [c_int]
+        L.oracle_set_threads.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def threads() -> int:
+    return lib().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
+
+
+def decode_table(fmt: str) -> np.ndarray:
+    n = 16 if fmt == "e2m1" else 256
+    out = np.empty(n, dtype=np.float64)
+    got = lib().oracle_decode_table(_FMT[fmt], _ptr(out))
+    assert got == n
+    return out
+
+
+def encode(fmt: str, values) -> np.ndarray:
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float64).reshape(-1))
+    out = np.empty(v.size, dtype=np.uint8)
+    lib().oracle_encode_array(_FMT[fmt], _ptr(v), v.size, _ptr(out))
+    return out.reshape(np.shape(values))
+
+
+def mx_exponent(amax: float) -> int:
+    return lib().oracle_mx_exponent(float(amax))
+
+
+def fp8_quantize(x: np.ndarray, fmt: str = "e4m3", tile_rows: int = FP8_TILE_ROWS):
+    """x: rows x k float32.  Returns (codes uint8 rows x k,
+    scales float32 [ceil(rows/tile_rows)][ceil(k/32)])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, k = x.shape
+    codes = np.zeros((rows, k), dtype=np.uint8)
+    scales = np.zeros(((rows + tile_rows - 1) // tile_rows, (k + 31) // 32), dtype=np.float32)
+    rc = lib().oracle_fp8_quantize(_ptr(x), rows, k, k, tile_rows, _FMT[fmt],
+                                   _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_fp8_quantize rc={rc}")
+    return codes, scales
+
+
+def mxfp4_quantize(x: np.ndarray):
+    """x: rows x k float32, k even.  Returns (packed uint8 rows x k/2,
+    E8M0 scales uint8 [rows][ceil(k/32)])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, k = x.shape
+    packed = np.zeros((rows, k // 2), dtype=np.uint8)
+    scales = np.zeros((rows, (k + 31) // 32), dtype=np.uint8)
+    rc = lib().oracle_mxfp4_quantize(_ptr(x), rows, k, k, _ptr(packed), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_mxfp4_quantize rc={rc}")
+    return packed, scales
+
+
+def _gemm_args(a_fmt, a, a_scales, b_fmt, b, b_scales):
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    a_scales = np.ascontiguousarray(a_scales)
+    b_scales = np.ascontiguousarray(b_scales)
+    M = a.shape[0]
+    N = b.shape[0]
+    K = a.shape[1] * (2 if a_fmt == "mxfp4" else 1)
+    return M, N, K, a, a_scales, b, b_scales
+
+
+def gemm_rows(a_fmt, a, a_scales, b_fmt, b, b_scales, row0=0, row1=None,
+              tile_rows: int = FP8_TILE_ROWS):
+    """Rows [row0, row1) of D = deq(A) deq(B)^T and S = sum |a b| (fp64).
+    A: M x K codes (M x K/2 packed for MXFP4); B: N x K codes (a K x N
+    column-major matrix)."""
+    M, N, K, a, a_scales, b, b_scales = _gemm_args(a_fmt, a, a_scales, b_fmt, b, b_scales)
+    row1 = M if row1 is None else row1
+    d = np.empty((row1 - row0, N), dtype=np.float64)
+    s = np.empty((row1 - row0, N), dtype=np.float64)
+    rc = lib().oracle_gemm_rows(M, N, K, tile_rows, _FMT[a_fmt], _ptr(a), _ptr(a_scales),
+                                _FMT[b_fmt], _ptr(b), _ptr(b_scales), row0, row1,
+                                _ptr(d), _ptr(s))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_rows rc={rc}")
+    return d, s
+
+
+def gemm_points(a_fmt, a, a_scales, b_fmt, b, b_scales, ii, jj,
+                tile_rows: int = FP8_TILE_ROWS):
+    """D and S at the output positions (ii[p], jj[p])."""
+    M, N, K, a, a_scales, b, b_scales = _gemm_args(a_fmt, a, a_scales, b_fmt, b, b_scales)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    d = np.empty(ii.size, dtype=np.float64)
+    s = np.empty(ii.size, dtype=np.float64)
+    rc = lib().oracle_gemm_points(M, N, K, tile_rows, _FMT[a_fmt], _ptr(a), _ptr(a_scales),
+                                  _FMT[b_fmt], _ptr(b), _ptr(b_scales), ii.size,
+                                  _ptr(ii), _ptr(jj), _ptr(d), _ptr(s))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_points rc={rc}")
+    return d, s
+
+
+def dequantize(fmt: str, q: np.ndarray, scales: np.ndarray, tile_rows: int = FP8_TILE_ROWS):
+    """Dequantised operand in fp64 (rows x K), by the oracle's tables."""
+    q = np.asarray(q)
+    if fmt == "mxfp4":
+        rows, kh = q.shape
+        lo = (q & 0xF).astype(np.int64)
+        hi = (q >> 4).astype(np.int64)
+        nib = np.empty((rows, 2 * kh), dtype=np.int64)
+        nib[:, 0::2] = lo
+        nib[:, 1::2] = hi
+        t4 = decode_table("e2m1")
+        t8 = decode_table("e8m0")
+        sc = np.repeat(t8[np.asarray(scales, dtype=np.int64)], 32, axis=1)[:, : 2 * kh]
+        return t4[nib] * sc
+    t = decode_table(fmt)
+    rows, k = q.shape
+    s = np.asarray(scales, dtype=np.float64)
+    sfull = np.repeat(np.repeat(s, tile_rows, axis=0)[:rows], 32, axis=1)[:, :k]
+    return t[q.astype(np.int64)] * sfull
