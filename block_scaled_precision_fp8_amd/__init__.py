@@ -1,0 +1,127 @@
+"""Block-scaled FP8 / MXFP4 quantisation and GEMM on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libbsfp8.so`` (C ABI in ``include/bsfp8.h``).
+It only marshals arguments: PyTorch provides the device memory and the
+stream, every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing, importing the functions
+raises, and a non-OK status raises ``RuntimeError``.
+
+Functions (same names as the C ABI):
+  fp8_quantize(x, fmt="e4m3", tile_rows=128) -> (codes, scales)
+  mxfp4_quantize(x) -> (packed, scales)
+  scaled_gemm(a, a_scales, b, b_scales, a_fmt, b_fmt, out="bf16", d=None) -> d
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("BSFP8_LIB", os.path.join(_HERE, "libbsfp8.so"))
+
+FORMATS = {"e4m3": 0, "e5m2": 1, "mxfp4": 2}
+OUTS = {"f32": 0, "bf16": 1}
+STATUS = {0: "BSFP8_OK", 1: "BSFP8_ERR_INVALID_ARG", 2: "BSFP8_ERR_UNSUPPORTED",
+          3: "BSFP8_ERR_HIP"}
+FP8_TILE_ROWS = 128
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbsfp8.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libbsfp8.so not found at {LIB_PATH}; build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` or "
+            "`python block_scaled_precision_fp8_amd/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    L.fp8_quantize.argtypes = [vp, i64, i64, i64, c_int, c_int, vp, vp, vp]
+    L.fp8_quantize.restype = c_int
+    L.mxfp4_quantize.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+    L.mxfp4_quantize.restype = c_int
+    L.scaled_gemm.argtypes = [i64, i64, i64, c_int, vp, vp, c_int, vp, vp, c_int, vp, i64, vp]
+    L.scaled_gemm.restype = c_int
+    L.bsfp8_status_string.argtypes = [c_int]
+    L.bsfp8_status_string.restype = ctypes.c_char_p
+    L.bsfp8_version.argtypes = []
+    L.bsfp8_version.restype = c_int
+    _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        name = lib().bsfp8_status_string(status).decode()
+        raise RuntimeError(f"{what} failed: {name}")
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev_ptr(t) -> int:
+    return t.data_ptr() if t.numel() > 0 else 0
+
+
+def fp8_quantize(x, fmt: str = "e4m3", tile_rows: int = FP8_TILE_ROWS,
+                 codes=None, scales=None):
+    """Quantise a rows x k FP32 CUDA tensor (row-major, unit column stride)
+    to FP8 codes with one FP32 scale per tile_rows x 32 tile."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 CUDA tensor with unit column stride")
+    rows, k = x.shape
+    if codes is None:
+        codes = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(((rows + tile_rows - 1) // tile_rows, (k + 31) // 32),
+                             dtype=torch.float32, device=x.device)
+    st = lib().fp8_quantize(_dev_ptr(x), rows, k, x.stride(0) if rows > 1 else k, tile_rows,
+                            FORMATS[fmt], _dev_ptr(codes), _dev_ptr(scales), _stream(x))
+    _check(st, "fp8_quantize")
+    return codes, scales
+
+
+def mxfp4_quantize(x, packed=None, scales=None):
+    """Quantise a rows x k FP32 CUDA tensor to packed E2M1 (two per byte)
+    with one E8M0 scale byte per 32-element block of a row."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 CUDA tensor with unit column stride")
+    rows, k = x.shape
+    if packed is None:
+        packed = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, (k + 31) // 32), dtype=torch.uint8, device=x.device)
+    st = lib().mxfp4_quantize(_dev_ptr(x), rows, k, x.stride(0) if rows > 1 else k,
+                              _dev_ptr(packed), _dev_ptr(scales), _stream(x))
+    _check(st, "mxfp4_quantize")
+    return packed, scales
+
+
+def scaled_gemm(a, a_scales, b, b_scales, a_fmt: str = "e4m3", b_fmt: str = "e4m3",
+                out: str = "bf16", d=None, K: Optional[int] = None):
+    """D = deq(A) deq(B): A is M x K codes (M x K/2 packed for MXFP4), B is
+    N x K codes (a K x N column-major matrix).  Returns D (M x N, float32 or
+    bfloat16)."""
+    import torch
+    M = a.shape[0]
+    N = b.shape[0]
+    if K is None:
+        K = a.shape[1] * (2 if a_fmt == "mxfp4" else 1)
+    if d is None:
+        dt = torch.float32 if out == "f32" else torch.bfloat16
+        d = torch.empty((M, N), dtype=dt, device=a.device)
+    ldd = d.stride(0) if M > 1 else N
+    st = lib().scaled_gemm(M, N, K, FORMATS[a_fmt], _dev_ptr(a), _dev_ptr(a_scales),
+                           FORMATS[b_fmt], _dev_ptr(b), _dev_ptr(b_scales), OUTS[out],
+                           _dev_ptr(d), ldd, _stream(a))
+    _check(st, "scaled_gemm")
+    return d

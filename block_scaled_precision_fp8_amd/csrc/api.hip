@@ -1,0 +1,88 @@
+// api.hip -- the C ABI of libbsfp8 (declared in include/bsfp8.h).
+// Validates every argument on the host, then launches; a non-OK status means
+// nothing was launched.  No allocation, no synchronisation, no global state.
+#include "internal.h"
+
+#include <limits>
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline bool is_fp8(int f) { return f == BSFP8_E4M3 || f == BSFP8_E5M2; }
+constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+
+inline bsfp8_status from_hip(hipError_t e) { return e == hipSuccess ? BSFP8_OK : BSFP8_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+bsfp8_status fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, int tile_rows,
+                          bsfp8_format fmt, uint8_t* codes, float* scales, hipStream_t stream) {
+    if (!is_fp8(fmt)) return BSFP8_ERR_UNSUPPORTED;
+    if (tile_rows != 128) return BSFP8_ERR_UNSUPPORTED;
+    if (rows < 0 || k < 0 || ld < k || (k % 32) != 0) return BSFP8_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return BSFP8_OK;
+    if (!x || !codes || !scales) return BSFP8_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || (ld % 4) != 0 || !aligned(codes, 4) || !aligned(scales, 4))
+        return BSFP8_ERR_INVALID_ARG;
+    const int64_t blocks = ((rows + 127) / 128) * ((k + 127) / 128);
+    if (blocks > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    return from_hip(bsfp8::launch_fp8_quantize(x, rows, k, ld, fmt, codes, scales, stream));
+}
+
+bsfp8_status mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
+                            uint8_t* packed, uint8_t* scales, hipStream_t stream) {
+    if (rows < 0 || k < 0 || ld < k || (k % 32) != 0) return BSFP8_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return BSFP8_OK;
+    if (!x || !packed || !scales) return BSFP8_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || (ld % 4) != 0 || !aligned(packed, 2)) return BSFP8_ERR_INVALID_ARG;
+    const int64_t blocks = (rows * (k / 4) + 255) / 256;
+    if (rows > kI32Max * 256 || blocks > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    return from_hip(bsfp8::launch_mxfp4_quantize(x, rows, k, ld, packed, scales, stream));
+}
+
+bsfp8_status scaled_gemm(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt, const void* a,
+                         const void* a_scales, bsfp8_format b_fmt, const void* b,
+                         const void* b_scales, bsfp8_out out, void* d, int64_t ldd,
+                         hipStream_t stream) {
+    const bool fp8 = is_fp8(a_fmt) && is_fp8(b_fmt);
+    const bool mx = a_fmt == BSFP8_MXFP4 && b_fmt == BSFP8_MXFP4;
+    if (!fp8 && !mx) return BSFP8_ERR_UNSUPPORTED;
+    if (out != BSFP8_OUT_F32 && out != BSFP8_OUT_BF16) return BSFP8_ERR_UNSUPPORTED;
+    if (M < 0 || N < 0 || K < 0 || (K % 32) != 0) return BSFP8_ERR_INVALID_ARG;
+    if (M > kI32Max || N > kI32Max || K > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return BSFP8_OK;
+    if (!d || ldd < N) return BSFP8_ERR_INVALID_ARG;
+    if (!aligned(d, out == BSFP8_OUT_F32 ? 4 : 2)) return BSFP8_ERR_INVALID_ARG;
+    if (K == 0) return from_hip(bsfp8::launch_fill_zero(M, N, out, d, ldd, stream));
+    if (!a || !b || !a_scales || !b_scales) return BSFP8_ERR_INVALID_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16)) return BSFP8_ERR_INVALID_ARG;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    if (fp8) {
+        if (!aligned(a_scales, 4) || !aligned(b_scales, 4)) return BSFP8_ERR_INVALID_ARG;
+        return from_hip(bsfp8::launch_gemm_fp8(
+            M, N, K, a_fmt, static_cast<const uint8_t*>(a), static_cast<const float*>(a_scales),
+            b_fmt, static_cast<const uint8_t*>(b), static_cast<const float*>(b_scales), out, d,
+            ldd, stream));
+    }
+    return from_hip(bsfp8::launch_gemm_mxfp4(
+        M, N, K, static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(a_scales),
+        static_cast<const uint8_t*>(b), static_cast<const uint8_t*>(b_scales), out, d, ldd,
+        stream));
+}
+
+const char* bsfp8_status_string(bsfp8_status s) {
+    switch (s) {
+    case BSFP8_OK: return "BSFP8_OK";
+    case BSFP8_ERR_INVALID_ARG: return "BSFP8_ERR_INVALID_ARG";
+    case BSFP8_ERR_UNSUPPORTED: return "BSFP8_ERR_UNSUPPORTED";
+    case BSFP8_ERR_HIP: return "BSFP8_ERR_HIP";
+    default: return "BSFP8_ERR_UNKNOWN";
+    }
+}
+
+int bsfp8_version(void) { return (0 << 16) | 1; }
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+// quantize.hip -- FP8 per-tile and MXFP4 per-block quantisation kernels for gfx950.
+//
+// Both kernels are HBM-bound streaming passes: each FP32 element is read once
+// with 16-byte loads, its tile or block maximum is reduced across the lanes
+// holding that tile (cross-lane shuffles, then LDS for FP8 tiles), and the
+// codes are written once.
+//
+// FP8 ("Why grind FP8 GEMM on CDNA4", sections 3.3 and 4.2): per 128 x 32
+// tile, s = fl32(amax / F) (1 for an all-zero tile), code = satRNE(fl32(x / s)).
+// The division is IEEE-correct (the compiler's correctly rounded sequence);
+// saturation is an explicit clamp to +-F, after which the hardware
+// v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 conversion is exact round-to-nearest-even
+// (checked element by element against the oracle, including every midpoint).
+//
+// MXFP4 ("Rubin FP4 GEMM deep dive", sections 2.1, 2.2, 3.1 and 4.2): per 32
+// consecutive K elements, e = smallest integer with 6 * 2^e >= amax, read off
+// the FP32 exponent and mantissa bits of amax; elements are scaled by the exact
+// power of two 2^-e and converted with v_cvt_scalef32_pk_fp4_f32 (unit scale),
+// which rounds to nearest even; two codes per byte, low nibble first.
+#include "internal.h"
+
+namespace bsfp8 {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float abs_max4(float4 v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// One workgroup quantises a 128-row x 128-column block = four 128 x 32 tiles.
+// Thread t holds 16-byte chunk (t % 32) of rows (t / 32) + 8 i, i = 0..15, so a
+// wave reads two full 512-byte row segments per load instruction and every
+// thread's 64 values belong to a single tile (chunk / 8).
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void fp8_quantize_kernel(
+    const float* __restrict__ x, int64_t rows, int64_t k, int64_t ld,
+    uint8_t* __restrict__ codes, float* __restrict__ scales, int64_t ncol_blocks) {
+    constexpr float F = FMT == BSFP8_E4M3 ? 448.0f : 57344.0f;
+    __shared__ float red[4][4];
+
+    const int64_t bid = blockIdx.x;
+    const int64_t rt = bid / ncol_blocks;
+    const int64_t cb = bid - rt * ncol_blocks;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int chunk = tid & 31;
+    const int ro = tid >> 5;
+    const int64_t col = cb * 128 + chunk * 4;
+    const bool col_ok = col < k;  // k is a multiple of 32: whole tiles are in or out
+    const int64_t r0 = rt * 128;
+    const int64_t nkb = k >> 5;
+
+    float4 v[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t r = r0 + ro + 8 * i;
+        if (col_ok && r < rows)
+            v[i] = *reinterpret_cast<const float4*>(x + r * ld + col);
+        else
+            v[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        amax = fmaxf(amax, abs_max4(v[i]));
+    }
+    // The 16 lanes of a wave that hold one tile differ in lane bits 0, 1, 2 and 5.
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if ((lane & 0x27) == 0) red[wave][(lane >> 3) & 3] = amax;
+    __syncthreads();
+
+    const int t = chunk >> 3;
+    amax = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+    float s = amax / F;
+    if (s == 0.0f) s = 1.0f;
+
+    if (tid < 4 && cb * 128 + tid * 32 < k) {
+        const float a = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+        float st = a / F;
+        if (st == 0.0f) st = 1.0f;
+        scales[rt * nkb + cb * 4 + tid] = st;
+    }
+
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t r = r0 + ro + 8 * i;
+        if (!(col_ok && r < rows)) continue;
+        const float q0 = fminf(fmaxf(v[i].x / s, -F), F);
+        const float q1 = fminf(fmaxf(v[i].y / s, -F), F);
+        const float q2 = fminf(fmaxf(v[i].z / s, -F), F);
+        const float q3 = fminf(fmaxf(v[i].w / s, -F), F);
+        int w;
+        if constexpr (FMT == BSFP8_E4M3) {
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
+        } else {
+            w = __builtin_amdgcn_cvt_pk_bf8_f32(q0, q1, 0, false);
+            w = __builtin_amdgcn_cvt_pk_bf8_f32(q2, q3, w, true);
+        }
+        *reinterpret_cast<uint32_t*>(codes + r * k + col) = static_cast<uint32_t>(w);
+    }
+}
+
+// One thread per 16-byte chunk (4 elements); the 8 consecutive lanes of a
+// 32-element block reduce their maximum with three shuffles.
+__global__ __launch_bounds__(kThreads) void mxfp4_quantize_kernel(
+    const float* __restrict__ x, int64_t k, int64_t ld, uint8_t* __restrict__ packed,
+    uint8_t* __restrict__ scales, int64_t chunks_per_row, int64_t total_chunks) {
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const bool ok = g < total_chunks;
+    const int64_t r = ok ? g / chunks_per_row : 0;
+    const int64_t c = ok ? g - r * chunks_per_row : 0;
+
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (ok) v = *reinterpret_cast<const float4*>(x + r * ld + 4 * c);
+    float amax = abs_max4(v);
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+
+    // e = ceil(log2(amax / 6)) from the bits of amax = f * 2^E, f in [1, 2):
+    // e = E - 2 when f <= 1.5, else E - 1; subnormal amax clamps to -127.
+    const uint32_t u = __float_as_uint(amax);
+    int e;
+    if (amax == 0.0f) {
+        e = 0;
+    } else if (u < 0x00800000u) {
+        e = -127;
+    } else {
+        e = static_cast<int>(u >> 23) - 127 - 2 + ((u & 0x007FFFFFu) > 0x00400000u ? 1 : 0);
+        if (e < -127) e = -127;
+    }
+    // 2^-e as an FP32 bit pattern; finite amax gives e <= 126, so the exponent field is >= 1.
+    const float y = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+
+    if (!ok) return;
+    int w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0, v.x * y, v.y * y, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v.z * y, v.w * y, 1.0f, 1);
+    *reinterpret_cast<uint16_t*>(packed + r * (k >> 1) + 2 * c) = static_cast<uint16_t>(w & 0xFFFF);
+    if ((c & 7) == 0) scales[r * (k >> 5) + (c >> 3)] = static_cast<uint8_t>(e + 127);
+}
+
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(int64_t M, int64_t N, int out,
+                                                              void* d, int64_t ldd) {
+    const int64_t total = M * N;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const int64_t r = i / N, c = i - r * N;
+        if (out == BSFP8_OUT_F32)
+            static_cast<float*>(d)[r * ldd + c] = 0.0f;
+        else
+            static_cast<uint16_t*>(d)[r * ldd + c] = 0;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, int fmt,
+                               uint8_t* codes, float* scales, hipStream_t stream) {
+    const int64_t nrt = (rows + 127) / 128;
+    const int64_t ncb = (k + 127) / 128;
+    const int64_t blocks = nrt * ncb;
+    if (blocks == 0) return hipSuccess;
+    if (fmt == BSFP8_E4M3)
+        hipLaunchKernelGGL(fp8_quantize_kernel<BSFP8_E4M3>, dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales, ncb);
+    else
+        hipLaunchKernelGGL(fp8_quantize_kernel<BSFP8_E5M2>, dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales, ncb);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
+                                 uint8_t* packed, uint8_t* scales, hipStream_t stream) {
+    const int64_t cpr = k / 4;
+    const int64_t total = rows * cpr;
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = (total + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(mxfp4_quantize_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
+                       0, stream, x, k, ld, packed, scales, cpr, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(int64_t M, int64_t N, int out, void* d, int64_t ldd,
+                            hipStream_t stream) {
+    const int64_t total = M * N;
+    if (total == 0) return hipSuccess;
+    int64_t blocks = (total + kThreads - 1) / kThreads;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0,
+                       stream, M, N, out, d, ldd);
+    return hipGetLastError();
+}
+
+}  // namespace bsfp8

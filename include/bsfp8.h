@@ -1,0 +1,132 @@
+/*
+ * bsfp8.h -- block-scaled FP8 / MXFP4 quantisation and GEMM on AMD MI355X (gfx950).
+ *
+ * A small C ABI over hand-written HIP kernels.  Every pointer argument is a
+ * DEVICE pointer owned by the caller; the library never allocates, frees or
+ * synchronises.  Every call is asynchronous on `stream` (0 = the null stream).
+ * All argument checks run on the host before anything is launched: a call
+ * that returns a status other than BSFP8_OK has launched nothing.  After a
+ * launch the HIP launch error, if any, is returned as BSFP8_ERR_HIP.  No
+ * global state: calls are thread-safe; calls that write the same output
+ * buffer concurrently race.
+ *
+ * Pages cited (by title and section):
+ *   [CDNA4-FP8] "Why grind FP8 GEMM on CDNA4" (dpshk.com article)
+ *   [RUBIN-FP4] "Rubin FP4 GEMM deep dive: from Blackwell to the next GPU"
+ *   [HOPPER-MMA] "FP8 MMA internals on Hopper"
+ *
+ * Layout conventions ([CDNA4-FP8] section 3.1, [RUBIN-FP4] section 3.1):
+ * A is M x K row-major (K contiguous); B is K x N column-major, i.e. stored as
+ * N rows of K contiguous elements; D is M x N row-major with leading
+ * dimension ldd (elements).  A "K block" is 32 consecutive K indices.
+ */
+#ifndef BSFP8_H
+#define BSFP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same typedef as the HIP runtime's; repeating it is harmless. */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+    BSFP8_OK = 0,
+    BSFP8_ERR_INVALID_ARG = 1,  /* null pointer, negative size, K not a multiple of 32, ld < k, ... */
+    BSFP8_ERR_UNSUPPORTED = 2,  /* undefined enum value or format mix, tile_rows != 128 */
+    BSFP8_ERR_HIP = 3           /* the HIP runtime reported a launch error */
+} bsfp8_status;
+
+typedef enum {
+    BSFP8_E4M3 = 0,   /* OCP E4M3 ("FN"): max 448, no infinity */
+    BSFP8_E5M2 = 1,   /* OCP E5M2: max 57344 */
+    BSFP8_MXFP4 = 2   /* E2M1 elements, two per byte, E8M0 scale per 32-element K block */
+} bsfp8_format;
+
+typedef enum {
+    BSFP8_OUT_F32 = 0,
+    BSFP8_OUT_BF16 = 1
+} bsfp8_out;
+
+/*
+ * fp8_quantize -- per-tile FP8 quantisation ([CDNA4-FP8] sections 3.3 and 4.2).
+ *
+ * x:      rows x k FP32, row-major, leading dimension ld (elements).
+ *         16-byte aligned, ld a multiple of 4, ld >= k.
+ * rows:   >= 0, any value; the last tile may have fewer than tile_rows rows.
+ * k:      >= 0, a multiple of 32.
+ * tile_rows: rows per scale tile; must be 128 (tiles are 128 x 32).
+ * fmt:    BSFP8_E4M3 (F = 448) or BSFP8_E5M2 (F = 57344).
+ * codes:  out, rows x k bytes, row stride k, 16-byte aligned.
+ * scales: out, FP32 [ceil(rows / 128)][k / 32], K-block index fastest.
+ *
+ * Per tile: amax = max |x|, s = amax / F rounded to FP32 (s = 1 when that is
+ * zero), code = saturating round-to-nearest-even of (x / s rounded to FP32).
+ * Output is bit-exact: the same bytes on every call and every launch shape.
+ * Finite inputs only.  A B operand (K x N column-major) is quantised by
+ * passing its N x K storage: rows = N, k = K, giving the 32 x 128 (K x N)
+ * tiles of the pages.
+ */
+bsfp8_status fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, int tile_rows,
+                          bsfp8_format fmt, uint8_t* codes, float* scales, hipStream_t stream);
+
+/*
+ * mxfp4_quantize -- MXFP4 block quantisation ([RUBIN-FP4] sections 2.1, 2.2, 3.1, 4.2).
+ *
+ * x:      rows x k FP32, row-major, leading dimension ld; 16-byte aligned,
+ *         ld a multiple of 4, ld >= k.  rows >= 0; k >= 0, a multiple of 32.
+ * packed: out, rows x (k / 2) bytes, row stride k / 2.  Element 2i sits in the
+ *         low nibble of byte i, element 2i+1 in the high nibble.
+ * scales: out, E8M0 bytes [rows][k / 32].
+ *
+ * Per 32-element block of a row: e = the smallest integer with 6 * 2^e >= amax
+ * (e = 0 when amax is 0), clamped to [-127, 127]; scale byte = e + 127;
+ * element code = round-to-nearest-even E2M1 of x * 2^-e (exact scaling).
+ * Bit-exact.  Finite inputs only.
+ */
+bsfp8_status mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
+                            uint8_t* packed, uint8_t* scales, hipStream_t stream);
+
+/*
+ * scaled_gemm -- D = deq(A) * deq(B) with FP32 accumulation
+ * ([CDNA4-FP8] sections 2.3, 3.2-3.4, 4.3, 4.4; [RUBIN-FP4] sections 2.2, 3.1-3.3).
+ *
+ * M, N >= 0 (any value; edge tiles are masked), K >= 0 a multiple of 32.
+ * FP8 operands (a_fmt, b_fmt each BSFP8_E4M3 or BSFP8_E5M2, any mix):
+ *   a: M x K codes (row stride K); a_scales: FP32 [ceil(M/128)][K/32]
+ *   b: N x K codes (row stride K); b_scales: FP32 [ceil(N/128)][K/32]
+ *   exactly the outputs of fp8_quantize with tile_rows = 128.
+ *   Each 32-wide K block's partial product is scaled by
+ *   a_scale(tile, block) * b_scale(tile, block) before it is accumulated.
+ * MXFP4 operands (a_fmt = b_fmt = BSFP8_MXFP4):
+ *   a: M x K/2 packed bytes; a_scales: E8M0 [M][K/32]
+ *   b: N x K/2 packed bytes; b_scales: E8M0 [N][K/32]
+ *   (the outputs of mxfp4_quantize).
+ * out:  BSFP8_OUT_F32 or BSFP8_OUT_BF16 (round to nearest even).
+ * d:    M x N row-major, leading dimension ldd >= N (elements).
+ * a, b must be 16-byte aligned.  K = 0 writes zeros.
+ *
+ * Accuracy: with S = sum_k |a_k b_k| (dequantised operands), every output
+ * satisfies |D - exact| <= 2^-19 S for FP32 output and <= 2^-7 S for bf16
+ * output on the synthetic workloads the library is tested on.  FP32 output
+ * uses matrix instructions that keep 24 alignment bits per product sum;
+ * bf16 output uses the FP8 instructions, which keep 13 (the truncation
+ * studied for Hopper in [HOPPER-MMA] is present on gfx950 too).
+ */
+bsfp8_status scaled_gemm(int64_t M, int64_t N, int64_t K,
+                         bsfp8_format a_fmt, const void* a, const void* a_scales,
+                         bsfp8_format b_fmt, const void* b, const void* b_scales,
+                         bsfp8_out out, void* d, int64_t ldd, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* bsfp8_status_string(bsfp8_status s);
+
+/* Library version, (major << 16) | minor. */
+int bsfp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSFP8_H */

@@ -1,0 +1,93 @@
+"""The C-ABI library loads, exports every function include/bsfp8.h declares,
+and rejects invalid arguments on the host before launching anything.  No GPU
+is needed: every call here returns from the host-side checks."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsfp8.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+E4M3, E5M2, MXFP4 = 0, 1, 2
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:bsfp8_status|const char\s*\*|int)\s+(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import block_scaled_precision_fp8_amd as b
+    return b.lib()
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("fp8_quantize", "mxfp4_quantize", "scaled_gemm", "bsfp8_status_string",
+              "bsfp8_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), f"missing export {n}"
+
+
+def test_status_strings(L):
+    assert L.bsfp8_status_string(0) == b"BSFP8_OK"
+    assert L.bsfp8_status_string(1) == b"BSFP8_ERR_INVALID_ARG"
+    assert L.bsfp8_status_string(2) == b"BSFP8_ERR_UNSUPPORTED"
+    assert L.bsfp8_status_string(3) == b"BSFP8_ERR_HIP"
+    assert L.bsfp8_status_string(99) == b"BSFP8_ERR_UNKNOWN"
+    assert L.bsfp8_version() >= 1
+
+
+P = 0x1000  # a fake, 4 KiB-aligned "device pointer": never dereferenced by these calls
+
+
+def test_fp8_quantize_argument_checks(L):
+    q = L.fp8_quantize
+    assert q(P, 128, 48, 48, 128, E4M3, P, P, None) == INVALID      # k % 32
+    assert q(P, -1, 64, 64, 128, E4M3, P, P, None) == INVALID       # negative rows
+    assert q(P, 128, 64, 32, 128, E4M3, P, P, None) == INVALID      # ld < k
+    assert q(P, 128, 64, 66, 128, E4M3, P, P, None) == INVALID      # ld % 4
+    assert q(P + 4, 128, 64, 64, 128, E4M3, P, P, None) == INVALID  # x not 16-byte aligned
+    assert q(0, 128, 64, 64, 128, E4M3, P, P, None) == INVALID      # null x
+    assert q(P, 128, 64, 64, 64, E4M3, P, P, None) == UNSUPPORTED   # tile_rows
+    assert q(P, 128, 64, 64, 128, MXFP4, P, P, None) == UNSUPPORTED
+    assert q(P, 128, 64, 64, 128, 7, P, P, None) == UNSUPPORTED
+    assert q(0, 0, 64, 64, 128, E4M3, 0, 0, None) == OK             # empty: nothing to do
+    assert q(0, 128, 0, 0, 128, E4M3, 0, 0, None) == OK
+
+
+def test_mxfp4_quantize_argument_checks(L):
+    q = L.mxfp4_quantize
+    assert q(P, 16, 48, 48, P, P, None) == INVALID
+    assert q(P, 16, 64, 60, P, P, None) == INVALID
+    assert q(P, -3, 64, 64, P, P, None) == INVALID
+    assert q(P, 16, 64, 64, 0, P, None) == INVALID
+    assert q(P + 8, 16, 64, 64, P, P, None) == INVALID
+    assert q(0, 0, 64, 64, 0, 0, None) == OK
+
+
+def test_scaled_gemm_argument_checks(L):
+    g = L.scaled_gemm
+    assert g(128, 128, 48, E4M3, P, P, E4M3, P, P, BF16, P, 128, None) == INVALID   # K % 32
+    assert g(-1, 128, 64, E4M3, P, P, E4M3, P, P, BF16, P, 128, None) == INVALID
+    assert g(128, 128, 64, E4M3, P, P, E4M3, P, P, BF16, P, 100, None) == INVALID  # ldd < N
+    assert g(128, 128, 64, E4M3, 0, P, E4M3, P, P, BF16, P, 128, None) == INVALID  # null a
+    assert g(128, 128, 64, E4M3, P, P, E4M3, P, 0, BF16, P, 128, None) == INVALID  # null scales
+    assert g(128, 128, 64, E4M3, P + 8, P, E4M3, P, P, BF16, P, 128, None) == INVALID
+    assert g(128, 128, 64, E4M3, P, P, E4M3, P, P, F32, P + 2, 128, None) == INVALID
+    assert g(128, 128, 64, E4M3, P, P, MXFP4, P, P, BF16, P, 128, None) == UNSUPPORTED
+    assert g(128, 128, 64, MXFP4, P, P, E5M2, P, P, BF16, P, 128, None) == UNSUPPORTED
+    assert g(128, 128, 64, E4M3, P, P, E4M3, P, P, 5, P, 128, None) == UNSUPPORTED
+    assert g(0, 128, 64, E4M3, 0, 0, E4M3, 0, 0, BF16, 0, 128, None) == OK      # empty
+    assert g(128, 0, 64, E4M3, 0, 0, E4M3, 0, 0, F32, 0, 0, None) == OK

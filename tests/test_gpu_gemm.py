@@ -1,0 +1,171 @@
+"""GEMM parity: the HIP scaled_gemm against the oracle's fp64 product of the
+dequantised operands, normalised by S = sum_k |a_k b_k|:
+    max |D - D_ref| / S <= 2^-19 (FP32 output), <= 2^-7 (bf16 output).
+Operand codes and scales come from the oracle's quantiser (so no oracle input
+is produced by the HIP path); one end-to-end test per workload also runs the
+HIP quantiser.  Runs through the C ABI (the Python binding)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_common import check_gemm, from_dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bsfp8():
+    import block_scaled_precision_fp8_amd as b
+    return b
+
+
+def oracle_quant(x, fmt):
+    return oracle.mxfp4_quantize(x) if fmt == "mxfp4" else oracle.fp8_quantize(x, fmt)
+
+
+def run_gpu_gemm(qa, sa, qb, sb, a_fmt, b_fmt, out, K):
+    import torch
+    d = bsfp8().scaled_gemm(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), a_fmt, b_fmt, out, K=K)
+    torch.cuda.synchronize()
+    return from_dev(d)
+
+
+def full_check(M, N, K, a_fmt, b_fmt, out, seed, label):
+    say(f"scaled_gemm {label} M={M} N={N} K={K} {a_fmt}x{b_fmt} -> {out}")
+    a = workloads.normal(seed, M, K) * np.float32(2.0)
+    b = workloads.normal(seed + 1, N, K)
+    if a_fmt == "e5m2":
+        a = workloads.laplace(seed, M, K, 1e-3)
+    qa, sa = oracle_quant(a, a_fmt)
+    qb, sb = oracle_quant(b, b_fmt)
+    d = run_gpu_gemm(qa, sa, qb, sb, a_fmt, b_fmt, out, K)
+    dr, sr = oracle.gemm_rows(a_fmt, qa, sa, b_fmt, qb, sb)
+    return check_gemm(d, dr, sr, out, label)
+
+
+def load_dot_examples():
+    out = []
+    with open(os.path.join(GOLDEN, "dot_examples.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            a, b, exact, bits, h100 = [p.strip() for p in line.split("|")]
+            out.append(([float(v) for v in a.split()], [float(v) for v in b.split()],
+                        float(exact), int(bits, 16)))
+    return out
+
+
+def test_dot_examples_fp32_output_exact():
+    """The pages' two dot examples through scaled_gemm with unit scales.  FP32
+    output keeps 24 alignment bits, so both come out exact (not truncated)."""
+    for a, b, exact, bits in load_dot_examples():
+        qa = np.zeros((128, 32), dtype=np.uint8)
+        qb = np.zeros((128, 32), dtype=np.uint8)
+        qa[0, : len(a)] = oracle.encode("e4m3", a)
+        qb[0, : len(b)] = oracle.encode("e4m3", b)
+        one = np.ones((1, 1), dtype=np.float32)
+        say(f"dot example {a} . {b}")
+        d = run_gpu_gemm(qa, one, qb, one, "e4m3", "e4m3", "f32", 32)
+        got = np.float32(d[0, 0]).view(np.uint32)
+        say(f"  FP32 result {d[0, 0]!r} bits {got:#010x} (exact {bits:#010x})")
+        assert got == bits
+        assert np.all(d.reshape(-1)[1:] == 0)
+        db = run_gpu_gemm(qa, one, qb, one, "e4m3", "e4m3", "bf16", 32)
+        assert abs(db[0, 0] - exact) <= 2.0 ** -7 * sum(abs(x * y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("fmts", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"),
+                                  ("e5m2", "e5m2")])
+@pytest.mark.parametrize("M,N,K", [(200, 328, 96), (1, 1, 32), (129, 255, 64),
+                                   (256, 384, 544), (383, 130, 160)])
+def test_fp8_small_ragged(M, N, K, fmts, out):
+    full_check(M, N, K, fmts[0], fmts[1], out, seed=M * 7 + N * 3 + K, label="small")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(200, 328, 96), (1, 1, 32), (129, 255, 64),
+                                   (256, 256, 512), (130, 260, 288), (64, 64, 2080)])
+def test_mxfp4_small_ragged(M, N, K, out):
+    full_check(M, N, K, "mxfp4", "mxfp4", out, seed=M * 5 + N + K, label="small mxfp4")
+
+
+def test_degenerate_shapes():
+    import torch
+    b = bsfp8()
+    say("scaled_gemm degenerate shapes")
+    # K = 0: D = 0
+    a = torch.zeros((130, 0), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((2, 0), dtype=torch.float32, device="cuda")
+    d = torch.full((130, 70), 7.0, dtype=torch.float32, device="cuda")
+    b.scaled_gemm(a, s, a[:70], s[:1], "e4m3", "e4m3", "f32", d=d, K=0)
+    torch.cuda.synchronize()
+    assert torch.all(d == 0)
+    # M = 0: nothing happens
+    e = torch.empty((0, 64), dtype=torch.uint8, device="cuda")
+    r = b.scaled_gemm(e, s, e, s, "e4m3", "e4m3", "bf16", K=64)
+    assert r.shape == (0, 0)
+    # all-zero codes: D = 0 exactly
+    qa = np.zeros((256, 128), dtype=np.uint8)
+    sa = np.ones((2, 4), dtype=np.float32)
+    d = run_gpu_gemm(qa, sa, qa[:130], sa, "e4m3", "e4m3", "f32", 128)
+    assert np.all(d == 0)
+
+
+def _points(M, N, rng, n=3000):
+    ii = np.concatenate([np.arange(128), rng.integers(0, M, n), [M - 1] * 4])
+    jj = np.concatenate([rng.integers(0, N, 128), rng.integers(0, N, n), [0, 1, N - 2, N - 1]])
+    return ii.astype(np.int64), jj.astype(np.int64)
+
+
+@pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
+def test_workload_full_size(name):
+    """Every workload at its full size, in the launch configuration the benchmark
+    times: whole tiny product; sampled outputs (a full 128-row tile's worth of
+    points plus random ones and the corners) for the large ones."""
+    w = workloads.by_name(name)
+    a, b = workloads.operands(w)
+    qa, sa = oracle_quant(a, w.a_fmt)
+    qb, sb = oracle_quant(b, w.b_fmt)
+    say(f"{name}: oracle codes ready; GPU scaled_gemm {w.M}x{w.N}x{w.K} -> {w.out}")
+    d = run_gpu_gemm(qa, sa, qb, sb, w.a_fmt, w.b_fmt, w.out, w.K)
+    if w.M * w.N <= 256 * 256:
+        dr, sr = oracle.gemm_rows(w.a_fmt, qa, sa, w.b_fmt, qb, sb)
+        check_gemm(d, dr, sr, w.out, name)
+    else:
+        rng = np.random.default_rng(w.index)
+        ii, jj = _points(w.M, w.N, rng)
+        dr, sr = oracle.gemm_points(w.a_fmt, qa, sa, w.b_fmt, qb, sb, ii, jj)
+        check_gemm(d[ii, jj], dr, sr, w.out, name)
+
+
+@pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
+def test_workload_end_to_end(name):
+    """HIP quantiser + HIP GEMM on the workload's FP32 operands against the
+    oracle's quantiser + product (sampled outputs)."""
+    import torch
+    w = workloads.by_name(name)
+    a, b = workloads.operands(w)
+    bs = bsfp8()
+    say(f"{name}: end to end on the GPU")
+    ad, bd = to_dev(a), to_dev(b)
+    if w.a_fmt == "mxfp4":
+        ga, gsa = bs.mxfp4_quantize(ad)
+        gb, gsb = bs.mxfp4_quantize(bd)
+    else:
+        ga, gsa = bs.fp8_quantize(ad, w.a_fmt)
+        gb, gsb = bs.fp8_quantize(bd, w.b_fmt)
+    d = bs.scaled_gemm(ga, gsa, gb, gsb, w.a_fmt, w.b_fmt, w.out, K=w.K)
+    torch.cuda.synchronize()
+    d = from_dev(d)
+    del ad, bd, ga, gb
+    qa, sa = oracle_quant(a, w.a_fmt)
+    qb, sb = oracle_quant(b, w.b_fmt)
+    rng = np.random.default_rng(100 + w.index)
+    ii, jj = _points(w.M, w.N, rng, n=1000)
+    dr, sr = oracle.gemm_points(w.a_fmt, qa, sa, w.b_fmt, qb, sb, ii, jj)
+    check_gemm(d[ii, jj], dr, sr, w.out, name + " end-to-end")

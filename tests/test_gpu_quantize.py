@@ -1,0 +1,172 @@
+"""Quantisation parity: the HIP kernels' codes and scales are byte-equal to the
+oracle's, on edge values, ragged shapes, degenerate inputs and every workload
+at full size.  Runs through the C ABI (the Python binding)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_common import from_dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def bsfp8():
+    import block_scaled_precision_fp8_amd as b
+    return b
+
+
+def gpu_fp8(x, fmt, ld=None):
+    import torch
+    b = bsfp8()
+    if ld is None:
+        xd = to_dev(x)
+    else:   # padded rows: leading dimension ld > k
+        buf = np.zeros((x.shape[0], ld), dtype=np.float32)
+        buf[:, : x.shape[1]] = x
+        xd = to_dev(buf)[:, : x.shape[1]]
+    codes, scales = b.fp8_quantize(xd, fmt)
+    torch.cuda.synchronize()
+    return from_dev(codes), from_dev(scales)
+
+
+def gpu_mx(x, ld=None):
+    import torch
+    b = bsfp8()
+    if ld is None:
+        xd = to_dev(x)
+    else:
+        buf = np.zeros((x.shape[0], ld), dtype=np.float32)
+        buf[:, : x.shape[1]] = x
+        xd = to_dev(buf)[:, : x.shape[1]]
+    packed, scales = b.mxfp4_quantize(xd)
+    torch.cuda.synchronize()
+    return from_dev(packed), from_dev(scales)
+
+
+def assert_fp8_equal(x, fmt, ld=None, label=""):
+    say(f"fp8_quantize {fmt} {x.shape} ld={ld} {label}")
+    c, s = gpu_fp8(x, fmt, ld)
+    rc, rs = oracle.fp8_quantize(x, fmt)
+    assert s.view(np.uint32).tobytes() == rs.view(np.uint32).tobytes(), f"{label}: scales differ"
+    bad = np.nonzero(c != rc)
+    assert bad[0].size == 0, (f"{label}: {bad[0].size} codes differ, first at {bad[0][0]},{bad[1][0]}:"
+                              f" x={x[bad[0][0], bad[1][0]]!r} gpu={c[bad][0]:#x} oracle={rc[bad][0]:#x}")
+
+
+def assert_mx_equal(x, ld=None, label=""):
+    say(f"mxfp4_quantize {x.shape} ld={ld} {label}")
+    p, s = gpu_mx(x, ld)
+    rp, rs = oracle.mxfp4_quantize(x)
+    assert np.array_equal(s, rs), f"{label}: scales differ"
+    bad = np.nonzero(p != rp)
+    assert bad[0].size == 0, f"{label}: {bad[0].size} packed bytes differ"
+
+
+def fp8_edge_tile(fmt):
+    """A 128 x 128 block where each 128 x 32 tile has amax == F (scale 1), so the
+    quantiser sees the probe values themselves: every code value, every midpoint,
+    their FP32 neighbours, both signs, zeros."""
+    t = oracle.decode_table(fmt)
+    top = 0x7E if fmt == "e4m3" else 0x7B
+    pos = t[: top + 1]
+    F = pos[-1]
+    vals = np.concatenate([pos, (pos[:-1] + pos[1:]) / 2]).astype(np.float32)
+    vals = np.concatenate([vals, np.nextafter(vals, np.float32(np.inf)),
+                           np.nextafter(vals, np.float32(-np.inf))])
+    vals = vals[np.abs(vals) <= F]
+    vals = np.concatenate([vals, -vals, np.array([0.0, -0.0], dtype=np.float32)])
+    n = 128 * 128
+    reps = np.resize(vals, n).reshape(128, 128)
+    reps[0, 0::32] = F          # each tile's maximum is exactly F -> scale 1
+    return reps.astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_edge_values(fmt):
+    x = fp8_edge_tile(fmt)
+    assert_fp8_equal(x, fmt, label="edge values, unit scale")
+    # the same values under non-trivial scales (tile maxima 3x and 1e-3x F)
+    y = x.copy()
+    y[:, 0:32] *= np.float32(3.0)
+    y[:, 32:64] *= np.float32(1e-3)
+    y[:, 64:96] *= np.float32(1.0 / 3.0)
+    assert_fp8_equal(y, fmt, label="edge values, scaled")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("rows,k,ld", [(300, 96, None), (1, 32, None), (129, 160, 164),
+                                       (127, 64, 68), (513, 256, None)])
+def test_fp8_ragged(fmt, rows, k, ld):
+    x = workloads.normal(100 + rows, rows, k) * np.float32(5.0)
+    x[rows // 2, :] *= np.float32(1e4)
+    assert_fp8_equal(x, fmt, ld, label="ragged")
+
+
+def test_fp8_degenerate():
+    assert_fp8_equal(np.zeros((130, 64), dtype=np.float32), "e4m3", label="all zero")
+    z = np.full((128, 32), -0.0, dtype=np.float32)
+    assert_fp8_equal(z, "e4m3", label="all negative zero")
+    tiny = (workloads.normal(5, 128, 64) * np.float32(1e-38)).astype(np.float32)   # subnormal scale
+    assert_fp8_equal(tiny, "e4m3", label="subnormal-scale tiles")
+    big = (workloads.normal(6, 128, 64) * np.float32(1e37)).astype(np.float32)
+    assert_fp8_equal(big, "e5m2", label="huge tiles")
+    b = bsfp8()
+    import torch
+    e = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    c, s = b.fp8_quantize(e)
+    assert c.shape == (0, 64) and s.shape == (0, 2)
+
+
+def test_fp8_deterministic():
+    x = workloads.normal(77, 512, 512)
+    c1, s1 = gpu_fp8(x, "e4m3")
+    c2, s2 = gpu_fp8(x, "e4m3")
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_mxfp4_edge_values():
+    # blocks whose maximum is 6 (e = 0) holding every E2M1 midpoint and neighbours
+    mids = np.array([0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6],
+                    dtype=np.float32)
+    vals = np.concatenate([mids, np.nextafter(mids, np.float32(10)), np.nextafter(mids, np.float32(-10))])
+    vals = np.concatenate([vals, -vals])
+    x = np.resize(vals, 64 * 256).reshape(64, 256).astype(np.float32)
+    x[:, 0::32] = 6.0
+    assert_mx_equal(x, label="E2M1 midpoints, e = 0")
+    # exponent boundaries: block maxima at 6 * 2^e and just above / below
+    rng = np.random.default_rng(1)
+    y = np.empty((64, 256), dtype=np.float32)
+    for r in range(64):
+        for b in range(8):
+            e = int(rng.integers(-125, 126))
+            base = np.float32(6.0 * 2.0 ** e)
+            m = [base, np.nextafter(base, np.float32(np.inf)), np.nextafter(base, np.float32(0))][(r + b) % 3]
+            blk = (rng.uniform(-0.9, 0.9, 32) * float(m)).astype(np.float32)
+            blk[(r + 3 * b) % 32] = -m if b % 2 else m
+            y[r, b * 32:(b + 1) * 32] = blk
+    assert_mx_equal(y, label="exponent boundaries")
+
+
+@pytest.mark.parametrize("rows,k,ld", [(300, 96, None), (1, 32, None), (129, 160, 164), (33, 64, 72)])
+def test_mxfp4_ragged(rows, k, ld):
+    x = workloads.normal(200 + rows, rows, k) * np.float32(7.0)
+    assert_mx_equal(x, ld, label="ragged")
+
+
+def test_mxfp4_degenerate():
+    assert_mx_equal(np.zeros((40, 64), dtype=np.float32), label="all zero")
+    assert_mx_equal((workloads.normal(8, 40, 64) * np.float32(1e-40)).astype(np.float32),
+                    label="subnormal blocks")
+
+
+@pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
+def test_workload_operands_full_size(name):
+    w = workloads.by_name(name)
+    a, b = workloads.operands(w)
+    if w.a_fmt == "mxfp4":
+        assert_mx_equal(a, label=f"{name} A")
+        assert_mx_equal(b, label=f"{name} B")
+    else:
+        assert_fp8_equal(a, w.a_fmt, label=f"{name} A")
+        assert_fp8_equal(b, w.b_fmt, label=f"{name} B")
