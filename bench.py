@@ -1,0 +1,278 @@
+"""Benchmark of the block-scaled FP8 / MXFP4 hot path on one MI355X.
+
+One step = one pass of the whole hot path over the workload's operands, which
+are resident in HBM before the timed region starts:
+    FP8 workloads:   fp8_quantize(A), fp8_quantize(B), scaled_gemm
+    MXFP4 workload:  mxfp4_quantize(A), mxfp4_quantize(B), scaled_gemm
+value = 2 M N K / (step time), in TFLOP/s, for the whole job.
+
+Also reported, on the same JSON line:
+  roofline      the GEMM kernel: algorithmic FLOPs per launch / its average
+                launch time (HIP events on the launch stream, over the timed
+                steps), against the dense MFMA peak of the input type;
+                traffic = HBM bytes per launch from the committed rocprofv3
+                counter summary when it was taken on the current kernel source,
+                else null;
+  cpu_baseline  the CPU oracle (plain C, fp64) on a bounded sample of the same
+                step, extrapolated to the whole job;
+  kernels       per-kernel times, GEMM TFLOP/s, quantiser GB/s against 8 TB/s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--copy-calibration]
+Only one GPU is supported; --gpus N with N > 1 exits with a message.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scaled-GEMM TFLOP/s and % of MI355X FP8/MXFP4 MFMA peak at 1 GPU"
+PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "bf16": 2500.0}
+HBM_GBPS = 8000.0
+DEFAULT_WORKLOAD = "square_e4m3_4096"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(workload, source_file):
+    """HBM bytes per GEMM launch from profiles/<kernel>_<workload>_traffic.txt,
+    only if it was measured on the current kernel source (digest line)."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None, None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    digest = kernel_source_digest(source_file)
+    if fields.get("kernel_source_sha256_16") != digest:
+        return None, "stale (kernel changed since the counters were taken)"
+    try:
+        return float(fields["hbm_bytes_per_launch"]), path
+    except (KeyError, ValueError):
+        return None, None
+
+
+def cpu_baseline(w, a, b, d_gpu, sample_rows):
+    """Time the oracle on a bounded sample: quantise all of B, `sample_rows`
+    rows of A, and the product rows for that sample; extrapolate the time to
+    the whole step (quantising all of A, all M rows of D)."""
+    import numpy as np
+    import oracle
+
+    cores = oracle.threads()
+    rows = min(sample_rows, w.M)
+    t0 = time.perf_counter()
+    if w.a_fmt == "mxfp4":
+        qb, sb = oracle.mxfp4_quantize(b)
+    else:
+        qb, sb = oracle.fp8_quantize(b, w.b_fmt)
+    t1 = time.perf_counter()
+    if w.a_fmt == "mxfp4":
+        qa, sa = oracle.mxfp4_quantize(a[:rows])
+    else:
+        qa, sa = oracle.fp8_quantize(a[:rows], w.a_fmt)
+    t2 = time.perf_counter()
+    d_ref, s_ref = oracle.gemm_rows(w.a_fmt, qa, sa, w.b_fmt, qb, sb)
+    t3 = time.perf_counter()
+    scale = w.M / rows
+    t_full = (t1 - t0) + (t2 - t1) * scale + (t3 - t2) * scale
+    value = w.flops / t_full / 1e12
+    # the GPU's rows of D for the same sample, normalised error against the oracle
+    err = np.abs(d_gpu[:rows].astype(np.float64) - d_ref)
+    nz = s_ref > 0
+    worst = float((err[nz] / s_ref[nz]).max()) if nz.any() else 0.0
+    return {
+        "value": value,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"oracle quantise of all of B ({w.N}x{w.K}) and of A rows 0..{rows - 1}, "
+                   f"oracle fp64 product of those {rows} rows x {w.N} columns; "
+                   f"measured {t3 - t0:.1f} s, extrapolated x{scale:g} on the A/product parts "
+                   f"to the full {w.M}x{w.N}x{w.K} step"),
+        "seconds_measured": round(t3 - t0, 3),
+        "gpu_vs_oracle_max_err_over_S_on_sample": worst,
+    }
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling rocprofv3's HBM byte counters."""
+    import torch
+    n = 64 * 1024 * 1024           # 256 MiB of float32
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 5 copies of {n * 4} bytes (read {n * 4}, write {n * 4} per copy)")
+
+
+def main():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-gflop", type=float, default=150.0,
+                   help="oracle product work to time (rows are chosen to match, whole 128-row tiles)")
+    p.add_argument("--copy-calibration", action="store_true")
+    args = p.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus must be 1 "
+              "(multi-GPU sharding is described in the design notes, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_fp8_amd as bs
+    import workloads
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    w = workloads.by_name(args.workload)
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} {w.a_fmt}x{w.b_fmt} -> {w.out}")
+    a_host, b_host = workloads.operands(w)
+    a = torch.from_numpy(a_host).to(dev)
+    b = torch.from_numpy(b_host).to(dev)
+    mx = w.a_fmt == "mxfp4"
+    # outputs allocated once, reused every step
+    if mx:
+        qa = torch.empty((w.M, w.K // 2), dtype=torch.uint8, device=dev)
+        qb = torch.empty((w.N, w.K // 2), dtype=torch.uint8, device=dev)
+        sa = torch.empty((w.M, w.K // 32), dtype=torch.uint8, device=dev)
+        sb = torch.empty((w.N, w.K // 32), dtype=torch.uint8, device=dev)
+    else:
+        qa = torch.empty((w.M, w.K), dtype=torch.uint8, device=dev)
+        qb = torch.empty((w.N, w.K), dtype=torch.uint8, device=dev)
+        sa = torch.empty(((w.M + 127) // 128, w.K // 32), dtype=torch.float32, device=dev)
+        sb = torch.empty(((w.N + 127) // 128, w.K // 32), dtype=torch.float32, device=dev)
+    d = torch.empty((w.M, w.N), dtype=torch.float32 if w.out == "f32" else torch.bfloat16,
+                    device=dev)
+
+    stream = torch.cuda.current_stream(dev)   # the library launches on this stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(marks=None):
+        if marks:
+            marks[0].record(stream)
+        if mx:
+            bs.mxfp4_quantize(a, qa, sa)
+            bs.mxfp4_quantize(b, qb, sb)
+        else:
+            bs.fp8_quantize(a, w.a_fmt, codes=qa, scales=sa)
+            if marks:
+                marks[1].record(stream)
+            bs.fp8_quantize(b, w.b_fmt, codes=qb, scales=sb)
+        if marks:
+            marks[2].record(stream)
+        bs.scaled_gemm(qa, sa, qb, sb, w.a_fmt, w.b_fmt, w.out, d=d, K=w.K)
+        if marks:
+            marks[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gemm_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    quant_ms = sum(e[0].elapsed_time(e[2]) for e in ev) / args.steps
+    if not mx:
+        qa_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+        qb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+
+    in_type = "fp4" if mx else "fp8"
+    gemm_tflops = w.flops / (gemm_ms * 1e-3) / 1e12
+    src = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc",
+                       "gemm_mxfp4.hip" if mx else "gemm_fp8.hip")
+    traffic, traffic_src = committed_traffic(w.name, src)
+
+    # quantiser bytes: read 4 B, write 1 B (FP8) or 0.5 B (MXFP4) per element, plus scales
+    def qbytes(rows):
+        if mx:
+            return rows * w.K * 4 + rows * w.K // 2 + rows * (w.K // 32)
+        return rows * w.K * 4 + rows * w.K + ((rows + 127) // 128) * (w.K // 32) * 4
+
+    kernels = {
+        "scaled_gemm_ms": round(gemm_ms, 4),
+        "scaled_gemm_tflops": round(gemm_tflops, 1),
+        "scaled_gemm_frac_of_peak": round(gemm_tflops / PEAK_TFLOPS[in_type], 4),
+        "quantize_AB_ms": round(quant_ms, 4),
+        "quantize_AB_gbps": round((qbytes(w.M) + qbytes(w.N)) / (quant_ms * 1e-3) / 1e9, 1),
+    }
+    if not mx:
+        kernels["quantize_A_ms"] = round(qa_ms, 4)
+        kernels["quantize_B_ms"] = round(qb_ms, 4)
+    kernels["quantize_AB_frac_of_hbm"] = round(kernels["quantize_AB_gbps"] / HBM_GBPS, 4)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4e2m1" if mx else ("fp8e4m3" if w.a_fmt == w.b_fmt == "e4m3" else "fp8e5m2xe4m3"),
+        "data": "synthetic (seeded numpy, distributions of the workload table)",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "a_fmt": w.a_fmt,
+                   "b_fmt": w.b_fmt, "out": w.out,
+                   "step": ("mxfp4_quantize(A)+mxfp4_quantize(B)+scaled_gemm" if mx else
+                            "fp8_quantize(A)+fp8_quantize(B)+scaled_gemm")},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_mxfp4_kernel" if mx else "gemm_fp8_kernel",
+            "achieved": round(gemm_tflops, 1),
+            "peak": PEAK_TFLOPS[in_type],
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_TFLOPS[in_type], 4),
+            "traffic": traffic,
+            "traffic_unit": "bytes per launch",
+            "traffic_source": traffic_src,
+        },
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        d_host = d.float().cpu().numpy()
+        log("cpu baseline: timing the oracle on a bounded sample ...")
+        rows = int(args.cpu_sample_gflop * 1e9 / (2.0 * w.N * w.K)) // 128 * 128
+        rows = max(128, min(w.M, rows))
+        result["cpu_baseline"] = cpu_baseline(w, a_host, b_host, d_host, rows)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
