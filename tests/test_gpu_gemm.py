@@ -169,3 +169,16 @@ def test_workload_end_to_end(name):
     ii, jj = _points(w.M, w.N, rng, n=1000)
     dr, sr = oracle.gemm_points(w.a_fmt, qa, sa, w.b_fmt, qb, sb, ii, jj)
     check_gemm(d[ii, jj], dr, sr, w.out, name + " end-to-end")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("fmts,M,N,K", [
+    (("mxfp4", "mxfp4"), 2088, 2072, 512),     # 256 x 256 MXFP4 kernel, ragged edges
+    (("mxfp4", "mxfp4"), 2048, 2048, 768),
+    (("e4m3", "e4m3"), 2088, 2072, 512),       # large-tile FP8 path, ragged edges
+    (("e5m2", "e4m3"), 2048, 2080, 384),
+])
+def test_medium_ragged_large_tile_kernels(fmts, M, N, K, out):
+    """Shapes big enough for the large-tile kernels, with partial edge tiles,
+    compared in full against the oracle."""
+    full_check(M, N, K, fmts[0], fmts[1], out, seed=M + N + K, label="medium")
