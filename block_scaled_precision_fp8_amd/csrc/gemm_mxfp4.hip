@@ -16,6 +16,8 @@
 // holds 4 consecutive output columns for vector stores.
 #include "internal.h"
 
+#include <utility>
+
 namespace bsfp8 {
 
 namespace {
@@ -238,12 +240,110 @@ constexpr int kBigOperandBytes = 256 * kStride;
 constexpr int kBigStageBytes = 2 * kBigOperandBytes;
 constexpr int kBigLdsBytes = 2 * kBigStageBytes;     // 147456 bytes
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
+
+// The main loop of the large-tile kernel issues its LDS traffic and MFMAs as
+// volatile inline assembly: volatile statements keep their program order, so
+// the fragment reads for the next K step, the staging writes and the MFMAs of
+// the current step interleave exactly as written (the compiler would otherwise
+// sink every read next to its first use and stall each MFMA on LDS latency).
+// The compiler does not track LDS completions of these statements, so each
+// consumer is preceded by an explicit lgkmcnt wait.
+template <int OFF>
+__device__ __forceinline__ void lds_read16(u32x4& v, uint32_t addr) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_write16(uint32_t addr, const u32x4& v) {
+    asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_wait_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// E2M1 x E2M1 MFMA with E8M0 block scales; byte SEL of each scale register is used.
+template <int SEL>
+__device__ __forceinline__ void mfma_fp4_sel(v16f& acc, const u32x4& x, const u32x4& y, uint32_t sx,
+                                             uint32_t sy) {
+    asm volatile(
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%5,0] "
+        "op_sel_hi:[%6,%6,0] cbsz:4 blgp:4"
+        : "+a"(acc)
+        : "v"(x), "v"(y), "v"(sx), "v"(sy), "i"(SEL & 1), "i"(SEL >> 1));
+}
+// Gather, for each of the 4 K steps of a stage, this lane's scale byte (block
+// 2 ks + half of the stage's 8 blocks) into byte ks of one register.  The
+// trailing wait states cover the VALU-write to MFMA-read dependency.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void gather_scales(uint32_t& w0, uint32_t& w1, uint32_t& w2, uint32_t& w3,
+                                              const u32x2& s0, const u32x2& s1, const u32x2& s2,
+                                              const u32x2& s3, uint32_t sel) {
+    asm volatile(
+        "v_perm_b32 %0, %5, %4, %12\n\t"
+        "v_perm_b32 %1, %7, %6, %12\n\t"
+        "v_perm_b32 %2, %9, %8, %12\n\t"
+        "v_perm_b32 %3, %11, %10, %12\n\t"
+        "s_nop 4"
+        : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
+        : "v"(s0.x), "v"(s0.y), "v"(s1.x), "v"(s1.y), "v"(s2.x), "v"(s2.y), "v"(s3.x),
+          "v"(s3.y), "v"(sel));
+}
+
+template <int... I, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Store 16 bytes of one output row: 8 bf16 or 4 FP32 values starting at column
+// n (masked at the bottom and right edges; vector store when vec16 says the
+// row stride and base allow 16-byte alignment).
+template <int OUT>
+__device__ __forceinline__ void store_chunk16(void* D, int64_t ldd, int m, int n, int M, int N,
+                                              int vec16, uint4 v) {
+    if (m >= M) return;
+    constexpr int per = OUT == BSFP8_OUT_F32 ? 4 : 8;
+    if (vec16 && n + per <= N) {
+        uint8_t* p = static_cast<uint8_t*>(D) +
+                     (static_cast<int64_t>(m) * ldd + n) * (OUT == BSFP8_OUT_F32 ? 4 : 2);
+        *reinterpret_cast<uint4*>(p) = v;
+        return;
+    }
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (OUT == BSFP8_OUT_F32) {
+        float* dp = static_cast<float*>(D) + static_cast<int64_t>(m) * ldd + n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (n + j < N) dp[j] = __uint_as_float(w[j]);
+    } else {
+        uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (n + j < N) dp[j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
+    }
+}
+
+// Large-tile LDS layout: per buffer, A then B, each 256 rows of 128 bytes
+// (unpadded, so that direct global-to-LDS loads can fill them).  Row R keeps
+// its 16-byte chunk g at position g ^ ((R >> 1) & 7): the 16 lanes of a
+// fragment-read phase (16 consecutive rows, one chunk) then hit 16 distinct
+// 4-bank groups.
+constexpr int kDmaRowBytes = 128;
+constexpr int kDmaOperandBytes = 256 * kDmaRowBytes;     // 32 KB
+constexpr int kDmaStageBytes = 2 * kDmaOperandBytes;     // 64 KB
+constexpr int kDmaLdsBytes = 2 * kDmaStageBytes;         // 128 KB
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int OUT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
     int64_t ldd, int tiles_m, int tiles_n, int vec_ok) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kBigLdsBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kDmaLdsBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -258,56 +358,80 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     const int kbytes = K >> 1;
     const int nkb = K >> 5;
     const int nst = K >> 8;          // K is a multiple of 256
+    const int last = nst - 1;
 
-    // staging: 256 rows x 128 bytes per operand per stage, 8 chunks per thread
-    const int crow = tid >> 3;
-    const int cch = tid & 7;
+    // Direct loads: instruction i of wave w fills LDS rows 32 i + 8 w .. + 7 of
+    // one operand (1 KB, 16 bytes per lane in lane order); lane l takes row
+    // 8 w + l / 8 (+ 32 i) and the global chunk that belongs at position l % 8.
+    // The row is part of the range-checked VGPR offset (rows past the matrix
+    // edge load zeros); the scalar offset carries only the stage's K offset.
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(A), 0, M * kbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(B), 0, N * kbytes, 0x00020000);
-    const int voff_a = (m0 + crow) * kbytes + cch * 16;
-    const int voff_b = (n0 + crow) * kbytes + cch * 16;
-    const int row_step = 32 * kbytes;
-    uint4 ra[8], rb[8];
+    const int drow = 8 * wave + (lane >> 3);
+    const int dchunk = (lane & 7) ^ ((drow >> 1) & 7);
+    const uint32_t dma_a = static_cast<uint32_t>(m0 + drow) * kbytes + dchunk * 16;
+    const uint32_t dma_b = static_cast<uint32_t>(n0 + drow) * kbytes + dchunk * 16;
+    const uint32_t row_step = 32u * static_cast<uint32_t>(kbytes);
+    // direct load j (0..15) of a stage: A for even j, B for odd j, rows 32 (j / 2) + ...
+    auto dma_one = [&](auto J, int stage, int buf) {
+        constexpr int j = J;
+        constexpr int i = j >> 1;
+        const int so = min(stage, last) * 128;
+        if constexpr ((j & 1) == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs_a, (lds_void*)(lds + buf * kDmaStageBytes + (32 * i + 8 * wave) * kDmaRowBytes), 16,
+                dma_a + i * row_step, so, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs_b, (lds_void*)(lds + buf * kDmaStageBytes + kDmaOperandBytes +
+                                  (32 * i + 8 * wave) * kDmaRowBytes), 16,
+                dma_b + i * row_step, so, 0, 0);
+    };
+    auto dma_stage = [&](int stage, int buf) {
+        static_for<16>([&](auto J) { dma_one(J, stage, buf); });
+    };
 
-    // scales: the 4 A rows and 4 B rows this lane feeds to the MFMAs, 8 blocks per stage
+    // Fragment reads: lane (frag_row r, half h) reads chunk 2 ks + h of rows
+    // wm*128 + 32 t + r (A) and wn*128 + 32 t + r (B); t is an immediate offset.
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
     const int frag_row = lane & 31;
     const int half = lane >> 5;
+    const int sw = (frag_row >> 1) & 7;
+    uint32_t rd_a[2][4], rd_b[2][4];
+#pragma unroll
+    for (int bf = 0; bf < 2; ++bf)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint32_t pos = static_cast<uint32_t>(((2 * ks + half) ^ sw) * 16);
+            rd_a[bf][ks] = lds0 + bf * kDmaStageBytes + (wm * 128 + frag_row) * kDmaRowBytes + pos;
+            rd_b[bf][ks] = lds0 + bf * kDmaStageBytes + kDmaOperandBytes +
+                           (wn * 128 + frag_row) * kDmaRowBytes + pos;
+        }
+
+    // Scales: this lane feeds rows wm*128 + 32 t + frag_row of A and
+    // wn*128 + 32 t + frag_row of B; a stage covers 8 scale blocks per row.
     const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(sA), 0, M * nkb, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(sB), 0, N * nkb, 0x00020000);
-    // one lane offset per operand; the row step (32 rows) and stage step go in SGPRs
-    const int soff_a = (m0 + wm * 128 + frag_row) * nkb;
-    const int soff_b = (n0 + wn * 128 + frag_row) * nkb;
-    const int srow_step = 32 * nkb;
-    uint2 sca[4], scb[4], nsca[4], nscb[4];
-
-    auto gload = [&](int s) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            auto va = __builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a, s * 128 + i * row_step, 0);
-            auto vb = __builtin_amdgcn_raw_buffer_load_b128(rs_b, voff_b, s * 128 + i * row_step, 0);
-            __builtin_memcpy(&ra[i], &va, 16);
-            __builtin_memcpy(&rb[i], &vb, 16);
-        }
+    const uint32_t soff_a = static_cast<uint32_t>(m0 + wm * 128 + frag_row) * nkb;
+    const uint32_t soff_b = static_cast<uint32_t>(n0 + wn * 128 + frag_row) * nkb;
+    const uint32_t srow_step = 32u * static_cast<uint32_t>(nkb);
+    const uint32_t perm_sel = 0x06040200u + 0x01010101u * static_cast<uint32_t>(half);
+    // Scale loads are issued as assembly as well, so that the compiler tracks
+    // no register-writing loads in the main loop: the waits for them (and for
+    // the direct loads) are the explicit vmcnt waits below.
+    u32x2 nsa[4], nsb[4];
+    auto load_scales = [&](int stage) {
+        const int so = min(stage, last) * 8;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            auto xa = __builtin_amdgcn_raw_buffer_load_b64(rs_sa, soff_a, s * 8 + t * srow_step, 0);
-            auto xb = __builtin_amdgcn_raw_buffer_load_b64(rs_sb, soff_b, s * 8 + t * srow_step, 0);
-            __builtin_memcpy(&nsca[t], &xa, 8);
-            __builtin_memcpy(&nscb[t], &xb, 8);
-        }
-    };
-    auto lstore = [&](int buf) {
-        uint8_t* la = lds + buf * kBigStageBytes;
-        uint8_t* lb = la + kBigOperandBytes;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = crow + 32 * i;
-            *reinterpret_cast<uint4*>(la + row * kStride + cch * 16) = ra[i];
-            *reinterpret_cast<uint4*>(lb + row * kStride + cch * 16) = rb[i];
+            asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
+                         : "=v"(nsa[t]) : "v"(soff_a + t * srow_step), "s"(rs_sa), "s"(so) : "memory");
+            asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
+                         : "=v"(nsb[t]) : "v"(soff_b + t * srow_step), "s"(rs_sb), "s"(so) : "memory");
         }
     };
 
@@ -317,97 +441,137 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-    // byte (2 ks + half) of a stage's 8 scale bytes
-    auto pick = [&](uint2 v, int ks) -> uint32_t {
-        const uint32_t w = ks < 2 ? v.x : v.y;
-        return (w >> (8 * (2 * (ks & 1) + half))) & 0xFFu;
-    };
+    struct Frag { u32x4 x[4], y[4]; };
+    Frag fr[2];
 
-    gload(0);
-    lstore(0);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) { sca[t] = nsca[t]; scb[t] = nscb[t]; }
-    __syncthreads();
+    // Prologue: stage 0 into buffer 0, its first fragments into registers, and
+    // stage 1 on its way into buffer 1.
+    dma_stage(0, 0);
+    load_scales(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_wait_barrier();
+    static_for<4>([&](auto t) {
+        lds_read16<t * 32 * kDmaRowBytes>(fr[0].x[t], rd_b[0][0]);
+        lds_read16<t * 32 * kDmaRowBytes>(fr[0].y[t], rd_a[0][0]);
+    });
+    dma_stage(1, 1);
+
     for (int s = 0; s < nst; ++s) {
-        if (s + 1 < nst) gload(s + 1);
-        const uint8_t* la = lds + (s & 1) * kBigStageBytes;
-        const uint8_t* lb = la + kBigOperandBytes;
-        // fragments of K step ks + 1 are read while the MFMAs of step ks run
-        struct Frag { uint4 x[4], y[4]; uint32_t sx[4], sy[4]; };
-        auto load_frag = [&](Frag& f, int ks) {
-            const int off = ks * 32 + 16 * half;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                f.x[t] = *reinterpret_cast<const uint4*>(lb + (wn * 128 + 32 * t + frag_row) * kStride + off);
-                f.y[t] = *reinterpret_cast<const uint4*>(la + (wm * 128 + 32 * t + frag_row) * kStride + off);
-                f.sx[t] = pick(scb[t], ks);
-                f.sy[t] = pick(sca[t], ks);
-            }
-        };
-        Frag fr[2];
-        load_frag(fr[0], 0);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (ks + 1 < 4) load_frag(fr[(ks + 1) & 1], ks + 1);
-            if (ks == 3 && s + 1 < nst) {
-                // The next stage's staged data goes to the other LDS buffer here:
-                // after three K steps of MFMAs have covered the global-load latency
-                // and before the last step's MFMAs.  MFMA builtins carry no memory
-                // dependence, so the compiler would move these writes (and their
-                // wait for the loads) above the MFMAs; the empty asm statements tie
-                // the staged registers to every accumulator as left by the previous
-                // steps, which pins the order.
-                uint32_t key = 0;
-                asm volatile(""
-                             : "+v"(key)
-                             : "a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[0][2]), "a"(acc[0][3]),
-                               "a"(acc[1][0]), "a"(acc[1][1]), "a"(acc[1][2]), "a"(acc[1][3]),
-                               "a"(acc[2][0]), "a"(acc[2][1]), "a"(acc[2][2]), "a"(acc[2][3]),
-                               "a"(acc[3][0]), "a"(acc[3][1]), "a"(acc[3][2]), "a"(acc[3][3]));
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    uint32_t ta = ra[i].x, tb = rb[i].x;
-                    asm volatile("" : "+v"(ta), "+v"(tb) : "v"(key));
-                    ra[i].x = ta;
-                    rb[i].x = tb;
-                }
-                lstore((s + 1) & 1);
-            }
-            const Frag& f = fr[ks & 1];
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                for (int tj = 0; tj < 4; ++tj)
-                    acc[ti][tj] = mfma_fp4(f.x[ti], f.y[tj], f.sx[ti], f.sy[tj], acc[ti][tj]);
-            if (ks + 1 < 4) {
-                // interleave the next step's 8 fragment reads with this step's 16 MFMAs
-#pragma unroll
-                for (int g = 0; g < 8; ++g) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-                }
-            }
-        }
-        if (s + 1 < nst) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) { sca[t] = nsca[t]; scb[t] = nscb[t]; }
-        }
-        __syncthreads();
-    }
+        const int cb = s & 1;
+        // this stage's scales were loaded one stage ago; only the 16 direct
+        // loads issued since may still be in flight
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        uint32_t wa[4], wb[4];
+        gather_scales(wa[0], wa[1], wa[2], wa[3], nsa[0], nsa[1], nsa[2], nsa[3], perm_sel);
+        gather_scales(wb[0], wb[1], wb[2], wb[3], nsb[0], nsb[1], nsb[2], nsb[3], perm_sel);
+        load_scales(s + 1);
 
+        // One K step (64 K values): 16 MFMAs on fragment set KS & 1 with the 8
+        // fragment reads of the next step in their shadows.  Step 3 follows the
+        // barrier that publishes stage s + 1: it reads that stage's first
+        // fragments and starts the direct loads of stage s + 2 into this
+        // stage's buffer, which no wave reads any more.
+        auto kstep = [&](auto KS) {
+            constexpr int ks = KS;
+            constexpr int nks = (ks + 1) & 3;
+            const Frag& f = fr[ks & 1];
+            Frag& g = fr[(ks + 1) & 1];
+            const int rb = ks == 3 ? cb ^ 1 : cb;
+            const uint32_t ra_addr = rb ? rd_a[1][nks] : rd_a[0][nks];
+            const uint32_t rb_addr = rb ? rd_b[1][nks] : rd_b[0][nks];
+            static_for<16>([&](auto J) {
+                constexpr int j = J;
+                constexpr int ti = j >> 2, tj = j & 3;
+                mfma_fp4_sel<ks>(acc[ti][tj], f.x[ti], f.y[tj], wb[ti], wa[tj]);
+                if constexpr (j < 8) {
+                    constexpr int t = j >> 1;
+                    if constexpr (j & 1)
+                        lds_read16<t * 32 * kDmaRowBytes>(g.y[t], ra_addr);
+                    else
+                        lds_read16<t * 32 * kDmaRowBytes>(g.x[t], rb_addr);
+                }
+                if constexpr (ks == 3) dma_one(J, s + 2, cb);
+            });
+        };
+        lds_wait();
+        kstep(std::integral_constant<int, 0>{});
+        lds_wait();
+        kstep(std::integral_constant<int, 1>{});
+        lds_wait();
+        kstep(std::integral_constant<int, 2>{});
+        // stage s + 1 has landed (only the 8 scale loads issued since may be
+        // outstanding); publish it
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        lds_wait_barrier();
+        kstep(std::integral_constant<int, 3>{});
+    }
+    // no direct load may still be writing LDS when the workgroup ends
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // MFMA results must settle before the accumulation registers are read.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                   "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]),
+                   "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
+                   "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
+
+    // Epilogue: the tile goes out through LDS (free now) so that every store
+    // instruction writes whole rows: a 64-lane store of 16 bytes per lane covers
+    // 1 KB of consecutive output, where the MFMA layout gives 32 rows of 16
+    // bytes.  16-byte chunk c of LDS row R sits at position c ^ (R & 15), which
+    // keeps both the scattered writes and the row reads free of bank conflicts.
+    __syncthreads();
+    if constexpr (OUT == BSFP8_OUT_BF16) {
+        // 256 rows x 512 bytes = the whole 128 KB
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
+        for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
-            const int m = m0 + wm * 128 + tj * 32 + frag_row;
-            if (m >= M) continue;
+            for (int tj = 0; tj < 4; ++tj)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * 128 + ti * 32 + q * 8 + half * 4;
-                store4<OUT>(D, ldd, m, n, N, vec_ok, acc[ti][tj][4 * q + 0], acc[ti][tj][4 * q + 1],
-                            acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]);
-            }
+                for (int q = 0; q < 4; ++q) {
+                    const int R = wm * 128 + tj * 32 + frag_row;
+                    const int c = wn * 16 + ti * 4 + q;
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    const bf16x4 v = {(__bf16)acc[ti][tj][4 * q + 0], (__bf16)acc[ti][tj][4 * q + 1],
+                                      (__bf16)acc[ti][tj][4 * q + 2], (__bf16)acc[ti][tj][4 * q + 3]};
+                    *reinterpret_cast<bf16x4*>(lds + R * 512 + ((c ^ (R & 15)) << 4) + 8 * half) = v;
+                }
+        __syncthreads();
+#pragma unroll 4
+        for (int i = 0; i < 32; ++i) {
+            const int R = wave * 64 + 2 * i + half;
+            const int c = lane & 31;
+            const uint4 v = *reinterpret_cast<const uint4*>(lds + R * 512 + ((c ^ (R & 15)) << 4));
+            store_chunk16<OUT>(D, ldd, m0 + R, n0 + c * 8, M, N, vec_ok, v);
         }
+    } else {
+        // two passes of 128 rows x 1 KB
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            if (wm == p) {
+#pragma unroll
+                for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                    for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int R = tj * 32 + frag_row;
+                            const int c = wn * 32 + ti * 8 + q * 2 + half;
+                            *reinterpret_cast<float4*>(lds + R * 1024 + ((c ^ (R & 15)) << 4)) =
+                                make_float4(acc[ti][tj][4 * q + 0], acc[ti][tj][4 * q + 1],
+                                            acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]);
+                        }
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int i = 0; i < 32; ++i) {
+                const int R = wave * 32 + i;
+                const int c = lane;
+                const uint4 v = *reinterpret_cast<const uint4*>(lds + R * 1024 + ((c ^ (R & 15)) << 4));
+                store_chunk16<OUT>(D, ldd, m0 + p * 128 + R, n0 + c * 4, M, N, vec_ok, v);
+            }
+            __syncthreads();
+        }
+    }
 }
 
 }  // namespace
@@ -422,14 +586,17 @@ hipError_t launch_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* a,
     if (K % 256 == 0 && big_tiles >= kBigTileThreshold && fits32) {
         const int tm = static_cast<int>((M + 255) / 256), tn = static_cast<int>((N + 255) / 256);
         const dim3 g(static_cast<uint32_t>(tm) * static_cast<uint32_t>(tn));
+        // 16-byte row stores: row stride and base both 16-byte aligned
+        const int esize = out == BSFP8_OUT_F32 ? 4 : 2;
+        const int vec16 = ((ldd * esize) % 16 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0);
         if (out == BSFP8_OUT_F32)
             hipLaunchKernelGGL(gemm_mxfp4_big_kernel<BSFP8_OUT_F32>, g, dim3(kThreads), 0, stream,
                                static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
-                               a_scales, b, b_scales, d, ldd, tm, tn, vec_ok);
+                               a_scales, b, b_scales, d, ldd, tm, tn, vec16);
         else
             hipLaunchKernelGGL(gemm_mxfp4_big_kernel<BSFP8_OUT_BF16>, g, dim3(kThreads), 0, stream,
                                static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
-                               a_scales, b, b_scales, d, ldd, tm, tn, vec_ok);
+                               a_scales, b, b_scales, d, ldd, tm, tn, vec16);
         return hipGetLastError();
     }
     const int tiles_m = static_cast<int>((M + BM - 1) / BM);
