@@ -32,6 +32,8 @@
 // or 8-byte (bf16) vectors.
 #include "internal.h"
 
+#include <utility>
+
 namespace bsfp8 {
 
 namespace {
@@ -293,6 +295,244 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
         }
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int... I, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <int OFF>
+__device__ __forceinline__ void lds_read16(u32x4& v, uint32_t addr) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// LDS: per buffer, A then B, 128 rows x 128 bytes each, unpadded (filled by
+// direct global-to-LDS loads); row R keeps 16-byte chunk g at g ^ ((R >> 1) & 7).
+constexpr int kDRow = 128;
+constexpr int kDOperand = 128 * kDRow;      // 16 KB
+constexpr int kDStage = 2 * kDOperand;      // 32 KB
+constexpr int kDLds = 2 * kDStage;          // 64 KB: two workgroups per CU
+
+template <int AF, int BF>
+__global__ __launch_bounds__(kThreads, 2) void gemm_fp8_bf16_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
+    const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D,
+    int64_t ldd, int tiles_m, int tiles_n, int vec_ok) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kDLds];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+    int tm, tn;
+    map_tile(blockIdx.x, tiles_m, tiles_n, 8, &tm, &tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int nkb = K >> 5;
+    const int nst = (nkb + 3) >> 2;          // 128 K per stage
+    const int last = nst - 1;
+
+    // direct loads: instruction i (0..3) of wave w fills rows 32 i + 8 w .. + 7
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(A), 0, M * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(B), 0, N * K, 0x00020000);
+    const int drow = 8 * wave + (lane >> 3);
+    const int dchunk = (lane & 7) ^ ((drow >> 1) & 7);
+    const uint32_t dma_a = static_cast<uint32_t>(m0 + drow) * K + dchunk * 16;
+    const uint32_t dma_b = static_cast<uint32_t>(n0 + drow) * K + dchunk * 16;
+    const uint32_t row_step = 32u * static_cast<uint32_t>(K);
+    auto dma_one = [&](auto J, int stage, int buf) {
+        constexpr int j = J;
+        constexpr int i = j >> 1;
+        const int so = min(stage, last) * 128;
+        if constexpr ((j & 1) == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs_a, (lds_void*)(lds + buf * kDStage + (32 * i + 8 * wave) * kDRow), 16,
+                dma_a + i * row_step, so, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs_b, (lds_void*)(lds + buf * kDStage + kDOperand + (32 * i + 8 * wave) * kDRow), 16,
+                dma_b + i * row_step, so, 0, 0);
+    };
+
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
+    const int frag_row = lane & 31;
+    const int half = lane >> 5;
+    const int sw = (frag_row >> 1) & 7;
+    // read base per buffer and block: chunk 2 kb + half of rows wm*64 + 32 t + r
+    uint32_t rd_a[2][4], rd_b[2][4];
+#pragma unroll
+    for (int bf = 0; bf < 2; ++bf)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const uint32_t pos = static_cast<uint32_t>(((2 * kb + half) ^ sw) * 16);
+            rd_a[bf][kb] = lds0 + bf * kDStage + (wm * 64 + frag_row) * kDRow + pos;
+            rd_b[bf][kb] = lds0 + bf * kDStage + kDOperand + (wn * 64 + frag_row) * kDRow + pos;
+        }
+
+    // scales of a stage: 4 floats of A's tile row and 4 of B's, loaded one stage ahead
+    const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(sA), 0, static_cast<int>(tiles_m) * nkb * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(sB), 0, static_cast<int>(tiles_n) * nkb * 4, 0x00020000);
+    const uint32_t so_a = static_cast<uint32_t>(tm) * nkb * 4;
+    const uint32_t so_b = static_cast<uint32_t>(tn) * nkb * 4;
+    u32x4 nsa, nsb;
+    auto load_scales = [&](int stage) {
+        const int so = min(stage, last) * 16;
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsa) : "v"(so_a), "s"(rs_sa), "s"(so) : "memory");
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsb) : "v"(so_b), "s"(rs_sb), "s"(so) : "memory");
+    };
+
+    v16f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+    u32x4 fx[2][2], fy[2][2];    // [set][t]
+
+    static_for<8>([&](auto J) { dma_one(J, 0, 0); });
+    load_scales(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    static_for<2>([&](auto t) {
+        lds_read16<t * 32 * kDRow>(fx[0][t], rd_b[0][0]);
+        lds_read16<t * 32 * kDRow>(fy[0][t], rd_a[0][0]);
+    });
+    static_for<8>([&](auto J) { dma_one(J, 1, 1); });
+
+    // full stages run unconditionally; a partial last stage (K not a multiple
+    // of 128) is finished by the tail below
+    const int nfull = nkb >> 2;
+    for (int s = 0; s < nfull; ++s) {
+        const int cb = s & 1;
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // this stage's scales
+        u32x4 ca = nsa, cbv = nsb;
+        asm volatile("" : "+v"(ca), "+v"(cbv));
+        float sig[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sig[k] = __uint_as_float(ca[k]) * __uint_as_float(cbv[k]);
+        load_scales(s + 1);
+
+        auto block = [&](auto KB) {
+            constexpr int kb = KB;
+            constexpr int nkb_ = (kb + 1) & 3;
+            const int rb = kb == 3 ? cb ^ 1 : cb;
+            u32x4 (&f)[2] = fx[kb & 1];
+            u32x4 (&g)[2] = fy[kb & 1];
+            if constexpr (kb == 3) {
+                asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            } else {
+                lds_wait();
+            }
+            // prefetch the next block's fragments
+            static_for<2>([&](auto t) {
+                lds_read16<t * 32 * kDRow>(fx[(kb + 1) & 1][t], rb ? rd_b[1][nkb_] : rd_b[0][nkb_]);
+                lds_read16<t * 32 * kDRow>(fy[(kb + 1) & 1][t], rb ? rd_a[1][nkb_] : rd_a[0][nkb_]);
+            });
+            if constexpr (kb == 3) static_for<8>([&](auto J) { dma_one(J, s + 2, cb); });
+            // the MFMAs below may only start after the prefetch is issued
+            asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(g[0]), "+v"(g[1]));
+            {
+                const float sigma = sig[kb];
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                    for (int tj = 0; tj < 2; ++tj) {
+                        const uint64_t xl = static_cast<uint64_t>(f[ti][0]) | (static_cast<uint64_t>(f[ti][1]) << 32);
+                        const uint64_t xh = static_cast<uint64_t>(f[ti][2]) | (static_cast<uint64_t>(f[ti][3]) << 32);
+                        const uint64_t yl = static_cast<uint64_t>(g[tj][0]) | (static_cast<uint64_t>(g[tj][1]) << 32);
+                        const uint64_t yh = static_cast<uint64_t>(g[tj][2]) | (static_cast<uint64_t>(g[tj][3]) << 32);
+                        v16f p = v16f{};
+                        p = mfma_codes<AF, BF>(xl, yl, p);
+                        p = mfma_codes<AF, BF>(xh, yh, p);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sigma, p[r], acc[ti][tj][r]);
+                    }
+            }
+            // close the block: its promotions finish before the next block's reads
+            asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+        };
+        block(std::integral_constant<int, 0>{});
+        block(std::integral_constant<int, 1>{});
+        block(std::integral_constant<int, 2>{});
+        block(std::integral_constant<int, 3>{});
+    }
+    if (nfull < nst) {
+        // partial stage: its data and block-0 fragments are already in place
+        const int cb = nfull & 1;
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        u32x4 ca = nsa, cbv = nsb;
+        asm volatile("" : "+v"(ca), "+v"(cbv));
+        const int nk = nkb - 4 * nfull;
+        for (int kb = 0; kb < nk; ++kb) {
+            lds_wait();
+            u32x4 x[2], y[2];
+            if (kb == 0) {
+                x[0] = fx[0][0]; x[1] = fx[0][1]; y[0] = fy[0][0]; y[1] = fy[0][1];
+            } else {
+                const uint32_t ra = (cb ? rd_a[1][0] : rd_a[0][0]) + ((((2 * kb + half) ^ sw) - (half ^ sw)) * 16);
+                const uint32_t rb = (cb ? rd_b[1][0] : rd_b[0][0]) + ((((2 * kb + half) ^ sw) - (half ^ sw)) * 16);
+                lds_read16<0>(x[0], rb);
+                lds_read16<32 * kDRow>(x[1], rb);
+                lds_read16<0>(y[0], ra);
+                lds_read16<32 * kDRow>(y[1], ra);
+                lds_wait();
+            }
+            // the MFMAs consume the fragments only after the wait above
+            asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
+            const float sigma = __uint_as_float(ca[kb]) * __uint_as_float(cbv[kb]);
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int tj = 0; tj < 2; ++tj) {
+                    const uint64_t xl = static_cast<uint64_t>(x[ti][0]) | (static_cast<uint64_t>(x[ti][1]) << 32);
+                    const uint64_t xh = static_cast<uint64_t>(x[ti][2]) | (static_cast<uint64_t>(x[ti][3]) << 32);
+                    const uint64_t yl = static_cast<uint64_t>(y[tj][0]) | (static_cast<uint64_t>(y[tj][1]) << 32);
+                    const uint64_t yh = static_cast<uint64_t>(y[tj][2]) | (static_cast<uint64_t>(y[tj][3]) << 32);
+                    v16f p = v16f{};
+                    p = mfma_codes<AF, BF>(xl, yl, p);
+                    p = mfma_codes<AF, BF>(xh, yh, p);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sigma, p[r], acc[ti][tj][r]);
+                }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) {
+            const int m = m0 + wm * 64 + tj * 32 + frag_row;
+            if (m >= M) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * 64 + ti * 32 + q * 8 + half * 4;
+                uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
+                const uint32_t b0 = f32_to_bf16_rne(acc[ti][tj][4 * q + 0]), b1 = f32_to_bf16_rne(acc[ti][tj][4 * q + 1]);
+                const uint32_t b2 = f32_to_bf16_rne(acc[ti][tj][4 * q + 2]), b3 = f32_to_bf16_rne(acc[ti][tj][4 * q + 3]);
+                if (vec_ok && n + 3 < N) {
+                    *reinterpret_cast<uint2*>(dp) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                } else {
+                    if (n + 0 < N) dp[0] = static_cast<uint16_t>(b0);
+                    if (n + 1 < N) dp[1] = static_cast<uint16_t>(b1);
+                    if (n + 2 < N) dp[2] = static_cast<uint16_t>(b2);
+                    if (n + 3 < N) dp[3] = static_cast<uint16_t>(b3);
+                }
+            }
+        }
+}
+
 template <int AF, int BF>
 hipError_t launch_typed(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
                         const uint8_t* b, const float* sb, int out, void* d, int64_t ldd,
@@ -307,7 +547,7 @@ hipError_t launch_typed(int64_t M, int64_t N, int64_t K, const uint8_t* a, const
                            stream, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
                            a, sa, b, sb, d, ldd, tiles_m, tiles_n, vec_ok);
     else
-        hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, BSFP8_OUT_BF16, false>), grid, dim3(kThreads),
+        hipLaunchKernelGGL((gemm_fp8_bf16_kernel<AF, BF>), grid, dim3(kThreads),
                            0, stream, static_cast<int>(M), static_cast<int>(N),
                            static_cast<int>(K), a, sa, b, sb, d, ldd, tiles_m, tiles_n, vec_ok);
     return hipGetLastError();
