@@ -460,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_bf16_kernel(
                     }
             }
             // close the block: its promotions finish before the next block's reads
-            asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+            asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]));
         };
         block(std::integral_constant<int, 0>{});
         block(std::integral_constant<int, 1>{});
@@ -509,28 +509,41 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_bf16_kernel(
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
+    // Epilogue through LDS (free now): 128 rows x 256 bytes of bf16; 16-byte
+    // chunk c of row R sits at c ^ (R & 15).  Each 64-lane store then covers
+    // 4 whole rows instead of 32 rows x 16 bytes.
+    __syncthreads();
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-        for (int tj = 0; tj < 2; ++tj) {
-            const int m = m0 + wm * 64 + tj * 32 + frag_row;
-            if (m >= M) continue;
+        for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * 64 + ti * 32 + q * 8 + half * 4;
-                uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
-                const uint32_t b0 = f32_to_bf16_rne(acc[ti][tj][4 * q + 0]), b1 = f32_to_bf16_rne(acc[ti][tj][4 * q + 1]);
-                const uint32_t b2 = f32_to_bf16_rne(acc[ti][tj][4 * q + 2]), b3 = f32_to_bf16_rne(acc[ti][tj][4 * q + 3]);
-                if (vec_ok && n + 3 < N) {
-                    *reinterpret_cast<uint2*>(dp) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-                } else {
-                    if (n + 0 < N) dp[0] = static_cast<uint16_t>(b0);
-                    if (n + 1 < N) dp[1] = static_cast<uint16_t>(b1);
-                    if (n + 2 < N) dp[2] = static_cast<uint16_t>(b2);
-                    if (n + 3 < N) dp[3] = static_cast<uint16_t>(b3);
-                }
+                const int R = wm * 64 + tj * 32 + frag_row;
+                const int c = wn * 8 + ti * 4 + q;
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                const bf16x4 v = {(__bf16)acc[ti][tj][4 * q + 0], (__bf16)acc[ti][tj][4 * q + 1],
+                                  (__bf16)acc[ti][tj][4 * q + 2], (__bf16)acc[ti][tj][4 * q + 3]};
+                *reinterpret_cast<bf16x4*>(lds + R * 256 + ((c ^ (R & 15)) << 4) + 8 * half) = v;
             }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int R = wave * 32 + i * 4 + (lane >> 4);
+        const int c = lane & 15;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + R * 256 + ((c ^ (R & 15)) << 4));
+        const int m = m0 + R, n = n0 + c * 8;
+        if (m >= M) continue;
+        uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
+        if (vec_ok && n + 8 <= N) {
+            *reinterpret_cast<uint4*>(dp) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (n + j < N) dp[j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
         }
+    }
 }
 
 template <int AF, int BF>
@@ -549,7 +562,8 @@ hipError_t launch_typed(int64_t M, int64_t N, int64_t K, const uint8_t* a, const
     else
         hipLaunchKernelGGL((gemm_fp8_bf16_kernel<AF, BF>), grid, dim3(kThreads),
                            0, stream, static_cast<int>(M), static_cast<int>(N),
-                           static_cast<int>(K), a, sa, b, sb, d, ldd, tiles_m, tiles_n, vec_ok);
+                           static_cast<int>(K), a, sa, b, sb, d, ldd, tiles_m, tiles_n,
+                           static_cast<int>((ldd % 8 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0)));
     return hipGetLastError();
 }
 
