@@ -68,6 +68,18 @@ def committed_traffic(workload, source_file):
         return None, None
 
 
+def gemm_kernel_name(w):
+    """The kernel scaled_gemm dispatches for this workload (mirrors the
+    launchers' selection)."""
+    if w.a_fmt == "mxfp4":
+        big_tiles = ((w.M + 255) // 256) * ((w.N + 255) // 256)
+        fits32 = w.M * (w.K // 2) < 2**31 and w.N * (w.K // 2) < 2**31
+        if w.K % 256 == 0 and big_tiles >= 64 and fits32:
+            return "gemm_mxfp4_big_kernel"
+        return "gemm_mxfp4_kernel"
+    return "gemm_fp8_bf16_kernel" if w.out == "bf16" else "gemm_fp8_kernel"
+
+
 def cpu_baseline(w, a, b, d_gpu, sample_rows):
     """Time the oracle on a bounded sample: quantise all of B, `sample_rows`
     rows of A, and the product rows for that sample; extrapolate the time to
@@ -252,7 +264,7 @@ def main():
                             "fp8_quantize(A)+fp8_quantize(B)+scaled_gemm")},
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_mxfp4_kernel" if mx else "gemm_fp8_kernel",
+            "kernel": gemm_kernel_name(w),
             "achieved": round(gemm_tflops, 1),
             "peak": PEAK_TFLOPS[in_type],
             "unit": "TFLOP/s",
