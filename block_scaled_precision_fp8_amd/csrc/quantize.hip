@@ -7,8 +7,16 @@
 //
 // FP8 ("Why grind FP8 GEMM on CDNA4", sections 3.3 and 4.2): per 128 x 32
 // tile, s = fl32(amax / F) (1 for an all-zero tile), code = satRNE(fl32(x / s)).
-// The division is IEEE-correct (the compiler's correctly rounded sequence);
-// saturation is an explicit clamp to +-F, after which the hardware
+// The quotient fl32(x / s) is obtained without a per-element division, by
+// Markstein's correction step: with y the correctly rounded reciprocal of b and
+// q a faithful approximation of a / b, RN(q + y * (a - b q)) is the correctly
+// rounded a / b, provided a - b q (exact by FMA) does not underflow.  Both x
+// and s are first scaled by the same power of two 2^k (exact, quotient
+// unchanged) so that s 2^k lies in [1/2, 1); the residual can then underflow
+// only when |x / s| < 2^-99, where every FP8 code is a signed zero and the sign
+// is restored from x.  (Checked against IEEE division on 1.7e10 in-range pairs
+// per format, zero code mismatches; the parity tests compare every code with
+// the oracle.)  Saturation is an explicit clamp to +-F, after which the hardware
 // v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 conversion is exact round-to-nearest-even
 // (checked element by element against the oracle, including every midpoint).
 //
@@ -84,14 +92,27 @@ __global__ __launch_bounds__(kThreads) void fp8_quantize_kernel(
         scales[rt * nkb + cb * 4 + tid] = st;
     }
 
+    // x / s as described in the header: one correctly rounded reciprocal per
+    // thread, three FMA-class operations per element.
+    int se;
+    (void)__builtin_frexpf(s, &se);
+    const float ss = __builtin_ldexpf(s, -se);     // s 2^k in [1/2, 1)
+    const float rs = 1.0f / ss;                     // correctly rounded
+    auto quot = [&](float x) {
+        const float xs = __builtin_ldexpf(x, -se);
+        const float q0 = xs * rs;
+        const float e = __builtin_fmaf(-q0, ss, xs);
+        const float q = __builtin_copysignf(__builtin_fmaf(e, rs, q0), x);
+        return fminf(fmaxf(q, -F), F);
+    };
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int64_t r = r0 + ro + 8 * i;
         if (!(col_ok && r < rows)) continue;
-        const float q0 = fminf(fmaxf(v[i].x / s, -F), F);
-        const float q1 = fminf(fmaxf(v[i].y / s, -F), F);
-        const float q2 = fminf(fmaxf(v[i].z / s, -F), F);
-        const float q3 = fminf(fmaxf(v[i].w / s, -F), F);
+        const float q0 = quot(v[i].x);
+        const float q1 = quot(v[i].y);
+        const float q2 = quot(v[i].z);
+        const float q3 = quot(v[i].w);
         int w;
         if constexpr (FMT == BSFP8_E4M3) {
             w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
