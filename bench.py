@@ -145,6 +145,11 @@ def main():
     p.add_argument("--cpu-sample-gflop", type=float, default=150.0,
                    help="oracle product work to time (rows are chosen to match, whole 128-row tiles)")
     p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--operand-layout", choices=["k-contiguous", "token-major"], default=None,
+                   help="FP8 only: token-major stores A and B transposed (K x M, K x N, as the "
+                        "gradient and activation of a weight-gradient product are) and quantises "
+                        "them with fp8_quantize_transposed; default token-major for the dW "
+                        "workload, k-contiguous otherwise")
     args = p.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -166,9 +171,15 @@ def main():
     dev = torch.device("cuda:0")
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} {w.a_fmt}x{w.b_fmt} -> {w.out}")
     a_host, b_host = workloads.operands(w)
-    a = torch.from_numpy(a_host).to(dev)
-    b = torch.from_numpy(b_host).to(dev)
     mx = w.a_fmt == "mxfp4"
+    layout = args.operand_layout or ("token-major" if w.name.startswith("dw_") else "k-contiguous")
+    token_major = layout == "token-major" and not mx
+    if token_major:     # G (K x M) and X (K x N) as stored in the backward pass
+        a = torch.from_numpy(np.ascontiguousarray(a_host.T)).to(dev)
+        b = torch.from_numpy(np.ascontiguousarray(b_host.T)).to(dev)
+    else:
+        a = torch.from_numpy(a_host).to(dev)
+        b = torch.from_numpy(b_host).to(dev)
     # outputs allocated once, reused every step
     if mx:
         qa = torch.empty((w.M, w.K // 2), dtype=torch.uint8, device=dev)
@@ -193,10 +204,11 @@ def main():
             bs.mxfp4_quantize(a, qa, sa)
             bs.mxfp4_quantize(b, qb, sb)
         else:
-            bs.fp8_quantize(a, w.a_fmt, codes=qa, scales=sa)
+            quant = bs.fp8_quantize_transposed if token_major else bs.fp8_quantize
+            quant(a, w.a_fmt, codes=qa, scales=sa)
             if marks:
                 marks[1].record(stream)
-            bs.fp8_quantize(b, w.b_fmt, codes=qb, scales=sb)
+            quant(b, w.b_fmt, codes=qb, scales=sb)
         if marks:
             marks[2].record(stream)
         bs.scaled_gemm(qa, sa, qb, sb, w.a_fmt, w.b_fmt, w.out, d=d, K=w.K)
@@ -260,8 +272,10 @@ def main():
         "data": "synthetic (seeded numpy, distributions of the workload table)",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "a_fmt": w.a_fmt,
                    "b_fmt": w.b_fmt, "out": w.out,
+                   "operand_layout": "k-contiguous" if not token_major else "token-major",
                    "step": ("mxfp4_quantize(A)+mxfp4_quantize(B)+scaled_gemm" if mx else
-                            "fp8_quantize(A)+fp8_quantize(B)+scaled_gemm")},
+                            "fp8_quantize_transposed(G)+fp8_quantize_transposed(X)+scaled_gemm"
+                            if token_major else "fp8_quantize(A)+fp8_quantize(B)+scaled_gemm")},
         "roofline": {
             "bound": "mfma",
             "kernel": gemm_kernel_name(w),

@@ -8,6 +8,7 @@ raises, and a non-OK status raises ``RuntimeError``.
 
 Functions (same names as the C ABI):
   fp8_quantize(x, fmt="e4m3", tile_rows=128) -> (codes, scales)
+  fp8_quantize_transposed(x, fmt="e4m3", tile_rows=128) -> (codes of x^T, scales)
   mxfp4_quantize(x) -> (packed, scales)
   scaled_gemm(a, a_scales, b, b_scales, a_fmt, b_fmt, out="bf16", d=None) -> d
 """
@@ -43,6 +44,8 @@ def lib() -> ctypes.CDLL:
     i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     L.fp8_quantize.argtypes = [vp, i64, i64, i64, c_int, c_int, vp, vp, vp]
     L.fp8_quantize.restype = c_int
+    L.fp8_quantize_transposed.argtypes = [vp, i64, i64, i64, c_int, c_int, vp, vp, vp]
+    L.fp8_quantize_transposed.restype = c_int
     L.mxfp4_quantize.argtypes = [vp, i64, i64, i64, vp, vp, vp]
     L.mxfp4_quantize.restype = c_int
     L.scaled_gemm.argtypes = [i64, i64, i64, c_int, vp, vp, c_int, vp, vp, c_int, vp, i64, vp]
@@ -88,6 +91,27 @@ def fp8_quantize(x, fmt: str = "e4m3", tile_rows: int = FP8_TILE_ROWS,
     _check(st, "fp8_quantize")
     return codes, scales
 
+
+
+def fp8_quantize_transposed(x, fmt: str = "e4m3", tile_rows: int = FP8_TILE_ROWS,
+                            codes=None, scales=None):
+    """Quantise the transpose of a k x rows FP32 CUDA tensor (row-major, unit
+    column stride): returns rows x k codes and FP32 scales per tile_rows x 32
+    tile of x^T, identical to fp8_quantize(x.t().contiguous())."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 CUDA tensor with unit column stride")
+    k, rows = x.shape
+    if codes is None:
+        codes = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(((rows + tile_rows - 1) // tile_rows, (k + 31) // 32),
+                             dtype=torch.float32, device=x.device)
+    st = lib().fp8_quantize_transposed(_dev_ptr(x), k, rows, x.stride(0) if k > 1 else rows,
+                                       tile_rows, FORMATS[fmt], _dev_ptr(codes),
+                                       _dev_ptr(scales), _stream(x))
+    _check(st, "fp8_quantize_transposed")
+    return codes, scales
 
 def mxfp4_quantize(x, packed=None, scales=None):
     """Quantise a rows x k FP32 CUDA tensor to packed E2M1 (two per byte)

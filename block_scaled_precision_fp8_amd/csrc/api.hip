@@ -31,6 +31,21 @@ bsfp8_status fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, i
     return from_hip(bsfp8::launch_fp8_quantize(x, rows, k, ld, fmt, codes, scales, stream));
 }
 
+bsfp8_status fp8_quantize_transposed(const float* x, int64_t k, int64_t rows, int64_t ld,
+                                     int tile_rows, bsfp8_format fmt, uint8_t* codes,
+                                     float* scales, hipStream_t stream) {
+    if (!is_fp8(fmt)) return BSFP8_ERR_UNSUPPORTED;
+    if (tile_rows != 128) return BSFP8_ERR_UNSUPPORTED;
+    if (rows < 0 || k < 0 || ld < rows || (k % 32) != 0) return BSFP8_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return BSFP8_OK;
+    if (!x || !codes || !scales) return BSFP8_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || (ld % 4) != 0 || !aligned(codes, 16) || !aligned(scales, 4))
+        return BSFP8_ERR_INVALID_ARG;
+    const int64_t blocks = ((rows + 127) / 128) * ((k + 127) / 128);
+    if (blocks > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    return from_hip(bsfp8::launch_fp8_quantize_t(x, k, rows, ld, fmt, codes, scales, stream));
+}
+
 bsfp8_status mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
                             uint8_t* packed, uint8_t* scales, hipStream_t stream) {
     if (rows < 0 || k < 0 || ld < k || (k % 32) != 0) return BSFP8_ERR_INVALID_ARG;

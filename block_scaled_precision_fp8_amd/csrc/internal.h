@@ -13,6 +13,8 @@ namespace bsfp8 {
 // layer and returns the launch status.
 hipError_t launch_fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, int fmt,
                                uint8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_fp8_quantize_t(const float* x, int64_t k, int64_t rows, int64_t ld, int fmt,
+                                 uint8_t* codes, float* scales, hipStream_t stream);
 hipError_t launch_mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
                                  uint8_t* packed, uint8_t* scales, hipStream_t stream);
 hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,

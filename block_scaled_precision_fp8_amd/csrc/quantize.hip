@@ -133,6 +133,132 @@ __global__ __launch_bounds__(kThreads) void fp8_quantize_kernel(
     }
 }
 
+// Transposing variant: x is k x rows row-major (for example a gradient or an
+// activation stored token-major) and the result is the quantisation of x^T,
+// i.e. rows x k codes with K contiguous, exactly as fp8_quantize would produce
+// from an explicitly transposed copy.  One workgroup takes a 128 (k) x 128
+// (rows) input block = four 32 x 128 tiles of x (128 x 32 tiles of x^T).
+// Thread (chunk = t % 32, g = t / 32) loads 16-byte chunk `chunk` of input rows
+// 4 g + 32 q + j (q, j = 0..3): each load instruction reads two whole
+// 512-byte row segments, and each thread's 4 x 4 values per tile give, per
+// column, 4 consecutive K codes that go to LDS as one 32-bit word.  The block
+// is written back row by row of x^T with 16-byte stores.
+constexpr int kTPitch = 132;    // LDS bytes per x^T row (128 codes + 4)
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void fp8_quantize_t_kernel(
+    const float* __restrict__ x, int64_t k, int64_t rows, int64_t ld,
+    uint8_t* __restrict__ codes, float* __restrict__ scales, int64_t nrb) {
+    constexpr float F = FMT == BSFP8_E4M3 ? 448.0f : 57344.0f;
+    __shared__ float red[4][4];
+    __shared__ __attribute__((aligned(16))) uint8_t tl[128 * kTPitch];
+
+    const int64_t bid = blockIdx.x;
+    const int64_t kt = bid / nrb;            // 128-wide K block
+    const int64_t rb = bid - kt * nrb;       // 128-wide block of x^T rows (columns of x)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int chunk = tid & 31;
+    const int g = tid >> 5;
+    const int64_t k0 = kt * 128;
+    const int64_t c0 = rb * 128 + chunk * 4;   // first x column of this thread
+    const int64_t nkb = k >> 5;
+
+    float4 v[4][4];
+    float tmax[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        tmax[q] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t kr = k0 + 4 * g + 32 * q + j;
+            float4 t = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (kr < k) {
+                const float* p = x + kr * ld + c0;
+                if (c0 + 3 < rows) {
+                    t = load_once(p);
+                } else {
+                    if (c0 + 0 < rows) t.x = p[0];
+                    if (c0 + 1 < rows) t.y = p[1];
+                    if (c0 + 2 < rows) t.z = p[2];
+                }
+            }
+            v[q][j] = t;
+            tmax[q] = fmaxf(tmax[q], abs_max4(t));
+        }
+    }
+    // every lane of a wave holds part of all four tiles: full-wave reductions
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) tmax[q] = fmaxf(tmax[q], __shfl_xor(tmax[q], m));
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[wave][q] = tmax[q];
+    }
+    __syncthreads();
+
+    float sc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float a = fmaxf(fmaxf(red[0][q], red[1][q]), fmaxf(red[2][q], red[3][q]));
+        float st = a / F;
+        if (st == 0.0f) st = 1.0f;
+        sc[q] = st;
+    }
+    if (tid < 4 && k0 + 32 * tid < k) scales[rb * nkb + kt * 4 + tid] = sc[tid];
+
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float s = sc[q];
+        int se;
+        (void)__builtin_frexpf(s, &se);
+        const float ss = __builtin_ldexpf(s, -se);
+        const float rs = 1.0f / ss;
+        auto code = [&](float xv) -> uint32_t {
+            const float xs = __builtin_ldexpf(xv, -se);
+            const float q0 = xs * rs;
+            const float e = __builtin_fmaf(-q0, ss, xs);
+            const float qq = fminf(fmaxf(__builtin_copysignf(__builtin_fmaf(e, rs, q0), xv), -F), F);
+            int w;
+            if constexpr (FMT == BSFP8_E4M3) w = __builtin_amdgcn_cvt_pk_fp8_f32(qq, qq, 0, false);
+            else w = __builtin_amdgcn_cvt_pk_bf8_f32(qq, qq, 0, false);
+            return static_cast<uint32_t>(w) & 0xFFu;
+        };
+        // column jj of this thread: K codes j = 0..3 packed into one word
+        uint32_t wcol[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            wcol[0] |= code(v[q][j].x) << (8 * j);
+            wcol[1] |= code(v[q][j].y) << (8 * j);
+            wcol[2] |= code(v[q][j].z) << (8 * j);
+            wcol[3] |= code(v[q][j].w) << (8 * j);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            *reinterpret_cast<uint32_t*>(tl + (chunk * 4 + jj) * kTPitch + 4 * g + 32 * q) = wcol[jj];
+    }
+    __syncthreads();
+
+    // write back: x^T row r (128 codes) as 8 x 16 bytes
+    const int part = tid & 7;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int r = pass * 32 + (tid >> 3);
+        const int64_t orow = rb * 128 + r;
+        const int64_t ocol = k0 + 16 * part;
+        if (orow >= rows || ocol >= k) continue;
+        const uint8_t* src = tl + r * kTPitch + 16 * part;
+        const uint4 w = make_uint4(*reinterpret_cast<const uint32_t*>(src),
+                                   *reinterpret_cast<const uint32_t*>(src + 4),
+                                   *reinterpret_cast<const uint32_t*>(src + 8),
+                                   *reinterpret_cast<const uint32_t*>(src + 12));
+        *reinterpret_cast<uint4*>(codes + orow * k + ocol) = w;
+    }
+}
+
 // One thread per 16-byte chunk (4 elements); the 8 consecutive lanes of a
 // 32-element block reduce their maximum with three shuffles.
 __global__ __launch_bounds__(kThreads) void mxfp4_quantize_kernel(
@@ -199,6 +325,21 @@ hipError_t launch_fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t 
     else
         hipLaunchKernelGGL(fp8_quantize_kernel<BSFP8_E5M2>, dim3(static_cast<uint32_t>(blocks)),
                            dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales, ncb);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize_t(const float* x, int64_t k, int64_t rows, int64_t ld, int fmt,
+                                 uint8_t* codes, float* scales, hipStream_t stream) {
+    const int64_t nkt = (k + 127) / 128;
+    const int64_t nrb = (rows + 127) / 128;
+    const int64_t blocks = nkt * nrb;
+    if (blocks == 0) return hipSuccess;
+    if (fmt == BSFP8_E4M3)
+        hipLaunchKernelGGL(fp8_quantize_t_kernel<BSFP8_E4M3>, dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kThreads), 0, stream, x, k, rows, ld, codes, scales, nrb);
+    else
+        hipLaunchKernelGGL(fp8_quantize_t_kernel<BSFP8_E5M2>, dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kThreads), 0, stream, x, k, rows, ld, codes, scales, nrb);
     return hipGetLastError();
 }
 

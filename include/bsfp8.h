@@ -73,6 +73,27 @@ bsfp8_status fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, i
                           bsfp8_format fmt, uint8_t* codes, float* scales, hipStream_t stream);
 
 /*
+ * fp8_quantize_transposed -- per-tile FP8 quantisation of x^T, for operands
+ * stored the other way round, such as the gradient G and activation X of a
+ * weight-gradient product dW = G^T X ([CDNA4-FP8] section 3.3's per-tile
+ * scales; section 2.2 of the same page puts gradients in E5M2).
+ *
+ * x:      k x rows FP32, row-major, leading dimension ld (elements):
+ *         16-byte aligned, ld a multiple of 4, ld >= rows.
+ * k:      >= 0, a multiple of 32 (the K dimension of the GEMM operand).
+ * rows:   >= 0, any value (M for an A operand, N for a B operand).
+ * tile_rows, fmt: as for fp8_quantize.
+ * codes:  out, rows x k bytes, row stride k, 16-byte aligned.
+ * scales: out, FP32 [ceil(rows / 128)][k / 32].
+ *
+ * The result is byte-for-byte that of fp8_quantize applied to an explicitly
+ * transposed copy of x (rows x k, row-major); no transposed copy is made.
+ */
+bsfp8_status fp8_quantize_transposed(const float* x, int64_t k, int64_t rows, int64_t ld,
+                                     int tile_rows, bsfp8_format fmt, uint8_t* codes,
+                                     float* scales, hipStream_t stream);
+
+/*
  * mxfp4_quantize -- MXFP4 block quantisation ([RUBIN-FP4] sections 2.1, 2.2, 3.1, 4.2).
  *
  * x:      rows x k FP32, row-major, leading dimension ld; 16-byte aligned,

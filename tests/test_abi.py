@@ -30,8 +30,8 @@ def L():
 
 def test_header_declares_the_three_calls():
     names = declared_functions()
-    for n in ("fp8_quantize", "mxfp4_quantize", "scaled_gemm", "bsfp8_status_string",
-              "bsfp8_version"):
+    for n in ("fp8_quantize", "fp8_quantize_transposed", "mxfp4_quantize", "scaled_gemm",
+              "bsfp8_status_string", "bsfp8_version"):
         assert n in names
 
 
@@ -65,6 +65,21 @@ def test_fp8_quantize_argument_checks(L):
     assert q(P, 128, 64, 64, 128, 7, P, P, None) == UNSUPPORTED
     assert q(0, 0, 64, 64, 128, E4M3, 0, 0, None) == OK             # empty: nothing to do
     assert q(0, 128, 0, 0, 128, E4M3, 0, 0, None) == OK
+
+
+def test_fp8_quantize_transposed_argument_checks(L):
+    q = L.fp8_quantize_transposed     # (x, k, rows, ld, tile_rows, fmt, codes, scales, stream)
+    assert q(P, 48, 128, 128, 128, E4M3, P, P, None) == INVALID     # k % 32
+    assert q(P, 64, -1, 64, 128, E4M3, P, P, None) == INVALID       # negative rows
+    assert q(P, 64, 128, 64, 128, E4M3, P, P, None) == INVALID      # ld < rows
+    assert q(P, 64, 128, 130, 128, E4M3, P, P, None) == INVALID     # ld % 4
+    assert q(P + 4, 64, 128, 128, 128, E4M3, P, P, None) == INVALID  # x alignment
+    assert q(P, 64, 128, 128, 128, E4M3, P + 4, P, None) == INVALID  # codes alignment
+    assert q(0, 64, 128, 128, 128, E4M3, P, P, None) == INVALID     # null x
+    assert q(P, 64, 128, 128, 64, E4M3, P, P, None) == UNSUPPORTED  # tile_rows
+    assert q(P, 64, 128, 128, 128, MXFP4, P, P, None) == UNSUPPORTED
+    assert q(0, 64, 0, 0, 128, E4M3, 0, 0, None) == OK              # empty
+    assert q(0, 0, 128, 128, 128, E4M3, 0, 0, None) == OK
 
 
 def test_mxfp4_quantize_argument_checks(L):

@@ -30,6 +30,36 @@ def gpu_fp8(x, fmt, ld=None):
     return from_dev(codes), from_dev(scales)
 
 
+def gpu_fp8_t(xt, fmt, ld=None):
+    """Transposing quantiser on xt (k x rows, as stored); returns codes and
+    scales of xt^T."""
+    import torch
+    b = bsfp8()
+    if ld is None:
+        xd = to_dev(xt)
+    else:
+        buf = np.zeros((xt.shape[0], ld), dtype=np.float32)
+        buf[:, : xt.shape[1]] = xt
+        xd = to_dev(buf)[:, : xt.shape[1]]
+    codes, scales = b.fp8_quantize_transposed(xd, fmt)
+    torch.cuda.synchronize()
+    return from_dev(codes), from_dev(scales)
+
+
+def assert_fp8_t_equal(x, fmt, ld=None, label=""):
+    """x is rows x k (the operand as the GEMM wants it); the GPU is given its
+    transpose, stored k x rows, and must produce exactly the oracle's
+    quantisation of x."""
+    xt = np.ascontiguousarray(x.T)
+    say(f"fp8_quantize_transposed {fmt} stored {xt.shape} ld={ld} {label}")
+    c, s = gpu_fp8_t(xt, fmt, ld)
+    rc, rs = oracle.fp8_quantize(x, fmt)
+    assert s.view(np.uint32).tobytes() == rs.view(np.uint32).tobytes(), f"{label}: scales differ"
+    bad = np.nonzero(c != rc)
+    assert bad[0].size == 0, (f"{label}: {bad[0].size} codes differ, first at {bad[0][0]},{bad[1][0]}:"
+                              f" x={x[bad[0][0], bad[1][0]]!r} gpu={c[bad][0]:#x} oracle={rc[bad][0]:#x}")
+
+
 def gpu_mx(x, ld=None):
     import torch
     b = bsfp8()
@@ -125,6 +155,38 @@ def test_fp8_deterministic():
     assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_transposed_edge_values(fmt):
+    x = fp8_edge_tile(fmt)
+    assert_fp8_t_equal(x, fmt, label="edge values, unit scale")
+    y = x.copy()
+    y[:, 0:32] *= np.float32(3.0)
+    y[:, 32:64] *= np.float32(1e-3)
+    y[:, 64:96] *= np.float32(1.0 / 3.0)
+    assert_fp8_t_equal(y, fmt, label="edge values, scaled")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("rows,k,ld", [(300, 96, None), (1, 32, 4), (129, 160, 132), (127, 64, 128),
+                                       (513, 256, None), (130, 288, 132), (3, 64, 8)])
+def test_fp8_transposed_ragged(fmt, rows, k, ld):
+    """ld is the stored (k x rows) array's leading dimension."""
+    x = workloads.normal(300 + rows, rows, k) * np.float32(5.0)
+    x[rows // 2, :] *= np.float32(1e4)
+    if ld is None and rows % 4:
+        ld = rows + (-rows) % 4
+    assert_fp8_t_equal(x, fmt, ld, label="ragged")
+
+
+def test_fp8_transposed_degenerate():
+    assert_fp8_t_equal(np.zeros((132, 64), dtype=np.float32), "e4m3", label="all zero")
+    assert_fp8_t_equal(np.full((128, 32), -0.0, dtype=np.float32), "e4m3", label="negative zero")
+    tiny = (workloads.normal(15, 128, 64) * np.float32(1e-38)).astype(np.float32)
+    assert_fp8_t_equal(tiny, "e4m3", label="subnormal-scale tiles")
+    big = (workloads.normal(16, 128, 64) * np.float32(1e37)).astype(np.float32)
+    assert_fp8_t_equal(big, "e5m2", label="huge tiles")
+
+
 def test_mxfp4_edge_values():
     # blocks whose maximum is 6 (e = 0) holding every E2M1 midpoint and neighbours
     mids = np.array([0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6],
@@ -170,3 +232,12 @@ def test_workload_operands_full_size(name):
     else:
         assert_fp8_equal(a, w.a_fmt, label=f"{name} A")
         assert_fp8_equal(b, w.b_fmt, label=f"{name} B")
+
+
+def test_workload_operands_transposed_full_size():
+    """The weight-gradient workload with its operands stored token-major (G and
+    X as K x M and K x N), quantised by the transposing kernel."""
+    w = workloads.by_name("dw_e5m2xe4m3_4096x4096x16384")
+    a, b = workloads.operands(w)
+    assert_fp8_t_equal(a, w.a_fmt, label=f"{w.name} A from G")
+    assert_fp8_t_equal(b, w.b_fmt, label=f"{w.name} B from X")
