@@ -77,7 +77,7 @@ def gemm_kernel_name(w):
         if w.K % 256 == 0 and big_tiles >= 64 and fits32:
             return "gemm_mxfp4_big_kernel"
         return "gemm_mxfp4_kernel"
-    return "gemm_fp8_bf16_kernel" if w.out == "bf16" else "gemm_fp8_kernel"
+    return "gemm_fp8_kernel"
 
 
 def cpu_baseline(w, a, b, d_gpu, sample_rows):

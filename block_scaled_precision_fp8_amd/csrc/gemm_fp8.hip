@@ -18,18 +18,29 @@
 //    the rest (the behaviour "FP8 MMA internals on Hopper" models for H100,
 //    measured on gfx950), i.e. at most 2^-8 of sum |a b| per block: inside the
 //    2^-7 bf16 tolerance.
-//  * FP32 output: codes are widened exactly to bf16 while staged into LDS
-//    (every E4M3/E5M2 value is a normal bf16) and multiplied with
-//    v_mfma_f32_32x32x16_bf16, which keeps 24 alignment bits: inside 2^-19.
+//  * FP32 output: each fragment is widened exactly to bf16 (every E4M3/E5M2
+//    value is a normal bf16) right before v_mfma_f32_32x32x16_bf16, which keeps
+//    24 alignment bits: inside 2^-19.
+// Only these K = 16 instructions keep each 32-wide block's sum apart; the
+// K = 64 F8F6F4 instructions would merge two blocks whose scale products are
+// unrelated FP32 numbers.
 //
 // Tiling: 128 x 128 output tile per workgroup (one A scale tile by one B scale
 // tile, so sigma_kb is uniform across the workgroup), 4 waves of 64 x 64, each
-// made of 2 x 2 MFMA 32 x 32 tiles.  A and B tiles are staged through LDS in
-// two buffers of 128 rows x 128 bytes (+16 bytes of padding per row, which
-// makes the 16-byte fragment reads of 8 consecutive rows cover all banks).
-// The MFMA's row operand is B and its column operand is A, so each lane ends
-// up holding 4 consecutive output columns: the epilogue writes 16-byte (FP32)
-// or 8-byte (bf16) vectors.
+// made of 2 x 2 MFMA 32 x 32 tiles, two workgroups per CU.  The MFMA's row
+// operand is B and its column operand is A, so each lane holds 4 consecutive
+// output columns.
+//
+// Data movement:
+//  * A and B are staged one stage (128 K = 4 blocks) ahead with direct
+//    global-to-LDS loads, into unpadded 128-byte LDS rows; 16-byte chunk g of
+//    row R is stored at position g ^ ((R >> 1) & 7), so the 16 lanes of a
+//    fragment-read phase hit 16 distinct 4-bank groups.
+//  * The fragments of block kb + 1 are read (ordered inline assembly) before
+//    block kb's MFMAs, which are tied to the prefetch so the compiler cannot
+//    hoist them above it.  The stage barrier sits before a stage's last block,
+//    so the next stage's first fragments load under that block's MFMAs.
+//  * The output tile leaves through LDS, so every store writes whole rows.
 #include "internal.h"
 
 #include <utility>
@@ -44,18 +55,6 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;
 constexpr int BM = 128;
 constexpr int BN = 128;
-constexpr int kRowBytes = 128;                // data bytes per LDS row per stage
-constexpr int kStride = kRowBytes + 16;       // padded LDS row stride
-constexpr int kOperandBytes = 128 * kStride;  // one operand tile
-constexpr int kStageBytes = 2 * kOperandBytes;
-constexpr int kLdsBytes = 2 * kStageBytes;    // double buffered: 73728 bytes
-
-__device__ __forceinline__ uint64_t lo64(uint4 v) {
-    return static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32);
-}
-__device__ __forceinline__ uint64_t hi64(uint4 v) {
-    return static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32);
-}
 
 // src0 holds B codes (format BF), src1 holds A codes (format AF).
 template <int AF, int BF>
@@ -71,228 +70,26 @@ __device__ __forceinline__ v16f mfma_codes(uint64_t x, uint64_t y, v16f c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf8_bf8(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ v16f mfma_bf16(uint4 x, uint4 y, v16f c) {
-    v8bf a, b;
-    __builtin_memcpy(&a, &x, 16);
-    __builtin_memcpy(&b, &y, 16);
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
-// Four FP8 codes (one dword) -> four bf16 (two dwords), exactly: the hardware
-// FP8 -> FP32 conversion is exact and an FP8 value's FP32 image has 16 zero
-// low bits, so its upper half is the bf16 encoding of the same value.
+// Eight FP8 codes (two dwords) -> eight bf16, exactly (every E4M3 and E5M2
+// value is a normal bf16; unit scale).  A and B fragments go through the same
+// mapping, so the K indices of the two operands still pair up.
 template <int FMT>
-__device__ __forceinline__ uint2 widen4(uint32_t w) {
-    float f0, f1, f2, f3;
+__device__ __forceinline__ v8bf widen8(uint32_t w0, uint32_t w1) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    bf2 a, b, c, d;
     if constexpr (FMT == BSFP8_E4M3) {
-        auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-        auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-        f0 = lo[0]; f1 = lo[1]; f2 = hi[0]; f3 = hi[1];
+        a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+        b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+        c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+        d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
     } else {
-        auto lo = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), false);
-        auto hi = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), true);
-        f0 = lo[0]; f1 = lo[1]; f2 = hi[0]; f3 = hi[1];
+        a = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, 1.0f, false);
+        b = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, 1.0f, true);
+        c = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, 1.0f, false);
+        d = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, 1.0f, true);
     }
-    uint2 r;
-    r.x = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
-    r.y = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
-    return r;
-}
-
-template <int FMT>
-__device__ __forceinline__ void widen16(uint4 v, uint4& lo, uint4& hi) {
-    const uint2 a = widen4<FMT>(v.x), b = widen4<FMT>(v.y);
-    const uint2 c = widen4<FMT>(v.z), d = widen4<FMT>(v.w);
-    lo = make_uint4(a.x, a.y, b.x, b.y);
-    hi = make_uint4(c.x, c.y, d.x, d.y);
-}
-
-template <int AF, int BF, int OUT, bool WIDE>
-__global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
-    int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
-    const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D,
-    int64_t ldd, int tiles_m, int tiles_n, int vec_ok) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-
-    constexpr int KPS = WIDE ? 64 : 128;     // K elements per stage (128 LDS bytes per row)
-    constexpr int KBS = KPS / 32;            // K blocks per stage
-    constexpr int CPR = KPS / 16;            // 16-byte global chunks per row per stage
-    constexpr int RSTEP = kThreads / CPR;    // rows between one thread's chunks
-    constexpr int NLD = 128 / RSTEP;         // chunks per thread per operand per stage
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave & 1;
-    const int wn = wave >> 1;
-
-    int tm, tn;
-    map_tile(blockIdx.x, tiles_m, tiles_n, 8, &tm, &tn);
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
-    const int nkb = K >> 5;
-    const int nst = (nkb + KBS - 1) / KBS;
-
-    // Global -> register staging: thread `tid` moves chunk (tid % CPR) of rows
-    // (tid / CPR) + RSTEP * i.  Rows past the matrix edge re-read the last row;
-    // their results are never stored.
-    const int crow = tid / CPR;
-    const int cch = tid % CPR;
-    const uint8_t* ga[NLD];
-    const uint8_t* gb[NLD];
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-        const int ra = min(m0 + crow + RSTEP * i, M - 1);
-        const int rb = min(n0 + crow + RSTEP * i, N - 1);
-        ga[i] = A + static_cast<int64_t>(ra) * K + cch * 16;
-        gb[i] = B + static_cast<int64_t>(rb) * K + cch * 16;
-    }
-    uint4 sa_reg[NLD], sb_reg[NLD];
-
-    auto gload = [&](int s) {
-        const int k0 = s * KPS;
-        const bool ok = k0 + cch * 16 < K;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            sa_reg[i] = ok ? *reinterpret_cast<const uint4*>(ga[i] + k0) : make_uint4(0, 0, 0, 0);
-            sb_reg[i] = ok ? *reinterpret_cast<const uint4*>(gb[i] + k0) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto lstore = [&](int buf) {
-        uint8_t* la = lds + buf * kStageBytes;
-        uint8_t* lb = la + kOperandBytes;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int row = crow + RSTEP * i;
-            if constexpr (!WIDE) {
-                *reinterpret_cast<uint4*>(la + row * kStride + cch * 16) = sa_reg[i];
-                *reinterpret_cast<uint4*>(lb + row * kStride + cch * 16) = sb_reg[i];
-            } else {
-                uint4 lo, hi;
-                widen16<AF>(sa_reg[i], lo, hi);
-                *reinterpret_cast<uint4*>(la + row * kStride + cch * 32) = lo;
-                *reinterpret_cast<uint4*>(la + row * kStride + cch * 32 + 16) = hi;
-                widen16<BF>(sb_reg[i], lo, hi);
-                *reinterpret_cast<uint4*>(lb + row * kStride + cch * 32) = lo;
-                *reinterpret_cast<uint4*>(lb + row * kStride + cch * 32 + 16) = hi;
-            }
-        }
-    };
-
-    v16f acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
-
-    const int frag_row = lane & 31;
-    const int half = lane >> 5;
-    const float* sa_row = sA + static_cast<int64_t>(tm) * nkb;
-    const float* sb_row = sB + static_cast<int64_t>(tn) * nkb;
-
-    auto compute_kb = [&](const uint8_t* la, const uint8_t* lb, int kb, int gkb) {
-        const float sigma = sa_row[gkb] * sb_row[gkb];
-        uint4 x0[2], x1[2], y0[2], y1[2];
-        if constexpr (!WIDE) {
-            // lane half h reads bytes 16h..16h+15 of the block: instruction 0 takes
-            // the first 8, instruction 1 the next 8 (same mapping for A and B).
-            const int off = kb * 32 + 16 * half;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                x0[t] = *reinterpret_cast<const uint4*>(lb + (wn * 64 + 32 * t + frag_row) * kStride + off);
-                y0[t] = *reinterpret_cast<const uint4*>(la + (wm * 64 + 32 * t + frag_row) * kStride + off);
-            }
-#pragma unroll
-            for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-                for (int tj = 0; tj < 2; ++tj) {
-                    v16f p = v16f{};
-                    p = mfma_codes<AF, BF>(lo64(x0[ti]), lo64(y0[tj]), p);
-                    p = mfma_codes<AF, BF>(hi64(x0[ti]), hi64(y0[tj]), p);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sigma, p[r], acc[ti][tj][r]);
-                }
-        } else {
-            // bf16: lane half h reads elements 16h..16h+15 (32 bytes) of the block.
-            const int off = kb * 64 + 32 * half;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const uint8_t* px = lb + (wn * 64 + 32 * t + frag_row) * kStride + off;
-                const uint8_t* py = la + (wm * 64 + 32 * t + frag_row) * kStride + off;
-                x0[t] = *reinterpret_cast<const uint4*>(px);
-                x1[t] = *reinterpret_cast<const uint4*>(px + 16);
-                y0[t] = *reinterpret_cast<const uint4*>(py);
-                y1[t] = *reinterpret_cast<const uint4*>(py + 16);
-            }
-#pragma unroll
-            for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-                for (int tj = 0; tj < 2; ++tj) {
-                    v16f p = v16f{};
-                    p = mfma_bf16(x0[ti], y0[tj], p);
-                    p = mfma_bf16(x1[ti], y1[tj], p);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sigma, p[r], acc[ti][tj][r]);
-                }
-        }
-    };
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int s = 0; s < nst; ++s) {
-        if (s + 1 < nst) gload(s + 1);
-        const uint8_t* la = lds + (s & 1) * kStageBytes;
-        const uint8_t* lb = la + kOperandBytes;
-        const int kb0 = s * KBS;
-        if (kb0 + KBS <= nkb) {
-#pragma unroll
-            for (int kb = 0; kb < KBS; ++kb) compute_kb(la, lb, kb, kb0 + kb);
-        } else {
-            for (int kb = 0; kb < nkb - kb0; ++kb) compute_kb(la, lb, kb, kb0 + kb);
-        }
-        if (s + 1 < nst) lstore((s + 1) & 1);
-        __syncthreads();
-    }
-
-    // Epilogue.  acc[ti][tj][r] is output row m = m0 + 64 wm + 32 tj + (lane % 32)
-    // and column n = n0 + 64 wn + 32 ti + 8 (r / 4) + 4 (lane / 32) + r % 4.
-#pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int tj = 0; tj < 2; ++tj) {
-            const int m = m0 + wm * 64 + tj * 32 + frag_row;
-            if (m >= M) continue;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * 64 + ti * 32 + q * 8 + half * 4;
-                const float v0 = acc[ti][tj][4 * q + 0], v1 = acc[ti][tj][4 * q + 1];
-                const float v2 = acc[ti][tj][4 * q + 2], v3 = acc[ti][tj][4 * q + 3];
-                if constexpr (OUT == BSFP8_OUT_F32) {
-                    float* dp = static_cast<float*>(D) + static_cast<int64_t>(m) * ldd + n;
-                    if (vec_ok && n + 3 < N) {
-                        *reinterpret_cast<float4*>(dp) = make_float4(v0, v1, v2, v3);
-                    } else {
-                        if (n + 0 < N) dp[0] = v0;
-                        if (n + 1 < N) dp[1] = v1;
-                        if (n + 2 < N) dp[2] = v2;
-                        if (n + 3 < N) dp[3] = v3;
-                    }
-                } else {
-                    uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
-                    const uint32_t b0 = f32_to_bf16_rne(v0), b1 = f32_to_bf16_rne(v1);
-                    const uint32_t b2 = f32_to_bf16_rne(v2), b3 = f32_to_bf16_rne(v3);
-                    if (vec_ok && n + 3 < N) {
-                        *reinterpret_cast<uint2*>(dp) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-                    } else {
-                        if (n + 0 < N) dp[0] = static_cast<uint16_t>(b0);
-                        if (n + 1 < N) dp[1] = static_cast<uint16_t>(b1);
-                        if (n + 2 < N) dp[2] = static_cast<uint16_t>(b2);
-                        if (n + 3 < N) dp[3] = static_cast<uint16_t>(b3);
-                    }
-                }
-            }
-        }
+    return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -320,8 +117,31 @@ constexpr int kDOperand = 128 * kDRow;      // 16 KB
 constexpr int kDStage = 2 * kDOperand;      // 32 KB
 constexpr int kDLds = 2 * kDStage;          // 64 KB: two workgroups per CU
 
-template <int AF, int BF>
-__global__ __launch_bounds__(kThreads, 2) void gemm_fp8_bf16_kernel(
+// Product of one 32 x 32 MFMA tile over one 32-wide K block.  Lane half h
+// holds K values 16h .. 16h+15 of its row in x (B, format BF) and y (A,
+// format AF); the first instruction takes the first 8, the second the next 8.
+//  * bf16 output: the FP8 codes go straight into the FP8 MFMA.
+//  * FP32 output: the codes are widened exactly to bf16 and multiplied with the
+//    bf16 MFMA, which keeps 24 alignment bits instead of 13.
+template <int AF, int BF, int OUT>
+__device__ __forceinline__ v16f tile_product(const u32x4& x, const u32x4& y) {
+    v16f p = v16f{};
+    if constexpr (OUT == BSFP8_OUT_BF16) {
+        const uint64_t xl = static_cast<uint64_t>(x[0]) | (static_cast<uint64_t>(x[1]) << 32);
+        const uint64_t xh = static_cast<uint64_t>(x[2]) | (static_cast<uint64_t>(x[3]) << 32);
+        const uint64_t yl = static_cast<uint64_t>(y[0]) | (static_cast<uint64_t>(y[1]) << 32);
+        const uint64_t yh = static_cast<uint64_t>(y[2]) | (static_cast<uint64_t>(y[3]) << 32);
+        p = mfma_codes<AF, BF>(xl, yl, p);
+        p = mfma_codes<AF, BF>(xh, yh, p);
+    } else {
+        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8<BF>(x[0], x[1]), widen8<AF>(y[0], y[1]), p, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8<BF>(x[2], x[3]), widen8<AF>(y[2], y[3]), p, 0, 0, 0);
+    }
+    return p;
+}
+
+template <int AF, int BF, int OUT>
+__global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
     const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D,
     int64_t ldd, int tiles_m, int tiles_n, int vec_ok) {
@@ -448,13 +268,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_bf16_kernel(
                 for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                     for (int tj = 0; tj < 2; ++tj) {
-                        const uint64_t xl = static_cast<uint64_t>(f[ti][0]) | (static_cast<uint64_t>(f[ti][1]) << 32);
-                        const uint64_t xh = static_cast<uint64_t>(f[ti][2]) | (static_cast<uint64_t>(f[ti][3]) << 32);
-                        const uint64_t yl = static_cast<uint64_t>(g[tj][0]) | (static_cast<uint64_t>(g[tj][1]) << 32);
-                        const uint64_t yh = static_cast<uint64_t>(g[tj][2]) | (static_cast<uint64_t>(g[tj][3]) << 32);
-                        v16f p = v16f{};
-                        p = mfma_codes<AF, BF>(xl, yl, p);
-                        p = mfma_codes<AF, BF>(xh, yh, p);
+                        const v16f p = tile_product<AF, BF, OUT>(f[ti], g[tj]);
 #pragma unroll
                         for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sigma, p[r], acc[ti][tj][r]);
                     }
@@ -495,13 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_bf16_kernel(
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                 for (int tj = 0; tj < 2; ++tj) {
-                    const uint64_t xl = static_cast<uint64_t>(x[ti][0]) | (static_cast<uint64_t>(x[ti][1]) << 32);
-                    const uint64_t xh = static_cast<uint64_t>(x[ti][2]) | (static_cast<uint64_t>(x[ti][3]) << 32);
-                    const uint64_t yl = static_cast<uint64_t>(y[tj][0]) | (static_cast<uint64_t>(y[tj][1]) << 32);
-                    const uint64_t yh = static_cast<uint64_t>(y[tj][2]) | (static_cast<uint64_t>(y[tj][3]) << 32);
-                    v16f p = v16f{};
-                    p = mfma_codes<AF, BF>(xl, yl, p);
-                    p = mfma_codes<AF, BF>(xh, yh, p);
+                    const v16f p = tile_product<AF, BF, OUT>(x[ti], y[tj]);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sigma, p[r], acc[ti][tj][r]);
                 }
@@ -509,39 +317,75 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_bf16_kernel(
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
-    // Epilogue through LDS (free now): 128 rows x 256 bytes of bf16; 16-byte
-    // chunk c of row R sits at c ^ (R & 15).  Each 64-lane store then covers
-    // 4 whole rows instead of 32 rows x 16 bytes.
+    // Epilogue through LDS (free now), so that each 64-lane store covers whole
+    // output rows instead of 32 rows x 16 bytes.  16-byte chunk c of LDS row R
+    // sits at c ^ (R & 15), which keeps the scattered writes and the row reads
+    // free of bank conflicts.
     __syncthreads();
+    if constexpr (OUT == BSFP8_OUT_BF16) {
+        // 128 rows x 256 bytes; a store covers 4 rows
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+        for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-        for (int tj = 0; tj < 2; ++tj)
+            for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int R = wm * 64 + tj * 32 + frag_row;
-                const int c = wn * 8 + ti * 4 + q;
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                const bf16x4 v = {(__bf16)acc[ti][tj][4 * q + 0], (__bf16)acc[ti][tj][4 * q + 1],
-                                  (__bf16)acc[ti][tj][4 * q + 2], (__bf16)acc[ti][tj][4 * q + 3]};
-                *reinterpret_cast<bf16x4*>(lds + R * 256 + ((c ^ (R & 15)) << 4) + 8 * half) = v;
+                for (int q = 0; q < 4; ++q) {
+                    const int R = wm * 64 + tj * 32 + frag_row;
+                    const int c = wn * 8 + ti * 4 + q;
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    const bf16x4 v = {(__bf16)acc[ti][tj][4 * q + 0], (__bf16)acc[ti][tj][4 * q + 1],
+                                      (__bf16)acc[ti][tj][4 * q + 2], (__bf16)acc[ti][tj][4 * q + 3]};
+                    *reinterpret_cast<bf16x4*>(lds + R * 256 + ((c ^ (R & 15)) << 4) + 8 * half) = v;
+                }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int R = wave * 32 + i * 4 + (lane >> 4);
+            const int c = lane & 15;
+            const uint4 v = *reinterpret_cast<const uint4*>(lds + R * 256 + ((c ^ (R & 15)) << 4));
+            const int m = m0 + R, n = n0 + c * 8;
+            if (m >= M) continue;
+            uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
+            if (vec_ok && n + 8 <= N) {
+                *reinterpret_cast<uint4*>(dp) = v;
+            } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (n + j < N) dp[j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
             }
-    __syncthreads();
+        }
+    } else {
+        // 128 rows x 512 bytes = the whole 64 KB; a store covers 2 rows
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int R = wave * 32 + i * 4 + (lane >> 4);
-        const int c = lane & 15;
-        const uint4 v = *reinterpret_cast<const uint4*>(lds + R * 256 + ((c ^ (R & 15)) << 4));
-        const int m = m0 + R, n = n0 + c * 8;
-        if (m >= M) continue;
-        uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
-        if (vec_ok && n + 8 <= N) {
-            *reinterpret_cast<uint4*>(dp) = v;
-        } else {
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (n + j < N) dp[j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
+            for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int R = wm * 64 + tj * 32 + frag_row;
+                    const int c = wn * 16 + ti * 8 + q * 2 + half;
+                    *reinterpret_cast<float4*>(lds + R * 512 + ((c ^ (R & 15)) << 4)) =
+                        make_float4(acc[ti][tj][4 * q + 0], acc[ti][tj][4 * q + 1],
+                                    acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]);
+                }
+        __syncthreads();
+#pragma unroll 4
+        for (int i = 0; i < 16; ++i) {
+            const int R = wave * 32 + i * 2 + (lane >> 5);
+            const int c = lane & 31;
+            const float4 v = *reinterpret_cast<const float4*>(lds + R * 512 + ((c ^ (R & 15)) << 4));
+            const int m = m0 + R, n = n0 + c * 4;
+            if (m >= M) continue;
+            float* dp = static_cast<float*>(D) + static_cast<int64_t>(m) * ldd + n;
+            if (vec_ok && n + 4 <= N) {
+                *reinterpret_cast<float4*>(dp) = v;
+            } else {
+                if (n + 0 < N) dp[0] = v.x;
+                if (n + 1 < N) dp[1] = v.y;
+                if (n + 2 < N) dp[2] = v.z;
+                if (n + 3 < N) dp[3] = v.w;
+            }
         }
     }
 }
@@ -553,17 +397,17 @@ hipError_t launch_typed(int64_t M, int64_t N, int64_t K, const uint8_t* a, const
     const int tiles_m = static_cast<int>((M + BM - 1) / BM);
     const int tiles_n = static_cast<int>((N + BN - 1) / BN);
     const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));
-    const int align = out == BSFP8_OUT_F32 ? 16 : 8;
-    const int vec_ok = (ldd % 4 == 0) && (reinterpret_cast<uintptr_t>(d) % align == 0);
+    // 16-byte row stores: row stride and base both 16-byte aligned
+    const int esize = out == BSFP8_OUT_F32 ? 4 : 2;
+    const int vec16 = ((ldd * esize) % 16 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0);
     if (out == BSFP8_OUT_F32)
-        hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, BSFP8_OUT_F32, true>), grid, dim3(kThreads), 0,
+        hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, BSFP8_OUT_F32>), grid, dim3(kThreads), 0,
                            stream, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
-                           a, sa, b, sb, d, ldd, tiles_m, tiles_n, vec_ok);
+                           a, sa, b, sb, d, ldd, tiles_m, tiles_n, vec16);
     else
-        hipLaunchKernelGGL((gemm_fp8_bf16_kernel<AF, BF>), grid, dim3(kThreads),
-                           0, stream, static_cast<int>(M), static_cast<int>(N),
-                           static_cast<int>(K), a, sa, b, sb, d, ldd, tiles_m, tiles_n,
-                           static_cast<int>((ldd % 8 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0)));
+        hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, BSFP8_OUT_BF16>), grid, dim3(kThreads), 0,
+                           stream, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
+                           a, sa, b, sb, d, ldd, tiles_m, tiles_n, vec16);
     return hipGetLastError();
 }
 
