@@ -11,6 +11,8 @@ Functions (same names as the C ABI):
   fp8_quantize_transposed(x, fmt="e4m3", tile_rows=128) -> (codes of x^T, scales)
   mxfp4_quantize(x) -> (packed, scales)
   scaled_gemm(a, a_scales, b, b_scales, a_fmt, b_fmt, out="bf16", d=None) -> d
+  scaled_gemm_ex(a, a_scales, b, b_scales, a_fmt, b_fmt, out="bf16", alpha=1.0,
+                 c=None, beta=0.0, d=None) -> d = alpha A B + beta C
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("BSFP8_LIB", os.path.join(_HERE, "libbsfp8.so"))
 
 FORMATS = {"e4m3": 0, "e5m2": 1, "mxfp4": 2}
-OUTS = {"f32": 0, "bf16": 1}
+OUTS = {"f32": 0, "bf16": 1, "f16": 2}
 STATUS = {0: "BSFP8_OK", 1: "BSFP8_ERR_INVALID_ARG", 2: "BSFP8_ERR_UNSUPPORTED",
           3: "BSFP8_ERR_HIP"}
 FP8_TILE_ROWS = 128
@@ -50,6 +52,9 @@ def lib() -> ctypes.CDLL:
     L.mxfp4_quantize.restype = c_int
     L.scaled_gemm.argtypes = [i64, i64, i64, c_int, vp, vp, c_int, vp, vp, c_int, vp, i64, vp]
     L.scaled_gemm.restype = c_int
+    L.scaled_gemm_ex.argtypes = [i64, i64, i64, c_int, vp, vp, c_int, vp, vp, ctypes.c_float, vp,
+                                 i64, ctypes.c_float, c_int, vp, i64, vp]
+    L.scaled_gemm_ex.restype = c_int
     L.bsfp8_status_string.argtypes = [c_int]
     L.bsfp8_status_string.restype = ctypes.c_char_p
     L.bsfp8_version.argtypes = []
@@ -130,22 +135,48 @@ def mxfp4_quantize(x, packed=None, scales=None):
     return packed, scales
 
 
+_OUT_DTYPES = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
+
+
 def scaled_gemm(a, a_scales, b, b_scales, a_fmt: str = "e4m3", b_fmt: str = "e4m3",
                 out: str = "bf16", d=None, K: Optional[int] = None):
     """D = deq(A) deq(B): A is M x K codes (M x K/2 packed for MXFP4), B is
-    N x K codes (a K x N column-major matrix).  Returns D (M x N, float32 or
-    bfloat16)."""
+    N x K codes (a K x N column-major matrix).  Returns D (M x N, float32,
+    bfloat16 or float16)."""
     import torch
     M = a.shape[0]
     N = b.shape[0]
     if K is None:
         K = a.shape[1] * (2 if a_fmt == "mxfp4" else 1)
     if d is None:
-        dt = torch.float32 if out == "f32" else torch.bfloat16
-        d = torch.empty((M, N), dtype=dt, device=a.device)
+        d = torch.empty((M, N), dtype=getattr(torch, _OUT_DTYPES[out]), device=a.device)
     ldd = d.stride(0) if M > 1 else N
     st = lib().scaled_gemm(M, N, K, FORMATS[a_fmt], _dev_ptr(a), _dev_ptr(a_scales),
                            FORMATS[b_fmt], _dev_ptr(b), _dev_ptr(b_scales), OUTS[out],
                            _dev_ptr(d), ldd, _stream(a))
     _check(st, "scaled_gemm")
+    return d
+
+
+def scaled_gemm_ex(a, a_scales, b, b_scales, a_fmt: str = "e4m3", b_fmt: str = "e4m3",
+                   out: str = "bf16", alpha: float = 1.0, c=None, beta: float = 0.0, d=None,
+                   K: Optional[int] = None):
+    """D = alpha deq(A) deq(B) + beta C.  C (M x N, the output dtype) is read
+    only when beta != 0; it may be d itself to accumulate in place."""
+    import torch
+    M = a.shape[0]
+    N = b.shape[0]
+    if K is None:
+        K = a.shape[1] * (2 if a_fmt == "mxfp4" else 1)
+    if d is None:
+        d = torch.empty((M, N), dtype=getattr(torch, _OUT_DTYPES[out]), device=a.device)
+    ldd = d.stride(0) if M > 1 else N
+    if c is None:
+        cptr, ldc = 0, 0
+    else:
+        cptr, ldc = _dev_ptr(c), (c.stride(0) if M > 1 else N)
+    st = lib().scaled_gemm_ex(M, N, K, FORMATS[a_fmt], _dev_ptr(a), _dev_ptr(a_scales),
+                              FORMATS[b_fmt], _dev_ptr(b), _dev_ptr(b_scales), float(alpha), cptr,
+                              ldc, float(beta), OUTS[out], _dev_ptr(d), ldd, _stream(a))
+    _check(st, "scaled_gemm_ex")
     return d

@@ -57,20 +57,24 @@ bsfp8_status mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
     return from_hip(bsfp8::launch_mxfp4_quantize(x, rows, k, ld, packed, scales, stream));
 }
 
-bsfp8_status scaled_gemm(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt, const void* a,
-                         const void* a_scales, bsfp8_format b_fmt, const void* b,
-                         const void* b_scales, bsfp8_out out, void* d, int64_t ldd,
-                         hipStream_t stream) {
+bsfp8_status scaled_gemm_ex(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt, const void* a,
+                            const void* a_scales, bsfp8_format b_fmt, const void* b,
+                            const void* b_scales, float alpha, const void* c, int64_t ldc,
+                            float beta, bsfp8_out out, void* d, int64_t ldd,
+                            hipStream_t stream) {
     const bool fp8 = is_fp8(a_fmt) && is_fp8(b_fmt);
     const bool mx = a_fmt == BSFP8_MXFP4 && b_fmt == BSFP8_MXFP4;
     if (!fp8 && !mx) return BSFP8_ERR_UNSUPPORTED;
-    if (out != BSFP8_OUT_F32 && out != BSFP8_OUT_BF16) return BSFP8_ERR_UNSUPPORTED;
+    if (out != BSFP8_OUT_F32 && out != BSFP8_OUT_BF16 && out != BSFP8_OUT_F16)
+        return BSFP8_ERR_UNSUPPORTED;
     if (M < 0 || N < 0 || K < 0 || (K % 32) != 0) return BSFP8_ERR_INVALID_ARG;
     if (M > kI32Max || N > kI32Max || K > kI32Max) return BSFP8_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return BSFP8_OK;
-    if (!d || ldd < N) return BSFP8_ERR_INVALID_ARG;
-    if (!aligned(d, out == BSFP8_OUT_F32 ? 4 : 2)) return BSFP8_ERR_INVALID_ARG;
-    if (K == 0) return from_hip(bsfp8::launch_fill_zero(M, N, out, d, ldd, stream));
+    const uintptr_t es = out == BSFP8_OUT_F32 ? 4 : 2;
+    if (!d || ldd < N || !aligned(d, es)) return BSFP8_ERR_INVALID_ARG;
+    if (beta != 0.0f && (!c || ldc < N || !aligned(c, es))) return BSFP8_ERR_INVALID_ARG;
+    const bsfp8::Epilogue ep{alpha, beta, beta != 0.0f ? c : nullptr, beta != 0.0f ? ldc : 0};
+    if (K == 0) return from_hip(bsfp8::launch_fill(M, N, out, d, ldd, ep, stream));
     if (!a || !b || !a_scales || !b_scales) return BSFP8_ERR_INVALID_ARG;
     if (!aligned(a, 16) || !aligned(b, 16)) return BSFP8_ERR_INVALID_ARG;
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
@@ -80,12 +84,20 @@ bsfp8_status scaled_gemm(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt, co
         return from_hip(bsfp8::launch_gemm_fp8(
             M, N, K, a_fmt, static_cast<const uint8_t*>(a), static_cast<const float*>(a_scales),
             b_fmt, static_cast<const uint8_t*>(b), static_cast<const float*>(b_scales), out, d,
-            ldd, stream));
+            ldd, ep, stream));
     }
     return from_hip(bsfp8::launch_gemm_mxfp4(
         M, N, K, static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(a_scales),
-        static_cast<const uint8_t*>(b), static_cast<const uint8_t*>(b_scales), out, d, ldd,
+        static_cast<const uint8_t*>(b), static_cast<const uint8_t*>(b_scales), out, d, ldd, ep,
         stream));
+}
+
+bsfp8_status scaled_gemm(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt, const void* a,
+                         const void* a_scales, bsfp8_format b_fmt, const void* b,
+                         const void* b_scales, bsfp8_out out, void* d, int64_t ldd,
+                         hipStream_t stream) {
+    return scaled_gemm_ex(M, N, K, a_fmt, a, a_scales, b_fmt, b, b_scales, 1.0f, nullptr, 0,
+                          0.0f, out, d, ldd, stream);
 }
 
 const char* bsfp8_status_string(bsfp8_status s) {
@@ -98,6 +110,6 @@ const char* bsfp8_status_string(bsfp8_status s) {
     }
 }
 
-int bsfp8_version(void) { return (0 << 16) | 1; }
+int bsfp8_version(void) { return (0 << 16) | 2; }
 
 }  // extern "C"

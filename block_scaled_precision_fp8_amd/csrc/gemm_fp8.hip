@@ -13,11 +13,11 @@
 // the MFMA temporaries and the resident accumulators play those roles).
 //
 // Two operand paths, chosen by output type:
-//  * bf16 output: v_mfma_f32_32x32x16_{fp8,bf8}_{fp8,bf8} on the codes.  These
+//  * bf16 / FP16 output: v_mfma_f32_32x32x16_{fp8,bf8}_{fp8,bf8} on the codes.  These
 //    instructions keep 13 bits below the largest product of a sum and truncate
 //    the rest (the behaviour "FP8 MMA internals on Hopper" models for H100,
 //    measured on gfx950), i.e. at most 2^-8 of sum |a b| per block: inside the
-//    2^-7 bf16 tolerance.
+//    2^-7 tolerance of the 16-bit outputs.
 //  * FP32 output: each fragment is widened exactly to bf16 (every E4M3/E5M2
 //    value is a normal bf16) right before v_mfma_f32_32x32x16_bf16, which keeps
 //    24 alignment bits: inside 2^-19.
@@ -120,13 +120,13 @@ constexpr int kDLds = 2 * kDStage;          // 64 KB: two workgroups per CU
 // Product of one 32 x 32 MFMA tile over one 32-wide K block.  Lane half h
 // holds K values 16h .. 16h+15 of its row in x (B, format BF) and y (A,
 // format AF); the first instruction takes the first 8, the second the next 8.
-//  * bf16 output: the FP8 codes go straight into the FP8 MFMA.
+//  * bf16 / FP16 output: the FP8 codes go straight into the FP8 MFMA.
 //  * FP32 output: the codes are widened exactly to bf16 and multiplied with the
 //    bf16 MFMA, which keeps 24 alignment bits instead of 13.
 template <int AF, int BF, int OUT>
 __device__ __forceinline__ v16f tile_product(const u32x4& x, const u32x4& y) {
     v16f p = v16f{};
-    if constexpr (OUT == BSFP8_OUT_BF16) {
+    if constexpr (OUT != BSFP8_OUT_F32) {
         const uint64_t xl = static_cast<uint64_t>(x[0]) | (static_cast<uint64_t>(x[1]) << 32);
         const uint64_t xh = static_cast<uint64_t>(x[2]) | (static_cast<uint64_t>(x[3]) << 32);
         const uint64_t yl = static_cast<uint64_t>(y[0]) | (static_cast<uint64_t>(y[1]) << 32);
@@ -144,7 +144,7 @@ template <int AF, int BF, int OUT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
     const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D,
-    int64_t ldd, int tiles_m, int tiles_n, int vec_ok) {
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kDLds];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -317,98 +317,103 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
-    // Epilogue through LDS (free now), so that each 64-lane store covers whole
-    // output rows instead of 32 rows x 16 bytes.  16-byte chunk c of LDS row R
-    // sits at c ^ (R & 15), which keeps the scattered writes and the row reads
-    // free of bank conflicts.
+    // Epilogue through LDS (free now): the tile is written in the MFMA layout
+    // and read back by rows, so that each 64-lane store covers whole output
+    // rows instead of 32 rows x 16 bytes.  16-byte chunk c of LDS row R sits at
+    // c ^ (R & 15), which keeps the scattered writes and the row reads free of
+    // bank conflicts.
     __syncthreads();
-    if constexpr (OUT == BSFP8_OUT_BF16) {
-        // 128 rows x 256 bytes; a store covers 4 rows
+    if constexpr (OUT != BSFP8_OUT_F32) {
+        if (ep.beta == 0.0f) {
+            // 16-bit output without C: alpha * acc converted while staged
+            // (128 rows x 256 bytes), a store covers 4 rows
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
+            for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 2; ++tj)
+                for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int R = wm * 64 + tj * 32 + frag_row;
-                    const int c = wn * 8 + ti * 4 + q;
-                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                    const bf16x4 v = {(__bf16)acc[ti][tj][4 * q + 0], (__bf16)acc[ti][tj][4 * q + 1],
-                                      (__bf16)acc[ti][tj][4 * q + 2], (__bf16)acc[ti][tj][4 * q + 3]};
-                    *reinterpret_cast<bf16x4*>(lds + R * 256 + ((c ^ (R & 15)) << 4) + 8 * half) = v;
-                }
-        __syncthreads();
+                    for (int q = 0; q < 4; ++q) {
+                        const int R = wm * 64 + tj * 32 + frag_row;
+                        const int c = wn * 8 + ti * 4 + q;
+                        const uint32_t h0 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 0]);
+                        const uint32_t h1 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 1]);
+                        const uint32_t h2 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 2]);
+                        const uint32_t h3 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 3]);
+                        *reinterpret_cast<uint2*>(lds + R * 256 + ((c ^ (R & 15)) << 4) + 8 * half) =
+                            make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                    }
+            __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int R = wave * 32 + i * 4 + (lane >> 4);
-            const int c = lane & 15;
-            const uint4 v = *reinterpret_cast<const uint4*>(lds + R * 256 + ((c ^ (R & 15)) << 4));
-            const int m = m0 + R, n = n0 + c * 8;
-            if (m >= M) continue;
-            uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
-            if (vec_ok && n + 8 <= N) {
-                *reinterpret_cast<uint4*>(dp) = v;
-            } else {
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (n + j < N) dp[j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
+            for (int i = 0; i < 8; ++i) {
+                const int R = wave * 32 + i * 4 + (lane >> 4);
+                const int c = lane & 15;
+                const uint4 w = *reinterpret_cast<const uint4*>(lds + R * 256 + ((c ^ (R & 15)) << 4));
+                store_half8(D, ldd, m0 + R, n0 + c * 8, M, N, vec_ok, w);
             }
+            return;
         }
-    } else {
-        // 128 rows x 512 bytes = the whole 64 KB; a store covers 2 rows
+    }
+    // General case: the FP32 tile (128 rows x 512 bytes, the whole 64 KB);
+    // alpha, beta * C and the output conversion are applied in the row phase.
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
+    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 2; ++tj)
+        for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int R = wm * 64 + tj * 32 + frag_row;
-                    const int c = wn * 16 + ti * 8 + q * 2 + half;
-                    *reinterpret_cast<float4*>(lds + R * 512 + ((c ^ (R & 15)) << 4)) =
-                        make_float4(acc[ti][tj][4 * q + 0], acc[ti][tj][4 * q + 1],
-                                    acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]);
-                }
-        __syncthreads();
+            for (int q = 0; q < 4; ++q) {
+                const int R = wm * 64 + tj * 32 + frag_row;
+                const int c = wn * 16 + ti * 8 + q * 2 + half;
+                *reinterpret_cast<float4*>(lds + R * 512 + ((c ^ (R & 15)) << 4)) =
+                    make_float4(acc[ti][tj][4 * q + 0], acc[ti][tj][4 * q + 1],
+                                acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]);
+            }
+    __syncthreads();
+    if constexpr (OUT == BSFP8_OUT_F32) {
+        // 4 values per lane: a store covers 2 rows
 #pragma unroll 4
         for (int i = 0; i < 16; ++i) {
             const int R = wave * 32 + i * 2 + (lane >> 5);
             const int c = lane & 31;
             const float4 v = *reinterpret_cast<const float4*>(lds + R * 512 + ((c ^ (R & 15)) << 4));
-            const int m = m0 + R, n = n0 + c * 4;
-            if (m >= M) continue;
-            float* dp = static_cast<float*>(D) + static_cast<int64_t>(m) * ldd + n;
-            if (vec_ok && n + 4 <= N) {
-                *reinterpret_cast<float4*>(dp) = v;
-            } else {
-                if (n + 0 < N) dp[0] = v.x;
-                if (n + 1 < N) dp[1] = v.y;
-                if (n + 2 < N) dp[2] = v.z;
-                if (n + 3 < N) dp[3] = v.w;
-            }
+            const float a4[4] = {v.x, v.y, v.z, v.w};
+            finish_row_chunk<OUT, 4>(D, ldd, ep, m0 + R, n0 + c * 4, M, N, vec_ok, a4);
+        }
+    } else {
+        // 8 values per lane: a store covers 4 rows
+#pragma unroll 4
+        for (int i = 0; i < 8; ++i) {
+            const int R = wave * 32 + i * 4 + (lane >> 4);
+            const int c = (lane & 15) * 2;
+            const float4 v0 = *reinterpret_cast<const float4*>(lds + R * 512 + ((c ^ (R & 15)) << 4));
+            const float4 v1 = *reinterpret_cast<const float4*>(lds + R * 512 + (((c + 1) ^ (R & 15)) << 4));
+            const float a8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            finish_row_chunk<OUT, 8>(D, ldd, ep, m0 + R, n0 + c * 4, M, N, vec_ok, a8);
         }
     }
+}
+
+template <int AF, int BF, int OUT>
+hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
+                      const uint8_t* b, const float* sb, void* d, int64_t ldd,
+                      const Epilogue& ep, hipStream_t stream) {
+    const int tiles_m = static_cast<int>((M + BM - 1) / BM);
+    const int tiles_n = static_cast<int>((N + BN - 1) / BN);
+    const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));
+    hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, OUT>), grid, dim3(kThreads), 0, stream,
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, sa, b, sb,
+                       d, ldd, ep, tiles_m, tiles_n, vec16_ok(OUT, d, ldd, ep));
+    return hipGetLastError();
 }
 
 template <int AF, int BF>
 hipError_t launch_typed(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
                         const uint8_t* b, const float* sb, int out, void* d, int64_t ldd,
-                        hipStream_t stream) {
-    const int tiles_m = static_cast<int>((M + BM - 1) / BM);
-    const int tiles_n = static_cast<int>((N + BN - 1) / BN);
-    const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));
-    // 16-byte row stores: row stride and base both 16-byte aligned
-    const int esize = out == BSFP8_OUT_F32 ? 4 : 2;
-    const int vec16 = ((ldd * esize) % 16 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0);
+                        const Epilogue& ep, hipStream_t stream) {
     if (out == BSFP8_OUT_F32)
-        hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, BSFP8_OUT_F32>), grid, dim3(kThreads), 0,
-                           stream, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
-                           a, sa, b, sb, d, ldd, tiles_m, tiles_n, vec16);
-    else
-        hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, BSFP8_OUT_BF16>), grid, dim3(kThreads), 0,
-                           stream, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
-                           a, sa, b, sb, d, ldd, tiles_m, tiles_n, vec16);
-    return hipGetLastError();
+        return launch_out<AF, BF, BSFP8_OUT_F32>(M, N, K, a, sa, b, sb, d, ldd, ep, stream);
+    if (out == BSFP8_OUT_BF16)
+        return launch_out<AF, BF, BSFP8_OUT_BF16>(M, N, K, a, sa, b, sb, d, ldd, ep, stream);
+    return launch_out<AF, BF, BSFP8_OUT_F16>(M, N, K, a, sa, b, sb, d, ldd, ep, stream);
 }
 
 }  // namespace
@@ -416,14 +421,14 @@ hipError_t launch_typed(int64_t M, int64_t N, int64_t K, const uint8_t* a, const
 hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,
                            const float* a_scales, int b_fmt, const uint8_t* b,
                            const float* b_scales, int out, void* d, int64_t ldd,
-                           hipStream_t stream) {
+                           const Epilogue& ep, hipStream_t stream) {
     if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E4M3)
-        return launch_typed<BSFP8_E4M3, BSFP8_E4M3>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, stream);
+        return launch_typed<BSFP8_E4M3, BSFP8_E4M3>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, stream);
     if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E5M2)
-        return launch_typed<BSFP8_E4M3, BSFP8_E5M2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, stream);
+        return launch_typed<BSFP8_E4M3, BSFP8_E5M2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, stream);
     if (a_fmt == BSFP8_E5M2 && b_fmt == BSFP8_E4M3)
-        return launch_typed<BSFP8_E5M2, BSFP8_E4M3>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, stream);
-    return launch_typed<BSFP8_E5M2, BSFP8_E5M2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, stream);
+        return launch_typed<BSFP8_E5M2, BSFP8_E4M3>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, stream);
+    return launch_typed<BSFP8_E5M2, BSFP8_E5M2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, stream);
 }
 
 }  // namespace bsfp8

@@ -47,40 +47,11 @@ __device__ __forceinline__ v16f mfma_fp4(uint4 x, uint4 y, uint32_t sx, uint32_t
                                                            static_cast<int>(sy));
 }
 
-// Store four consecutive output columns n..n+3 of row m (masked at the right edge).
-template <int OUT>
-__device__ __forceinline__ void store4(void* D, int64_t ldd, int m, int n, int N, int vec_ok,
-                                       float v0, float v1, float v2, float v3) {
-    if constexpr (OUT == BSFP8_OUT_F32) {
-        float* dp = static_cast<float*>(D) + static_cast<int64_t>(m) * ldd + n;
-        if (vec_ok && n + 3 < N) {
-            *reinterpret_cast<float4*>(dp) = make_float4(v0, v1, v2, v3);
-        } else {
-            if (n + 0 < N) dp[0] = v0;
-            if (n + 1 < N) dp[1] = v1;
-            if (n + 2 < N) dp[2] = v2;
-            if (n + 3 < N) dp[3] = v3;
-        }
-    } else {
-        uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
-        const uint32_t b0 = f32_to_bf16_rne(v0), b1 = f32_to_bf16_rne(v1);
-        const uint32_t b2 = f32_to_bf16_rne(v2), b3 = f32_to_bf16_rne(v3);
-        if (vec_ok && n + 3 < N) {
-            *reinterpret_cast<uint2*>(dp) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-        } else {
-            if (n + 0 < N) dp[0] = static_cast<uint16_t>(b0);
-            if (n + 1 < N) dp[1] = static_cast<uint16_t>(b1);
-            if (n + 2 < N) dp[2] = static_cast<uint16_t>(b2);
-            if (n + 3 < N) dp[3] = static_cast<uint16_t>(b3);
-        }
-    }
-}
-
 template <int OUT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
-    int64_t ldd, int tiles_m, int tiles_n, int vec_ok) {
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
 
     const int tid = threadIdx.x;
@@ -221,8 +192,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_kernel(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int n = n0 + wn * 64 + ti * 32 + q * 8 + half * 4;
-                store4<OUT>(D, ldd, m, n, N, vec_ok, acc[ti][tj][4 * q + 0], acc[ti][tj][4 * q + 1],
-                            acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]);
+                const float a4[4] = {acc[ti][tj][4 * q + 0], acc[ti][tj][4 * q + 1],
+                                     acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]};
+                finish_row_chunk<OUT, 4>(D, ldd, ep, m, n, M, N, vec_ok, a4);
             }
         }
 }
@@ -299,34 +271,6 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Store 16 bytes of one output row: 8 bf16 or 4 FP32 values starting at column
-// n (masked at the bottom and right edges; vector store when vec16 says the
-// row stride and base allow 16-byte alignment).
-template <int OUT>
-__device__ __forceinline__ void store_chunk16(void* D, int64_t ldd, int m, int n, int M, int N,
-                                              int vec16, uint4 v) {
-    if (m >= M) return;
-    constexpr int per = OUT == BSFP8_OUT_F32 ? 4 : 8;
-    if (vec16 && n + per <= N) {
-        uint8_t* p = static_cast<uint8_t*>(D) +
-                     (static_cast<int64_t>(m) * ldd + n) * (OUT == BSFP8_OUT_F32 ? 4 : 2);
-        *reinterpret_cast<uint4*>(p) = v;
-        return;
-    }
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    if constexpr (OUT == BSFP8_OUT_F32) {
-        float* dp = static_cast<float*>(D) + static_cast<int64_t>(m) * ldd + n;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (n + j < N) dp[j] = __uint_as_float(w[j]);
-    } else {
-        uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (n + j < N) dp[j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
-    }
-}
-
 // Large-tile LDS layout: per buffer, A then B, each 256 rows of 128 bytes
 // (unpadded, so that direct global-to-LDS loads can fill them).  Row R keeps
 // its 16-byte chunk g at position g ^ ((R >> 1) & 7): the 16 lanes of a
@@ -342,7 +286,7 @@ template <int OUT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
-    int64_t ldd, int tiles_m, int tiles_n, int vec_ok) {
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kDmaLdsBytes];
 
     const int tid = threadIdx.x;
@@ -515,102 +459,118 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
                    "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
 
     // Epilogue: the tile goes out through LDS (free now) so that every store
-    // instruction writes whole rows: a 64-lane store of 16 bytes per lane covers
-    // 1 KB of consecutive output, where the MFMA layout gives 32 rows of 16
-    // bytes.  16-byte chunk c of LDS row R sits at position c ^ (R & 15), which
-    // keeps both the scattered writes and the row reads free of bank conflicts.
+    // instruction writes whole rows (the MFMA layout would give 32 rows x 16
+    // bytes).  16-byte chunk c of LDS row R sits at c ^ (R & 15), which keeps
+    // both the scattered writes and the row reads free of bank conflicts.
     __syncthreads();
-    if constexpr (OUT == BSFP8_OUT_BF16) {
-        // 256 rows x 512 bytes = the whole 128 KB
+    if constexpr (OUT != BSFP8_OUT_F32) {
+        if (ep.beta == 0.0f) {
+            // 16-bit output without C: alpha * acc converted while staged,
+            // 256 rows x 512 bytes = the whole 128 KB in one pass
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+            for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
+                for (int tj = 0; tj < 4; ++tj)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int R = wm * 128 + tj * 32 + frag_row;
-                    const int c = wn * 16 + ti * 4 + q;
-                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                    const bf16x4 v = {(__bf16)acc[ti][tj][4 * q + 0], (__bf16)acc[ti][tj][4 * q + 1],
-                                      (__bf16)acc[ti][tj][4 * q + 2], (__bf16)acc[ti][tj][4 * q + 3]};
-                    *reinterpret_cast<bf16x4*>(lds + R * 512 + ((c ^ (R & 15)) << 4) + 8 * half) = v;
-                }
-        __syncthreads();
-#pragma unroll 4
-        for (int i = 0; i < 32; ++i) {
-            const int R = wave * 64 + 2 * i + half;
-            const int c = lane & 31;
-            const uint4 v = *reinterpret_cast<const uint4*>(lds + R * 512 + ((c ^ (R & 15)) << 4));
-            store_chunk16<OUT>(D, ldd, m0 + R, n0 + c * 8, M, N, vec_ok, v);
-        }
-    } else {
-        // two passes of 128 rows x 1 KB
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            if (wm == p) {
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                    for (int tj = 0; tj < 4; ++tj)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int R = tj * 32 + frag_row;
-                            const int c = wn * 32 + ti * 8 + q * 2 + half;
-                            *reinterpret_cast<float4*>(lds + R * 1024 + ((c ^ (R & 15)) << 4)) =
-                                make_float4(acc[ti][tj][4 * q + 0], acc[ti][tj][4 * q + 1],
-                                            acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]);
-                        }
-            }
+                    for (int q = 0; q < 4; ++q) {
+                        const int R = wm * 128 + tj * 32 + frag_row;
+                        const int c = wn * 16 + ti * 4 + q;
+                        const uint32_t h0 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 0]);
+                        const uint32_t h1 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 1]);
+                        const uint32_t h2 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 2]);
+                        const uint32_t h3 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 3]);
+                        *reinterpret_cast<uint2*>(lds + R * 512 + ((c ^ (R & 15)) << 4) + 8 * half) =
+                            make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                    }
             __syncthreads();
+#pragma unroll 4
+            for (int i = 0; i < 32; ++i) {
+                const int R = wave * 64 + 2 * i + half;
+                const int c = lane & 31;
+                const uint4 w = *reinterpret_cast<const uint4*>(lds + R * 512 + ((c ^ (R & 15)) << 4));
+                store_half8(D, ldd, m0 + R, n0 + c * 8, M, N, vec_ok, w);
+            }
+            return;
+        }
+    }
+    // General case: the FP32 tile in two passes of 128 rows x 1 KB; alpha,
+    // beta * C and the output conversion are applied in the row phase.
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        if (wm == p) {
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int R = tj * 32 + frag_row;
+                        const int c = wn * 32 + ti * 8 + q * 2 + half;
+                        *reinterpret_cast<float4*>(lds + R * 1024 + ((c ^ (R & 15)) << 4)) =
+                            make_float4(acc[ti][tj][4 * q + 0], acc[ti][tj][4 * q + 1],
+                                        acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]);
+                    }
+        }
+        __syncthreads();
+        if constexpr (OUT == BSFP8_OUT_F32) {
 #pragma unroll 4
             for (int i = 0; i < 32; ++i) {
                 const int R = wave * 32 + i;
                 const int c = lane;
-                const uint4 v = *reinterpret_cast<const uint4*>(lds + R * 1024 + ((c ^ (R & 15)) << 4));
-                store_chunk16<OUT>(D, ldd, m0 + p * 128 + R, n0 + c * 4, M, N, vec_ok, v);
+                const float4 v = *reinterpret_cast<const float4*>(lds + R * 1024 + ((c ^ (R & 15)) << 4));
+                const float a4[4] = {v.x, v.y, v.z, v.w};
+                finish_row_chunk<OUT, 4>(D, ldd, ep, m0 + p * 128 + R, n0 + c * 4, M, N, vec_ok, a4);
             }
-            __syncthreads();
+        } else {
+#pragma unroll 4
+            for (int i = 0; i < 16; ++i) {
+                const int R = wave * 32 + i * 2 + half;
+                const int c = (lane & 31) * 2;
+                const float4 v0 = *reinterpret_cast<const float4*>(lds + R * 1024 + ((c ^ (R & 15)) << 4));
+                const float4 v1 = *reinterpret_cast<const float4*>(lds + R * 1024 + (((c + 1) ^ (R & 15)) << 4));
+                const float a8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                finish_row_chunk<OUT, 8>(D, ldd, ep, m0 + p * 128 + R, n0 + c * 4, M, N, vec_ok, a8);
+            }
         }
+        __syncthreads();
     }
+}
+
+template <int OUT>
+hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* a_scales,
+                      const uint8_t* b, const uint8_t* b_scales, void* d, int64_t ldd,
+                      const Epilogue& ep, hipStream_t stream) {
+    const int vec = vec16_ok(OUT, d, ldd, ep);
+    const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    const bool fits32 = M * (K / 2) < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31);
+    if (K % 256 == 0 && big_tiles >= kBigTileThreshold && fits32) {
+        const int tm = static_cast<int>((M + 255) / 256), tn = static_cast<int>((N + 255) / 256);
+        const dim3 g(static_cast<uint32_t>(tm) * static_cast<uint32_t>(tn));
+        hipLaunchKernelGGL(gemm_mxfp4_big_kernel<OUT>, g, dim3(kThreads), 0, stream,
+                           static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
+                           a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
+        return hipGetLastError();
+    }
+    const int tiles_m = static_cast<int>((M + BM - 1) / BM);
+    const int tiles_n = static_cast<int>((N + BN - 1) / BN);
+    const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));
+    hipLaunchKernelGGL(gemm_mxfp4_kernel<OUT>, grid, dim3(kThreads), 0, stream,
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, a_scales,
+                       b, b_scales, d, ldd, ep, tiles_m, tiles_n, vec);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                              const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
-                             int out, void* d, int64_t ldd, hipStream_t stream) {
-    const int align = out == BSFP8_OUT_F32 ? 16 : 8;
-    const int vec_ok = (ldd % 4 == 0) && (reinterpret_cast<uintptr_t>(d) % align == 0);
-    const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    const bool fits32 = M * (K / 2) < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31);
-    if (K % 256 == 0 && big_tiles >= kBigTileThreshold && fits32) {
-        const int tm = static_cast<int>((M + 255) / 256), tn = static_cast<int>((N + 255) / 256);
-        const dim3 g(static_cast<uint32_t>(tm) * static_cast<uint32_t>(tn));
-        // 16-byte row stores: row stride and base both 16-byte aligned
-        const int esize = out == BSFP8_OUT_F32 ? 4 : 2;
-        const int vec16 = ((ldd * esize) % 16 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0);
-        if (out == BSFP8_OUT_F32)
-            hipLaunchKernelGGL(gemm_mxfp4_big_kernel<BSFP8_OUT_F32>, g, dim3(kThreads), 0, stream,
-                               static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
-                               a_scales, b, b_scales, d, ldd, tm, tn, vec16);
-        else
-            hipLaunchKernelGGL(gemm_mxfp4_big_kernel<BSFP8_OUT_BF16>, g, dim3(kThreads), 0, stream,
-                               static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
-                               a_scales, b, b_scales, d, ldd, tm, tn, vec16);
-        return hipGetLastError();
-    }
-    const int tiles_m = static_cast<int>((M + BM - 1) / BM);
-    const int tiles_n = static_cast<int>((N + BN - 1) / BN);
-    const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));
+                             int out, void* d, int64_t ldd, const Epilogue& ep,
+                             hipStream_t stream) {
     if (out == BSFP8_OUT_F32)
-        hipLaunchKernelGGL(gemm_mxfp4_kernel<BSFP8_OUT_F32>, grid, dim3(kThreads), 0, stream,
-                           static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
-                           a_scales, b, b_scales, d, ldd, tiles_m, tiles_n, vec_ok);
-    else
-        hipLaunchKernelGGL(gemm_mxfp4_kernel<BSFP8_OUT_BF16>, grid, dim3(kThreads), 0, stream,
-                           static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
-                           a_scales, b, b_scales, d, ldd, tiles_m, tiles_n, vec_ok);
-    return hipGetLastError();
+        return launch_out<BSFP8_OUT_F32>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+    if (out == BSFP8_OUT_BF16)
+        return launch_out<BSFP8_OUT_BF16>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+    return launch_out<BSFP8_OUT_F16>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
 }
 
 }  // namespace bsfp8

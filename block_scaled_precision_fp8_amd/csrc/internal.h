@@ -17,26 +17,139 @@ hipError_t launch_fp8_quantize_t(const float* x, int64_t k, int64_t rows, int64_
                                  uint8_t* codes, float* scales, hipStream_t stream);
 hipError_t launch_mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
                                  uint8_t* packed, uint8_t* scales, hipStream_t stream);
+// The GEMM epilogue: D = alpha * (A B) + beta * C, C of D's element type.
+// beta == 0 means C is not read (c may be null).
+struct Epilogue {
+    float alpha;
+    float beta;
+    const void* c;
+    int64_t ldc;
+};
+
 hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,
                            const float* a_scales, int b_fmt, const uint8_t* b,
                            const float* b_scales, int out, void* d, int64_t ldd,
-                           hipStream_t stream);
+                           const Epilogue& ep, hipStream_t stream);
 hipError_t launch_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                              const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
-                             int out, void* d, int64_t ldd, hipStream_t stream);
-hipError_t launch_fill_zero(int64_t M, int64_t N, int out, void* d, int64_t ldd,
-                            hipStream_t stream);
+                             int out, void* d, int64_t ldd, const Epilogue& ep,
+                             hipStream_t stream);
+// K = 0: D = beta * C (zeros when beta == 0).
+hipError_t launch_fill(int64_t M, int64_t N, int out, void* d, int64_t ldd, const Epilogue& ep,
+                       hipStream_t stream);
+// 16-byte row stores of D (and loads of C) are allowed: row strides and base
+// pointers all 16-byte aligned.
+inline int vec16_ok(int out, const void* d, int64_t ldd, const Epilogue& ep) {
+    const int64_t es = out == BSFP8_OUT_F32 ? 4 : 2;
+    const bool dok = (ldd * es) % 16 == 0 && reinterpret_cast<uintptr_t>(d) % 16 == 0;
+    const bool cok = ep.beta == 0.0f ||
+                     ((ep.ldc * es) % 16 == 0 && reinterpret_cast<uintptr_t>(ep.c) % 16 == 0);
+    return dok && cok ? 1 : 0;
+}
 
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------
 
-// FP32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // quiet NaN
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// Output element conversions, round to nearest even (FP16 overflows to +-inf).
+template <int OUT>
+__device__ __forceinline__ uint16_t to_half_bits(float v) {
+    if constexpr (OUT == BSFP8_OUT_BF16) return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+    else return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+template <int OUT>
+__device__ __forceinline__ float from_half_bits(uint16_t h) {
+    if constexpr (OUT == BSFP8_OUT_BF16) return __uint_as_float(static_cast<uint32_t>(h) << 16);
+    else return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Finish NV (4 or 8) consecutive outputs D[m][n .. n+NV-1]: v = alpha * acc
+// (+ beta * C), converted to the output type; masked at the edges, one
+// 16-byte store when vec allows (NV = 4 for FP32, 8 for 16-bit outputs).
+template <int OUT, int NV>
+__device__ __forceinline__ void finish_row_chunk(void* D, int64_t ldd, const Epilogue& ep, int m,
+                                                 int n, int M, int N, int vec, const float* acc) {
+    if (m >= M) return;
+    float v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = ep.alpha * acc[j];
+    const bool full = vec && n + NV <= N;
+    if (ep.beta != 0.0f) {
+        if constexpr (OUT == BSFP8_OUT_F32) {
+            const float* cp = static_cast<const float*>(ep.c) + static_cast<int64_t>(m) * ep.ldc + n;
+            if (full) {
+                const float4 c4 = *reinterpret_cast<const float4*>(cp);
+                v[0] = fmaf(ep.beta, c4.x, v[0]); v[1] = fmaf(ep.beta, c4.y, v[1]);
+                v[2] = fmaf(ep.beta, c4.z, v[2]); v[3] = fmaf(ep.beta, c4.w, v[3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+                    if (n + j < N) v[j] = fmaf(ep.beta, cp[j], v[j]);
+            }
+        } else {
+            const uint16_t* cp = static_cast<const uint16_t*>(ep.c) + static_cast<int64_t>(m) * ep.ldc + n;
+            if (full) {
+                uint32_t w[4];
+                if constexpr (NV == 8) {
+                    const uint4 c4 = *reinterpret_cast<const uint4*>(cp);
+                    w[0] = c4.x; w[1] = c4.y; w[2] = c4.z; w[3] = c4.w;
+                } else {
+                    const uint2 c2 = *reinterpret_cast<const uint2*>(cp);
+                    w[0] = c2.x; w[1] = c2.y; w[2] = 0u; w[3] = 0u;
+                }
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+                    v[j] = fmaf(ep.beta, from_half_bits<OUT>(static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)))), v[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+                    if (n + j < N) v[j] = fmaf(ep.beta, from_half_bits<OUT>(cp[j]), v[j]);
+            }
+        }
+    }
+    if constexpr (OUT == BSFP8_OUT_F32) {
+        float* dp = static_cast<float*>(D) + static_cast<int64_t>(m) * ldd + n;
+        if (full) {
+            *reinterpret_cast<float4*>(dp) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                if (n + j < N) dp[j] = v[j];
+        }
+    } else {
+        uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
+        uint16_t h[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) h[j] = to_half_bits<OUT>(v[j]);
+        if (full) {
+            if constexpr (NV == 8)
+                *reinterpret_cast<uint4*>(dp) =
+                    make_uint4(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16),
+                               h[4] | (static_cast<uint32_t>(h[5]) << 16), h[6] | (static_cast<uint32_t>(h[7]) << 16));
+            else
+                *reinterpret_cast<uint2*>(dp) =
+                    make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16));
+        } else {
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+                if (n + j < N) dp[j] = h[j];
+        }
+    }
+}
+
+// Store 8 already converted 16-bit outputs D[m][n .. n+7] (masked at the edges).
+__device__ __forceinline__ void store_half8(void* D, int64_t ldd, int m, int n, int M, int N,
+                                            int vec, uint4 w) {
+    if (m >= M) return;
+    uint16_t* dp = static_cast<uint16_t*>(D) + static_cast<int64_t>(m) * ldd + n;
+    if (vec && n + 8 <= N) {
+        *reinterpret_cast<uint4*>(dp) = w;
+        return;
+    }
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (n + j < N) dp[j] = static_cast<uint16_t>(ww[j >> 1] >> (16 * (j & 1)));
 }
 
 // Map a linear workgroup id to an output tile (tm, tn).

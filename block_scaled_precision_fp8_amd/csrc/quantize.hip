@@ -298,16 +298,25 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quantize_kernel(
     if ((c & 7) == 0) scales[r * (k >> 5) + (c >> 3)] = static_cast<uint8_t>(e + 127);
 }
 
-__global__ __launch_bounds__(kThreads) void fill_zero_kernel(int64_t M, int64_t N, int out,
-                                                              void* d, int64_t ldd) {
+// K = 0: D = beta * C, or zeros.
+template <int OUT>
+__global__ __launch_bounds__(kThreads) void fill_kernel(int64_t M, int64_t N, void* d, int64_t ldd,
+                                                         Epilogue ep) {
     const int64_t total = M * N;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
          i += static_cast<int64_t>(gridDim.x) * kThreads) {
         const int64_t r = i / N, c = i - r * N;
-        if (out == BSFP8_OUT_F32)
-            static_cast<float*>(d)[r * ldd + c] = 0.0f;
+        float v = 0.0f;
+        if (ep.beta != 0.0f) {
+            if constexpr (OUT == BSFP8_OUT_F32)
+                v = ep.beta * static_cast<const float*>(ep.c)[r * ep.ldc + c];
+            else
+                v = ep.beta * from_half_bits<OUT>(static_cast<const uint16_t*>(ep.c)[r * ep.ldc + c]);
+        }
+        if constexpr (OUT == BSFP8_OUT_F32)
+            static_cast<float*>(d)[r * ldd + c] = v;
         else
-            static_cast<uint16_t*>(d)[r * ldd + c] = 0;
+            static_cast<uint16_t*>(d)[r * ldd + c] = to_half_bits<OUT>(v);
     }
 }
 
@@ -354,14 +363,19 @@ hipError_t launch_mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_
     return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(int64_t M, int64_t N, int out, void* d, int64_t ldd,
-                            hipStream_t stream) {
+hipError_t launch_fill(int64_t M, int64_t N, int out, void* d, int64_t ldd, const Epilogue& ep,
+                       hipStream_t stream) {
     const int64_t total = M * N;
     if (total == 0) return hipSuccess;
     int64_t blocks = (total + kThreads - 1) / kThreads;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0,
-                       stream, M, N, out, d, ldd);
+    const dim3 g(static_cast<uint32_t>(blocks));
+    if (out == BSFP8_OUT_F32)
+        hipLaunchKernelGGL(fill_kernel<BSFP8_OUT_F32>, g, dim3(kThreads), 0, stream, M, N, d, ldd, ep);
+    else if (out == BSFP8_OUT_BF16)
+        hipLaunchKernelGGL(fill_kernel<BSFP8_OUT_BF16>, g, dim3(kThreads), 0, stream, M, N, d, ldd, ep);
+    else
+        hipLaunchKernelGGL(fill_kernel<BSFP8_OUT_F16>, g, dim3(kThreads), 0, stream, M, N, d, ldd, ep);
     return hipGetLastError();
 }
 

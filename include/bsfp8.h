@@ -47,7 +47,8 @@ typedef enum {
 
 typedef enum {
     BSFP8_OUT_F32 = 0,
-    BSFP8_OUT_BF16 = 1
+    BSFP8_OUT_BF16 = 1,
+    BSFP8_OUT_F16 = 2   /* IEEE binary16, round to nearest even, overflow to +-inf */
 } bsfp8_out;
 
 /*
@@ -125,21 +126,48 @@ bsfp8_status mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
  *   a: M x K/2 packed bytes; a_scales: E8M0 [M][K/32]
  *   b: N x K/2 packed bytes; b_scales: E8M0 [N][K/32]
  *   (the outputs of mxfp4_quantize).
- * out:  BSFP8_OUT_F32 or BSFP8_OUT_BF16 (round to nearest even).
- * d:    M x N row-major, leading dimension ldd >= N (elements).
+ * out:  BSFP8_OUT_F32, BSFP8_OUT_BF16 or BSFP8_OUT_F16 (the last two round
+ *       to nearest even; [CDNA4-FP8] section 4.4 writes 16-bit results to halve
+ *       the output traffic).
+ * d:    M x N row-major, leading dimension ldd >= N (elements), aligned to
+ *       its element size.
  * a, b must be 16-byte aligned.  K = 0 writes zeros.
  *
  * Accuracy: with S = sum_k |a_k b_k| (dequantised operands), every output
- * satisfies |D - exact| <= 2^-19 S for FP32 output and <= 2^-7 S for bf16
- * output on the synthetic workloads the library is tested on.  FP32 output
- * uses matrix instructions that keep 24 alignment bits per product sum;
- * bf16 output uses the FP8 instructions, which keep 13 (the truncation
- * studied for Hopper in [HOPPER-MMA] is present on gfx950 too).
+ * satisfies |D - exact| <= 2^-19 S for FP32 output and <= 2^-7 S for bf16 and
+ * FP16 output on the synthetic workloads the library is tested on.  FP32
+ * output uses matrix instructions that keep 24 alignment bits per product
+ * sum; 16-bit outputs use the FP8 instructions, which keep 13 (the
+ * truncation studied for Hopper in [HOPPER-MMA] is present on gfx950 too).
  */
 bsfp8_status scaled_gemm(int64_t M, int64_t N, int64_t K,
                          bsfp8_format a_fmt, const void* a, const void* a_scales,
                          bsfp8_format b_fmt, const void* b, const void* b_scales,
                          bsfp8_out out, void* d, int64_t ldd, hipStream_t stream);
+
+/*
+ * scaled_gemm_ex -- D = alpha * deq(A) deq(B) + beta * C (the alpha/beta
+ * epilogue of the CUTLASS argument list in [RUBIN-FP4] section 3.4).
+ *
+ * All arguments as for scaled_gemm, plus:
+ * alpha: scales the FP32 accumulator (alpha * acc is rounded to FP32).
+ * c:     M x N row-major, the same element type as d, leading dimension
+ *        ldc >= N, aligned to its element size.  Read only when beta != 0
+ *        (then it must not be null); it may be d itself (with ldc == ldd) to
+ *        accumulate in place.  Any other overlap of c and d is undefined.
+ * beta:  beta * C is added to alpha * acc with one FP32 fused multiply-add,
+ *        then the sum is converted to the output type.
+ * K = 0 writes beta * C (zeros when beta == 0).
+ * scaled_gemm(...) is scaled_gemm_ex(..., 1.0f, NULL, 0, 0.0f, ...).
+ *
+ * Accuracy: |D - (alpha exact + beta C)| <= tau (|alpha| S + |beta C|), with
+ * tau as for scaled_gemm (plus one FP32 rounding for FP32 output).
+ */
+bsfp8_status scaled_gemm_ex(int64_t M, int64_t N, int64_t K,
+                            bsfp8_format a_fmt, const void* a, const void* a_scales,
+                            bsfp8_format b_fmt, const void* b, const void* b_scales,
+                            float alpha, const void* c, int64_t ldc, float beta,
+                            bsfp8_out out, void* d, int64_t ldd, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* bsfp8_status_string(bsfp8_status s);

@@ -12,7 +12,7 @@ HEADER = os.path.join(ROOT, "include", "bsfp8.h")
 
 OK, INVALID, UNSUPPORTED = 0, 1, 2
 E4M3, E5M2, MXFP4 = 0, 1, 2
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 
 
 def declared_functions():
@@ -31,7 +31,7 @@ def L():
 def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("fp8_quantize", "fp8_quantize_transposed", "mxfp4_quantize", "scaled_gemm",
-              "bsfp8_status_string", "bsfp8_version"):
+              "scaled_gemm_ex", "bsfp8_status_string", "bsfp8_version"):
         assert n in names
 
 
@@ -106,3 +106,15 @@ def test_scaled_gemm_argument_checks(L):
     assert g(128, 128, 64, E4M3, P, P, E4M3, P, P, 5, P, 128, None) == UNSUPPORTED
     assert g(0, 128, 64, E4M3, 0, 0, E4M3, 0, 0, BF16, 0, 128, None) == OK      # empty
     assert g(128, 0, 64, E4M3, 0, 0, E4M3, 0, 0, F32, 0, 0, None) == OK
+
+
+
+def test_scaled_gemm_ex_argument_checks(L):
+    g = L.scaled_gemm_ex   # (M, N, K, af, a, sa, bf, b, sb, alpha, c, ldc, beta, out, d, ldd, stream)
+    ok = (128, 128, 64, E4M3, P, P, E4M3, P, P)
+    assert g(*ok, 1.0, 0, 0, 1.0, BF16, P, 128, None) == INVALID          # beta != 0, null C
+    assert g(*ok, 1.0, P, 100, 1.0, BF16, P, 128, None) == INVALID        # ldc < N
+    assert g(*ok, 1.0, P + 1, 128, 1.0, F16, P, 128, None) == INVALID     # C alignment
+    assert g(*ok, 1.0, P, 128, 0.5, 3, P, 128, None) == UNSUPPORTED       # bad output type
+    assert g(128, 128, 48, E4M3, P, P, E4M3, P, P, 1.0, 0, 0, 0.0, F32, P, 128, None) == INVALID
+    assert g(0, 128, 64, E4M3, 0, 0, E4M3, 0, 0, 1.0, 0, 0, 1.0, F16, 0, 128, None) == OK  # empty

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_common import check_gemm, from_dev, say, to_dev
+from gpu_common import check_gemm, check_gemm_ex, from_dev, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -78,7 +78,7 @@ def test_dot_examples_fp32_output_exact():
         assert abs(db[0, 0] - exact) <= 2.0 ** -7 * sum(abs(x * y) for x, y in zip(a, b))
 
 
-@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("fmts", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"),
                                   ("e5m2", "e5m2")])
 @pytest.mark.parametrize("M,N,K", [(200, 328, 96), (1, 1, 32), (129, 255, 64),
@@ -87,7 +87,7 @@ def test_fp8_small_ragged(M, N, K, fmts, out):
     full_check(M, N, K, fmts[0], fmts[1], out, seed=M * 7 + N * 3 + K, label="small")
 
 
-@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("M,N,K", [(200, 328, 96), (1, 1, 32), (129, 255, 64),
                                    (256, 256, 512), (130, 260, 288), (64, 64, 2080)])
 def test_mxfp4_small_ragged(M, N, K, out):
@@ -171,7 +171,7 @@ def test_workload_end_to_end(name):
     check_gemm(d[ii, jj], dr, sr, w.out, name + " end-to-end")
 
 
-@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("fmts,M,N,K", [
     (("mxfp4", "mxfp4"), 2088, 2072, 512),     # 256 x 256 MXFP4 kernel, ragged edges
     (("mxfp4", "mxfp4"), 2048, 2048, 768),
@@ -182,3 +182,60 @@ def test_medium_ragged_large_tile_kernels(fmts, M, N, K, out):
     """Shapes big enough for the large-tile kernels, with partial edge tiles,
     compared in full against the oracle."""
     full_check(M, N, K, fmts[0], fmts[1], out, seed=M + N + K, label="medium")
+
+
+_TORCH_DT = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fmts,M,N,K", [
+    (("e4m3", "e4m3"), 200, 328, 160),
+    (("e5m2", "e4m3"), 2088, 2072, 512),     # FP8 kernel, ragged edges
+    (("mxfp4", "mxfp4"), 130, 260, 288),      # small MXFP4 kernel
+    (("mxfp4", "mxfp4"), 2088, 2072, 512),    # 256 x 256 MXFP4 kernel
+])
+def test_alpha_beta_epilogue(fmts, M, N, K, out):
+    """D = alpha A B + beta C through scaled_gemm_ex, C in the output type;
+    then in place (C is D) with beta = 1; then beta = 0 (C not read)."""
+    import torch
+    a_fmt, b_fmt = fmts
+    seed = M + 3 * N + K
+    a = workloads.normal(seed, M, K) * np.float32(2.0)
+    b = workloads.normal(seed + 1, N, K)
+    qa, sa = oracle_quant(a, a_fmt)
+    qb, sb = oracle_quant(b, b_fmt)
+    dr, sr = oracle.gemm_rows(a_fmt, qa, sa, b_fmt, qb, sb)
+    dt = getattr(torch, _TORCH_DT[out])
+    c = (torch.from_numpy(workloads.normal(seed + 2, M, N) * np.float32(30.0))).to(dt).cuda()
+    c_host = from_dev(c)
+    bs = bsfp8()
+    args = (to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), a_fmt, b_fmt, out)
+    say(f"scaled_gemm_ex alpha/beta {M}x{N}x{K} {a_fmt}x{b_fmt} -> {out}")
+    d = bs.scaled_gemm_ex(*args, alpha=-0.75, c=c, beta=1.5, K=K)
+    torch.cuda.synchronize()
+    check_gemm_ex(from_dev(d), dr, sr, -0.75, 1.5, c_host, out, "alpha/beta")
+    # in place: D <- 0.5 A B + D
+    d2 = c.clone()
+    bs.scaled_gemm_ex(*args, alpha=0.5, c=d2, beta=1.0, d=d2, K=K)
+    torch.cuda.synchronize()
+    check_gemm_ex(from_dev(d2), dr, sr, 0.5, 1.0, c_host, out, "in place")
+    # beta = 0: C is not read (NaN-filled C must not leak into D)
+    junk = torch.full_like(c, float("nan"))
+    d3 = bs.scaled_gemm_ex(*args, alpha=2.0, c=junk, beta=0.0, K=K)
+    torch.cuda.synchronize()
+    check_gemm_ex(from_dev(d3), dr, sr, 2.0, 0.0, None, out, "beta = 0")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+def test_k_zero_writes_beta_c(out):
+    import torch
+    dt = getattr(torch, _TORCH_DT[out])
+    c = torch.from_numpy(workloads.normal(9, 130, 70)).to(dt).cuda()
+    e = torch.zeros((130, 0), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((2, 0), dtype=torch.float32, device="cuda")
+    say(f"scaled_gemm_ex K = 0 -> {out}")
+    d = bsfp8().scaled_gemm_ex(e, s, e[:70], s[:1], "e4m3", "e4m3", out, alpha=3.0, c=c,
+                               beta=-2.0, K=0)
+    torch.cuda.synchronize()
+    expect = (-2.0 * c.float()).to(dt)   # one FP32 product, then the output rounding
+    assert torch.equal(d, expect)
