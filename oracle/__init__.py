@@ -16,7 +16,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB points the pins at another build of oracle.c (the mutation tests
+# build copies with planted mistakes and check that some pin fails).
+_LIB_PATH = os.environ.get("ORACLE_LIB", os.path.join(_HERE, "liboracle.so"))
 
 _FMT = {"e4m3": 0, "e5m2": 1, "e2m1": 2, "e8m0": 3, "mxfp4": 2}
 FP8_TILE_ROWS = 128

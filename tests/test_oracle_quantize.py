@@ -134,3 +134,35 @@ def test_mxfp4_packing_low_nibble_first():
     assert scales[0, 0] == 127
     assert packed[0, 0] == (0x1 | (0x7 << 4))       # 0.5 low, 6 high
     assert packed[0, 1] == (0xA | (0x5 << 4))       # -1 low, 3 high
+
+
+# fl32(x / s) lands exactly on an E4M3 rounding midpoint, while x * fl32(1 / s)
+# lands one FP32 step off it, towards the odd neighbour.  The quantiser divides
+# (the pages divide each element by the scale), so the tie goes to the even
+# code.  Bit patterns of the codes from the E4M3 definition (3 mantissa bits:
+# 8 values per binade): 1.0 = 0x38, 1.125 = 0x39, 1.25 = 0x3A, 3.0 = 0x44,
+# 3.25 = 0x45, 96 = 0x6C, 104 = 0x6D.
+# (amax bits, x bits, midpoint, even code, odd code); cases found by a search
+# over random tiles in numpy float32.
+DIVISION_TIES = [
+    (0x4178B033, 0x3D16FD44, 1.0625, 0x38, 0x39),
+    (0x4BC1FA3E, 0x4783A0AA, 1.1875, 0x3A, 0x39),
+    (0x3CED1854, 0x3BD3B127, 100.0, 0x6C, 0x6D),
+    (0x3F4D4E11, 0x3BB74ED9, 3.125, 0x44, 0x45),
+]
+
+
+def test_fp8_quotient_is_a_division_not_a_reciprocal_product():
+    for amax_bits, x_bits, mid, even, odd in DIVISION_TIES:
+        amax = np.array([amax_bits], dtype=np.uint32).view(np.float32)[0]
+        x = np.array([x_bits], dtype=np.uint32).view(np.float32)[0]
+        s = np.float32(amax / np.float32(448.0))
+        assert np.float32(x / s) == np.float32(mid)                       # an exact tie
+        assert np.float32(x * np.float32(np.float32(1.0) / s)) != np.float32(mid)
+        tile = np.zeros((128, 32), dtype=np.float32)
+        tile[0, 0] = amax
+        tile[1, 0] = x
+        tile[2, 0] = -x
+        codes, scales = oracle.fp8_quantize(tile, "e4m3")
+        assert scales[0, 0] == s
+        assert codes[1, 0] == even and codes[2, 0] == (even | 0x80), (hex(codes[1, 0]), hex(odd))
