@@ -1,0 +1,152 @@
+"""Python side of the matrix-core probe (test instrument).
+
+`dot(instr, a, b, c, sa=None, sb=None)` evaluates one dot product per row of the
+numpy arrays `a` and `b` (operand storage as described for `mfma_probe_dot` in
+mfma_probe.hip) with a single gfx950 MFMA instruction and returns the FP32
+results.  `encode_*` turn exactly representable values into operand bit
+patterns; they reject anything that would need rounding, so every probe input
+is the value the test states.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmfmaprobe.so")
+
+FP8_FP8, FP8_BF8, BF8_FP8, BF8_BF8, BF16, SCALE_FP4, SCALE_E4M3, SCALE_E5M2 = range(8)
+# instruction -> (A element format, B element format, K)
+INSTR = {
+    FP8_FP8: ("e4m3", "e4m3", 16), FP8_BF8: ("e4m3", "e5m2", 16),
+    BF8_FP8: ("e5m2", "e4m3", 16), BF8_BF8: ("e5m2", "e5m2", 16),
+    BF16: ("bf16", "bf16", 16), SCALE_FP4: ("e2m1", "e2m1", 64),
+    SCALE_E4M3: ("e4m3", "e4m3", 64), SCALE_E5M2: ("e5m2", "e5m2", 64),
+}
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not built; run tests/mfma_probe/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        L.mfma_probe_dot.argtypes = [ctypes.c_int, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp]
+        L.mfma_probe_dot.restype = ctypes.c_int
+        L.mfma_probe_k.argtypes = [ctypes.c_int]
+        L.mfma_probe_k.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------- encoders
+def _minifloat_values(ebits, mbits, bias, has_inf_nan_exp):
+    """code -> value for the non-negative codes of a small float format."""
+    vals = {}
+    for e in range(1 << ebits):
+        for m in range(1 << mbits):
+            code = (e << mbits) | m
+            if has_inf_nan_exp == "ieee" and e == (1 << ebits) - 1:
+                continue
+            if has_inf_nan_exp == "fn" and e == (1 << ebits) - 1 and m == (1 << mbits) - 1:
+                continue
+            if e == 0:
+                v = math.ldexp(m, 1 - bias - mbits)
+            else:
+                v = math.ldexp((1 << mbits) | m, e - bias - mbits)
+            vals[code] = v
+    return vals
+
+
+_TABLES = {
+    "e4m3": (_minifloat_values(4, 3, 7, "fn"), 0x80),
+    "e5m2": (_minifloat_values(5, 2, 15, "ieee"), 0x80),
+    "e2m1": (_minifloat_values(2, 1, 1, "none"), 0x8),
+}
+_REVERSE = {f: {v: c for c, v in t.items()} for f, (t, _) in _TABLES.items()}
+
+
+def encode(fmt, v):
+    """Exact code of value v in fmt ('e4m3', 'e5m2', 'e2m1', 'bf16')."""
+    v = float(v)
+    if fmt == "bf16":
+        u = int(np.array([v], dtype=np.float32).view(np.uint32)[0])
+        if float(np.float32(v)) != v or (u & 0xFFFF):
+            raise ValueError(f"{v!r} is not a bf16 value")
+        return u >> 16
+    table, sign = _REVERSE[fmt], _TABLES[fmt][1]
+    mag = abs(v)
+    if mag not in table:
+        raise ValueError(f"{v!r} is not an {fmt} value")
+    code = table[mag]
+    return code | sign if math.copysign(1.0, v) < 0 else code
+
+
+def representable(fmt, v):
+    try:
+        encode(fmt, v)
+        return True
+    except ValueError:
+        return False
+
+
+def pack_operand(fmt, rows, K):
+    """rows: list of length-K value lists -> operand storage for one side."""
+    n = len(rows)
+    if fmt == "bf16":
+        out = np.zeros((n, K), dtype=np.uint16)
+        for i, r in enumerate(rows):
+            for k, v in enumerate(r):
+                out[i, k] = encode(fmt, v)
+        return out
+    if fmt == "e2m1":
+        out = np.zeros((n, K // 2), dtype=np.uint8)
+        for i, r in enumerate(rows):
+            for k, v in enumerate(r):
+                out[i, k // 2] |= encode(fmt, v) << (4 * (k & 1))
+        return out
+    out = np.zeros((n, K), dtype=np.uint8)
+    for i, r in enumerate(rows):
+        for k, v in enumerate(r):
+            out[i, k] = encode(fmt, v)
+    return out
+
+
+# ---------------------------------------------------------------- evaluation
+def dot(instr, a, b, c, sa=None, sb=None, device="cuda:0"):
+    """Run the instruction on every case; a, b: operand storage (numpy), c: FP32 per case."""
+    import torch
+
+    n = a.shape[0]
+    c = np.ascontiguousarray(np.asarray(c, dtype=np.float32).reshape(n))
+    dev = torch.device(device)
+    ta = torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1).copy()).to(dev)
+    tb = torch.from_numpy(np.ascontiguousarray(b).view(np.uint8).reshape(-1).copy()).to(dev)
+    tc = torch.from_numpy(c.copy()).to(dev)
+    td = torch.full((n,), float("nan"), dtype=torch.float32, device=dev)
+    if instr >= SCALE_FP4:
+        if sa is None or sb is None:
+            raise ValueError("scaled instructions need E8M0 scales for both operands")
+        tsa = torch.from_numpy(np.ascontiguousarray(sa, dtype=np.uint8).reshape(-1).copy()).to(dev)
+        tsb = torch.from_numpy(np.ascontiguousarray(sb, dtype=np.uint8).reshape(-1).copy()).to(dev)
+        psa, psb = tsa.data_ptr(), tsb.data_ptr()
+    else:
+        psa = psb = None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().mfma_probe_dot(instr, n, ta.data_ptr(), tb.data_ptr(), psa, psb, tc.data_ptr(),
+                              td.data_ptr(), stream)
+    if rc != 0:
+        raise RuntimeError(f"mfma_probe_dot returned {rc}")
+    torch.cuda.synchronize(dev)
+    return td.cpu().numpy()
+
+
+def dot_values(instr, xs, ys, cs, sa=None, sb=None):
+    """Like dot() but from lists of exactly representable values (zero-padded to K)."""
+    fa, fb, K = INSTR[instr]
+    pad = lambda rows: [list(r) + [0.0] * (K - len(r)) for r in rows]
+    return dot(instr, pack_operand(fa, pad(xs), K), pack_operand(fb, pad(ys), K), cs, sa, sb)

@@ -118,3 +118,19 @@ def test_scaled_gemm_ex_argument_checks(L):
     assert g(*ok, 1.0, P, 128, 0.5, 3, P, 128, None) == UNSUPPORTED       # bad output type
     assert g(128, 128, 48, E4M3, P, P, E4M3, P, P, 1.0, 0, 0, 0.0, F32, P, 128, None) == INVALID
     assert g(0, 128, 64, E4M3, 0, 0, E4M3, 0, 0, 1.0, 0, 0, 1.0, F16, 0, 128, None) == OK  # empty
+
+
+def test_mfma_probe_loads_and_rejects_bad_arguments():
+    """The matrix-core test probe (a test instrument) loads without a GPU and
+    rejects bad arguments before any launch."""
+    import mfma_probe
+    P = mfma_probe.lib()
+    assert [P.mfma_probe_k(i) for i in range(8)] == [16, 16, 16, 16, 16, 64, 64, 64]
+    assert P.mfma_probe_k(8) == 0 and P.mfma_probe_k(-1) == 0
+    buf = ctypes.create_string_buffer(256)
+    p = ctypes.addressof(buf)
+    assert P.mfma_probe_dot(8, 1, p, p, None, None, p, p, None) == 1      # unknown instruction
+    assert P.mfma_probe_dot(0, -1, p, p, None, None, p, p, None) == 1     # negative count
+    assert P.mfma_probe_dot(0, 1, None, p, None, None, p, p, None) == 1   # null operand
+    assert P.mfma_probe_dot(5, 1, p, p, None, p, p, p, None) == 1         # scaled without scales
+    assert P.mfma_probe_dot(0, 0, None, None, None, None, None, None, None) == 0   # nothing to do
