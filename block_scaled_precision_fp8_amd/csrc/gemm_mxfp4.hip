@@ -282,7 +282,11 @@ constexpr int kDmaStageBytes = 2 * kDmaOperandBytes;     // 64 KB
 constexpr int kDmaLdsBytes = 2 * kDmaStageBytes;         // 128 KB
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int OUT>
+// STAGE16: 16-bit output with beta == 0, converted while staged (one pass).
+// It is a template parameter rather than a branch on beta so that each
+// instantiation holds only one epilogue: with both, the 256 live accumulators
+// at the branch spilled to scratch.
+template <int OUT, bool STAGE16>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
@@ -463,8 +467,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     // bytes).  16-byte chunk c of LDS row R sits at c ^ (R & 15), which keeps
     // both the scattered writes and the row reads free of bank conflicts.
     __syncthreads();
-    if constexpr (OUT != BSFP8_OUT_F32) {
-        if (ep.beta == 0.0f) {
+    if constexpr (STAGE16) {
+        static_assert(OUT != BSFP8_OUT_F32, "converted staging is for 16-bit outputs");
+        {
             // 16-bit output without C: alpha * acc converted while staged,
             // 256 rows x 512 bytes = the whole 128 KB in one pass
 #pragma unroll
@@ -546,7 +551,15 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const u
     if (K % 256 == 0 && big_tiles >= kBigTileThreshold && fits32) {
         const int tm = static_cast<int>((M + 255) / 256), tn = static_cast<int>((N + 255) / 256);
         const dim3 g(static_cast<uint32_t>(tm) * static_cast<uint32_t>(tn));
-        hipLaunchKernelGGL(gemm_mxfp4_big_kernel<OUT>, g, dim3(kThreads), 0, stream,
+        if constexpr (OUT != BSFP8_OUT_F32) {
+            if (ep.beta == 0.0f) {
+                hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, true>), g, dim3(kThreads), 0, stream,
+                                   static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
+                                   a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
+                return hipGetLastError();
+            }
+        }
+        hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, false>), g, dim3(kThreads), 0, stream,
                            static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
                            a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
         return hipGetLastError();
