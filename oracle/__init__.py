@@ -46,6 +46,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_mx_exponent.restype = c_int
         L.oracle_fp8_quantize.argtypes = [vp, i64, i64, i64, i64, c_int, vp, vp]
         L.oracle_fp8_quantize.restype = c_int
+        L.oracle_fp8_quantize_groups.argtypes = [vp, i64, i64, i64, i64, i64, c_int, vp, vp]
+        L.oracle_fp8_quantize_groups.restype = c_int
         L.oracle_mxfp4_quantize.argtypes = [vp, i64, i64, i64, vp, vp]
         L.oracle_mxfp4_quantize.restype = c_int
         L.oracle_gemm_rows.argtypes = [i64, i64, i64, i64, c_int, vp, vp, c_int, vp, vp,
@@ -105,6 +107,64 @@ def fp8_quantize(x: np.ndarray, fmt: str = "e4m3", tile_rows: int = FP8_TILE_ROW
     if rc != 0:
         raise ValueError(f"oracle_fp8_quantize rc={rc}")
     return codes, scales
+
+
+GRANULARITIES = ("tile", "row", "tensor")
+
+
+def _group_shape(granularity: str, rows: int, k: int):
+    """(group_rows, group_k) of one scale: tile 128 x 32, row 1 x k, tensor rows x k."""
+    if granularity == "tile":
+        return FP8_TILE_ROWS, 32
+    if granularity == "row":
+        return 1, max(k, 1)
+    if granularity == "tensor":
+        return max(rows, 1), max(k, 1)
+    raise ValueError(f"unknown granularity {granularity!r}")
+
+
+def fp8_quantize_granular(x: np.ndarray, fmt: str = "e4m3", granularity: str = "tile"):
+    """FP8 quantisation with one scale per 128 x 32 tile ("tile"), per row of x
+    ("row": per row of an A operand, per column of a B operand stored N x K)
+    or for all of x ("tensor").  Returns (codes uint8 rows x k, scales float32:
+    [ceil(rows/128)][ceil(k/32)], [rows] or [1])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, k = x.shape
+    gr, gk = _group_shape(granularity, rows, k)
+    codes = np.zeros((rows, k), dtype=np.uint8)
+    scales = np.zeros(((rows + gr - 1) // gr, (k + gk - 1) // gk), dtype=np.float32)
+    rc = lib().oracle_fp8_quantize_groups(_ptr(x), rows, k, k, gr, gk, _FMT[fmt],
+                                          _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_fp8_quantize_groups rc={rc}")
+    if granularity == "row":
+        scales = scales.reshape(rows)
+    elif granularity == "tensor":
+        scales = np.ones(1, dtype=np.float32) if rows * k == 0 else scales.reshape(1)
+    return codes, scales
+
+
+def dequantize_granular(fmt: str, q: np.ndarray, scales: np.ndarray, granularity: str):
+    """Dequantised FP8 operand in fp64 (rows x K) for any granularity."""
+    if granularity == "tile":
+        return dequantize(fmt, q, scales)
+    t = decode_table(fmt)
+    vals = t[np.asarray(q).astype(np.int64)]
+    s = np.asarray(scales, dtype=np.float64)
+    if granularity == "row":
+        return vals * s.reshape(-1, 1)
+    if granularity == "tensor":
+        return vals * s.reshape(1)[0]
+    raise ValueError(f"unknown granularity {granularity!r}")
+
+
+def gemm_granular(a_fmt, a, a_scales, a_gran, b_fmt, b, b_scales, b_gran):
+    """D = deq(A) deq(B)^T and S = |deq(A)| |deq(B)|^T in fp64, for FP8 operands of
+    any granularity (A: M x K codes, B: N x K codes).  The fp64 products of the
+    dequantised operands are exact; the sums round at most K 2^-53 S."""
+    ad = dequantize_granular(a_fmt, a, a_scales, a_gran)
+    bd = dequantize_granular(b_fmt, b, b_scales, b_gran)
+    return ad @ bd.T, np.abs(ad) @ np.abs(bd).T
 
 
 def mxfp4_quantize(x: np.ndarray):

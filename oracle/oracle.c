@@ -154,29 +154,33 @@ void oracle_encode_array(int fmt, const double* v, int64_t n, uint8_t* codes) {
 }
 
 /* ------------------------------------------------------------------------ */
-/* FP8 per-tile quantisation  ([CDNA4-FP8] sections 3.3 and 4.2)            */
+/* FP8 quantisation with per-tile, per-row or per-tensor scales             */
+/* ([CDNA4-FP8] sections 3.3 and 4.2; the granularities of section 3.3)     */
 /* ------------------------------------------------------------------------ */
 
 static float fp8_denominator(int fmt) { return fmt == ORC_E4M3 ? 448.0f : 57344.0f; }
 
-/* x: rows x k FP32, row stride ld.  Tiles are tile_rows x 32 along (row, k);
- * edge tiles may be partial.  codes: rows x k (stride k).  scales: FP32
- * [ceil(rows / tile_rows)][ceil(k / 32)], K-block index fastest.
- * Per tile: amax = max |x|; s = fl32(amax / F) (1.0 if that is zero);
- * code = encode(fl32(x / s)). */
-int oracle_fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
-                        int64_t tile_rows, int fmt, uint8_t* codes, float* scales) {
+/* x: rows x k FP32, row stride ld.  One scale per group of group_rows x
+ * group_k elements along (row, k); edge groups may be partial.  codes: rows x
+ * k (stride k).  scales: FP32 [ceil(rows / group_rows)][ceil(k / group_k)],
+ * K-group index fastest.
+ * Per group: amax = max |x|; s = fl32(amax / F) (1.0 if that is zero);
+ * code = encode(fl32(x / s)).
+ * Per tile: group 128 x 32.  Per row: 1 x k.  Per tensor: rows x k. */
+int oracle_fp8_quantize_groups(const float* x, int64_t rows, int64_t k, int64_t ld,
+                               int64_t group_rows, int64_t group_k, int fmt, uint8_t* codes,
+                               float* scales) {
     if (fmt != ORC_E4M3 && fmt != ORC_E5M2) return -1;
-    if (rows < 0 || k < 0 || ld < k || tile_rows < 1) return -1;
+    if (rows < 0 || k < 0 || ld < k || group_rows < 1 || group_k < 1) return -1;
     build_tables();
     const float F = fp8_denominator(fmt);
-    int64_t tr = (rows + tile_rows - 1) / tile_rows;
-    int64_t tk = (k + 31) / 32;
+    int64_t tr = (rows + group_rows - 1) / group_rows;
+    int64_t tk = (k + group_k - 1) / group_k;
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t ti = 0; ti < tr; ++ti) {
         for (int64_t tj = 0; tj < tk; ++tj) {
-            int64_t r0 = ti * tile_rows, r1 = r0 + tile_rows < rows ? r0 + tile_rows : rows;
-            int64_t c0 = tj * 32, c1 = c0 + 32 < k ? c0 + 32 : k;
+            int64_t r0 = ti * group_rows, r1 = r0 + group_rows < rows ? r0 + group_rows : rows;
+            int64_t c0 = tj * group_k, c1 = c0 + group_k < k ? c0 + group_k : k;
             float amax = 0.0f;
             for (int64_t r = r0; r < r1; ++r)
                 for (int64_t c = c0; c < c1; ++c) {
@@ -194,6 +198,12 @@ int oracle_fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
         }
     }
     return 0;
+}
+
+/* Per-tile scales: tiles of tile_rows x 32. */
+int oracle_fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
+                        int64_t tile_rows, int fmt, uint8_t* codes, float* scales) {
+    return oracle_fp8_quantize_groups(x, rows, k, ld, tile_rows, 32, fmt, codes, scales);
 }
 
 /* ------------------------------------------------------------------------ */

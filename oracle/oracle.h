@@ -21,6 +21,9 @@ int oracle_mx_exponent(double amax);
 
 int oracle_fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
                         int64_t tile_rows, int fmt, uint8_t* codes, float* scales);
+int oracle_fp8_quantize_groups(const float* x, int64_t rows, int64_t k, int64_t ld,
+                               int64_t group_rows, int64_t group_k, int fmt, uint8_t* codes,
+                               float* scales);
 int oracle_mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
                           uint8_t* packed, uint8_t* scales);
 

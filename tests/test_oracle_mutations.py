@@ -13,7 +13,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ORACLE_C = os.path.join(ROOT, "oracle", "oracle.c")
-PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_quantize.py", "tests/test_oracle_gemm.py"]
+PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_quantize.py", "tests/test_oracle_gemm.py",
+        "tests/test_oracle_granular.py"]
 
 # (name, text in oracle.c, replacement): each a mistake someone could make.
 # Left out as equivalent (no result can differ): reading both GEMM operands'
@@ -39,8 +40,11 @@ MUTATIONS = [
      "            scales[ti * tk + tj] = s;"),
     ("reciprocal-multiply", "float q = x[r * ld + c] / s;  /* IEEE binary32 division */",
      "float q = x[r * ld + c] * (1.0f / s);"),
-    ("tile-columns-64", "int64_t c0 = tj * 32, c1 = c0 + 32 < k ? c0 + 32 : k;",
-     "int64_t c0 = tj * 32, c1 = c0 + 64 < k ? c0 + 64 : k;"),
+    ("tile-columns-64", "oracle_fp8_quantize_groups(x, rows, k, ld, tile_rows, 32, fmt, codes, scales)",
+     "oracle_fp8_quantize_groups(x, rows, k, ld, tile_rows, 64, fmt, codes, scales)"),
+    ("group-column-end", "int64_t c0 = tj * group_k, c1 = c0 + group_k < k ? c0 + group_k : k;",
+     "int64_t c0 = tj * group_k, c1 = c0 + group_k < k ? c0 + group_k : k - 1;"),
+    ("group-row-start", "int64_t r0 = ti * group_rows, r1", "int64_t r0 = ti * group_rows + (ti > 0), r1"),
     ("mx-exponent-clamp", "if (e < -127) e = -127;", "if (e < -126) e = -126;"),
     ("mx-exponent-off-by-one", "    if (e > 127) e = 127;\n    return e;",
      "    if (e > 127) e = 127;\n    return e + 1;"),
