@@ -25,6 +25,7 @@ LIB_PATH = os.environ.get("BSFP8_LIB", os.path.join(_HERE, "libbsfp8.so"))
 
 FORMATS = {"e4m3": 0, "e5m2": 1, "mxfp4": 2}
 OUTS = {"f32": 0, "bf16": 1, "f16": 2}
+GRANULARITIES = {"tile": 0, "row": 1, "tensor": 2, "mx32": 3}
 STATUS = {0: "BSFP8_OK", 1: "BSFP8_ERR_INVALID_ARG", 2: "BSFP8_ERR_UNSUPPORTED",
           3: "BSFP8_ERR_HIP"}
 FP8_TILE_ROWS = 128
@@ -55,6 +56,11 @@ def lib() -> ctypes.CDLL:
     L.scaled_gemm_ex.argtypes = [i64, i64, i64, c_int, vp, vp, c_int, vp, vp, ctypes.c_float, vp,
                                  i64, ctypes.c_float, c_int, vp, i64, vp]
     L.scaled_gemm_ex.restype = c_int
+    L.fp8_quantize_granular.argtypes = [vp, i64, i64, i64, c_int, c_int, vp, vp, vp]
+    L.fp8_quantize_granular.restype = c_int
+    L.scaled_gemm_granular.argtypes = [i64, i64, i64, c_int, vp, vp, c_int, c_int, vp, vp, c_int,
+                                       ctypes.c_float, vp, i64, ctypes.c_float, c_int, vp, i64, vp]
+    L.scaled_gemm_granular.restype = c_int
     L.bsfp8_status_string.argtypes = [c_int]
     L.bsfp8_status_string.restype = ctypes.c_char_p
     L.bsfp8_version.argtypes = []
@@ -118,6 +124,28 @@ def fp8_quantize_transposed(x, fmt: str = "e4m3", tile_rows: int = FP8_TILE_ROWS
     _check(st, "fp8_quantize_transposed")
     return codes, scales
 
+def fp8_quantize_granular(x, fmt: str = "e4m3", granularity: str = "tile", codes=None, scales=None):
+    """Quantise a rows x k FP32 CUDA tensor to FP8 with one scale per 128 x 32
+    tile ("tile"), per row ("row"; per column for a B operand stored N x K) or
+    for the whole tensor ("tensor").  Scales: [ceil(rows/128)][k/32], [rows]
+    or [1] float32."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 CUDA tensor with unit column stride")
+    rows, k = x.shape
+    if codes is None:
+        codes = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        shape = {"tile": ((rows + FP8_TILE_ROWS - 1) // FP8_TILE_ROWS, (k + 31) // 32),
+                 "row": (rows,), "tensor": (1,)}[granularity]
+        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    st = lib().fp8_quantize_granular(_dev_ptr(x), rows, k, x.stride(0) if rows > 1 else k,
+                                     GRANULARITIES[granularity], FORMATS[fmt], _dev_ptr(codes),
+                                     _dev_ptr(scales), _stream(x))
+    _check(st, "fp8_quantize_granular")
+    return codes, scales
+
+
 def mxfp4_quantize(x, packed=None, scales=None):
     """Quantise a rows x k FP32 CUDA tensor to packed E2M1 (two per byte)
     with one E8M0 scale byte per 32-element block of a row."""
@@ -179,4 +207,30 @@ def scaled_gemm_ex(a, a_scales, b, b_scales, a_fmt: str = "e4m3", b_fmt: str = "
                               FORMATS[b_fmt], _dev_ptr(b), _dev_ptr(b_scales), float(alpha), cptr,
                               ldc, float(beta), OUTS[out], _dev_ptr(d), ldd, _stream(a))
     _check(st, "scaled_gemm_ex")
+    return d
+
+
+def scaled_gemm_granular(a, a_scales, b, b_scales, a_fmt: str = "e4m3", b_fmt: str = "e4m3",
+                         a_gran: str = "tile", b_gran: str = "tile", out: str = "bf16",
+                         alpha: float = 1.0, c=None, beta: float = 0.0, d=None,
+                         K: Optional[int] = None):
+    """scaled_gemm_ex with a scale granularity per operand ("tile", "row",
+    "tensor" for FP8; "mx32" for MXFP4)."""
+    import torch
+    M = a.shape[0]
+    N = b.shape[0]
+    if K is None:
+        K = a.shape[1] * (2 if a_fmt == "mxfp4" else 1)
+    if d is None:
+        d = torch.empty((M, N), dtype=getattr(torch, _OUT_DTYPES[out]), device=a.device)
+    ldd = d.stride(0) if M > 1 else N
+    if c is None:
+        cptr, ldc = 0, 0
+    else:
+        cptr, ldc = _dev_ptr(c), (c.stride(0) if M > 1 else N)
+    st = lib().scaled_gemm_granular(M, N, K, FORMATS[a_fmt], _dev_ptr(a), _dev_ptr(a_scales),
+                                    GRANULARITIES[a_gran], FORMATS[b_fmt], _dev_ptr(b),
+                                    _dev_ptr(b_scales), GRANULARITIES[b_gran], float(alpha), cptr,
+                                    ldc, float(beta), OUTS[out], _dev_ptr(d), ldd, _stream(a))
+    _check(st, "scaled_gemm_granular")
     return d

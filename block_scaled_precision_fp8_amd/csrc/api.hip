@@ -46,6 +46,24 @@ bsfp8_status fp8_quantize_transposed(const float* x, int64_t k, int64_t rows, in
     return from_hip(bsfp8::launch_fp8_quantize_t(x, k, rows, ld, fmt, codes, scales, stream));
 }
 
+bsfp8_status fp8_quantize_granular(const float* x, int64_t rows, int64_t k, int64_t ld,
+                                   bsfp8_granularity g, bsfp8_format fmt, uint8_t* codes,
+                                   float* scales, hipStream_t stream) {
+    if (g == BSFP8_GRAN_TILE) return fp8_quantize(x, rows, k, ld, 128, fmt, codes, scales, stream);
+    if (g != BSFP8_GRAN_ROW && g != BSFP8_GRAN_TENSOR) return BSFP8_ERR_UNSUPPORTED;
+    if (!is_fp8(fmt)) return BSFP8_ERR_UNSUPPORTED;
+    if (rows < 0 || k < 0 || ld < k || (k % 32) != 0) return BSFP8_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return BSFP8_OK;
+    if (!x || !codes || !scales) return BSFP8_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || (ld % 4) != 0 || !aligned(codes, 4) || !aligned(scales, 4))
+        return BSFP8_ERR_INVALID_ARG;
+    if (g == BSFP8_GRAN_ROW) {
+        if ((rows + 3) / 4 > kI32Max) return BSFP8_ERR_INVALID_ARG;
+        return from_hip(bsfp8::launch_fp8_quantize_rows(x, rows, k, ld, fmt, codes, scales, stream));
+    }
+    return from_hip(bsfp8::launch_fp8_quantize_tensor(x, rows, k, ld, fmt, codes, scales, stream));
+}
+
 bsfp8_status mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
                             uint8_t* packed, uint8_t* scales, hipStream_t stream) {
     if (rows < 0 || k < 0 || ld < k || (k % 32) != 0) return BSFP8_ERR_INVALID_ARG;
@@ -57,16 +75,37 @@ bsfp8_status mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
     return from_hip(bsfp8::launch_mxfp4_quantize(x, rows, k, ld, packed, scales, stream));
 }
 
-bsfp8_status scaled_gemm_ex(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt, const void* a,
-                            const void* a_scales, bsfp8_format b_fmt, const void* b,
-                            const void* b_scales, float alpha, const void* c, int64_t ldc,
-                            float beta, bsfp8_out out, void* d, int64_t ldd,
-                            hipStream_t stream) {
+bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt,
+                                  const void* a, const void* a_scales, bsfp8_granularity a_g,
+                                  bsfp8_format b_fmt, const void* b, const void* b_scales,
+                                  bsfp8_granularity b_g, float alpha, const void* c, int64_t ldc,
+                                  float beta, bsfp8_out out, void* d, int64_t ldd,
+                                  hipStream_t stream) {
     const bool fp8 = is_fp8(a_fmt) && is_fp8(b_fmt);
     const bool mx = a_fmt == BSFP8_MXFP4 && b_fmt == BSFP8_MXFP4;
     if (!fp8 && !mx) return BSFP8_ERR_UNSUPPORTED;
     if (out != BSFP8_OUT_F32 && out != BSFP8_OUT_BF16 && out != BSFP8_OUT_F16)
         return BSFP8_ERR_UNSUPPORTED;
+    // which kernel: per-tile FP8 (0), FP8 with scales constant along K (1), MXFP4 (2)
+    int path;
+    int tensor_mask = 0;
+    if (mx) {
+        if (a_g != BSFP8_GRAN_MX32 || b_g != BSFP8_GRAN_MX32) return BSFP8_ERR_UNSUPPORTED;
+        path = 2;
+    } else {
+        const auto fp8_g = [](bsfp8_granularity g) {
+            return g == BSFP8_GRAN_TILE || g == BSFP8_GRAN_ROW || g == BSFP8_GRAN_TENSOR;
+        };
+        if (!fp8_g(a_g) || !fp8_g(b_g)) return BSFP8_ERR_UNSUPPORTED;
+        if (a_g != BSFP8_GRAN_TILE && b_g != BSFP8_GRAN_TILE) {
+            path = 1;
+        } else {
+            // per-tile scales on one side: the other side may be per tile or per tensor
+            if (a_g == BSFP8_GRAN_ROW || b_g == BSFP8_GRAN_ROW) return BSFP8_ERR_UNSUPPORTED;
+            path = 0;
+            tensor_mask = (a_g == BSFP8_GRAN_TENSOR ? 1 : 0) | (b_g == BSFP8_GRAN_TENSOR ? 2 : 0);
+        }
+    }
     if (M < 0 || N < 0 || K < 0 || (K % 32) != 0) return BSFP8_ERR_INVALID_ARG;
     if (M > kI32Max || N > kI32Max || K > kI32Max) return BSFP8_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return BSFP8_OK;
@@ -79,17 +118,34 @@ bsfp8_status scaled_gemm_ex(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt,
     if (!aligned(a, 16) || !aligned(b, 16)) return BSFP8_ERR_INVALID_ARG;
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles > kI32Max) return BSFP8_ERR_INVALID_ARG;
-    if (fp8) {
-        if (!aligned(a_scales, 4) || !aligned(b_scales, 4)) return BSFP8_ERR_INVALID_ARG;
-        return from_hip(bsfp8::launch_gemm_fp8(
-            M, N, K, a_fmt, static_cast<const uint8_t*>(a), static_cast<const float*>(a_scales),
-            b_fmt, static_cast<const uint8_t*>(b), static_cast<const float*>(b_scales), out, d,
-            ldd, ep, stream));
-    }
-    return from_hip(bsfp8::launch_gemm_mxfp4(
-        M, N, K, static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(a_scales),
-        static_cast<const uint8_t*>(b), static_cast<const uint8_t*>(b_scales), out, d, ldd, ep,
-        stream));
+    const uint8_t* a8 = static_cast<const uint8_t*>(a);
+    const uint8_t* b8 = static_cast<const uint8_t*>(b);
+    if (path == 2)
+        return from_hip(bsfp8::launch_gemm_mxfp4(M, N, K, a8, static_cast<const uint8_t*>(a_scales), b8,
+                                                 static_cast<const uint8_t*>(b_scales), out, d, ldd, ep,
+                                                 stream));
+    if (!aligned(a_scales, 4) || !aligned(b_scales, 4)) return BSFP8_ERR_INVALID_ARG;
+    const float* sa = static_cast<const float*>(a_scales);
+    const float* sb = static_cast<const float*>(b_scales);
+    if (path == 0)
+        return from_hip(bsfp8::launch_gemm_fp8(M, N, K, a_fmt, a8, sa, b_fmt, b8, sb, out, d, ldd, ep,
+                                               stream, tensor_mask));
+    // the K-constant kernel addresses a 256-row band of an operand with 32-bit offsets
+    if (K >= (int64_t(1) << 23)) return BSFP8_ERR_UNSUPPORTED;
+    return from_hip(bsfp8::launch_gemm_fp8_outer(M, N, K, a_fmt, a8, sa, a_g == BSFP8_GRAN_ROW ? 1 : 0,
+                                                 b_fmt, b8, sb, b_g == BSFP8_GRAN_ROW ? 1 : 0, out, d,
+                                                 ldd, ep, stream));
+}
+
+bsfp8_status scaled_gemm_ex(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt, const void* a,
+                            const void* a_scales, bsfp8_format b_fmt, const void* b,
+                            const void* b_scales, float alpha, const void* c, int64_t ldc,
+                            float beta, bsfp8_out out, void* d, int64_t ldd,
+                            hipStream_t stream) {
+    const bsfp8_granularity g = a_fmt == BSFP8_MXFP4 ? BSFP8_GRAN_MX32 : BSFP8_GRAN_TILE;
+    const bsfp8_granularity gb = b_fmt == BSFP8_MXFP4 ? BSFP8_GRAN_MX32 : BSFP8_GRAN_TILE;
+    return scaled_gemm_granular(M, N, K, a_fmt, a, a_scales, g, b_fmt, b, b_scales, gb, alpha, c,
+                                ldc, beta, out, d, ldd, stream);
 }
 
 bsfp8_status scaled_gemm(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt, const void* a,
@@ -110,6 +166,6 @@ const char* bsfp8_status_string(bsfp8_status s) {
     }
 }
 
-int bsfp8_version(void) { return (0 << 16) | 2; }
+int bsfp8_version(void) { return (0 << 16) | 3; }
 
 }  // extern "C"

@@ -145,7 +145,7 @@ template <int AF, int BF, int OUT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
     const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D,
-    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok, int tensor_mask) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kDLds];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -200,17 +200,32 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
         }
 
     // scales of a stage: 4 floats of A's tile row and 4 of B's, loaded one stage ahead
+    // An operand with one scale per tensor (bit 0 of tensor_mask: A, bit 1: B)
+    // has a one-float scale array: its stage loads read past that float as
+    // zero and are not used; sa0 / sb0 stand in for them.
+    const bool a_tensor = (tensor_mask & 1) != 0;
+    const bool b_tensor = (tensor_mask & 2) != 0;
     const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(sA), 0, static_cast<int>(tiles_m) * nkb * 4, 0x00020000);
+        const_cast<float*>(sA), 0, a_tensor ? 4 : static_cast<int>(tiles_m) * nkb * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(sB), 0, static_cast<int>(tiles_n) * nkb * 4, 0x00020000);
-    const uint32_t so_a = static_cast<uint32_t>(tm) * nkb * 4;
-    const uint32_t so_b = static_cast<uint32_t>(tn) * nkb * 4;
+        const_cast<float*>(sB), 0, b_tensor ? 4 : static_cast<int>(tiles_n) * nkb * 4, 0x00020000);
+    const uint32_t so_a = a_tensor ? 0u : static_cast<uint32_t>(tm) * nkb * 4;
+    const uint32_t so_b = b_tensor ? 0u : static_cast<uint32_t>(tn) * nkb * 4;
+    const float sa0 = sA[0];
+    const float sb0 = sB[0];
+    auto sigma = [&](uint32_t a_bits, uint32_t b_bits) {
+        return (a_tensor ? sa0 : __uint_as_float(a_bits)) * (b_tensor ? sb0 : __uint_as_float(b_bits));
+    };
     u32x4 nsa, nsb;
+    // The stage offset goes in the scalar offset, which the range check does
+    // not cover; a per-tensor side keeps it at zero so that its loads stay
+    // inside the one-float array (the rest of the 16 bytes reads as zero).
     auto load_scales = [&](int stage) {
         const int so = min(stage, last) * 16;
-        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsa) : "v"(so_a), "s"(rs_sa), "s"(so) : "memory");
-        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsb) : "v"(so_b), "s"(rs_sb), "s"(so) : "memory");
+        const int so_sa = a_tensor ? 0 : so;
+        const int so_sb = b_tensor ? 0 : so;
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsa) : "v"(so_a), "s"(rs_sa), "s"(so_sa) : "memory");
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsb) : "v"(so_b), "s"(rs_sb), "s"(so_sb) : "memory");
     };
 
     v16f acc[2][2];
@@ -240,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
         asm volatile("" : "+v"(ca), "+v"(cbv));
         float sig[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) sig[k] = __uint_as_float(ca[k]) * __uint_as_float(cbv[k]);
+        for (int k = 0; k < 4; ++k) sig[k] = sigma(ca[k], cbv[k]);
         load_scales(s + 1);
 
         auto block = [&](auto KB) {
@@ -264,14 +279,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
             // the MFMAs below may only start after the prefetch is issued
             asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(g[0]), "+v"(g[1]));
             {
-                const float sigma = sig[kb];
+                const float sig_kb = sig[kb];
 #pragma unroll
                 for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                     for (int tj = 0; tj < 2; ++tj) {
                         const v16f p = tile_product<AF, BF, OUT>(f[ti], g[tj]);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sigma, p[r], acc[ti][tj][r]);
+                        for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sig_kb, p[r], acc[ti][tj][r]);
                     }
             }
             // close the block: its promotions finish before the next block's reads
@@ -305,14 +320,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
             }
             // the MFMAs consume the fragments only after the wait above
             asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
-            const float sigma = __uint_as_float(ca[kb]) * __uint_as_float(cbv[kb]);
+            const float sig_kb = sigma(ca[kb], cbv[kb]);
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                 for (int tj = 0; tj < 2; ++tj) {
                     const v16f p = tile_product<AF, BF, OUT>(x[ti], y[tj]);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sigma, p[r], acc[ti][tj][r]);
+                    for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sig_kb, p[r], acc[ti][tj][r]);
                 }
         }
     }
@@ -396,25 +411,25 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
 template <int AF, int BF, int OUT>
 hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
                       const uint8_t* b, const float* sb, void* d, int64_t ldd,
-                      const Epilogue& ep, hipStream_t stream) {
+                      const Epilogue& ep, int tensor_mask, hipStream_t stream) {
     const int tiles_m = static_cast<int>((M + BM - 1) / BM);
     const int tiles_n = static_cast<int>((N + BN - 1) / BN);
     const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));
     hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, OUT>), grid, dim3(kThreads), 0, stream,
                        static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, sa, b, sb,
-                       d, ldd, ep, tiles_m, tiles_n, vec16_ok(OUT, d, ldd, ep));
+                       d, ldd, ep, tiles_m, tiles_n, vec16_ok(OUT, d, ldd, ep), tensor_mask);
     return hipGetLastError();
 }
 
 template <int AF, int BF>
 hipError_t launch_typed(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
                         const uint8_t* b, const float* sb, int out, void* d, int64_t ldd,
-                        const Epilogue& ep, hipStream_t stream) {
+                        const Epilogue& ep, int tm, hipStream_t stream) {
     if (out == BSFP8_OUT_F32)
-        return launch_out<AF, BF, BSFP8_OUT_F32>(M, N, K, a, sa, b, sb, d, ldd, ep, stream);
+        return launch_out<AF, BF, BSFP8_OUT_F32>(M, N, K, a, sa, b, sb, d, ldd, ep, tm, stream);
     if (out == BSFP8_OUT_BF16)
-        return launch_out<AF, BF, BSFP8_OUT_BF16>(M, N, K, a, sa, b, sb, d, ldd, ep, stream);
-    return launch_out<AF, BF, BSFP8_OUT_F16>(M, N, K, a, sa, b, sb, d, ldd, ep, stream);
+        return launch_out<AF, BF, BSFP8_OUT_BF16>(M, N, K, a, sa, b, sb, d, ldd, ep, tm, stream);
+    return launch_out<AF, BF, BSFP8_OUT_F16>(M, N, K, a, sa, b, sb, d, ldd, ep, tm, stream);
 }
 
 }  // namespace
@@ -422,14 +437,14 @@ hipError_t launch_typed(int64_t M, int64_t N, int64_t K, const uint8_t* a, const
 hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,
                            const float* a_scales, int b_fmt, const uint8_t* b,
                            const float* b_scales, int out, void* d, int64_t ldd,
-                           const Epilogue& ep, hipStream_t stream) {
+                           const Epilogue& ep, hipStream_t stream, int tensor_mask) {
     if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E4M3)
-        return launch_typed<BSFP8_E4M3, BSFP8_E4M3>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, stream);
+        return launch_typed<BSFP8_E4M3, BSFP8_E4M3>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, stream);
     if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E5M2)
-        return launch_typed<BSFP8_E4M3, BSFP8_E5M2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, stream);
+        return launch_typed<BSFP8_E4M3, BSFP8_E5M2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, stream);
     if (a_fmt == BSFP8_E5M2 && b_fmt == BSFP8_E4M3)
-        return launch_typed<BSFP8_E5M2, BSFP8_E4M3>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, stream);
-    return launch_typed<BSFP8_E5M2, BSFP8_E5M2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, stream);
+        return launch_typed<BSFP8_E5M2, BSFP8_E4M3>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, stream);
+    return launch_typed<BSFP8_E5M2, BSFP8_E5M2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, stream);
 }
 
 }  // namespace bsfp8

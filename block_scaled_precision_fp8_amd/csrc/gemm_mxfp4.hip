@@ -14,15 +14,13 @@
 // 64 x 64 (2 x 2 MFMA tiles), A and B staged through padded LDS rows of 128
 // bytes (256 K values) in two buffers; B is the MFMA row operand so each lane
 // holds 4 consecutive output columns for vector stores.
-#include "internal.h"
-
-#include <utility>
+#include "big_tile.h"
 
 namespace bsfp8 {
 
 namespace {
 
-typedef float v16f __attribute__((ext_vector_type(16)));
+using namespace big_tile;
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
@@ -212,28 +210,6 @@ constexpr int kBigOperandBytes = 256 * kStride;
 constexpr int kBigStageBytes = 2 * kBigOperandBytes;
 constexpr int kBigLdsBytes = 2 * kBigStageBytes;     // 147456 bytes
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint8_t lds_byte;
-
-// The main loop of the large-tile kernel issues its LDS traffic and MFMAs as
-// volatile inline assembly: volatile statements keep their program order, so
-// the fragment reads for the next K step, the staging writes and the MFMAs of
-// the current step interleave exactly as written (the compiler would otherwise
-// sink every read next to its first use and stall each MFMA on LDS latency).
-// The compiler does not track LDS completions of these statements, so each
-// consumer is preceded by an explicit lgkmcnt wait.
-template <int OFF>
-__device__ __forceinline__ void lds_read16(u32x4& v, uint32_t addr) {
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-}
-template <int OFF>
-__device__ __forceinline__ void lds_write16(uint32_t addr, const u32x4& v) {
-    asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
-}
-__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void lds_wait_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 // E2M1 x E2M1 MFMA with E8M0 block scales; byte SEL of each scale register is used.
 template <int SEL>
 __device__ __forceinline__ void mfma_fp4_sel(v16f& acc, const u32x4& x, const u32x4& y, uint32_t sx,
@@ -260,15 +236,6 @@ __device__ __forceinline__ void gather_scales(uint32_t& w0, uint32_t& w1, uint32
         : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
         : "v"(s0.x), "v"(s0.y), "v"(s1.x), "v"(s1.y), "v"(s2.x), "v"(s2.y), "v"(s3.x),
           "v"(s3.y), "v"(sel));
-}
-
-template <int... I, typename F>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Large-tile LDS layout: per buffer, A then B, each 256 rows of 128 bytes
@@ -462,83 +429,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
                    "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
                    "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
 
-    // Epilogue: the tile goes out through LDS (free now) so that every store
-    // instruction writes whole rows (the MFMA layout would give 32 rows x 16
-    // bytes).  16-byte chunk c of LDS row R sits at c ^ (R & 15), which keeps
-    // both the scattered writes and the row reads free of bank conflicts.
-    __syncthreads();
-    if constexpr (STAGE16) {
-        static_assert(OUT != BSFP8_OUT_F32, "converted staging is for 16-bit outputs");
-        {
-            // 16-bit output without C: alpha * acc converted while staged,
-            // 256 rows x 512 bytes = the whole 128 KB in one pass
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                for (int tj = 0; tj < 4; ++tj)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int R = wm * 128 + tj * 32 + frag_row;
-                        const int c = wn * 16 + ti * 4 + q;
-                        const uint32_t h0 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 0]);
-                        const uint32_t h1 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 1]);
-                        const uint32_t h2 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 2]);
-                        const uint32_t h3 = to_half_bits<OUT>(ep.alpha * acc[ti][tj][4 * q + 3]);
-                        *reinterpret_cast<uint2*>(lds + R * 512 + ((c ^ (R & 15)) << 4) + 8 * half) =
-                            make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-                    }
-            __syncthreads();
-#pragma unroll 4
-            for (int i = 0; i < 32; ++i) {
-                const int R = wave * 64 + 2 * i + half;
-                const int c = lane & 31;
-                const uint4 w = *reinterpret_cast<const uint4*>(lds + R * 512 + ((c ^ (R & 15)) << 4));
-                store_half8(D, ldd, m0 + R, n0 + c * 8, M, N, vec_ok, w);
-            }
-            return;
-        }
-    }
-    // General case: the FP32 tile in two passes of 128 rows x 1 KB; alpha,
-    // beta * C and the output conversion are applied in the row phase.
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        if (wm == p) {
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                for (int tj = 0; tj < 4; ++tj)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int R = tj * 32 + frag_row;
-                        const int c = wn * 32 + ti * 8 + q * 2 + half;
-                        *reinterpret_cast<float4*>(lds + R * 1024 + ((c ^ (R & 15)) << 4)) =
-                            make_float4(acc[ti][tj][4 * q + 0], acc[ti][tj][4 * q + 1],
-                                        acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]);
-                    }
-        }
-        __syncthreads();
-        if constexpr (OUT == BSFP8_OUT_F32) {
-#pragma unroll 4
-            for (int i = 0; i < 32; ++i) {
-                const int R = wave * 32 + i;
-                const int c = lane;
-                const float4 v = *reinterpret_cast<const float4*>(lds + R * 1024 + ((c ^ (R & 15)) << 4));
-                const float a4[4] = {v.x, v.y, v.z, v.w};
-                finish_row_chunk<OUT, 4>(D, ldd, ep, m0 + p * 128 + R, n0 + c * 4, M, N, vec_ok, a4);
-            }
-        } else {
-#pragma unroll 4
-            for (int i = 0; i < 16; ++i) {
-                const int R = wave * 32 + i * 2 + half;
-                const int c = (lane & 31) * 2;
-                const float4 v0 = *reinterpret_cast<const float4*>(lds + R * 1024 + ((c ^ (R & 15)) << 4));
-                const float4 v1 = *reinterpret_cast<const float4*>(lds + R * 1024 + (((c + 1) ^ (R & 15)) << 4));
-                const float a8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-                finish_row_chunk<OUT, 8>(D, ldd, ep, m0 + p * 128 + R, n0 + c * 4, M, N, vec_ok, a8);
-            }
-        }
-        __syncthreads();
-    }
+    NoScale none;
+    big_tile::epilogue<OUT, STAGE16>(acc, lds, wave, lane, m0, n0, M, N, D, ldd, ep, vec_ok, none);
 }
 
 template <int OUT>

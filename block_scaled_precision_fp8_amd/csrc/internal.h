@@ -15,6 +15,10 @@ hipError_t launch_fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t 
                                uint8_t* codes, float* scales, hipStream_t stream);
 hipError_t launch_fp8_quantize_t(const float* x, int64_t k, int64_t rows, int64_t ld, int fmt,
                                  uint8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_fp8_quantize_rows(const float* x, int64_t rows, int64_t k, int64_t ld, int fmt,
+                                    uint8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_fp8_quantize_tensor(const float* x, int64_t rows, int64_t k, int64_t ld, int fmt,
+                                      uint8_t* codes, float* scales, hipStream_t stream);
 hipError_t launch_mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
                                  uint8_t* packed, uint8_t* scales, hipStream_t stream);
 // The GEMM epilogue: D = alpha * (A B) + beta * C, C of D's element type.
@@ -26,10 +30,18 @@ struct Epilogue {
     int64_t ldc;
 };
 
+// Per-tile FP8 scales; bit 0 (bit 1) of tensor_mask marks a_scales (b_scales)
+// as one scale for the whole operand instead.
 hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,
                            const float* a_scales, int b_fmt, const uint8_t* b,
                            const float* b_scales, int out, void* d, int64_t ldd,
-                           const Epilogue& ep, hipStream_t stream);
+                           const Epilogue& ep, hipStream_t stream, int tensor_mask = 0);
+// FP8 operands whose scales are constant along K: a_scales[m * a_step] and
+// b_scales[n * b_step] (step 1 for per-row scales, 0 for one per tensor).
+hipError_t launch_gemm_fp8_outer(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,
+                                 const float* a_scales, int a_step, int b_fmt, const uint8_t* b,
+                                 const float* b_scales, int b_step, int out, void* d, int64_t ldd,
+                                 const Epilogue& ep, hipStream_t stream);
 hipError_t launch_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                              const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
                              int out, void* d, int64_t ldd, const Epilogue& ep,

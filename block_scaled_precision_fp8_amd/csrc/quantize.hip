@@ -45,6 +45,46 @@ __device__ __forceinline__ float abs_max4(float4 v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
+// fl32(x / s), correctly rounded and clamped to +-F, as described in the
+// header: one correctly rounded reciprocal per scale, three FMA-class
+// operations per element.
+struct Fp8Quotient {
+    int se;
+    float ss, rs;
+    __device__ explicit Fp8Quotient(float s) {
+        (void)__builtin_frexpf(s, &se);
+        ss = __builtin_ldexpf(s, -se);     // s 2^k in [1/2, 1)
+        rs = 1.0f / ss;                    // correctly rounded
+    }
+    __device__ float operator()(float x, float F) const {
+        const float xs = __builtin_ldexpf(x, -se);
+        const float q0 = xs * rs;
+        const float e = __builtin_fmaf(-q0, ss, xs);
+        const float q = __builtin_copysignf(__builtin_fmaf(e, rs, q0), x);
+        return fminf(fmaxf(q, -F), F);
+    }
+};
+
+// Four clamped quotients -> four FP8 codes (round to nearest even), byte i = qi.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_pack4(float q0, float q1, float q2, float q3) {
+    int w;
+    if constexpr (FMT == BSFP8_E4M3) {
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
+    } else {
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(q0, q1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(q2, q3, w, true);
+    }
+    return static_cast<uint32_t>(w);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_codes4(const Fp8Quotient& qt, float4 v) {
+    constexpr float F = FMT == BSFP8_E4M3 ? 448.0f : 57344.0f;
+    return fp8_pack4<FMT>(qt(v.x, F), qt(v.y, F), qt(v.z, F), qt(v.w, F));
+}
+
 // One workgroup quantises a 128-row x 128-column block = four 128 x 32 tiles.
 // Thread t holds 16-byte chunk (t % 32) of rows (t / 32) + 8 i, i = 0..15, so a
 // wave reads two full 512-byte row segments per load instruction and every
@@ -100,36 +140,12 @@ __global__ __launch_bounds__(kThreads) void fp8_quantize_kernel(
         scales[rt * nkb + cb * 4 + tid] = st;
     }
 
-    // x / s as described in the header: one correctly rounded reciprocal per
-    // thread, three FMA-class operations per element.
-    int se;
-    (void)__builtin_frexpf(s, &se);
-    const float ss = __builtin_ldexpf(s, -se);     // s 2^k in [1/2, 1)
-    const float rs = 1.0f / ss;                     // correctly rounded
-    auto quot = [&](float x) {
-        const float xs = __builtin_ldexpf(x, -se);
-        const float q0 = xs * rs;
-        const float e = __builtin_fmaf(-q0, ss, xs);
-        const float q = __builtin_copysignf(__builtin_fmaf(e, rs, q0), x);
-        return fminf(fmaxf(q, -F), F);
-    };
+    const Fp8Quotient qt(s);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int64_t r = r0 + ro + 8 * i;
         if (!(col_ok && r < rows)) continue;
-        const float q0 = quot(v[i].x);
-        const float q1 = quot(v[i].y);
-        const float q2 = quot(v[i].z);
-        const float q3 = quot(v[i].w);
-        int w;
-        if constexpr (FMT == BSFP8_E4M3) {
-            w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-            w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
-        } else {
-            w = __builtin_amdgcn_cvt_pk_bf8_f32(q0, q1, 0, false);
-            w = __builtin_amdgcn_cvt_pk_bf8_f32(q2, q3, w, true);
-        }
-        *reinterpret_cast<uint32_t*>(codes + r * k + col) = static_cast<uint32_t>(w);
+        *reinterpret_cast<uint32_t*>(codes + r * k + col) = fp8_codes4<FMT>(qt, v[i]);
     }
 }
 
@@ -212,30 +228,13 @@ __global__ __launch_bounds__(kThreads) void fp8_quantize_t_kernel(
 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const float s = sc[q];
-        int se;
-        (void)__builtin_frexpf(s, &se);
-        const float ss = __builtin_ldexpf(s, -se);
-        const float rs = 1.0f / ss;
-        auto code = [&](float xv) -> uint32_t {
-            const float xs = __builtin_ldexpf(xv, -se);
-            const float q0 = xs * rs;
-            const float e = __builtin_fmaf(-q0, ss, xs);
-            const float qq = fminf(fmaxf(__builtin_copysignf(__builtin_fmaf(e, rs, q0), xv), -F), F);
-            int w;
-            if constexpr (FMT == BSFP8_E4M3) w = __builtin_amdgcn_cvt_pk_fp8_f32(qq, qq, 0, false);
-            else w = __builtin_amdgcn_cvt_pk_bf8_f32(qq, qq, 0, false);
-            return static_cast<uint32_t>(w) & 0xFFu;
-        };
-        // column jj of this thread: K codes j = 0..3 packed into one word
-        uint32_t wcol[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            wcol[0] |= code(v[q][j].x) << (8 * j);
-            wcol[1] |= code(v[q][j].y) << (8 * j);
-            wcol[2] |= code(v[q][j].z) << (8 * j);
-            wcol[3] |= code(v[q][j].w) << (8 * j);
-        }
+        const Fp8Quotient qt(sc[q]);
+        // column jj of this thread: its K codes j = 0..3 packed into one word
+        uint32_t wcol[4];
+        wcol[0] = fp8_pack4<FMT>(qt(v[q][0].x, F), qt(v[q][1].x, F), qt(v[q][2].x, F), qt(v[q][3].x, F));
+        wcol[1] = fp8_pack4<FMT>(qt(v[q][0].y, F), qt(v[q][1].y, F), qt(v[q][2].y, F), qt(v[q][3].y, F));
+        wcol[2] = fp8_pack4<FMT>(qt(v[q][0].z, F), qt(v[q][1].z, F), qt(v[q][2].z, F), qt(v[q][3].z, F));
+        wcol[3] = fp8_pack4<FMT>(qt(v[q][0].w, F), qt(v[q][1].w, F), qt(v[q][2].w, F), qt(v[q][3].w, F));
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
             *reinterpret_cast<uint32_t*>(tl + (chunk * 4 + jj) * kTPitch + 4 * g + 32 * q) = wcol[jj];
@@ -256,6 +255,120 @@ __global__ __launch_bounds__(kThreads) void fp8_quantize_t_kernel(
                                    *reinterpret_cast<const uint32_t*>(src + 8),
                                    *reinterpret_cast<const uint32_t*>(src + 12));
         *reinterpret_cast<uint4*>(codes + orow * k + ocol) = w;
+    }
+}
+
+// Per-row scales ("Why grind FP8 GEMM on CDNA4", section 3.3 weighs per-row,
+// per-column and per-tensor scales against per-tile ones): one wave per row,
+// amax reduced across the wave, s = fl32(amax / F), then the codes.  Rows of up
+// to 4096 elements stay in registers between the two steps; longer rows are
+// read twice (the second time mostly from cache).  The per-row scales of a B
+// operand stored N x K are its per-column scales.
+template <int FMT, bool INREG>
+__global__ __launch_bounds__(kThreads) void fp8_quantize_rows_kernel(
+    const float* __restrict__ x, int64_t rows, int64_t k, int64_t ld,
+    uint8_t* __restrict__ codes, float* __restrict__ scales) {
+    constexpr float F = FMT == BSFP8_E4M3 ? 448.0f : 57344.0f;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;                    // the whole wave leaves together
+    const float* xr = x + row * ld;
+    uint8_t* cr = codes + row * k;
+    auto wave_max = [](float a) {
+        a = fmaxf(a, __shfl_xor(a, 1));
+        a = fmaxf(a, __shfl_xor(a, 2));
+        a = fmaxf(a, __shfl_xor(a, 4));
+        a = fmaxf(a, __shfl_xor(a, 8));
+        a = fmaxf(a, __shfl_xor(a, 16));
+        return fmaxf(a, __shfl_xor(a, 32));
+    };
+    float amax = 0.0f;
+    if constexpr (INREG) {
+        float4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t c = (static_cast<int64_t>(i) * 64 + lane) * 4;
+            v[i] = c < k ? load_once(xr + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            amax = fmaxf(amax, abs_max4(v[i]));
+        }
+        amax = wave_max(amax);
+        float s = amax / F;
+        if (s == 0.0f) s = 1.0f;
+        if (lane == 0) scales[row] = s;
+        const Fp8Quotient qt(s);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t c = (static_cast<int64_t>(i) * 64 + lane) * 4;
+            if (c < k) *reinterpret_cast<uint32_t*>(cr + c) = fp8_codes4<FMT>(qt, v[i]);
+        }
+    } else {
+        for (int64_t c = lane * 4; c < k; c += 256)
+            amax = fmaxf(amax, abs_max4(*reinterpret_cast<const float4*>(xr + c)));
+        amax = wave_max(amax);
+        float s = amax / F;
+        if (s == 0.0f) s = 1.0f;
+        if (lane == 0) scales[row] = s;
+        const Fp8Quotient qt(s);
+        for (int64_t c = lane * 4; c < k; c += 256)
+            *reinterpret_cast<uint32_t*>(cr + c) = fp8_codes4<FMT>(qt, load_once(xr + c));
+    }
+}
+
+// Per-tensor scale, in four launches on one stream: the scale word is
+// cleared, every wave folds its maximum |x| into it with one atomic maximum on
+// the FP32 bit pattern (non-negative floats order like their bits), the codes
+// are computed from s = fl32(amax / F), and the word is replaced by s.
+__global__ __launch_bounds__(64) void clear_word_kernel(uint32_t* word) {
+    if (threadIdx.x == 0) *word = 0u;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_kernel(const float* __restrict__ x, int64_t rows,
+                                                        int64_t k, int64_t ld, uint32_t* word) {
+    const int64_t per_row = k >> 2;                 // float4 chunks per row
+    const int64_t total = rows * per_row;
+    float amax = 0.0f;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const int64_t r = i / per_row;
+        const int64_t c = (i - r * per_row) * 4;
+        amax = fmaxf(amax, abs_max4(*reinterpret_cast<const float4*>(x + r * ld + c)));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    amax = fmaxf(amax, __shfl_xor(amax, 8));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if ((threadIdx.x & 63) == 0) atomicMax(word, __float_as_uint(amax));
+}
+
+template <int FMT>
+__device__ __forceinline__ float tensor_scale(const uint32_t* word) {
+    constexpr float F = FMT == BSFP8_E4M3 ? 448.0f : 57344.0f;
+    float s = __uint_as_float(*word) / F;
+    return s == 0.0f ? 1.0f : s;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void fp8_quantize_tensor_kernel(
+    const float* __restrict__ x, int64_t rows, int64_t k, int64_t ld, const uint32_t* word,
+    uint8_t* __restrict__ codes) {
+    const Fp8Quotient qt(tensor_scale<FMT>(word));
+    const int64_t per_row = k >> 2;
+    const int64_t total = rows * per_row;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const int64_t r = i / per_row;
+        const int64_t c = (i - r * per_row) * 4;
+        *reinterpret_cast<uint32_t*>(codes + r * k + c) = fp8_codes4<FMT>(qt, load_once(x + r * ld + c));
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(64) void tensor_scale_kernel(uint32_t* word) {
+    if (threadIdx.x == 0) {
+        const float s = tensor_scale<FMT>(word);
+        *word = __float_as_uint(s);
     }
 }
 
@@ -349,6 +462,38 @@ hipError_t launch_fp8_quantize_t(const float* x, int64_t k, int64_t rows, int64_
     else
         hipLaunchKernelGGL(fp8_quantize_t_kernel<BSFP8_E5M2>, dim3(static_cast<uint32_t>(blocks)),
                            dim3(kThreads), 0, stream, x, k, rows, ld, codes, scales, nrb);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize_rows(const float* x, int64_t rows, int64_t k, int64_t ld, int fmt,
+                                    uint8_t* codes, float* scales, hipStream_t stream) {
+    const dim3 grid(static_cast<uint32_t>((rows + 3) / 4));
+    const bool inreg = k <= 4096;
+    if (fmt == BSFP8_E4M3) {
+        if (inreg) hipLaunchKernelGGL((fp8_quantize_rows_kernel<BSFP8_E4M3, true>), grid, dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales);
+        else hipLaunchKernelGGL((fp8_quantize_rows_kernel<BSFP8_E4M3, false>), grid, dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales);
+    } else {
+        if (inreg) hipLaunchKernelGGL((fp8_quantize_rows_kernel<BSFP8_E5M2, true>), grid, dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales);
+        else hipLaunchKernelGGL((fp8_quantize_rows_kernel<BSFP8_E5M2, false>), grid, dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize_tensor(const float* x, int64_t rows, int64_t k, int64_t ld, int fmt,
+                                      uint8_t* codes, float* scales, hipStream_t stream) {
+    uint32_t* word = reinterpret_cast<uint32_t*>(scales);
+    const int64_t chunks = rows * (k >> 2);
+    const int64_t want = (chunks + kThreads - 1) / kThreads;
+    const dim3 grid(static_cast<uint32_t>(want < 4096 ? want : 4096));
+    hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, stream, word);
+    hipLaunchKernelGGL(amax_kernel, grid, dim3(kThreads), 0, stream, x, rows, k, ld, word);
+    if (fmt == BSFP8_E4M3) {
+        hipLaunchKernelGGL(fp8_quantize_tensor_kernel<BSFP8_E4M3>, grid, dim3(kThreads), 0, stream, x, rows, k, ld, word, codes);
+        hipLaunchKernelGGL(tensor_scale_kernel<BSFP8_E4M3>, dim3(1), dim3(64), 0, stream, word);
+    } else {
+        hipLaunchKernelGGL(fp8_quantize_tensor_kernel<BSFP8_E5M2>, grid, dim3(kThreads), 0, stream, x, rows, k, ld, word, codes);
+        hipLaunchKernelGGL(tensor_scale_kernel<BSFP8_E5M2>, dim3(1), dim3(64), 0, stream, word);
+    }
     return hipGetLastError();
 }
 

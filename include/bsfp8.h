@@ -172,6 +172,60 @@ bsfp8_status scaled_gemm_ex(int64_t M, int64_t N, int64_t K,
                             float alpha, const void* c, int64_t ldc, float beta,
                             bsfp8_out out, void* d, int64_t ldd, hipStream_t stream);
 
+/*
+ * Scale granularity of an operand ([CDNA4-FP8] section 3.3 weighs per-row,
+ * per-column and per-tensor scales against per-tile ones and keeps per tile;
+ * its closing section keeps a per-matrix scale for evenly distributed data).
+ * The rows are those of the operand's rows x K storage: per-row scales of A
+ * are per output row, per-row scales of B (stored N x K) are per output column.
+ */
+typedef enum {
+    BSFP8_GRAN_TILE = 0,    /* FP8: FP32 [ceil(rows / 128)][K / 32], one per 128 x 32 tile */
+    BSFP8_GRAN_ROW = 1,     /* FP8: FP32 [rows], one per row, constant along K */
+    BSFP8_GRAN_TENSOR = 2,  /* FP8: FP32 [1], one for the whole operand */
+    BSFP8_GRAN_MX32 = 3     /* MXFP4: E8M0 [rows][K / 32], one per 32-element K block */
+} bsfp8_granularity;
+
+/*
+ * fp8_quantize_granular -- FP8 quantisation with the scale granularity g.
+ *
+ * x, rows, k, ld, fmt, codes: as for fp8_quantize.
+ * g: BSFP8_GRAN_TILE (exactly fp8_quantize with tile_rows = 128),
+ *    BSFP8_GRAN_ROW or BSFP8_GRAN_TENSOR; BSFP8_GRAN_MX32 is UNSUPPORTED.
+ * scales: out, FP32, the shape g names (4-byte aligned).
+ *
+ * Per scale group (tile, row or whole operand): amax = max |x|, s = amax / F
+ * rounded to FP32 (s = 1 when that is zero), code = saturating round-to-
+ * nearest-even of (x / s rounded to FP32).  Bit-exact.  rows == 0 or k == 0
+ * writes nothing.  BSFP8_GRAN_TENSOR uses scales[0] as its working word
+ * between its launches, so concurrent reads of scales[0] race with the call.
+ */
+bsfp8_status fp8_quantize_granular(const float* x, int64_t rows, int64_t k, int64_t ld,
+                                   bsfp8_granularity g, bsfp8_format fmt, uint8_t* codes,
+                                   float* scales, hipStream_t stream);
+
+/*
+ * scaled_gemm_granular -- scaled_gemm_ex with a scale granularity per operand:
+ * D = alpha * deq(A) deq(B) + beta * C, deq(X)[r][k] = code * scale(r, k).
+ *
+ * All arguments as for scaled_gemm_ex, plus a_g and b_g, the granularities of
+ * a_scales and b_scales.  Supported combinations:
+ *   FP8, both scales constant along K (ROW or TENSOR on each side): the scale
+ *     product multiplies the FP32 sum over all of K once, at write-back.
+ *   FP8, TILE with TILE or TENSOR: the product of the two K block scales
+ *     multiplies each 32-wide K block's partial sum, as in scaled_gemm.
+ *   MXFP4: MX32 on both sides (as scaled_gemm).
+ * Other combinations (TILE with ROW) return BSFP8_ERR_UNSUPPORTED.
+ * Accuracy as for scaled_gemm_ex.
+ */
+bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K,
+                                  bsfp8_format a_fmt, const void* a, const void* a_scales,
+                                  bsfp8_granularity a_g,
+                                  bsfp8_format b_fmt, const void* b, const void* b_scales,
+                                  bsfp8_granularity b_g,
+                                  float alpha, const void* c, int64_t ldc, float beta,
+                                  bsfp8_out out, void* d, int64_t ldd, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* bsfp8_status_string(bsfp8_status s);
 

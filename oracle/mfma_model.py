@@ -88,6 +88,8 @@ INSTRUCTIONS = {
     "v_mfma_scale_f32_32x32x64_f8f6f4.e2m1": ("e2m1", "e2m1", 64, True, _SCALED_FP4),
     "v_mfma_scale_f32_32x32x64_f8f6f4.e4m3": ("e4m3", "e4m3", 64, True, _SCALED_FP8),
     "v_mfma_scale_f32_32x32x64_f8f6f4.e5m2": ("e5m2", "e5m2", 64, True, _SCALED_FP8),
+    "v_mfma_f32_32x32x64_f8f6f4.e4m3": ("e4m3", "e4m3", 64, False, _SCALED_FP8),
+    "v_mfma_f32_32x32x64_f8f6f4.e5m2": ("e5m2", "e5m2", 64, False, _SCALED_FP8),
 }
 
 # The page's H100 model for an m64n8k32 E4M3 WGMMA ("FP8 MMA internals on

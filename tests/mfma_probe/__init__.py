@@ -16,13 +16,14 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmfmaprobe.so")
 
-FP8_FP8, FP8_BF8, BF8_FP8, BF8_BF8, BF16, SCALE_FP4, SCALE_E4M3, SCALE_E5M2 = range(8)
+FP8_FP8, FP8_BF8, BF8_FP8, BF8_BF8, BF16, SCALE_FP4, SCALE_E4M3, SCALE_E5M2, K64_E4M3, K64_E5M2 = range(10)
 # instruction -> (A element format, B element format, K)
 INSTR = {
     FP8_FP8: ("e4m3", "e4m3", 16), FP8_BF8: ("e4m3", "e5m2", 16),
     BF8_FP8: ("e5m2", "e4m3", 16), BF8_BF8: ("e5m2", "e5m2", 16),
     BF16: ("bf16", "bf16", 16), SCALE_FP4: ("e2m1", "e2m1", 64),
     SCALE_E4M3: ("e4m3", "e4m3", 64), SCALE_E5M2: ("e5m2", "e5m2", 64),
+    K64_E4M3: ("e4m3", "e4m3", 64), K64_E5M2: ("e5m2", "e5m2", 64),
 }
 
 _lib = None
@@ -128,7 +129,7 @@ def dot(instr, a, b, c, sa=None, sb=None, device="cuda:0"):
     tb = torch.from_numpy(np.ascontiguousarray(b).view(np.uint8).reshape(-1).copy()).to(dev)
     tc = torch.from_numpy(c.copy()).to(dev)
     td = torch.full((n,), float("nan"), dtype=torch.float32, device=dev)
-    if instr >= SCALE_FP4:
+    if SCALE_FP4 <= instr <= SCALE_E5M2:
         if sa is None or sb is None:
             raise ValueError("scaled instructions need E8M0 scales for both operands")
         tsa = torch.from_numpy(np.ascontiguousarray(sa, dtype=np.uint8).reshape(-1).copy()).to(dev)

@@ -33,7 +33,9 @@ enum Instr {
     kScaleFp4 = 5,  // v_mfma_scale_f32_32x32x64_f8f6f4, E2M1 x E2M1, E8M0 scales, K = 64
     kScaleE4m3 = 6, // the same instruction, E4M3 x E4M3, E8M0 scales, K = 64
     kScaleE5m2 = 7, // the same instruction, E5M2 x E5M2, E8M0 scales, K = 64
-    kNumInstr = 8
+    kK64E4m3 = 8,   // v_mfma_f32_32x32x64_f8f6f4 (no scales), E4M3 x E4M3, K = 64
+    kK64E5m2 = 9,   // the same, E5M2 x E5M2
+    kNumInstr = 10
 };
 
 __device__ __forceinline__ int out_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
@@ -83,6 +85,29 @@ __global__ __launch_bounds__(64) void probe_kernel(int instr, int64_t ncases, co
         __builtin_memcpy(&a, xa, 16);
         __builtin_memcpy(&b, xb, 16);
         d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    } else if (instr >= kK64E4m3) {
+        // same operand layout as the scaled instruction with 8-bit elements
+        uint8_t lo_a[16], hi_a[16], lo_b[16], hi_b[16];
+        load_bytes(lo_a, A + mycase * 64 + 16 * half, ok);
+        load_bytes(hi_a, A + mycase * 64 + 32 + 16 * half, ok);
+        load_bytes(lo_b, B + mycase * 64 + 16 * half, ok);
+        load_bytes(hi_b, B + mycase * 64 + 32 + 16 * half, ok);
+        uint8_t xa[32], xb[32];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            xa[i] = lo_a[i]; xa[16 + i] = hi_a[i];
+            xb[i] = lo_b[i]; xb[16 + i] = hi_b[i];
+        }
+        v8i a, b;
+        __builtin_memcpy(&a, xa, 32);
+        __builtin_memcpy(&b, xb, 32);
+        d = c;
+        if (instr == kK64E4m3)
+            asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0 cbsz:0 blgp:0" : "+v"(d) : "v"(a), "v"(b));
+        else
+            asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+v"(d) : "v"(a), "v"(b));
+        // the result must settle before it is read
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
     } else {
         // Lane (row, half) supplies the E8M0 scale of K block `half` (K values
         // 32 half .. 32 half + 31) in byte 0 of its scale register.  E2M1
@@ -139,7 +164,7 @@ extern "C" {
 // K of one instruction (products per dot product), or 0 for an unknown selector.
 int mfma_probe_k(int instr) {
     if (instr < 0 || instr >= kNumInstr) return 0;
-    return instr <= kBf16 ? 16 : 64;
+    return instr <= kBf16 ? 16 : 64;   // 5..9: K = 64
 }
 
 // Evaluate `ncases` dot products with instruction `instr` (see Instr above).
@@ -147,7 +172,7 @@ int mfma_probe_k(int instr) {
 //   instr 0-3: a, b: 16 FP8 codes each (a in the A format, b in the B format)
 //   instr 4:   a, b: 16 bf16 bit patterns each (little-endian uint16)
 //   instr 5:   a, b: 64 E2M1 values in 32 bytes, element 2i in the low nibble of byte i
-//   instr 6,7: a, b: 64 FP8 codes each
+//   instr 6-9: a, b: 64 FP8 codes each
 //   instr 5-7: sa, sb: 2 E8M0 bytes per case (K values 0-31, then 32-63); unused otherwise
 //   c: ncases FP32 accumulator inputs; d: ncases FP32 results.
 // Returns 0 on success, 1 for a bad argument, 2 for a launch error.
@@ -156,7 +181,7 @@ int mfma_probe_dot(int instr, int64_t ncases, const void* a, const void* b, cons
     if (instr < 0 || instr >= kNumInstr || ncases < 0) return 1;
     if (ncases == 0) return 0;
     if (!a || !b || !c || !d) return 1;
-    if (instr >= kScaleFp4 && (!sa || !sb)) return 1;
+    if (instr >= kScaleFp4 && instr <= kScaleE5m2 && (!sa || !sb)) return 1;
     const int64_t waves = (ncases + 31) / 32;
     if (waves > 0x7fffffff) return 1;
     hipLaunchKernelGGL(probe_kernel, dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream, instr, ncases,

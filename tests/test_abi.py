@@ -30,8 +30,9 @@ def L():
 
 def test_header_declares_the_three_calls():
     names = declared_functions()
-    for n in ("fp8_quantize", "fp8_quantize_transposed", "mxfp4_quantize", "scaled_gemm",
-              "scaled_gemm_ex", "bsfp8_status_string", "bsfp8_version"):
+    for n in ("fp8_quantize", "fp8_quantize_transposed", "fp8_quantize_granular", "mxfp4_quantize",
+              "scaled_gemm", "scaled_gemm_ex", "scaled_gemm_granular", "bsfp8_status_string",
+              "bsfp8_version"):
         assert n in names
 
 
@@ -125,12 +126,47 @@ def test_mfma_probe_loads_and_rejects_bad_arguments():
     rejects bad arguments before any launch."""
     import mfma_probe
     P = mfma_probe.lib()
-    assert [P.mfma_probe_k(i) for i in range(8)] == [16, 16, 16, 16, 16, 64, 64, 64]
-    assert P.mfma_probe_k(8) == 0 and P.mfma_probe_k(-1) == 0
+    assert [P.mfma_probe_k(i) for i in range(10)] == [16, 16, 16, 16, 16, 64, 64, 64, 64, 64]
+    assert P.mfma_probe_k(10) == 0 and P.mfma_probe_k(-1) == 0
     buf = ctypes.create_string_buffer(256)
     p = ctypes.addressof(buf)
-    assert P.mfma_probe_dot(8, 1, p, p, None, None, p, p, None) == 1      # unknown instruction
+    assert P.mfma_probe_dot(10, 1, p, p, None, None, p, p, None) == 1     # unknown instruction
     assert P.mfma_probe_dot(0, -1, p, p, None, None, p, p, None) == 1     # negative count
     assert P.mfma_probe_dot(0, 1, None, p, None, None, p, p, None) == 1   # null operand
     assert P.mfma_probe_dot(5, 1, p, p, None, p, p, p, None) == 1         # scaled without scales
     assert P.mfma_probe_dot(0, 0, None, None, None, None, None, None, None) == 0   # nothing to do
+
+
+TILE, ROW, TENSOR, MX32 = 0, 1, 2, 3
+
+
+def test_fp8_quantize_granular_argument_checks(L):
+    q = L.fp8_quantize_granular   # (x, rows, k, ld, granularity, fmt, codes, scales, stream)
+    assert q(P, 4, 64, 64, 4, E4M3, P, P, None) == UNSUPPORTED         # unknown granularity
+    assert q(P, 4, 64, 64, MX32, E4M3, P, P, None) == UNSUPPORTED      # MX blocks are MXFP4 only
+    assert q(P, 4, 64, 64, ROW, MXFP4, P, P, None) == UNSUPPORTED      # not an FP8 format
+    assert q(P, 4, 48, 64, ROW, E4M3, P, P, None) == INVALID           # k % 32
+    assert q(P, 4, 64, 32, TENSOR, E4M3, P, P, None) == INVALID        # ld < k
+    assert q(0, 4, 64, 64, ROW, E4M3, P, P, None) == INVALID           # null x
+    assert q(P + 4, 4, 64, 64, TENSOR, E5M2, P, P, None) == INVALID    # x alignment
+    assert q(P, 4, 64, 64, TENSOR, E5M2, P, P + 2, None) == INVALID    # scales alignment
+    assert q(0, 0, 64, 64, ROW, E4M3, 0, 0, None) == OK                # empty
+    assert q(0, 4, 0, 0, TENSOR, E4M3, 0, 0, None) == OK
+
+
+def test_scaled_gemm_granular_argument_checks(L):
+    g = L.scaled_gemm_granular
+    # (M, N, K, af, a, sa, ag, bf, b, sb, bg, alpha, c, ldc, beta, out, d, ldd, stream)
+    def call(ag, bg, af=E4M3, bf=E4M3, K=64, out=BF16):
+        return g(128, 128, K, af, P, P, ag, bf, P, P, bg, 1.0, 0, 0, 0.0, out, P, 128, None)
+    assert call(TILE, ROW) == UNSUPPORTED          # per-row with per-tile: not built
+    assert call(ROW, TILE) == UNSUPPORTED
+    assert call(TILE, MX32) == UNSUPPORTED         # E8M0 blocks with FP8 operands
+    assert call(MX32, MX32, af=MXFP4, bf=E4M3) == UNSUPPORTED
+    assert call(TILE, TILE, af=MXFP4, bf=MXFP4) == UNSUPPORTED
+    assert call(ROW, 7) == UNSUPPORTED
+    assert call(ROW, ROW, K=1 << 23) == UNSUPPORTED   # K beyond the K-constant kernel's range
+    assert call(ROW, TENSOR, K=48) == INVALID
+    assert g(128, 128, 64, E4M3, P, 0, ROW, E4M3, P, P, ROW, 1.0, 0, 0, 0.0, BF16, P, 128, None) == INVALID
+    assert g(128, 128, 64, E4M3, P, P + 2, ROW, E4M3, P, P, TENSOR, 1.0, 0, 0, 0.0, BF16, P, 128, None) == INVALID
+    assert g(0, 128, 64, E4M3, 0, 0, ROW, E4M3, 0, 0, TENSOR, 1.0, 0, 0, 0.0, F32, 0, 128, None) == OK

@@ -34,6 +34,8 @@ SELECTOR = {
     "v_mfma_scale_f32_32x32x64_f8f6f4.e2m1": P.SCALE_FP4,
     "v_mfma_scale_f32_32x32x64_f8f6f4.e4m3": P.SCALE_E4M3,
     "v_mfma_scale_f32_32x32x64_f8f6f4.e5m2": P.SCALE_E5M2,
+    "v_mfma_f32_32x32x64_f8f6f4.e4m3": P.K64_E4M3,
+    "v_mfma_f32_32x32x64_f8f6f4.e5m2": P.K64_E5M2,
 }
 NAMES = list(SELECTOR)
 
