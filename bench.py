@@ -17,8 +17,13 @@ Also reported, on the same JSON line:
                 step, extrapolated to the whole job;
   kernels       per-kernel times, GEMM TFLOP/s, quantiser GB/s against 8 TB/s.
 
+FP8 workloads can also be run with scales constant along K
+(--granularity row: per-row A and per-column B, or tensor: one scale per
+operand); the step then uses fp8_quantize_granular and scaled_gemm_granular.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--copy-calibration]
+                       [--granularity tile|row|tensor] [--no-cpu-baseline]
+                       [--copy-calibration]
 Only one GPU is supported; --gpus N with N > 1 exits with a message.
 """
 import argparse
@@ -68,9 +73,11 @@ def committed_traffic(workload, source_file):
         return None, None
 
 
-def gemm_kernel_name(w):
+def gemm_kernel_name(w, gran="tile"):
     """The kernel scaled_gemm dispatches for this workload (mirrors the
     launchers' selection)."""
+    if w.a_fmt != "mxfp4" and gran != "tile":
+        return "gemm_fp8_outer_kernel"
     if w.a_fmt == "mxfp4":
         big_tiles = ((w.M + 255) // 256) * ((w.N + 255) // 256)
         fits32 = w.M * (w.K // 2) < 2**31 and w.N * (w.K // 2) < 2**31
@@ -80,15 +87,41 @@ def gemm_kernel_name(w):
     return "gemm_fp8_kernel"
 
 
-def cpu_baseline(w, a, b, d_gpu, sample_rows):
+def cpu_baseline(w, a, b, d_gpu, sample_rows, gran="tile"):
     """Time the oracle on a bounded sample: quantise all of B, `sample_rows`
     rows of A, and the product rows for that sample; extrapolate the time to
-    the whole step (quantising all of A, all M rows of D)."""
+    the whole step (quantising all of A, all M rows of D).  With per-row or
+    per-tensor scales all of A is quantised (a per-tensor scale needs every
+    row) and only the product is sampled."""
     import numpy as np
     import oracle
 
     cores = oracle.threads()
     rows = min(sample_rows, w.M)
+    if gran != "tile" and w.a_fmt != "mxfp4":
+        t0 = time.perf_counter()
+        qb, sb = oracle.fp8_quantize_granular(b, w.b_fmt, gran)
+        qa, sa = oracle.fp8_quantize_granular(a, w.a_fmt, gran)
+        t1 = time.perf_counter()
+        sa_rows = sa[:rows] if gran == "row" else sa
+        d_ref, s_ref = oracle.gemm_granular(w.a_fmt, qa[:rows], sa_rows, gran, w.b_fmt, qb, sb, gran)
+        t2 = time.perf_counter()
+        scale = w.M / rows
+        t_full = (t1 - t0) + (t2 - t1) * scale
+        err = np.abs(d_gpu[:rows].astype(np.float64) - d_ref)
+        nz = s_ref > 0
+        worst = float((err[nz] / s_ref[nz]).max()) if nz.any() else 0.0
+        return {
+            "value": w.flops / t_full / 1e12,
+            "unit": "TFLOP/s",
+            "cores": cores,
+            "kind": "oracle",
+            "sample": (f"oracle {gran} quantise of all of A and B, oracle fp64 product of A rows "
+                       f"0..{rows - 1} x {w.N} columns; measured {t2 - t0:.1f} s, extrapolated "
+                       f"x{scale:g} on the product to the full {w.M}x{w.N}x{w.K} step"),
+            "seconds_measured": round(t2 - t0, 3),
+            "gpu_vs_oracle_max_err_over_S_on_sample": worst,
+        }
     t0 = time.perf_counter()
     if w.a_fmt == "mxfp4":
         qb, sb = oracle.mxfp4_quantize(b)
@@ -150,6 +183,9 @@ def main():
                         "gradient and activation of a weight-gradient product are) and quantises "
                         "them with fp8_quantize_transposed; default token-major for the dW "
                         "workload, k-contiguous otherwise")
+    p.add_argument("--granularity", choices=["tile", "row", "tensor"], default="tile",
+                   help="FP8 only: scale granularity of both operands (row = per-row A and "
+                        "per-column B)")
     args = p.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -172,8 +208,13 @@ def main():
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} {w.a_fmt}x{w.b_fmt} -> {w.out}")
     a_host, b_host = workloads.operands(w)
     mx = w.a_fmt == "mxfp4"
-    layout = args.operand_layout or ("token-major" if w.name.startswith("dw_") else "k-contiguous")
+    gran = "tile" if mx else args.granularity
+    layout = args.operand_layout or ("token-major" if w.name.startswith("dw_") and gran == "tile"
+                                     else "k-contiguous")
     token_major = layout == "token-major" and not mx
+    if token_major and gran != "tile":
+        print("bench.py: the token-major layout is quantised with per-tile scales only", file=sys.stderr)
+        sys.exit(2)
     if token_major:     # G (K x M) and X (K x N) as stored in the backward pass
         a = torch.from_numpy(np.ascontiguousarray(a_host.T)).to(dev)
         b = torch.from_numpy(np.ascontiguousarray(b_host.T)).to(dev)
@@ -189,8 +230,10 @@ def main():
     else:
         qa = torch.empty((w.M, w.K), dtype=torch.uint8, device=dev)
         qb = torch.empty((w.N, w.K), dtype=torch.uint8, device=dev)
-        sa = torch.empty(((w.M + 127) // 128, w.K // 32), dtype=torch.float32, device=dev)
-        sb = torch.empty(((w.N + 127) // 128, w.K // 32), dtype=torch.float32, device=dev)
+        def scale_shape(rows):
+            return {"tile": ((rows + 127) // 128, w.K // 32), "row": (rows,), "tensor": (1,)}[gran]
+        sa = torch.empty(scale_shape(w.M), dtype=torch.float32, device=dev)
+        sb = torch.empty(scale_shape(w.N), dtype=torch.float32, device=dev)
     d = torch.empty((w.M, w.N), dtype=torch.float32 if w.out == "f32" else torch.bfloat16,
                     device=dev)
 
@@ -203,6 +246,11 @@ def main():
         if mx:
             bs.mxfp4_quantize(a, qa, sa)
             bs.mxfp4_quantize(b, qb, sb)
+        elif gran != "tile":
+            bs.fp8_quantize_granular(a, w.a_fmt, gran, codes=qa, scales=sa)
+            if marks:
+                marks[1].record(stream)
+            bs.fp8_quantize_granular(b, w.b_fmt, gran, codes=qb, scales=sb)
         else:
             quant = bs.fp8_quantize_transposed if token_major else bs.fp8_quantize
             quant(a, w.a_fmt, codes=qa, scales=sa)
@@ -211,7 +259,10 @@ def main():
             quant(b, w.b_fmt, codes=qb, scales=sb)
         if marks:
             marks[2].record(stream)
-        bs.scaled_gemm(qa, sa, qb, sb, w.a_fmt, w.b_fmt, w.out, d=d, K=w.K)
+        if gran != "tile":
+            bs.scaled_gemm_granular(qa, sa, qb, sb, w.a_fmt, w.b_fmt, gran, gran, w.out, d=d, K=w.K)
+        else:
+            bs.scaled_gemm(qa, sa, qb, sb, w.a_fmt, w.b_fmt, w.out, d=d, K=w.K)
         if marks:
             marks[3].record(stream)
 
@@ -236,14 +287,16 @@ def main():
     in_type = "fp4" if mx else "fp8"
     gemm_tflops = w.flops / (gemm_ms * 1e-3) / 1e12
     src = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc",
-                       "gemm_mxfp4.hip" if mx else "gemm_fp8.hip")
-    traffic, traffic_src = committed_traffic(w.name, src)
+                       "gemm_mxfp4.hip" if mx else ("gemm_fp8.hip" if gran == "tile" else "gemm_fp8_outer.hip"))
+    profile_tag = w.name if gran == "tile" else f"{w.name}_{gran}"
+    traffic, traffic_src = committed_traffic(profile_tag, src)
 
     # quantiser bytes: read 4 B, write 1 B (FP8) or 0.5 B (MXFP4) per element, plus scales
     def qbytes(rows):
         if mx:
             return rows * w.K * 4 + rows * w.K // 2 + rows * (w.K // 32)
-        return rows * w.K * 4 + rows * w.K + ((rows + 127) // 128) * (w.K // 32) * 4
+        nscales = {"tile": ((rows + 127) // 128) * (w.K // 32), "row": rows, "tensor": 1}[gran]
+        return rows * w.K * 4 + rows * w.K + nscales * 4
 
     kernels = {
         "scaled_gemm_ms": round(gemm_ms, 4),
@@ -273,12 +326,18 @@ def main():
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "a_fmt": w.a_fmt,
                    "b_fmt": w.b_fmt, "out": w.out,
                    "operand_layout": "k-contiguous" if not token_major else "token-major",
+                   "scale_granularity": ("E8M0 per 32-element K block" if mx else
+                                         {"tile": "FP32 per 128x32 tile",
+                                          "row": "FP32 per row of A and per column of B",
+                                          "tensor": "FP32 per tensor"}[gran]),
                    "step": ("mxfp4_quantize(A)+mxfp4_quantize(B)+scaled_gemm" if mx else
+                            "fp8_quantize_granular(A)+fp8_quantize_granular(B)+scaled_gemm_granular"
+                            if gran != "tile" else
                             "fp8_quantize_transposed(G)+fp8_quantize_transposed(X)+scaled_gemm"
                             if token_major else "fp8_quantize(A)+fp8_quantize(B)+scaled_gemm")},
         "roofline": {
             "bound": "mfma",
-            "kernel": gemm_kernel_name(w),
+            "kernel": gemm_kernel_name(w, gran),
             "achieved": round(gemm_tflops, 1),
             "peak": PEAK_TFLOPS[in_type],
             "unit": "TFLOP/s",
@@ -294,7 +353,7 @@ def main():
         log("cpu baseline: timing the oracle on a bounded sample ...")
         rows = int(args.cpu_sample_gflop * 1e9 / (2.0 * w.N * w.K)) // 128 * 128
         rows = max(128, min(w.M, rows))
-        result["cpu_baseline"] = cpu_baseline(w, a_host, b_host, d_host, rows)
+        result["cpu_baseline"] = cpu_baseline(w, a_host, b_host, d_host, rows, gran)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

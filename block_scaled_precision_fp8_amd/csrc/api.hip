@@ -57,10 +57,9 @@ bsfp8_status fp8_quantize_granular(const float* x, int64_t rows, int64_t k, int6
     if (!x || !codes || !scales) return BSFP8_ERR_INVALID_ARG;
     if (!aligned(x, 16) || (ld % 4) != 0 || !aligned(codes, 4) || !aligned(scales, 4))
         return BSFP8_ERR_INVALID_ARG;
-    if (g == BSFP8_GRAN_ROW) {
-        if ((rows + 3) / 4 > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    if ((rows + 3) / 4 > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    if (g == BSFP8_GRAN_ROW)
         return from_hip(bsfp8::launch_fp8_quantize_rows(x, rows, k, ld, fmt, codes, scales, stream));
-    }
     return from_hip(bsfp8::launch_fp8_quantize_tensor(x, rows, k, ld, fmt, codes, scales, stream));
 }
 

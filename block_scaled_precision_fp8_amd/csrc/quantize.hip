@@ -315,23 +315,26 @@ __global__ __launch_bounds__(kThreads) void fp8_quantize_rows_kernel(
 }
 
 // Per-tensor scale, in four launches on one stream: the scale word is
-// cleared, every wave folds its maximum |x| into it with one atomic maximum on
-// the FP32 bit pattern (non-negative floats order like their bits), the codes
-// are computed from s = fl32(amax / F), and the word is replaced by s.
+// cleared, every workgroup folds its maximum |x| into it with one atomic
+// maximum on the FP32 bit pattern (non-negative floats order like their bits),
+// the codes are computed from s = fl32(amax / F), and the word is replaced by s.
 __global__ __launch_bounds__(64) void clear_word_kernel(uint32_t* word) {
     if (threadIdx.x == 0) *word = 0u;
 }
 
+// One wave per row, as in the per-row kernel; each workgroup folds the
+// maximum of its four rows into the word with one atomic.
 __global__ __launch_bounds__(kThreads) void amax_kernel(const float* __restrict__ x, int64_t rows,
                                                         int64_t k, int64_t ld, uint32_t* word) {
-    const int64_t per_row = k >> 2;                 // float4 chunks per row
-    const int64_t total = rows * per_row;
+    __shared__ float red[4];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
     float amax = 0.0f;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
-         i += static_cast<int64_t>(gridDim.x) * kThreads) {
-        const int64_t r = i / per_row;
-        const int64_t c = (i - r * per_row) * 4;
-        amax = fmaxf(amax, abs_max4(*reinterpret_cast<const float4*>(x + r * ld + c)));
+    if (row < rows) {
+        const float* xr = x + row * ld;
+        for (int64_t c = lane * 4; c < k; c += 256)
+            amax = fmaxf(amax, abs_max4(*reinterpret_cast<const float4*>(xr + c)));
     }
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
@@ -339,7 +342,10 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const float* __restrict_
     amax = fmaxf(amax, __shfl_xor(amax, 8));
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
-    if ((threadIdx.x & 63) == 0) atomicMax(word, __float_as_uint(amax));
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        atomicMax(word, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
 template <int FMT>
@@ -353,15 +359,14 @@ template <int FMT>
 __global__ __launch_bounds__(kThreads) void fp8_quantize_tensor_kernel(
     const float* __restrict__ x, int64_t rows, int64_t k, int64_t ld, const uint32_t* word,
     uint8_t* __restrict__ codes) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;                    // the whole wave leaves together
     const Fp8Quotient qt(tensor_scale<FMT>(word));
-    const int64_t per_row = k >> 2;
-    const int64_t total = rows * per_row;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
-         i += static_cast<int64_t>(gridDim.x) * kThreads) {
-        const int64_t r = i / per_row;
-        const int64_t c = (i - r * per_row) * 4;
-        *reinterpret_cast<uint32_t*>(codes + r * k + c) = fp8_codes4<FMT>(qt, load_once(x + r * ld + c));
-    }
+    const float* xr = x + row * ld;
+    uint8_t* cr = codes + row * k;
+    for (int64_t c = lane * 4; c < k; c += 256)
+        *reinterpret_cast<uint32_t*>(cr + c) = fp8_codes4<FMT>(qt, load_once(xr + c));
 }
 
 template <int FMT>
@@ -482,9 +487,7 @@ hipError_t launch_fp8_quantize_rows(const float* x, int64_t rows, int64_t k, int
 hipError_t launch_fp8_quantize_tensor(const float* x, int64_t rows, int64_t k, int64_t ld, int fmt,
                                       uint8_t* codes, float* scales, hipStream_t stream) {
     uint32_t* word = reinterpret_cast<uint32_t*>(scales);
-    const int64_t chunks = rows * (k >> 2);
-    const int64_t want = (chunks + kThreads - 1) / kThreads;
-    const dim3 grid(static_cast<uint32_t>(want < 4096 ? want : 4096));
+    const dim3 grid(static_cast<uint32_t>((rows + 3) / 4));
     hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, stream, word);
     hipLaunchKernelGGL(amax_kernel, grid, dim3(kThreads), 0, stream, x, rows, k, ld, word);
     if (fmt == BSFP8_E4M3) {
