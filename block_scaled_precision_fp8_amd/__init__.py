@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
     L.scaled_gemm_granular.argtypes = [i64, i64, i64, c_int, vp, vp, c_int, c_int, vp, vp, c_int,
                                        ctypes.c_float, vp, i64, ctypes.c_float, c_int, vp, i64, vp]
     L.scaled_gemm_granular.restype = c_int
+    L.scaled_gemm_quantize_a.argtypes = [i64, i64, i64, vp, i64, c_int, c_int, vp, vp, c_int,
+                                         ctypes.c_float, vp, i64, ctypes.c_float, c_int, vp, i64,
+                                         vp, vp, vp]
+    L.scaled_gemm_quantize_a.restype = c_int
     L.bsfp8_status_string.argtypes = [c_int]
     L.bsfp8_status_string.restype = ctypes.c_char_p
     L.bsfp8_version.argtypes = []
@@ -233,4 +237,38 @@ def scaled_gemm_granular(a, a_scales, b, b_scales, a_fmt: str = "e4m3", b_fmt: s
                                     _dev_ptr(b_scales), GRANULARITIES[b_gran], float(alpha), cptr,
                                     ldc, float(beta), OUTS[out], _dev_ptr(d), ldd, _stream(a))
     _check(st, "scaled_gemm_granular")
+    return d
+
+
+def scaled_gemm_quantize_a(x, b, b_scales, a_fmt: str = "e4m3", b_fmt: str = "e4m3",
+                           b_gran: str = "tile", out: str = "bf16", alpha: float = 1.0, c=None,
+                           beta: float = 0.0, d=None, a_codes=None, a_scales=None,
+                           return_a: bool = False):
+    """D = alpha * deq(Q(x)) deq(B) + beta * C with the FP32 A operand x
+    quantised per 128 x 32 tile inside the GEMM.  With return_a (or given
+    a_codes / a_scales buffers) A's codes and scales are written as well and
+    (d, a_codes, a_scales) is returned; otherwise d."""
+    import torch
+    M, K = x.shape
+    N = b.shape[0]
+    ldx = x.stride(0) if M > 1 else K
+    if d is None:
+        d = torch.empty((M, N), dtype=getattr(torch, _OUT_DTYPES[out]), device=x.device)
+    ldd = d.stride(0) if M > 1 else N
+    if c is None:
+        cptr, ldc = 0, 0
+    else:
+        cptr, ldc = _dev_ptr(c), (c.stride(0) if M > 1 else N)
+    if return_a and a_codes is None:
+        a_codes = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        a_scales = torch.empty(((M + FP8_TILE_ROWS - 1) // FP8_TILE_ROWS, K // 32),
+                               dtype=torch.float32, device=x.device)
+    st = lib().scaled_gemm_quantize_a(M, N, K, _dev_ptr(x), ldx, FORMATS[a_fmt], FORMATS[b_fmt],
+                                      _dev_ptr(b), _dev_ptr(b_scales), GRANULARITIES[b_gran],
+                                      float(alpha), cptr, ldc, float(beta), OUTS[out], _dev_ptr(d),
+                                      ldd, _dev_ptr(a_codes) if a_codes is not None else 0,
+                                      _dev_ptr(a_scales) if a_scales is not None else 0, _stream(x))
+    _check(st, "scaled_gemm_quantize_a")
+    if a_codes is not None:
+        return d, a_codes, a_scales
     return d

@@ -136,6 +136,48 @@ bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K, bsfp8_format 
                                                  ldd, ep, stream));
 }
 
+bsfp8_status scaled_gemm_quantize_a(int64_t M, int64_t N, int64_t K, const float* x, int64_t ldx,
+                                    bsfp8_format a_fmt, bsfp8_format b_fmt, const void* b,
+                                    const void* b_scales, bsfp8_granularity b_g, float alpha,
+                                    const void* c, int64_t ldc, float beta, bsfp8_out out, void* d,
+                                    int64_t ldd, uint8_t* a_codes, float* a_scales,
+                                    hipStream_t stream) {
+    if (!is_fp8(a_fmt) || !is_fp8(b_fmt)) return BSFP8_ERR_UNSUPPORTED;
+    if (b_g != BSFP8_GRAN_TILE && b_g != BSFP8_GRAN_TENSOR) return BSFP8_ERR_UNSUPPORTED;
+    if (out != BSFP8_OUT_F32 && out != BSFP8_OUT_BF16 && out != BSFP8_OUT_F16)
+        return BSFP8_ERR_UNSUPPORTED;
+    if (M < 0 || N < 0 || K < 0 || (K % 32) != 0 || ldx < K) return BSFP8_ERR_INVALID_ARG;
+    if (M > kI32Max || N > kI32Max || K > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    if ((a_codes == nullptr) != (a_scales == nullptr)) return BSFP8_ERR_INVALID_ARG;
+    if (a_codes && (!aligned(a_codes, 4) || !aligned(a_scales, 4))) return BSFP8_ERR_INVALID_ARG;
+    if (M == 0) return BSFP8_OK;
+    if (K > 0) {
+        if (!x || !aligned(x, 16) || (ldx % 4) != 0) return BSFP8_ERR_INVALID_ARG;
+        // the kernel addresses a 128-row band of x with 32-bit byte offsets
+        if (ldx >= (int64_t(1) << 22)) return BSFP8_ERR_UNSUPPORTED;
+    }
+    if (N == 0) {
+        // no output tile carries the quantisation: the codes come from the quantiser itself
+        if (a_codes && K > 0)
+            return from_hip(bsfp8::launch_fp8_quantize(x, M, K, ldx, a_fmt, a_codes, a_scales, stream));
+        return BSFP8_OK;
+    }
+    const uintptr_t es = out == BSFP8_OUT_F32 ? 4 : 2;
+    if (!d || ldd < N || !aligned(d, es)) return BSFP8_ERR_INVALID_ARG;
+    if (beta != 0.0f && (!c || ldc < N || !aligned(c, es))) return BSFP8_ERR_INVALID_ARG;
+    const bsfp8::Epilogue ep{alpha, beta, beta != 0.0f ? c : nullptr, beta != 0.0f ? ldc : 0};
+    if (K == 0) return from_hip(bsfp8::launch_fill(M, N, out, d, ldd, ep, stream));
+    if (!b || !b_scales || !aligned(b, 16) || !aligned(b_scales, 4)) return BSFP8_ERR_INVALID_ARG;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    const bsfp8::OnlineA qa{x, ldx, a_codes, a_scales};
+    return from_hip(bsfp8::launch_gemm_fp8_online_a(M, N, K, a_fmt, qa, b_fmt,
+                                                    static_cast<const uint8_t*>(b),
+                                                    static_cast<const float*>(b_scales),
+                                                    b_g == BSFP8_GRAN_TENSOR ? 1 : 0, out, d, ldd,
+                                                    ep, stream));
+}
+
 bsfp8_status scaled_gemm_ex(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt, const void* a,
                             const void* a_scales, bsfp8_format b_fmt, const void* b,
                             const void* b_scales, float alpha, const void* c, int64_t ldc,
@@ -165,6 +207,6 @@ const char* bsfp8_status_string(bsfp8_status s) {
     }
 }
 
-int bsfp8_version(void) { return (0 << 16) | 3; }
+int bsfp8_version(void) { return (0 << 16) | 4; }
 
 }  // extern "C"

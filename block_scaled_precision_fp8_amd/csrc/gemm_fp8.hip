@@ -42,7 +42,7 @@
 //    hoist them above it.  The stage barrier sits before a stage's last block,
 //    so the next stage's first fragments load under that block's MFMAs.
 //  * The output tile leaves through LDS, so every store writes whole rows.
-#include "internal.h"
+#include "fp8_codec.h"
 
 #include <utility>
 
@@ -110,6 +110,20 @@ __device__ __forceinline__ void lds_read16(u32x4& v, uint32_t addr) {
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
 }
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// A fragment read as inline assembly (ASM: ordered with the other volatile
+// statements, completion awaited by explicit lgkmcnt waits) or as an ordinary
+// LDS load whose completion the compiler tracks.  The ordinary form is needed
+// where registers run short: the compiler may copy an asm result to another
+// register before the explicit wait, i.e. before the data has arrived.
+template <int OFF, bool ASM>
+__device__ __forceinline__ void frag_read(u32x4& v, uint32_t addr) {
+    if constexpr (ASM) {
+        lds_read16<OFF>(v, addr);
+    } else {
+        typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+        v = *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(addr + OFF));
+    }
+}
 
 // LDS: per buffer, A then B, 128 rows x 128 bytes each, unpadded (filled by
 // direct global-to-LDS loads); row R keeps 16-byte chunk g at g ^ ((R >> 1) & 7).
@@ -141,12 +155,25 @@ __device__ __forceinline__ v16f tile_product(const u32x4& x, const u32x4& y) {
     return p;
 }
 
-template <int AF, int BF, int OUT>
-__global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
+// QA: the A operand arrives in FP32 and is quantised on its way to LDS
+// ("Why grind FP8 GEMM on CDNA4", section 4.2 converts and scales while
+// loading; section 3.3 overlaps the online scale computation with the loads).
+// Thread (xc = tid % 32, xr = tid / 32) holds 16-byte chunk xc of the stage's
+// 512-byte FP32 row segments of rows xr + 8 i, i = 0..15: each load instruction
+// of a wave reads two whole row segments, and all 64 values of a thread belong
+// to the tile of K block xc / 8 (the quantiser's own layout).  Stage t's
+// values are loaded during stage t - 2; their tile maxima are reduced across
+// lanes and published in LDS before the barrier of that stage's last block;
+// during blocks 0 and 1 of stage t - 1 the scales are formed, the values
+// encoded into LDS buffer t % 2 (free since that barrier) and the registers
+// reloaded with stage t + 1's values.  The codes are those of fp8_quantize.
+template <int AF, int BF, int OUT, bool QA>
+__global__ __launch_bounds__(kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
     const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D,
-    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok, int tensor_mask) {
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok, int tensor_mask, OnlineA qa) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kDLds];
+    __shared__ float red[2][4][4];      // QA: [stage parity][wave][K block] tile maxima
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -162,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
 
     // direct loads: instruction i (0..3) of wave w fills rows 32 i + 8 w .. + 7
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(A), 0, M * K, 0x00020000);
+        const_cast<uint8_t*>(A), 0, QA ? 0 : M * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(B), 0, N * K, 0x00020000);
     const int drow = 8 * wave + (lane >> 3);
@@ -174,14 +201,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
         constexpr int j = J;
         constexpr int i = j >> 1;
         const int so = min(stage, last) * 128;
-        if constexpr ((j & 1) == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs_a, (lds_void*)(lds + buf * kDStage + (32 * i + 8 * wave) * kDRow), 16,
-                dma_a + i * row_step, so, 0, 0);
-        else
+        if constexpr ((j & 1) == 0) {
+            if constexpr (!QA)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs_a, (lds_void*)(lds + buf * kDStage + (32 * i + 8 * wave) * kDRow), 16,
+                    dma_a + i * row_step, so, 0, 0);
+        } else {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rs_b, (lds_void*)(lds + buf * kDStage + kDOperand + (32 * i + 8 * wave) * kDRow), 16,
                 dma_b + i * row_step, so, 0, 0);
+        }
     };
 
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
@@ -203,20 +232,21 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
     // An operand with one scale per tensor (bit 0 of tensor_mask: A, bit 1: B)
     // has a one-float scale array: its stage loads read past that float as
     // zero and are not used; sa0 / sb0 stand in for them.
-    const bool a_tensor = (tensor_mask & 1) != 0;
+    const bool a_tensor = !QA && (tensor_mask & 1) != 0;
     const bool b_tensor = (tensor_mask & 2) != 0;
     const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(sA), 0, a_tensor ? 4 : static_cast<int>(tiles_m) * nkb * 4, 0x00020000);
+        const_cast<float*>(sA), 0, QA ? 0 : a_tensor ? 4 : static_cast<int>(tiles_m) * nkb * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(sB), 0, b_tensor ? 4 : static_cast<int>(tiles_n) * nkb * 4, 0x00020000);
     const uint32_t so_a = a_tensor ? 0u : static_cast<uint32_t>(tm) * nkb * 4;
     const uint32_t so_b = b_tensor ? 0u : static_cast<uint32_t>(tn) * nkb * 4;
-    const float sa0 = sA[0];
+    float sa0 = 0.0f;
+    if constexpr (!QA) sa0 = sA[0];
     const float sb0 = sB[0];
     auto sigma = [&](uint32_t a_bits, uint32_t b_bits) {
         return (a_tensor ? sa0 : __uint_as_float(a_bits)) * (b_tensor ? sb0 : __uint_as_float(b_bits));
     };
-    u32x4 nsa, nsb;
+    u32x4 nsa = u32x4{}, nsb;
     // The stage offset goes in the scalar offset, which the range check does
     // not cover; a per-tensor side keeps it at zero so that its loads stay
     // inside the one-float array (the rest of the 16 bytes reads as zero).
@@ -224,8 +254,96 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
         const int so = min(stage, last) * 16;
         const int so_sa = a_tensor ? 0 : so;
         const int so_sb = b_tensor ? 0 : so;
-        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsa) : "v"(so_a), "s"(rs_sa), "s"(so_sa) : "memory");
-        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsb) : "v"(so_b), "s"(rs_sb), "s"(so_sb) : "memory");
+        if constexpr (!QA) {
+            asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsa) : "v"(so_a), "s"(rs_sa), "s"(so_sa) : "memory");
+            asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsb) : "v"(so_b), "s"(rs_sb), "s"(so_sb) : "memory");
+        } else {
+            // a load whose completion the compiler tracks (see frag_read)
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_sb, static_cast<int>(so_b), so_sb, 0);
+            nsb = u32x4{v[0], v[1], v[2], v[3]};
+        }
+    };
+
+    // ---- QA state and steps (unused otherwise)
+    const int xc = tid & 31;
+    const int xr = tid >> 5;
+    const int xkb = xc >> 3;
+    const int rows_here = min(BM, M - m0);
+    // FP32 A rows of this tile; every offset is range checked (the resource
+    // starts at the tile's first row, so offsets stay below 128 ldx 4 < 2^31)
+    const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
+        QA ? const_cast<float*>(qa.x + static_cast<int64_t>(m0) * qa.ldx) : nullptr, 0,
+        QA ? rows_here * static_cast<int>(qa.ldx) * 4 : 0, 0x00020000);
+    const uint32_t x_off0 = static_cast<uint32_t>((xr * static_cast<int>(qa.ldx) + xc * 4) * 4);
+    const uint32_t x_row8 = static_cast<uint32_t>(32 * qa.ldx);
+    const bool write_a = QA && qa.codes != nullptr && tn == 0;
+    float4 xa[16];
+    float sa_cur[4], sa_next[4];
+    // item i of stage `stage` (clamped to the last stage); rows past M and
+    // columns past K read as zero
+    auto load_x = [&](auto I, int stage) {
+        constexpr int i = I;
+        const int st = min(stage, last);
+        const bool ok = xr + 8 * i < rows_here && st * 128 + xc * 4 < K;
+        const uint32_t vo = ok ? x_off0 + i * x_row8 + st * 512 : 0x80000000u;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_x, static_cast<int>(vo), 0, 0);
+        xa[i] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                            __uint_as_float(v[3]));
+    };
+    // the tile maxima of the values in xa, published in red[par] (the
+    // 16 lanes of a wave that hold one tile differ in lane bits 0, 1, 2 and 5)
+    auto publish_amax = [&](int par) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, abs_max4(xa[i]));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if ((lane & 0x27) == 0) red[par][wave][xkb] = m;
+    };
+    // this lane's tile scale from red[par]; all four go to sa_next
+    auto form_scales = [&](int par) {
+        constexpr float F = fp8_max<AF>();
+        const float am = fmaxf(fmaxf(red[par][0][xkb], red[par][1][xkb]),
+                               fmaxf(red[par][2][xkb], red[par][3][xkb]));
+        float s = am / F;
+        if (s == 0.0f) s = 1.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            sa_next[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 8 * k));
+        return s;
+    };
+    // encode items I0 .. I0 + 7 of stage `stage` into LDS buffer buf; code
+    // dword of item i: row R = xr + 8 i, bytes 4 xc .. 4 xc + 3 of the stage,
+    // i.e. 16-byte chunk xc / 4 stored at (xc / 4) ^ ((R >> 1) & 7)
+    auto encode = [&](auto I0, int stage, int buf, float s) {
+        uint32_t w[8];
+        if (__all(s >= kNearScaleMin)) {
+            const Fp8QuotientNear qt(s);
+            static_for<8>([&](auto J) { w[J] = fp8_codes4<AF>(qt, xa[I0 + J]); });
+        } else {
+            const Fp8Quotient qt(s);
+            static_for<8>([&](auto J) { w[J] = fp8_codes4<AF>(qt, xa[I0 + J]); });
+        }
+        static_for<8>([&](auto J) {
+            constexpr int i = I0 + J;
+            const int R = xr + 8 * i;
+            const int off = buf * kDStage + R * kDRow + (((xc >> 2) ^ ((R >> 1) & 7)) << 4) + (xc & 3) * 4;
+            *reinterpret_cast<uint32_t*>(lds + off) = w[J];
+        });
+        if (write_a && stage <= last) {
+            static_for<8>([&](auto J) {
+                constexpr int i = I0 + J;
+                const int R = xr + 8 * i;
+                const int col = stage * 128 + xc * 4;
+                if (R < rows_here && col < K)
+                    *reinterpret_cast<uint32_t*>(qa.codes + static_cast<int64_t>(m0 + R) * K + col) = w[J];
+            });
+            if constexpr (I0 == 0)
+                if (wave == 0 && (lane & 0x27) == 0 && stage * 4 + xkb < nkb)
+                    qa.scales[static_cast<int64_t>(tm) * nkb + stage * 4 + xkb] = s;
+        }
     };
 
     v16f acc[2][2];
@@ -235,28 +353,66 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
         for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
     u32x4 fx[2][2], fy[2][2];    // [set][t]
 
-    static_for<8>([&](auto J) { dma_one(J, 0, 0); });
-    load_scales(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    static_for<2>([&](auto t) {
-        lds_read16<t * 32 * kDRow>(fx[0][t], rd_b[0][0]);
-        lds_read16<t * 32 * kDRow>(fy[0][t], rd_a[0][0]);
-    });
-    static_for<8>([&](auto J) { dma_one(J, 1, 1); });
+    if constexpr (QA) {
+        // stage 0 quantised here; stage 1's maxima published
+        static_for<16>([&](auto I) { load_x(I, 0); });
+        static_for<8>([&](auto J) { dma_one(J, 0, 0); });
+        load_scales(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        publish_amax(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        {
+            const float s0 = form_scales(0);
+            encode(std::integral_constant<int, 0>{}, 0, 0, s0);
+            encode(std::integral_constant<int, 8>{}, 0, 0, s0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sa_cur[k] = sa_next[k];
+        static_for<16>([&](auto I) { load_x(I, 1); });
+        static_for<8>([&](auto J) { dma_one(J, 1, 1); });
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        publish_amax(1);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        static_for<2>([&](auto t) {
+            frag_read<t * 32 * kDRow, !QA>(fx[0][t], rd_b[0][0]);
+            frag_read<t * 32 * kDRow, !QA>(fy[0][t], rd_a[0][0]);
+        });
+    } else {
+        static_for<8>([&](auto J) { dma_one(J, 0, 0); });
+        load_scales(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        static_for<2>([&](auto t) {
+            frag_read<t * 32 * kDRow, !QA>(fx[0][t], rd_b[0][0]);
+            frag_read<t * 32 * kDRow, !QA>(fy[0][t], rd_a[0][0]);
+        });
+        static_for<8>([&](auto J) { dma_one(J, 1, 1); });
+    }
 
     // full stages run unconditionally; a partial last stage (K not a multiple
     // of 128) is finished by the tail below
     const int nfull = nkb >> 2;
     for (int s = 0; s < nfull; ++s) {
         const int cb = s & 1;
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // this stage's scales
+        // this stage's scales: issued one stage ago, followed by that stage's
+        // direct loads (8 without QA; with QA 16 FP32 loads and 4 direct
+        // loads, and in write_a workgroups code stores, hence the full wait)
+        if constexpr (QA) {
+            if (write_a) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        }
         u32x4 ca = nsa, cbv = nsb;
         asm volatile("" : "+v"(ca), "+v"(cbv));
         float sig[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) sig[k] = sigma(ca[k], cbv[k]);
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (QA) sig[k] = sa_cur[k] * (b_tensor ? sb0 : __uint_as_float(cbv[k]));
+            else sig[k] = sigma(ca[k], cbv[k]);
+        }
         load_scales(s + 1);
+        [[maybe_unused]] float s_own = 0.0f;
 
         auto block = [&](auto KB) {
             constexpr int kb = KB;
@@ -265,19 +421,26 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
             u32x4 (&f)[2] = fx[kb & 1];
             u32x4 (&g)[2] = fy[kb & 1];
             if constexpr (kb == 3) {
-                asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+                if constexpr (QA) {
+                    // stage s + 2's values are in (the compiler also waits for
+                    // its own loads before their first use); publish their maxima
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                                publish_amax(cb);
+                } else {
+                    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+                }
                 asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             } else {
                 lds_wait();
             }
             // prefetch the next block's fragments
             static_for<2>([&](auto t) {
-                lds_read16<t * 32 * kDRow>(fx[(kb + 1) & 1][t], rb ? rd_b[1][nkb_] : rd_b[0][nkb_]);
-                lds_read16<t * 32 * kDRow>(fy[(kb + 1) & 1][t], rb ? rd_a[1][nkb_] : rd_a[0][nkb_]);
+                frag_read<t * 32 * kDRow, !QA>(fx[(kb + 1) & 1][t], rb ? rd_b[1][nkb_] : rd_b[0][nkb_]);
+                frag_read<t * 32 * kDRow, !QA>(fy[(kb + 1) & 1][t], rb ? rd_a[1][nkb_] : rd_a[0][nkb_]);
             });
             if constexpr (kb == 3) static_for<8>([&](auto J) { dma_one(J, s + 2, cb); });
             // the MFMAs below may only start after the prefetch is issued
-            asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(g[0]), "+v"(g[1]));
+            if constexpr (!QA) asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(g[0]), "+v"(g[1]));
             {
                 const float sig_kb = sig[kb];
 #pragma unroll
@@ -289,6 +452,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
                         for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sig_kb, p[r], acc[ti][tj][r]);
                     }
             }
+            if constexpr (QA && kb < 2) {
+                // stage s + 1: encode half of the values into buffer cb ^ 1,
+                // then reload those registers with stage s + 2
+                if constexpr (kb == 0) s_own = form_scales(cb ^ 1);
+                encode(std::integral_constant<int, 8 * kb>{}, s + 1, cb ^ 1, s_own);
+                static_for<8>([&](auto J) { load_x(std::integral_constant<int, 8 * kb + J>{}, s + 2); });
+            }
             // close the block: its promotions finish before the next block's reads
             asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]));
         };
@@ -296,11 +466,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
         block(std::integral_constant<int, 1>{});
         block(std::integral_constant<int, 2>{});
         block(std::integral_constant<int, 3>{});
+        if constexpr (QA) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sa_cur[k] = sa_next[k];
+        }
     }
     if (nfull < nst) {
         // partial stage: its data and block-0 fragments are already in place
         const int cb = nfull & 1;
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        if constexpr (QA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         u32x4 ca = nsa, cbv = nsb;
         asm volatile("" : "+v"(ca), "+v"(cbv));
         const int nk = nkb - 4 * nfull;
@@ -312,15 +487,21 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
             } else {
                 const uint32_t ra = (cb ? rd_a[1][0] : rd_a[0][0]) + ((((2 * kb + half) ^ sw) - (half ^ sw)) * 16);
                 const uint32_t rb = (cb ? rd_b[1][0] : rd_b[0][0]) + ((((2 * kb + half) ^ sw) - (half ^ sw)) * 16);
-                lds_read16<0>(x[0], rb);
-                lds_read16<32 * kDRow>(x[1], rb);
-                lds_read16<0>(y[0], ra);
-                lds_read16<32 * kDRow>(y[1], ra);
+                frag_read<0, !QA>(x[0], rb);
+                frag_read<32 * kDRow, !QA>(x[1], rb);
+                frag_read<0, !QA>(y[0], ra);
+                frag_read<32 * kDRow, !QA>(y[1], ra);
                 lds_wait();
             }
             // the MFMAs consume the fragments only after the wait above
             asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
-            const float sig_kb = sigma(ca[kb], cbv[kb]);
+            float sig_kb;
+            if constexpr (QA) {
+                const float sak = kb == 0 ? sa_cur[0] : kb == 1 ? sa_cur[1] : sa_cur[2];
+                sig_kb = sak * (b_tensor ? sb0 : __uint_as_float(cbv[kb]));
+            } else {
+                sig_kb = sigma(ca[kb], cbv[kb]);
+            }
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
@@ -408,28 +589,42 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_kernel(
     }
 }
 
-template <int AF, int BF, int OUT>
+template <int AF, int BF, int OUT, bool QA>
 hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
                       const uint8_t* b, const float* sb, void* d, int64_t ldd,
-                      const Epilogue& ep, int tensor_mask, hipStream_t stream) {
+                      const Epilogue& ep, int tensor_mask, const OnlineA& qa, hipStream_t stream) {
     const int tiles_m = static_cast<int>((M + BM - 1) / BM);
     const int tiles_n = static_cast<int>((N + BN - 1) / BN);
     const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));
-    hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, OUT>), grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, OUT, QA>), grid, dim3(kThreads), 0, stream,
                        static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, sa, b, sb,
-                       d, ldd, ep, tiles_m, tiles_n, vec16_ok(OUT, d, ldd, ep), tensor_mask);
+                       d, ldd, ep, tiles_m, tiles_n, vec16_ok(OUT, d, ldd, ep), tensor_mask, qa);
     return hipGetLastError();
 }
 
-template <int AF, int BF>
+template <int AF, int BF, bool QA>
 hipError_t launch_typed(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
                         const uint8_t* b, const float* sb, int out, void* d, int64_t ldd,
-                        const Epilogue& ep, int tm, hipStream_t stream) {
+                        const Epilogue& ep, int tm, const OnlineA& qa, hipStream_t stream) {
     if (out == BSFP8_OUT_F32)
-        return launch_out<AF, BF, BSFP8_OUT_F32>(M, N, K, a, sa, b, sb, d, ldd, ep, tm, stream);
+        return launch_out<AF, BF, BSFP8_OUT_F32, QA>(M, N, K, a, sa, b, sb, d, ldd, ep, tm, qa, stream);
     if (out == BSFP8_OUT_BF16)
-        return launch_out<AF, BF, BSFP8_OUT_BF16>(M, N, K, a, sa, b, sb, d, ldd, ep, tm, stream);
-    return launch_out<AF, BF, BSFP8_OUT_F16>(M, N, K, a, sa, b, sb, d, ldd, ep, tm, stream);
+        return launch_out<AF, BF, BSFP8_OUT_BF16, QA>(M, N, K, a, sa, b, sb, d, ldd, ep, tm, qa, stream);
+    return launch_out<AF, BF, BSFP8_OUT_F16, QA>(M, N, K, a, sa, b, sb, d, ldd, ep, tm, qa, stream);
+}
+
+template <bool QA>
+hipError_t launch_formats(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,
+                          const float* a_scales, int b_fmt, const uint8_t* b, const float* b_scales,
+                          int out, void* d, int64_t ldd, const Epilogue& ep, int tensor_mask,
+                          const OnlineA& qa, hipStream_t stream) {
+    if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E4M3)
+        return launch_typed<BSFP8_E4M3, BSFP8_E4M3, QA>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, qa, stream);
+    if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E5M2)
+        return launch_typed<BSFP8_E4M3, BSFP8_E5M2, QA>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, qa, stream);
+    if (a_fmt == BSFP8_E5M2 && b_fmt == BSFP8_E4M3)
+        return launch_typed<BSFP8_E5M2, BSFP8_E4M3, QA>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, qa, stream);
+    return launch_typed<BSFP8_E5M2, BSFP8_E5M2, QA>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, qa, stream);
 }
 
 }  // namespace
@@ -438,13 +633,17 @@ hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, int a_fmt, const uin
                            const float* a_scales, int b_fmt, const uint8_t* b,
                            const float* b_scales, int out, void* d, int64_t ldd,
                            const Epilogue& ep, hipStream_t stream, int tensor_mask) {
-    if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E4M3)
-        return launch_typed<BSFP8_E4M3, BSFP8_E4M3>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, stream);
-    if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E5M2)
-        return launch_typed<BSFP8_E4M3, BSFP8_E5M2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, stream);
-    if (a_fmt == BSFP8_E5M2 && b_fmt == BSFP8_E4M3)
-        return launch_typed<BSFP8_E5M2, BSFP8_E4M3>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, stream);
-    return launch_typed<BSFP8_E5M2, BSFP8_E5M2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, stream);
+    const OnlineA none{nullptr, 0, nullptr, nullptr};
+    return launch_formats<false>(M, N, K, a_fmt, a, a_scales, b_fmt, b, b_scales, out, d, ldd, ep,
+                                 tensor_mask, none, stream);
+}
+
+hipError_t launch_gemm_fp8_online_a(int64_t M, int64_t N, int64_t K, int a_fmt, const OnlineA& qa,
+                                    int b_fmt, const uint8_t* b, const float* b_scales,
+                                    int b_tensor, int out, void* d, int64_t ldd,
+                                    const Epilogue& ep, hipStream_t stream) {
+    return launch_formats<true>(M, N, K, a_fmt, nullptr, nullptr, b_fmt, b, b_scales, out, d, ldd,
+                                ep, b_tensor ? 2 : 0, qa, stream);
 }
 
 }  // namespace bsfp8

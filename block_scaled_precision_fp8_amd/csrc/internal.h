@@ -42,6 +42,21 @@ hipError_t launch_gemm_fp8_outer(int64_t M, int64_t N, int64_t K, int a_fmt, con
                                  const float* a_scales, int a_step, int b_fmt, const uint8_t* b,
                                  const float* b_scales, int b_step, int out, void* d, int64_t ldd,
                                  const Epilogue& ep, hipStream_t stream);
+// The A operand given in FP32 (x, M x K, leading dimension ldx elements) and
+// quantised per 128 x 32 tile inside the per-tile FP8 GEMM, exactly as
+// launch_fp8_quantize would; codes / scales, when not null, receive copies of
+// A's codes (M x K, row stride K) and scales ([ceil(M / 128)][K / 32]).
+struct OnlineA {
+    const float* x;
+    int64_t ldx;
+    uint8_t* codes;
+    float* scales;
+};
+// b_tensor: b_scales is one scale for the whole of B.
+hipError_t launch_gemm_fp8_online_a(int64_t M, int64_t N, int64_t K, int a_fmt, const OnlineA& qa,
+                                    int b_fmt, const uint8_t* b, const float* b_scales,
+                                    int b_tensor, int out, void* d, int64_t ldd,
+                                    const Epilogue& ep, hipStream_t stream);
 hipError_t launch_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                              const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
                              int out, void* d, int64_t ldd, const Epilogue& ep,

@@ -7,25 +7,14 @@
 //
 // FP8 ("Why grind FP8 GEMM on CDNA4", sections 3.3 and 4.2): per 128 x 32
 // tile, s = fl32(amax / F) (1 for an all-zero tile), code = satRNE(fl32(x / s)).
-// The quotient fl32(x / s) is obtained without a per-element division, by
-// Markstein's correction step: with y the correctly rounded reciprocal of b and
-// q a faithful approximation of a / b, RN(q + y * (a - b q)) is the correctly
-// rounded a / b, provided a - b q (exact by FMA) does not underflow.  Both x
-// and s are first scaled by the same power of two 2^k (exact, quotient
-// unchanged) so that s 2^k lies in [1/2, 1); the residual can then underflow
-// only when |x / s| < 2^-99, where every FP8 code is a signed zero and the sign
-// is restored from x.  (Checked against IEEE division on 1.7e10 in-range pairs
-// per format, zero code mismatches; the parity tests compare every code with
-// the oracle.)  Saturation is an explicit clamp to +-F, after which the hardware
-// v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 conversion is exact round-to-nearest-even
-// (checked element by element against the oracle, including every midpoint).
+// The quotient, its clamp and the code conversion are in fp8_codec.h.
 //
 // MXFP4 ("Rubin FP4 GEMM deep dive", sections 2.1, 2.2, 3.1 and 4.2): per 32
 // consecutive K elements, e = smallest integer with 6 * 2^e >= amax, read off
 // the FP32 exponent and mantissa bits of amax; elements are scaled by the exact
 // power of two 2^-e and converted with v_cvt_scalef32_pk_fp4_f32 (unit scale),
 // which rounds to nearest even; two codes per byte, low nibble first.
-#include "internal.h"
+#include "fp8_codec.h"
 
 namespace bsfp8 {
 
@@ -39,50 +28,6 @@ __device__ __forceinline__ float4 load_once(const float* p) {
     typedef float f4v __attribute__((ext_vector_type(4)));
     const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
     return make_float4(t[0], t[1], t[2], t[3]);
-}
-
-__device__ __forceinline__ float abs_max4(float4 v) {
-    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-}
-
-// fl32(x / s), correctly rounded and clamped to +-F, as described in the
-// header: one correctly rounded reciprocal per scale, three FMA-class
-// operations per element.
-struct Fp8Quotient {
-    int se;
-    float ss, rs;
-    __device__ explicit Fp8Quotient(float s) {
-        (void)__builtin_frexpf(s, &se);
-        ss = __builtin_ldexpf(s, -se);     // s 2^k in [1/2, 1)
-        rs = 1.0f / ss;                    // correctly rounded
-    }
-    __device__ float operator()(float x, float F) const {
-        const float xs = __builtin_ldexpf(x, -se);
-        const float q0 = xs * rs;
-        const float e = __builtin_fmaf(-q0, ss, xs);
-        const float q = __builtin_copysignf(__builtin_fmaf(e, rs, q0), x);
-        return fminf(fmaxf(q, -F), F);
-    }
-};
-
-// Four clamped quotients -> four FP8 codes (round to nearest even), byte i = qi.
-template <int FMT>
-__device__ __forceinline__ uint32_t fp8_pack4(float q0, float q1, float q2, float q3) {
-    int w;
-    if constexpr (FMT == BSFP8_E4M3) {
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
-    } else {
-        w = __builtin_amdgcn_cvt_pk_bf8_f32(q0, q1, 0, false);
-        w = __builtin_amdgcn_cvt_pk_bf8_f32(q2, q3, w, true);
-    }
-    return static_cast<uint32_t>(w);
-}
-
-template <int FMT>
-__device__ __forceinline__ uint32_t fp8_codes4(const Fp8Quotient& qt, float4 v) {
-    constexpr float F = FMT == BSFP8_E4M3 ? 448.0f : 57344.0f;
-    return fp8_pack4<FMT>(qt(v.x, F), qt(v.y, F), qt(v.z, F), qt(v.w, F));
 }
 
 // One workgroup quantises a 128-row x 128-column block = four 128 x 32 tiles.

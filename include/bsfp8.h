@@ -226,6 +226,41 @@ bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K,
                                   float alpha, const void* c, int64_t ldc, float beta,
                                   bsfp8_out out, void* d, int64_t ldd, hipStream_t stream);
 
+/*
+ * scaled_gemm_quantize_a -- D = alpha * deq(Q(x)) deq(B) + beta * C, where
+ * Q(x) is the per-tile FP8 quantisation of the FP32 matrix x, carried out
+ * inside the GEMM while x is loaded (activations quantised online:
+ * [CDNA4-FP8] section 4.2 converts and scales on load, section 3.3 computes
+ * each tile's scale from its maximum; [RUBIN-FP4] section 4.2, step 4).
+ *
+ * x:       M x K FP32, row-major, leading dimension ldx (elements): 16-byte
+ *          aligned, ldx a multiple of 4, K <= ldx < 2^22.
+ * a_fmt:   the FP8 format of A's codes (E4M3 or E5M2).
+ * b_fmt, b, b_scales: as for scaled_gemm; b_g is BSFP8_GRAN_TILE (b_scales
+ *          FP32 [ceil(N/128)][K/32]) or BSFP8_GRAN_TENSOR (b_scales FP32 [1]).
+ * alpha, c, ldc, beta, out, d, ldd: as for scaled_gemm_ex.
+ * a_codes, a_scales: both NULL, or both non-NULL and 4-byte aligned: then
+ *          they receive A's codes (M x K bytes, row stride K) and scales
+ *          (FP32 [ceil(M/128)][K/32]), byte-for-byte what fp8_quantize with
+ *          tile_rows = 128 writes for x (for instance to keep the quantised
+ *          activations for a backward pass).
+ *
+ * The codes the GEMM multiplies are exactly those of fp8_quantize, so D is
+ * that of fp8_quantize followed by scaled_gemm_ex, with the same accuracy.
+ * M, N >= 0 (any value), K >= 0 a multiple of 32.  K = 0 writes beta * C.
+ * N = 0 writes only a_codes / a_scales (when given).  x must not overlap d,
+ * a_codes or a_scales.  The per-tile tile maximum is recomputed by every
+ * output tile that reads the same rows of x, so on wide outputs the separate
+ * quantisation pass is cheaper; this call removes that pass, its launch and
+ * its code traffic.
+ */
+bsfp8_status scaled_gemm_quantize_a(int64_t M, int64_t N, int64_t K, const float* x, int64_t ldx,
+                                    bsfp8_format a_fmt, bsfp8_format b_fmt, const void* b,
+                                    const void* b_scales, bsfp8_granularity b_g, float alpha,
+                                    const void* c, int64_t ldc, float beta, bsfp8_out out,
+                                    void* d, int64_t ldd, uint8_t* a_codes, float* a_scales,
+                                    hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* bsfp8_status_string(bsfp8_status s);
 

@@ -31,7 +31,8 @@ def L():
 def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("fp8_quantize", "fp8_quantize_transposed", "fp8_quantize_granular", "mxfp4_quantize",
-              "scaled_gemm", "scaled_gemm_ex", "scaled_gemm_granular", "bsfp8_status_string",
+              "scaled_gemm", "scaled_gemm_ex", "scaled_gemm_granular", "scaled_gemm_quantize_a",
+              "bsfp8_status_string",
               "bsfp8_version"):
         assert n in names
 
@@ -170,3 +171,33 @@ def test_scaled_gemm_granular_argument_checks(L):
     assert g(128, 128, 64, E4M3, P, 0, ROW, E4M3, P, P, ROW, 1.0, 0, 0, 0.0, BF16, P, 128, None) == INVALID
     assert g(128, 128, 64, E4M3, P, P + 2, ROW, E4M3, P, P, TENSOR, 1.0, 0, 0, 0.0, BF16, P, 128, None) == INVALID
     assert g(0, 128, 64, E4M3, 0, 0, ROW, E4M3, 0, 0, TENSOR, 1.0, 0, 0, 0.0, F32, 0, 128, None) == OK
+
+
+def test_scaled_gemm_quantize_a_argument_checks(L):
+    g = L.scaled_gemm_quantize_a
+    # (M, N, K, x, ldx, af, bf, b, sb, bg, alpha, c, ldc, beta, out, d, ldd, a_codes, a_scales, stream)
+    def call(M=128, N=128, K=64, x=P, ldx=64, af=E4M3, bf=E4M3, b=P, sb=P, bg=TILE, c=0, ldc=0,
+             beta=0.0, out=BF16, d=P, ldd=128, ac=0, asc=0):
+        return g(M, N, K, x, ldx, af, bf, b, sb, bg, 1.0, c, ldc, beta, out, d, ldd, ac, asc, None)
+    assert call(af=MXFP4) == UNSUPPORTED
+    assert call(bf=MXFP4) == UNSUPPORTED
+    assert call(bg=ROW) == UNSUPPORTED               # per-row B: not built with online A
+    assert call(bg=MX32) == UNSUPPORTED
+    assert call(out=7) == UNSUPPORTED
+    assert call(K=48, ldx=48) == INVALID              # K not a multiple of 32
+    assert call(ldx=32) == INVALID                    # ldx < K
+    assert call(ldx=66) == INVALID                    # ldx not a multiple of 4
+    assert call(x=P + 4) == INVALID                   # x not 16-byte aligned
+    assert call(x=0) == INVALID
+    assert call(ldx=1 << 22, K=64) == UNSUPPORTED     # beyond the kernel's 32-bit band offsets
+    assert call(ac=P) == INVALID                      # codes without scales
+    assert call(asc=P) == INVALID
+    assert call(ac=P + 2, asc=P) == INVALID
+    assert call(b=0) == INVALID
+    assert call(sb=P + 2) == INVALID
+    assert call(d=0) == INVALID
+    assert call(ldd=100) == INVALID
+    assert call(beta=1.0) == INVALID                  # beta != 0 needs C
+    assert call(M=-1) == INVALID
+    assert call(M=0, x=0, d=0) == OK                  # nothing to do
+    assert call(N=0, d=0) == OK                       # no output and no codes requested
