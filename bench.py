@@ -20,9 +20,12 @@ Also reported, on the same JSON line:
 FP8 workloads can also be run with scales constant along K
 (--granularity row: per-row A and per-column B, or tensor: one scale per
 operand); the step then uses fp8_quantize_granular and scaled_gemm_granular.
+With --a-path online (per-tile scales) A is quantised inside the GEMM:
+fp8_quantize(B), scaled_gemm_quantize_a(A) without code output.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--granularity tile|row|tensor] [--no-cpu-baseline]
+                       [--granularity tile|row|tensor] [--a-path separate|online]
+                       [--no-cpu-baseline]
                        [--copy-calibration]
 Only one GPU is supported; --gpus N with N > 1 exits with a message.
 """
@@ -73,9 +76,11 @@ def committed_traffic(workload, source_file):
         return None, None
 
 
-def gemm_kernel_name(w, gran="tile"):
+def gemm_kernel_name(w, gran="tile", online=False):
     """The kernel scaled_gemm dispatches for this workload (mirrors the
     launchers' selection)."""
+    if online:
+        return "gemm_fp8_kernel (A quantised by quantiser waves)"
     if w.a_fmt != "mxfp4" and gran != "tile":
         return "gemm_fp8_outer_kernel"
     if w.a_fmt == "mxfp4":
@@ -186,6 +191,9 @@ def main():
     p.add_argument("--granularity", choices=["tile", "row", "tensor"], default="tile",
                    help="FP8 only: scale granularity of both operands (row = per-row A and "
                         "per-column B)")
+    p.add_argument("--a-path", choices=["separate", "online"], default="separate",
+                   help="FP8 per-tile only: online quantises A inside the GEMM "
+                        "(scaled_gemm_quantize_a) instead of a separate fp8_quantize pass")
     args = p.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -214,6 +222,11 @@ def main():
     token_major = layout == "token-major" and not mx
     if token_major and gran != "tile":
         print("bench.py: the token-major layout is quantised with per-tile scales only", file=sys.stderr)
+        sys.exit(2)
+    online = args.a_path == "online"
+    if online and (mx or gran != "tile" or token_major):
+        print("bench.py: --a-path online needs FP8 per-tile scales and K-contiguous operands",
+              file=sys.stderr)
         sys.exit(2)
     if token_major:     # G (K x M) and X (K x N) as stored in the backward pass
         a = torch.from_numpy(np.ascontiguousarray(a_host.T)).to(dev)
@@ -246,6 +259,10 @@ def main():
         if mx:
             bs.mxfp4_quantize(a, qa, sa)
             bs.mxfp4_quantize(b, qb, sb)
+        elif online:
+            if marks:
+                marks[1].record(stream)
+            bs.fp8_quantize(b, w.b_fmt, codes=qb, scales=sb)
         elif gran != "tile":
             bs.fp8_quantize_granular(a, w.a_fmt, gran, codes=qa, scales=sa)
             if marks:
@@ -259,7 +276,9 @@ def main():
             quant(b, w.b_fmt, codes=qb, scales=sb)
         if marks:
             marks[2].record(stream)
-        if gran != "tile":
+        if online:
+            bs.scaled_gemm_quantize_a(a, qb, sb, w.a_fmt, w.b_fmt, "tile", w.out, d=d)
+        elif gran != "tile":
             bs.scaled_gemm_granular(qa, sa, qb, sb, w.a_fmt, w.b_fmt, gran, gran, w.out, d=d, K=w.K)
         else:
             bs.scaled_gemm(qa, sa, qb, sb, w.a_fmt, w.b_fmt, w.out, d=d, K=w.K)
@@ -288,7 +307,7 @@ def main():
     gemm_tflops = w.flops / (gemm_ms * 1e-3) / 1e12
     src = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc",
                        "gemm_mxfp4.hip" if mx else ("gemm_fp8.hip" if gran == "tile" else "gemm_fp8_outer.hip"))
-    profile_tag = w.name if gran == "tile" else f"{w.name}_{gran}"
+    profile_tag = f"{w.name}_online" if online else (w.name if gran == "tile" else f"{w.name}_{gran}")
     traffic, traffic_src = committed_traffic(profile_tag, src)
 
     # quantiser bytes: read 4 B, write 1 B (FP8) or 0.5 B (MXFP4) per element, plus scales
@@ -303,7 +322,7 @@ def main():
         "scaled_gemm_tflops": round(gemm_tflops, 1),
         "scaled_gemm_frac_of_peak": round(gemm_tflops / PEAK_TFLOPS[in_type], 4),
         "quantize_AB_ms": round(quant_ms, 4),
-        "quantize_AB_gbps": round((qbytes(w.M) + qbytes(w.N)) / (quant_ms * 1e-3) / 1e9, 1),
+        "quantize_AB_gbps": round(((0 if online else qbytes(w.M)) + qbytes(w.N)) / (quant_ms * 1e-3) / 1e9, 1),
     }
     if not mx:
         kernels["quantize_A_ms"] = round(qa_ms, 4)
@@ -330,14 +349,16 @@ def main():
                                          {"tile": "FP32 per 128x32 tile",
                                           "row": "FP32 per row of A and per column of B",
                                           "tensor": "FP32 per tensor"}[gran]),
+                   "a_path": "quantised inside the GEMM" if online else "separate quantiser",
                    "step": ("mxfp4_quantize(A)+mxfp4_quantize(B)+scaled_gemm" if mx else
+                            "fp8_quantize(B)+scaled_gemm_quantize_a(A)" if online else
                             "fp8_quantize_granular(A)+fp8_quantize_granular(B)+scaled_gemm_granular"
                             if gran != "tile" else
                             "fp8_quantize_transposed(G)+fp8_quantize_transposed(X)+scaled_gemm"
                             if token_major else "fp8_quantize(A)+fp8_quantize(B)+scaled_gemm")},
         "roofline": {
             "bound": "mfma",
-            "kernel": gemm_kernel_name(w, gran),
+            "kernel": gemm_kernel_name(w, gran, online),
             "achieved": round(gemm_tflops, 1),
             "peak": PEAK_TFLOPS[in_type],
             "unit": "TFLOP/s",

@@ -10,6 +10,12 @@ namespace {
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline bool is_fp8(int f) { return f == BSFP8_E4M3 || f == BSFP8_E5M2; }
 constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+// scaled_gemm_quantize_a: from this many 128-wide output column tiles on, a
+// call that also asks for A's codes quantises A once and runs the per-tile
+// GEMM (measured on MI355X: the in-kernel quantisation costs about one GEMM's
+// time again, the separate pass about M K 5 bytes at 5.5 TB/s, which it
+// undercuts below about 450 output columns)
+constexpr int64_t kOnlineMaxColumnTiles = 4;
 
 inline bsfp8_status from_hip(hipError_t e) { return e == hipSuccess ? BSFP8_OK : BSFP8_ERR_HIP; }
 
@@ -170,11 +176,21 @@ bsfp8_status scaled_gemm_quantize_a(int64_t M, int64_t N, int64_t K, const float
     if (!b || !b_scales || !aligned(b, 16) || !aligned(b_scales, 4)) return BSFP8_ERR_INVALID_ARG;
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    const uint8_t* b8 = static_cast<const uint8_t*>(b);
+    const float* sb = static_cast<const float*>(b_scales);
+    if (a_codes && tiles / ((M + 127) / 128) >= kOnlineMaxColumnTiles) {
+        // A wide output re-quantises every A tile once per column of output
+        // tiles; with somewhere to put the codes it is cheaper to quantise
+        // once and run the per-tile GEMM on them (the same codes and the same
+        // accumulation, so the same D).
+        const hipError_t e = bsfp8::launch_fp8_quantize(x, M, K, ldx, a_fmt, a_codes, a_scales, stream);
+        if (e != hipSuccess) return BSFP8_ERR_HIP;
+        return from_hip(bsfp8::launch_gemm_fp8(M, N, K, a_fmt, a_codes, a_scales, b_fmt, b8, sb, out, d,
+                                               ldd, ep, stream, b_g == BSFP8_GRAN_TENSOR ? 2 : 0));
+    }
     const bsfp8::OnlineA qa{x, ldx, a_codes, a_scales};
     return from_hip(bsfp8::launch_gemm_fp8_online_a(M, N, K, a_fmt, qa, b_fmt,
-                                                    static_cast<const uint8_t*>(b),
-                                                    static_cast<const float*>(b_scales),
-                                                    b_g == BSFP8_GRAN_TENSOR ? 1 : 0, out, d, ldd,
+                                                    b8, sb, b_g == BSFP8_GRAN_TENSOR ? 1 : 0, out, d, ldd,
                                                     ep, stream));
 }
 

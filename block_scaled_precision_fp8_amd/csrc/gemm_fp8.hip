@@ -110,20 +110,6 @@ __device__ __forceinline__ void lds_read16(u32x4& v, uint32_t addr) {
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
 }
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// A fragment read as inline assembly (ASM: ordered with the other volatile
-// statements, completion awaited by explicit lgkmcnt waits) or as an ordinary
-// LDS load whose completion the compiler tracks.  The ordinary form is needed
-// where registers run short: the compiler may copy an asm result to another
-// register before the explicit wait, i.e. before the data has arrived.
-template <int OFF, bool ASM>
-__device__ __forceinline__ void frag_read(u32x4& v, uint32_t addr) {
-    if constexpr (ASM) {
-        lds_read16<OFF>(v, addr);
-    } else {
-        typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-        v = *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(addr + OFF));
-    }
-}
 
 // LDS: per buffer, A then B, 128 rows x 128 bytes each, unpadded (filled by
 // direct global-to-LDS loads); row R keeps 16-byte chunk g at g ^ ((R >> 1) & 7).
@@ -155,25 +141,41 @@ __device__ __forceinline__ v16f tile_product(const u32x4& x, const u32x4& y) {
     return p;
 }
 
-// QA: the A operand arrives in FP32 and is quantised on its way to LDS
-// ("Why grind FP8 GEMM on CDNA4", section 4.2 converts and scales while
-// loading; section 3.3 overlaps the online scale computation with the loads).
-// Thread (xc = tid % 32, xr = tid / 32) holds 16-byte chunk xc of the stage's
-// 512-byte FP32 row segments of rows xr + 8 i, i = 0..15: each load instruction
-// of a wave reads two whole row segments, and all 64 values of a thread belong
-// to the tile of K block xc / 8 (the quantiser's own layout).  Stage t's
-// values are loaded during stage t - 2; their tile maxima are reduced across
-// lanes and published in LDS before the barrier of that stage's last block;
-// during blocks 0 and 1 of stage t - 1 the scales are formed, the values
-// encoded into LDS buffer t % 2 (free since that barrier) and the registers
-// reloaded with stage t + 1's values.  The codes are those of fp8_quantize.
+// QA: the A operand arrives in FP32 and is quantised inside the kernel on its
+// way to LDS ("Why grind FP8 GEMM on CDNA4", section 4.2 converts and scales
+// while loading; section 3.3 overlaps the online scale computation with the
+// loads).  The workgroup then has 8 waves: waves 0-3 run the GEMM exactly as
+// without QA (B still arrives by direct loads), waves 4-7 quantise A.  Each
+// SIMD runs one GEMM wave and one quantiser wave, so the quantisation's VALU
+// work interleaves with the other wave's MFMAs, and the GEMM waves keep their
+// whole register budget.
+//
+// Quantiser thread q = tid - 256 (xc = q % 32, xr = q / 32) holds 16-byte chunk
+// xc of the stage's 512-byte FP32 row segments of rows xr + 8 i, i = 0..15:
+// each load instruction of a wave reads two whole row segments, and all 64
+// values of a thread belong to the tile of K block xc / 8 (the quantiser's own
+// layout).  Two register sets alternate.  Between the stage barriers s - 1 and
+// s the quantiser waves
+//   1. issue the loads of stage s + 2's values,
+//   2. form stage s + 1's tile scales from the maxima published before barrier
+//      s - 1, and store them in LDS for the GEMM waves,
+//   3. encode stage s + 1's values into LDS buffer (s + 1) % 2 (free since
+//      barrier s - 1; the GEMM waves read it after barrier s),
+//   4. reduce the tile maxima of stage s + 2's values (lane shuffles, then one
+//      value per wave in LDS), to be combined after barrier s.
+// The codes are those of fp8_quantize; tn == 0 workgroups can also store them.
+constexpr int kQThreads = 512;
+// __syncthreads() calls in the epilogue, matched by the quantiser waves
+constexpr int kEpilogueBarriers = 2;
+
 template <int AF, int BF, int OUT, bool QA>
-__global__ __launch_bounds__(kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
+__global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
     const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D,
     int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok, int tensor_mask, OnlineA qa) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kDLds];
-    __shared__ float red[2][4][4];      // QA: [stage parity][wave][K block] tile maxima
+    __shared__ float red[2][4][4];      // QA: [stage parity][quantiser wave][K block] tile maxima
+    __shared__ float sa_lds[2][4];      // QA: [stage parity][K block] A tile scales
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,6 +188,127 @@ __global__ __launch_bounds__(kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
     const int nkb = K >> 5;
     const int nst = (nkb + 3) >> 2;          // 128 K per stage
     const int last = nst - 1;
+    const int nfull = nkb >> 2;              // full stages; a partial last stage follows
+
+    if constexpr (QA) {
+        if (wave >= 4) {
+            const int q = tid - 256;
+            const int cw = wave - 4;
+            const int xc = q & 31;
+            const int xr = q >> 5;
+            const int xkb = xc >> 3;
+            const int rows_here = min(BM, M - m0);
+            // FP32 A rows of this tile; every offset is range checked (the
+            // resource starts at the tile's first row, so offsets stay below
+            // 128 ldx 4 < 2^31)
+            const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(qa.x + static_cast<int64_t>(m0) * qa.ldx), 0,
+                rows_here * static_cast<int>(qa.ldx) * 4, 0x00020000);
+            const uint32_t x_off0 = static_cast<uint32_t>((xr * static_cast<int>(qa.ldx) + xc * 4) * 4);
+            const uint32_t x_row8 = static_cast<uint32_t>(32 * qa.ldx);
+            const bool write_a = qa.codes != nullptr && tn == 0;
+            float4 xa[16], xb[16];
+            // stage `stage`'s values (clamped to the last stage); rows past M
+            // and columns past K read as zero
+            auto load = [&](float4 (&v)[16], int stage) {
+                const int st = min(stage, last);
+                const bool col_ok = st * 128 + xc * 4 < K;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const bool ok = col_ok && xr + 8 * i < rows_here;
+                    const uint32_t vo = ok ? x_off0 + i * x_row8 + st * 512 : 0x80000000u;
+                    const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs_x, static_cast<int>(vo), 0, 0);
+                    v[i] = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]),
+                                       __uint_as_float(w[2]), __uint_as_float(w[3]));
+                }
+            };
+            // this wave's tile maxima of v into red[par] (the 16 lanes of a
+            // wave that hold one tile differ in lane bits 0, 1, 2 and 5)
+            auto publish = [&](const float4 (&v)[16], int par) {
+                float m = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m = fmaxf(m, abs_max4(v[i]));
+                m = fmaxf(m, __shfl_xor(m, 1));
+                m = fmaxf(m, __shfl_xor(m, 2));
+                m = fmaxf(m, __shfl_xor(m, 4));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                if ((lane & 0x27) == 0) red[par][cw][xkb] = m;
+            };
+            // this lane's tile scale of stage `stage` from red[stage % 2]; the
+            // four scales also go to sa_lds for the GEMM waves (and to
+            // qa.scales in write_a workgroups)
+            auto form = [&](int stage) {
+                constexpr float F = fp8_max<AF>();
+                const int par = stage & 1;
+                const float am = fmaxf(fmaxf(red[par][0][xkb], red[par][1][xkb]),
+                                       fmaxf(red[par][2][xkb], red[par][3][xkb]));
+                float sc = am / F;
+                if (sc == 0.0f) sc = 1.0f;
+                if (cw == 0 && (lane & 0x27) == 0) {
+                    sa_lds[par][xkb] = sc;
+                    if (write_a && stage <= last && stage * 4 + xkb < nkb)
+                        qa.scales[static_cast<int64_t>(tm) * nkb + stage * 4 + xkb] = sc;
+                }
+                return sc;
+            };
+            // encode v (stage `stage`) into LDS buffer stage % 2: the code
+            // dword of item i is row R = xr + 8 i, bytes 4 xc .. 4 xc + 3 of
+            // the stage, i.e. in 16-byte chunk xc / 4, stored at
+            // (xc / 4) ^ ((R >> 1) & 7) like the direct loads of B
+            auto encode = [&](const float4 (&v)[16], int stage, float sc) {
+                uint32_t w[16];
+                if (__all(sc >= kNearScaleMin)) {
+                    const Fp8QuotientNear qt(sc);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) w[i] = fp8_codes4<AF>(qt, v[i]);
+                } else {
+                    const Fp8Quotient qt(sc);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) w[i] = fp8_codes4<AF>(qt, v[i]);
+                }
+                const int buf = stage & 1;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int R = xr + 8 * i;
+                    const int off = buf * kDStage + R * kDRow + (((xc >> 2) ^ ((R >> 1) & 7)) << 4) + (xc & 3) * 4;
+                    *reinterpret_cast<uint32_t*>(lds + off) = w[i];
+                }
+                if (write_a && stage <= last) {
+                    const int col = stage * 128 + xc * 4;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int R = xr + 8 * i;
+                        if (R < rows_here && col < K)
+                            *reinterpret_cast<uint32_t*>(qa.codes + static_cast<int64_t>(m0 + R) * K + col) = w[i];
+                    }
+                }
+            };
+            auto barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+            // between stage barriers s - 1 and s: cur holds stage s + 1, nxt
+            // receives stage s + 2
+            auto step = [&](float4 (&cur)[16], float4 (&nxt)[16], int s) {
+                load(nxt, s + 2);
+                encode(cur, s + 1, form(s + 1));
+                publish(nxt, s & 1);
+                barrier();
+            };
+            // the GEMM waves' two prologue barriers
+            load(xa, 0);
+            publish(xa, 0);
+            barrier();
+            load(xb, 1);
+            encode(xa, 0, form(0));
+            publish(xb, 1);
+            barrier();
+            for (int s = 0; s < nfull; s += 2) {
+                step(xb, xa, s);
+                if (s + 1 < nfull) step(xa, xb, s + 1);
+            }
+#pragma unroll
+            for (int i = 0; i < kEpilogueBarriers; ++i) __syncthreads();
+            return;
+        }
+    }
 
     // direct loads: instruction i (0..3) of wave w fills rows 32 i + 8 w .. + 7
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
@@ -197,6 +320,7 @@ __global__ __launch_bounds__(kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
     const uint32_t dma_a = static_cast<uint32_t>(m0 + drow) * K + dchunk * 16;
     const uint32_t dma_b = static_cast<uint32_t>(n0 + drow) * K + dchunk * 16;
     const uint32_t row_step = 32u * static_cast<uint32_t>(K);
+    // direct loads of a stage: A (without QA) and B, alternating
     auto dma_one = [&](auto J, int stage, int buf) {
         constexpr int j = J;
         constexpr int i = j >> 1;
@@ -229,6 +353,7 @@ __global__ __launch_bounds__(kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
         }
 
     // scales of a stage: 4 floats of A's tile row and 4 of B's, loaded one stage ahead
+    // (with QA, A's come from the quantiser waves through LDS)
     // An operand with one scale per tensor (bit 0 of tensor_mask: A, bit 1: B)
     // has a one-float scale array: its stage loads read past that float as
     // zero and are not used; sa0 / sb0 stand in for them.
@@ -254,96 +379,9 @@ __global__ __launch_bounds__(kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
         const int so = min(stage, last) * 16;
         const int so_sa = a_tensor ? 0 : so;
         const int so_sb = b_tensor ? 0 : so;
-        if constexpr (!QA) {
+        if constexpr (!QA)
             asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsa) : "v"(so_a), "s"(rs_sa), "s"(so_sa) : "memory");
-            asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsb) : "v"(so_b), "s"(rs_sb), "s"(so_sb) : "memory");
-        } else {
-            // a load whose completion the compiler tracks (see frag_read)
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_sb, static_cast<int>(so_b), so_sb, 0);
-            nsb = u32x4{v[0], v[1], v[2], v[3]};
-        }
-    };
-
-    // ---- QA state and steps (unused otherwise)
-    const int xc = tid & 31;
-    const int xr = tid >> 5;
-    const int xkb = xc >> 3;
-    const int rows_here = min(BM, M - m0);
-    // FP32 A rows of this tile; every offset is range checked (the resource
-    // starts at the tile's first row, so offsets stay below 128 ldx 4 < 2^31)
-    const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
-        QA ? const_cast<float*>(qa.x + static_cast<int64_t>(m0) * qa.ldx) : nullptr, 0,
-        QA ? rows_here * static_cast<int>(qa.ldx) * 4 : 0, 0x00020000);
-    const uint32_t x_off0 = static_cast<uint32_t>((xr * static_cast<int>(qa.ldx) + xc * 4) * 4);
-    const uint32_t x_row8 = static_cast<uint32_t>(32 * qa.ldx);
-    const bool write_a = QA && qa.codes != nullptr && tn == 0;
-    float4 xa[16];
-    float sa_cur[4], sa_next[4];
-    // item i of stage `stage` (clamped to the last stage); rows past M and
-    // columns past K read as zero
-    auto load_x = [&](auto I, int stage) {
-        constexpr int i = I;
-        const int st = min(stage, last);
-        const bool ok = xr + 8 * i < rows_here && st * 128 + xc * 4 < K;
-        const uint32_t vo = ok ? x_off0 + i * x_row8 + st * 512 : 0x80000000u;
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs_x, static_cast<int>(vo), 0, 0);
-        xa[i] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
-                            __uint_as_float(v[3]));
-    };
-    // the tile maxima of the values in xa, published in red[par] (the
-    // 16 lanes of a wave that hold one tile differ in lane bits 0, 1, 2 and 5)
-    auto publish_amax = [&](int par) {
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, abs_max4(xa[i]));
-        m = fmaxf(m, __shfl_xor(m, 1));
-        m = fmaxf(m, __shfl_xor(m, 2));
-        m = fmaxf(m, __shfl_xor(m, 4));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        if ((lane & 0x27) == 0) red[par][wave][xkb] = m;
-    };
-    // this lane's tile scale from red[par]; all four go to sa_next
-    auto form_scales = [&](int par) {
-        constexpr float F = fp8_max<AF>();
-        const float am = fmaxf(fmaxf(red[par][0][xkb], red[par][1][xkb]),
-                               fmaxf(red[par][2][xkb], red[par][3][xkb]));
-        float s = am / F;
-        if (s == 0.0f) s = 1.0f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            sa_next[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 8 * k));
-        return s;
-    };
-    // encode items I0 .. I0 + 7 of stage `stage` into LDS buffer buf; code
-    // dword of item i: row R = xr + 8 i, bytes 4 xc .. 4 xc + 3 of the stage,
-    // i.e. 16-byte chunk xc / 4 stored at (xc / 4) ^ ((R >> 1) & 7)
-    auto encode = [&](auto I0, int stage, int buf, float s) {
-        uint32_t w[8];
-        if (__all(s >= kNearScaleMin)) {
-            const Fp8QuotientNear qt(s);
-            static_for<8>([&](auto J) { w[J] = fp8_codes4<AF>(qt, xa[I0 + J]); });
-        } else {
-            const Fp8Quotient qt(s);
-            static_for<8>([&](auto J) { w[J] = fp8_codes4<AF>(qt, xa[I0 + J]); });
-        }
-        static_for<8>([&](auto J) {
-            constexpr int i = I0 + J;
-            const int R = xr + 8 * i;
-            const int off = buf * kDStage + R * kDRow + (((xc >> 2) ^ ((R >> 1) & 7)) << 4) + (xc & 3) * 4;
-            *reinterpret_cast<uint32_t*>(lds + off) = w[J];
-        });
-        if (write_a && stage <= last) {
-            static_for<8>([&](auto J) {
-                constexpr int i = I0 + J;
-                const int R = xr + 8 * i;
-                const int col = stage * 128 + xc * 4;
-                if (R < rows_here && col < K)
-                    *reinterpret_cast<uint32_t*>(qa.codes + static_cast<int64_t>(m0 + R) * K + col) = w[J];
-            });
-            if constexpr (I0 == 0)
-                if (wave == 0 && (lane & 0x27) == 0 && stage * 4 + xkb < nkb)
-                    qa.scales[static_cast<int64_t>(tm) * nkb + stage * 4 + xkb] = s;
-        }
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsb) : "v"(so_b), "s"(rs_sb), "s"(so_sb) : "memory");
     };
 
     v16f acc[2][2];
@@ -353,66 +391,35 @@ __global__ __launch_bounds__(kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
         for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
     u32x4 fx[2][2], fy[2][2];    // [set][t]
 
-    if constexpr (QA) {
-        // stage 0 quantised here; stage 1's maxima published
-        static_for<16>([&](auto I) { load_x(I, 0); });
-        static_for<8>([&](auto J) { dma_one(J, 0, 0); });
-        load_scales(0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        publish_amax(0);
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        {
-            const float s0 = form_scales(0);
-            encode(std::integral_constant<int, 0>{}, 0, 0, s0);
-            encode(std::integral_constant<int, 8>{}, 0, 0, s0);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) sa_cur[k] = sa_next[k];
-        static_for<16>([&](auto I) { load_x(I, 1); });
-        static_for<8>([&](auto J) { dma_one(J, 1, 1); });
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        publish_amax(1);
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        static_for<2>([&](auto t) {
-            frag_read<t * 32 * kDRow, !QA>(fx[0][t], rd_b[0][0]);
-            frag_read<t * 32 * kDRow, !QA>(fy[0][t], rd_a[0][0]);
-        });
-    } else {
-        static_for<8>([&](auto J) { dma_one(J, 0, 0); });
-        load_scales(0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        static_for<2>([&](auto t) {
-            frag_read<t * 32 * kDRow, !QA>(fx[0][t], rd_b[0][0]);
-            frag_read<t * 32 * kDRow, !QA>(fy[0][t], rd_a[0][0]);
-        });
-        static_for<8>([&](auto J) { dma_one(J, 1, 1); });
-    }
+    static_for<8>([&](auto J) { dma_one(J, 0, 0); });
+    load_scales(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // with QA, a second barrier: stage 0's A codes and scales are in LDS
+    if constexpr (QA) asm volatile("s_barrier" ::: "memory");
+    static_for<2>([&](auto t) {
+        lds_read16<t * 32 * kDRow>(fx[0][t], rd_b[0][0]);
+        lds_read16<t * 32 * kDRow>(fy[0][t], rd_a[0][0]);
+    });
+    static_for<8>([&](auto J) { dma_one(J, 1, 1); });
 
     // full stages run unconditionally; a partial last stage (K not a multiple
     // of 128) is finished by the tail below
-    const int nfull = nkb >> 2;
     for (int s = 0; s < nfull; ++s) {
         const int cb = s & 1;
-        // this stage's scales: issued one stage ago, followed by that stage's
-        // direct loads (8 without QA; with QA 16 FP32 loads and 4 direct
-        // loads, and in write_a workgroups code stores, hence the full wait)
-        if constexpr (QA) {
-            if (write_a) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        }
+        // this stage's scales: issued one stage ago, followed by the direct
+        // loads of the next stage (8 of them, 4 with QA)
+        if constexpr (QA) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         u32x4 ca = nsa, cbv = nsb;
         asm volatile("" : "+v"(ca), "+v"(cbv));
         float sig[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            if constexpr (QA) sig[k] = sa_cur[k] * (b_tensor ? sb0 : __uint_as_float(cbv[k]));
+            if constexpr (QA) sig[k] = sa_lds[cb][k] * (b_tensor ? sb0 : __uint_as_float(cbv[k]));
             else sig[k] = sigma(ca[k], cbv[k]);
         }
         load_scales(s + 1);
-        [[maybe_unused]] float s_own = 0.0f;
 
         auto block = [&](auto KB) {
             constexpr int kb = KB;
@@ -421,26 +428,22 @@ __global__ __launch_bounds__(kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
             u32x4 (&f)[2] = fx[kb & 1];
             u32x4 (&g)[2] = fy[kb & 1];
             if constexpr (kb == 3) {
-                if constexpr (QA) {
-                    // stage s + 2's values are in (the compiler also waits for
-                    // its own loads before their first use); publish their maxima
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                                publish_amax(cb);
-                } else {
-                    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-                }
+                // the next stage's direct loads are in (only its scales, one
+                // load, or two without QA, may be outstanding)
+                if constexpr (QA) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
                 asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             } else {
                 lds_wait();
             }
             // prefetch the next block's fragments
             static_for<2>([&](auto t) {
-                frag_read<t * 32 * kDRow, !QA>(fx[(kb + 1) & 1][t], rb ? rd_b[1][nkb_] : rd_b[0][nkb_]);
-                frag_read<t * 32 * kDRow, !QA>(fy[(kb + 1) & 1][t], rb ? rd_a[1][nkb_] : rd_a[0][nkb_]);
+                lds_read16<t * 32 * kDRow>(fx[(kb + 1) & 1][t], rb ? rd_b[1][nkb_] : rd_b[0][nkb_]);
+                lds_read16<t * 32 * kDRow>(fy[(kb + 1) & 1][t], rb ? rd_a[1][nkb_] : rd_a[0][nkb_]);
             });
             if constexpr (kb == 3) static_for<8>([&](auto J) { dma_one(J, s + 2, cb); });
             // the MFMAs below may only start after the prefetch is issued
-            if constexpr (!QA) asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(g[0]), "+v"(g[1]));
+            asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(g[0]), "+v"(g[1]));
             {
                 const float sig_kb = sig[kb];
 #pragma unroll
@@ -452,13 +455,6 @@ __global__ __launch_bounds__(kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
                         for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sig_kb, p[r], acc[ti][tj][r]);
                     }
             }
-            if constexpr (QA && kb < 2) {
-                // stage s + 1: encode half of the values into buffer cb ^ 1,
-                // then reload those registers with stage s + 2
-                if constexpr (kb == 0) s_own = form_scales(cb ^ 1);
-                encode(std::integral_constant<int, 8 * kb>{}, s + 1, cb ^ 1, s_own);
-                static_for<8>([&](auto J) { load_x(std::integral_constant<int, 8 * kb + J>{}, s + 2); });
-            }
             // close the block: its promotions finish before the next block's reads
             asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]));
         };
@@ -466,15 +462,11 @@ __global__ __launch_bounds__(kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
         block(std::integral_constant<int, 1>{});
         block(std::integral_constant<int, 2>{});
         block(std::integral_constant<int, 3>{});
-        if constexpr (QA) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) sa_cur[k] = sa_next[k];
-        }
     }
     if (nfull < nst) {
         // partial stage: its data and block-0 fragments are already in place
         const int cb = nfull & 1;
-        if constexpr (QA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (QA) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         u32x4 ca = nsa, cbv = nsb;
         asm volatile("" : "+v"(ca), "+v"(cbv));
@@ -487,21 +479,17 @@ __global__ __launch_bounds__(kThreads, QA ? 1 : 2) void gemm_fp8_kernel(
             } else {
                 const uint32_t ra = (cb ? rd_a[1][0] : rd_a[0][0]) + ((((2 * kb + half) ^ sw) - (half ^ sw)) * 16);
                 const uint32_t rb = (cb ? rd_b[1][0] : rd_b[0][0]) + ((((2 * kb + half) ^ sw) - (half ^ sw)) * 16);
-                frag_read<0, !QA>(x[0], rb);
-                frag_read<32 * kDRow, !QA>(x[1], rb);
-                frag_read<0, !QA>(y[0], ra);
-                frag_read<32 * kDRow, !QA>(y[1], ra);
+                lds_read16<0>(x[0], rb);
+                lds_read16<32 * kDRow>(x[1], rb);
+                lds_read16<0>(y[0], ra);
+                lds_read16<32 * kDRow>(y[1], ra);
                 lds_wait();
             }
             // the MFMAs consume the fragments only after the wait above
             asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
             float sig_kb;
-            if constexpr (QA) {
-                const float sak = kb == 0 ? sa_cur[0] : kb == 1 ? sa_cur[1] : sa_cur[2];
-                sig_kb = sak * (b_tensor ? sb0 : __uint_as_float(cbv[kb]));
-            } else {
-                sig_kb = sigma(ca[kb], cbv[kb]);
-            }
+            if constexpr (QA) sig_kb = sa_lds[cb][kb] * (b_tensor ? sb0 : __uint_as_float(cbv[kb]));
+            else sig_kb = sigma(ca[kb], cbv[kb]);
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
@@ -596,7 +584,7 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const f
     const int tiles_m = static_cast<int>((M + BM - 1) / BM);
     const int tiles_n = static_cast<int>((N + BN - 1) / BN);
     const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));
-    hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, OUT, QA>), grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((gemm_fp8_kernel<AF, BF, OUT, QA>), grid, dim3(QA ? kQThreads : kThreads), 0, stream,
                        static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, sa, b, sb,
                        d, ldd, ep, tiles_m, tiles_n, vec16_ok(OUT, d, ldd, ep), tensor_mask, qa);
     return hipGetLastError();

@@ -243,16 +243,18 @@ bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K,
  *          they receive A's codes (M x K bytes, row stride K) and scales
  *          (FP32 [ceil(M/128)][K/32]), byte-for-byte what fp8_quantize with
  *          tile_rows = 128 writes for x (for instance to keep the quantised
- *          activations for a backward pass).
+ *          activations for a backward pass).  With them and N > 384 the call
+ *          runs fp8_quantize into them and then the GEMM (two launches, the
+ *          same result): quantising every A tile once beats re-quantising it
+ *          for every column of output tiles.
  *
  * The codes the GEMM multiplies are exactly those of fp8_quantize, so D is
  * that of fp8_quantize followed by scaled_gemm_ex, with the same accuracy.
  * M, N >= 0 (any value), K >= 0 a multiple of 32.  K = 0 writes beta * C.
  * N = 0 writes only a_codes / a_scales (when given).  x must not overlap d,
- * a_codes or a_scales.  The per-tile tile maximum is recomputed by every
- * output tile that reads the same rows of x, so on wide outputs the separate
- * quantisation pass is cheaper; this call removes that pass, its launch and
- * its code traffic.
+ * a_codes or a_scales.  Every output tile that reads the same rows of x
+ * quantises them again, so the single-launch form pays off on narrow outputs
+ * (a few hundred columns) and small, launch-bound products.
  */
 bsfp8_status scaled_gemm_quantize_a(int64_t M, int64_t N, int64_t K, const float* x, int64_t ldx,
                                     bsfp8_format a_fmt, bsfp8_format b_fmt, const void* b,

@@ -12,6 +12,10 @@
   per-tensor B.
 * The full 4096^3 launch of the square workload: every A code and scale, and
   sampled outputs.
+With A's codes requested and more than three 128-wide column tiles of output
+the call quantises A first and runs the per-tile GEMM; the single-launch
+kernel runs otherwise, and the tests cover both (wide outputs without code
+output included).
 """
 import numpy as np
 import pytest
@@ -207,3 +211,34 @@ def test_online_a_square_4096_full_codes_sampled_outputs():
     err = np.abs(d[ii, jj].astype(np.float64) - dr) / sr
     say(f"sampled max |D-Dref|/S = {err.max():.3e}")
     assert err.max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("M,N,K,out", [(256, 1024, 512, "bf16"), (130, 700, 288, "f32"),
+                                       (4096, 4096, 4096, "bf16")])
+def test_online_a_wide_output_single_launch(M, N, K, out):
+    """Without code output every shape runs the single-launch kernel; at
+    4096^3 (the square workload's launch) outputs are sampled."""
+    import torch
+    say(f"scaled_gemm_quantize_a single launch M={M} N={N} K={K} -> {out}")
+    if M == 4096:
+        w = workloads.by_name("square_e4m3_4096")
+        x, bh = workloads.operands(w)
+        qb, sb = oracle.fp8_quantize(bh, "e4m3")
+    else:
+        x = inputs(M + N + K, M, K, "tiles")
+        qb, sb = b_operand(N + 9, N, K, "e4m3", kind="normal")
+    d = bsfp8().scaled_gemm_quantize_a(to_dev(x), to_dev(qb), to_dev(sb), "e4m3", "e4m3", "tile", out)
+    torch.cuda.synchronize()
+    d = from_dev(d)
+    rq, rs = oracle.fp8_quantize(x, "e4m3")
+    if M == 4096:
+        rng = np.random.default_rng(131)
+        ii = np.concatenate([rng.integers(0, M, 300), [0, M - 1, 127, 128]])
+        jj = np.concatenate([rng.integers(0, N, 300), [N - 1, 0, 128, 127]])
+        dr, sr = oracle.gemm_points("e4m3", rq, rs, "e4m3", qb, sb, ii, jj)
+        err = np.abs(d[ii, jj].astype(np.float64) - dr) / sr
+        say(f"sampled max |D-Dref|/S = {err.max():.3e}")
+        assert err.max() <= TOL[out]
+    else:
+        dr, sr = oracle.gemm_granular("e4m3", rq, rs, "tile", "e4m3", qb, sb, "tile")
+        check_gemm(d, dr, sr, out, f"single launch {M}x{N}x{K} {out}")
