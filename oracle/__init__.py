@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_fp8_quantize_groups.restype = c_int
         L.oracle_mxfp4_quantize.argtypes = [vp, i64, i64, i64, vp, vp]
         L.oracle_mxfp4_quantize.restype = c_int
+        L.oracle_mx_quantize.argtypes = [vp, i64, i64, i64, i64, c_int, vp, vp]
+        L.oracle_mx_quantize.restype = c_int
         L.oracle_gemm_rows.argtypes = [i64, i64, i64, i64, c_int, vp, vp, c_int, vp, vp,
                                        i64, i64, vp, vp]
         L.oracle_gemm_rows.restype = c_int
@@ -164,6 +166,58 @@ def gemm_granular(a_fmt, a, a_scales, a_gran, b_fmt, b, b_scales, b_gran):
     dequantised operands are exact; the sums round at most K 2^-53 S."""
     ad = dequantize_granular(a_fmt, a, a_scales, a_gran)
     bd = dequantize_granular(b_fmt, b, b_scales, b_gran)
+    return ad @ bd.T, np.abs(ad) @ np.abs(bd).T
+
+
+MX_BLOCKS = (32, 16, 8)
+MX_SCALES = {"e8m0": 0, "f16": 1, "bf16": 2}
+
+
+def mx_quantize(x: np.ndarray, block: int = 32, scale: str = "e8m0"):
+    """E2M1 block quantisation with blocks of `block` (32, 16 or 8) consecutive
+    K elements and block scales of format `scale` ("e8m0", "f16", "bf16").
+    x: rows x k float32, k a multiple of block.  Returns (packed uint8
+    rows x k/2, low nibble first; scales [rows][k/block]: uint8 E8M0 codes or
+    uint16 FP16 / BF16 bit patterns)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, k = x.shape
+    packed = np.zeros((rows, k // 2), dtype=np.uint8)
+    sdt = np.uint8 if scale == "e8m0" else np.uint16
+    scales = np.zeros((rows, k // block), dtype=sdt)
+    rc = lib().oracle_mx_quantize(_ptr(x), rows, k, k, block, MX_SCALES[scale], _ptr(packed),
+                                  _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_mx_quantize rc={rc}")
+    return packed, scales
+
+
+def mx_scale_values(scales: np.ndarray, scale: str) -> np.ndarray:
+    """Block scale values in fp64: E8M0 by the oracle's table, FP16 by numpy's
+    binary16, BF16 as the upper half of a binary32."""
+    scales = np.asarray(scales)
+    if scale == "e8m0":
+        return decode_table("e8m0")[scales.astype(np.int64)]
+    if scale == "f16":
+        return scales.astype(np.uint16).view(np.float16).astype(np.float64)
+    return (scales.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def dequantize_mx(packed: np.ndarray, scales: np.ndarray, block: int = 32, scale: str = "e8m0"):
+    """rows x k fp64 values code * scale of an MX-variant operand."""
+    packed = np.asarray(packed)
+    rows, kh = packed.shape
+    nib = np.empty((rows, 2 * kh), dtype=np.int64)
+    nib[:, 0::2] = packed & 0xF
+    nib[:, 1::2] = packed >> 4
+    sv = np.repeat(mx_scale_values(scales, scale), block, axis=1)
+    return decode_table("e2m1")[nib] * sv
+
+
+def gemm_mx(a, a_scales, b, b_scales, block: int = 32, scale: str = "e8m0"):
+    """D = deq(A) deq(B)^T and S = |deq(A)| |deq(B)|^T in fp64 for MX-variant
+    operands (A: M x K/2 packed, B: N x K/2 packed)."""
+    ad = dequantize_mx(a, a_scales, block, scale)
+    bd = dequantize_mx(b, b_scales, block, scale)
     return ad @ bd.T, np.abs(ad) @ np.abs(bd).T
 
 

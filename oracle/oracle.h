@@ -12,6 +12,8 @@ extern "C" {
 #endif
 
 enum { ORC_E4M3 = 0, ORC_E5M2 = 1, ORC_E2M1 = 2, ORC_E8M0 = 3, ORC_MXFP4 = 2 };
+/* block scale formats of oracle_mx_quantize */
+enum { ORC_SCALE_E8M0 = 0, ORC_SCALE_F16 = 1, ORC_SCALE_BF16 = 2 };
 
 int oracle_decode_table(int fmt, double* out);          /* returns entry count */
 double oracle_decode(int fmt, unsigned code);
@@ -26,6 +28,8 @@ int oracle_fp8_quantize_groups(const float* x, int64_t rows, int64_t k, int64_t 
                                float* scales);
 int oracle_mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
                           uint8_t* packed, uint8_t* scales);
+int oracle_mx_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, int64_t block,
+                       int sfmt, uint8_t* packed, void* scales);
 
 int oracle_gemm_rows(int64_t M, int64_t N, int64_t K, int64_t tile_rows,
                      int a_fmt, const uint8_t* a, const void* a_scales,

@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ORACLE_C = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_quantize.py", "tests/test_oracle_gemm.py",
-        "tests/test_oracle_granular.py"]
+        "tests/test_oracle_granular.py", "tests/test_oracle_mx_variants.py"]
 
 # (name, text in oracle.c, replacement): each a mistake someone could make.
 # Left out as equivalent (no result can differ): reading both GEMM operands'
@@ -62,6 +62,19 @@ MUTATIONS = [
     ("product-sign", "                        double p = ar[c] * bj[c];\n                        acc += p;",
      "                        double p = ar[c] * bj[c];\n                        acc += (c % 2) ? -p : p;"),
     ("magnitude-signed", "                        mag += fabs(p);", "                        mag += p;"),
+    ("mx-variant-half-block", "int64_t c0 = b * block, c1 = c0 + block;",
+     "int64_t c0 = b * block, c1 = c0 + block / 2;"),
+    ("f16-scale-precision", "*p = 11; *emin = -14; *bias = 15; *vmax = 65504.0;",
+     "*p = 10; *emin = -14; *bias = 15; *vmax = 65504.0;"),
+    ("bf16-scale-precision", "*p = 8; *emin = -126; *bias = 127;", "*p = 9; *emin = -126; *bias = 127;"),
+    ("scale-ties-up", "(2.0 * rem == ulp && fmod(n, 2.0) != 0.0)", "(2.0 * rem == ulp)"),
+    ("scale-truncated", "if (2.0 * rem > ulp || (2.0 * rem == ulp", "if (2.0 * rem > 2.0 * ulp || (2.0 * rem == ulp"),
+    ("scale-unsaturated", "return r > vmax ? vmax : r;", "return r;"),
+    ("scale-zero-kept", "if (sd == 0.0) sd = 1.0;", "if (sd == 0.0) sd = 0.5;"),
+    ("subnormal-scale-bits", "return (unsigned)ldexp(v, p - 1 - emin);", "return (unsigned)ldexp(v, p - emin);"),
+    ("scale-denominator", "round_to_format(amax / 6.0, p, emin, vmax)", "round_to_format(amax / 4.0, p, emin, vmax)"),
+    ("wide-scale-reciprocal", "float y = x[r * ld + c] / sf;  /* IEEE binary32 division */",
+     "float y = x[r * ld + c] * (1.0f / sf);"),
     ("dropped-last-term", "                    for (int64_t c = 0; c < K; ++c) {\n                        double p = ar[c] * bj[c];",
      "                    for (int64_t c = 0; c + 1 < K; ++c) {\n                        double p = ar[c] * bj[c];"),
 ]
