@@ -26,6 +26,7 @@ LIB_PATH = os.environ.get("BSFP8_LIB", os.path.join(_HERE, "libbsfp8.so"))
 FORMATS = {"e4m3": 0, "e5m2": 1, "mxfp4": 2}
 OUTS = {"f32": 0, "bf16": 1, "f16": 2}
 GRANULARITIES = {"tile": 0, "row": 1, "tensor": 2, "mx32": 3}
+MX_SCALES = {"e8m0": 0, "f16": 1, "bf16": 2}
 STATUS = {0: "BSFP8_OK", 1: "BSFP8_ERR_INVALID_ARG", 2: "BSFP8_ERR_UNSUPPORTED",
           3: "BSFP8_ERR_HIP"}
 FP8_TILE_ROWS = 128
@@ -65,6 +66,11 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_float, vp, i64, ctypes.c_float, c_int, vp, i64,
                                          vp, vp, vp]
     L.scaled_gemm_quantize_a.restype = c_int
+    L.mx_quantize.argtypes = [vp, i64, i64, i64, c_int, c_int, vp, vp, vp]
+    L.mx_quantize.restype = c_int
+    L.scaled_gemm_mx.argtypes = [i64, i64, i64, c_int, c_int, vp, vp, vp, vp, ctypes.c_float, vp, i64,
+                                 ctypes.c_float, c_int, vp, i64, vp]
+    L.scaled_gemm_mx.restype = c_int
     L.bsfp8_status_string.argtypes = [c_int]
     L.bsfp8_status_string.restype = ctypes.c_char_p
     L.bsfp8_version.argtypes = []
@@ -271,4 +277,47 @@ def scaled_gemm_quantize_a(x, b, b_scales, a_fmt: str = "e4m3", b_fmt: str = "e4
     _check(st, "scaled_gemm_quantize_a")
     if a_codes is not None:
         return d, a_codes, a_scales
+    return d
+
+
+def mx_quantize(x, block: int = 32, scale: str = "e8m0", packed=None, scales=None):
+    """E2M1 quantisation with blocks of `block` (32, 16, 8) K elements and
+    block scales of format `scale` ("e8m0" bytes, "f16" / "bf16" 16-bit
+    patterns).  Returns (packed rows x k/2 uint8, scales [rows][k/block])."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32 CUDA tensor with unit column stride")
+    rows, k = x.shape
+    if packed is None:
+        packed = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        sdt = torch.uint8 if scale == "e8m0" else torch.int16
+        scales = torch.empty((rows, k // block), dtype=sdt, device=x.device)
+    st = lib().mx_quantize(_dev_ptr(x), rows, k, x.stride(0) if rows > 1 else k, block,
+                           MX_SCALES[scale], _dev_ptr(packed), _dev_ptr(scales), _stream(x))
+    _check(st, "mx_quantize")
+    return packed, scales
+
+
+def scaled_gemm_mx(a, a_scales, b, b_scales, block: int = 32, scale: str = "e8m0",
+                   out: str = "bf16", alpha: float = 1.0, c=None, beta: float = 0.0, d=None,
+                   K: Optional[int] = None):
+    """D = alpha * deq(A) deq(B) + beta * C for mx_quantize operands (A: M x K/2,
+    B: N x K/2 packed, scales [rows][K/block])."""
+    import torch
+    M = a.shape[0]
+    N = b.shape[0]
+    if K is None:
+        K = a.shape[1] * 2
+    if d is None:
+        d = torch.empty((M, N), dtype=getattr(torch, _OUT_DTYPES[out]), device=a.device)
+    ldd = d.stride(0) if M > 1 else N
+    if c is None:
+        cptr, ldc = 0, 0
+    else:
+        cptr, ldc = _dev_ptr(c), (c.stride(0) if M > 1 else N)
+    st = lib().scaled_gemm_mx(M, N, K, block, MX_SCALES[scale], _dev_ptr(a), _dev_ptr(a_scales),
+                              _dev_ptr(b), _dev_ptr(b_scales), float(alpha), cptr, ldc, float(beta),
+                              OUTS[out], _dev_ptr(d), ldd, _stream(a))
+    _check(st, "scaled_gemm_mx")
     return d

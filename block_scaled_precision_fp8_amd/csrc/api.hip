@@ -80,6 +80,21 @@ bsfp8_status mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
     return from_hip(bsfp8::launch_mxfp4_quantize(x, rows, k, ld, packed, scales, stream));
 }
 
+bsfp8_status mx_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, int block,
+                         bsfp8_mx_scale sfmt, uint8_t* packed, void* scales, hipStream_t stream) {
+    if (block != 32 && block != 16 && block != 8) return BSFP8_ERR_UNSUPPORTED;
+    if (sfmt != BSFP8_MX_E8M0 && sfmt != BSFP8_MX_F16 && sfmt != BSFP8_MX_BF16)
+        return BSFP8_ERR_UNSUPPORTED;
+    if (rows < 0 || k < 0 || ld < k || (k % 32) != 0) return BSFP8_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return BSFP8_OK;
+    if (!x || !packed || !scales) return BSFP8_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || (ld % 4) != 0 || !aligned(packed, 2)) return BSFP8_ERR_INVALID_ARG;
+    if (sfmt != BSFP8_MX_E8M0 && !aligned(scales, 2)) return BSFP8_ERR_INVALID_ARG;
+    const int64_t blocks = (rows * (k / 4) + 255) / 256;
+    if (rows > kI32Max * 256 || blocks > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    return from_hip(bsfp8::launch_mx_quantize(x, rows, k, ld, block, sfmt, packed, scales, stream));
+}
+
 bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K, bsfp8_format a_fmt,
                                   const void* a, const void* a_scales, bsfp8_granularity a_g,
                                   bsfp8_format b_fmt, const void* b, const void* b_scales,
@@ -140,6 +155,38 @@ bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K, bsfp8_format 
     return from_hip(bsfp8::launch_gemm_fp8_outer(M, N, K, a_fmt, a8, sa, a_g == BSFP8_GRAN_ROW ? 1 : 0,
                                                  b_fmt, b8, sb, b_g == BSFP8_GRAN_ROW ? 1 : 0, out, d,
                                                  ldd, ep, stream));
+}
+
+bsfp8_status scaled_gemm_mx(int64_t M, int64_t N, int64_t K, int block, bsfp8_mx_scale sfmt,
+                            const void* a, const void* a_scales, const void* b,
+                            const void* b_scales, float alpha, const void* c, int64_t ldc,
+                            float beta, bsfp8_out out, void* d, int64_t ldd, hipStream_t stream) {
+    if (block != 32 && block != 16 && block != 8) return BSFP8_ERR_UNSUPPORTED;
+    if (sfmt != BSFP8_MX_E8M0 && sfmt != BSFP8_MX_F16 && sfmt != BSFP8_MX_BF16)
+        return BSFP8_ERR_UNSUPPORTED;
+    if (out != BSFP8_OUT_F32 && out != BSFP8_OUT_BF16 && out != BSFP8_OUT_F16)
+        return BSFP8_ERR_UNSUPPORTED;
+    if (block == 32 && sfmt == BSFP8_MX_E8M0)   // the hardware-scaled MXFP4 GEMM
+        return scaled_gemm_granular(M, N, K, BSFP8_MXFP4, a, a_scales, BSFP8_GRAN_MX32, BSFP8_MXFP4,
+                                    b, b_scales, BSFP8_GRAN_MX32, alpha, c, ldc, beta, out, d, ldd,
+                                    stream);
+    if (M < 0 || N < 0 || K < 0 || (K % 32) != 0) return BSFP8_ERR_INVALID_ARG;
+    if (M > kI32Max || N > kI32Max || K > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return BSFP8_OK;
+    const uintptr_t es = out == BSFP8_OUT_F32 ? 4 : 2;
+    if (!d || ldd < N || !aligned(d, es)) return BSFP8_ERR_INVALID_ARG;
+    if (beta != 0.0f && (!c || ldc < N || !aligned(c, es))) return BSFP8_ERR_INVALID_ARG;
+    const bsfp8::Epilogue ep{alpha, beta, beta != 0.0f ? c : nullptr, beta != 0.0f ? ldc : 0};
+    if (K == 0) return from_hip(bsfp8::launch_fill(M, N, out, d, ldd, ep, stream));
+    if (!a || !b || !a_scales || !b_scales) return BSFP8_ERR_INVALID_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16)) return BSFP8_ERR_INVALID_ARG;
+    if (sfmt != BSFP8_MX_E8M0 && (!aligned(a_scales, 2) || !aligned(b_scales, 2)))
+        return BSFP8_ERR_INVALID_ARG;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    return from_hip(bsfp8::launch_gemm_mx(M, N, K, block, sfmt, static_cast<const uint8_t*>(a), a_scales,
+                                          static_cast<const uint8_t*>(b), b_scales, out, d, ldd, ep,
+                                          stream));
 }
 
 bsfp8_status scaled_gemm_quantize_a(int64_t M, int64_t N, int64_t K, const float* x, int64_t ldx,
@@ -223,6 +270,6 @@ const char* bsfp8_status_string(bsfp8_status s) {
     }
 }
 
-int bsfp8_version(void) { return (0 << 16) | 4; }
+int bsfp8_version(void) { return (0 << 16) | 5; }
 
 }  // extern "C"

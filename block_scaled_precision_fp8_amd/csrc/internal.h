@@ -21,6 +21,9 @@ hipError_t launch_fp8_quantize_tensor(const float* x, int64_t rows, int64_t k, i
                                       uint8_t* codes, float* scales, hipStream_t stream);
 hipError_t launch_mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
                                  uint8_t* packed, uint8_t* scales, hipStream_t stream);
+// E2M1 with blocks of `block` (32, 16, 8) K elements and sfmt block scales
+hipError_t launch_mx_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, int block,
+                              int sfmt, uint8_t* packed, void* scales, hipStream_t stream);
 // The GEMM epilogue: D = alpha * (A B) + beta * C, C of D's element type.
 // beta == 0 means C is not read (c may be null).
 struct Epilogue {
@@ -61,6 +64,11 @@ hipError_t launch_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                              const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
                              int out, void* d, int64_t ldd, const Epilogue& ep,
                              hipStream_t stream);
+// E2M1 operands with blocks of `block` K values and sfmt block scales
+// (not the hardware-scaled block = 32 / E8M0 case), dequantised to bf16.
+hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, int block, int sfmt, const uint8_t* a,
+                          const void* a_scales, const uint8_t* b, const void* b_scales, int out,
+                          void* d, int64_t ldd, const Epilogue& ep, hipStream_t stream);
 // K = 0: D = beta * C (zeros when beta == 0).
 hipError_t launch_fill(int64_t M, int64_t N, int out, void* d, int64_t ldd, const Epilogue& ep,
                        hipStream_t stream);

@@ -227,6 +227,57 @@ bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K,
                                   bsfp8_out out, void* d, int64_t ldd, hipStream_t stream);
 
 /*
+ * MX variants ([RUBIN-FP4] section 5.3 offers blocks of 16 or 8 elements where
+ * 32 is too coarse; section 3.2 offers FP16 or BF16 block scales where a power
+ * of two is too coarse, at twice the scale storage).
+ */
+typedef enum {
+    BSFP8_MX_E8M0 = 0,  /* one byte, 2^(code - 127) */
+    BSFP8_MX_F16 = 1,   /* IEEE binary16 bit pattern */
+    BSFP8_MX_BF16 = 2   /* bfloat16 bit pattern (upper half of a binary32) */
+} bsfp8_mx_scale;
+/*
+ * mx_quantize -- E2M1 quantisation with blocks of `block` consecutive K
+ * elements (32, 16 or 8) and block scales of format sfmt.
+ *
+ * x:      rows x k FP32, row-major, leading dimension ld; 16-byte aligned,
+ *         ld a multiple of 4, ld >= k.  rows >= 0; k >= 0, a multiple of 32.
+ * packed: out, rows x (k / 2) bytes, row stride k / 2, low nibble first.
+ * scales: out, [rows][k / block]: bytes (E8M0) or 16-bit patterns (FP16,
+ *         BF16, 2-byte aligned).
+ *
+ * Per block, amax = max |x|:
+ *   E8M0: as mxfp4_quantize (block = 32 with E8M0 is exactly mxfp4_quantize);
+ *   FP16 / BF16: s = the format's value nearest to amax / 6 (ties to even),
+ *         the largest finite value when beyond it, 1 when it is zero (or
+ *         amax is 0); code = saturating round-to-nearest-even E2M1 of
+ *         (x / s rounded to FP32).
+ * Bit-exact.  Finite inputs only.
+ */
+bsfp8_status mx_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, int block,
+                         bsfp8_mx_scale sfmt, uint8_t* packed, void* scales, hipStream_t stream);
+
+/*
+ * scaled_gemm_mx -- D = alpha * deq(A) deq(B) + beta * C for E2M1 operands
+ * with blocks of `block` (32, 16, 8) K values and sfmt block scales, as
+ * mx_quantize writes them.
+ *
+ * a: M x K/2 packed bytes, a_scales [M][K/block]; b: N x K/2 packed bytes
+ * (the K x N column-major operand), b_scales [N][K/block]; both 16-byte
+ * aligned, wide scales 2-byte aligned.  M, N >= 0; K >= 0 a multiple of 32.
+ * alpha, c, ldc, beta, out, d, ldd: as for scaled_gemm_ex.
+ * block = 32 with E8M0 scales runs the block-scaled MXFP4 GEMM of
+ * scaled_gemm.  Every other combination is beyond the matrix instructions'
+ * block scaling (one E8M0 scale per 32 K values): its operands are
+ * dequantised exactly to bf16 (a wide scale as an exact bf16 pair) and
+ * multiplied with FP32 accumulation.  Accuracy as for scaled_gemm_ex.
+ */
+bsfp8_status scaled_gemm_mx(int64_t M, int64_t N, int64_t K, int block, bsfp8_mx_scale sfmt,
+                            const void* a, const void* a_scales, const void* b,
+                            const void* b_scales, float alpha, const void* c, int64_t ldc,
+                            float beta, bsfp8_out out, void* d, int64_t ldd, hipStream_t stream);
+
+/*
  * scaled_gemm_quantize_a -- D = alpha * deq(Q(x)) deq(B) + beta * C, where
  * Q(x) is the per-tile FP8 quantisation of the FP32 matrix x, carried out
  * inside the GEMM while x is loaded (activations quantised online:

@@ -32,6 +32,7 @@ def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("fp8_quantize", "fp8_quantize_transposed", "fp8_quantize_granular", "mxfp4_quantize",
               "scaled_gemm", "scaled_gemm_ex", "scaled_gemm_granular", "scaled_gemm_quantize_a",
+              "mx_quantize", "scaled_gemm_mx",
               "bsfp8_status_string",
               "bsfp8_version"):
         assert n in names
@@ -201,3 +202,32 @@ def test_scaled_gemm_quantize_a_argument_checks(L):
     assert call(M=-1) == INVALID
     assert call(M=0, x=0, d=0) == OK                  # nothing to do
     assert call(N=0, d=0) == OK                       # no output and no codes requested
+
+
+def test_mx_quantize_argument_checks(L):
+    q = L.mx_quantize
+    # (x, rows, k, ld, block, sfmt, packed, scales, stream)
+    assert q(P, 4, 64, 64, 4, 0, P, P, None) == UNSUPPORTED        # block size
+    assert q(P, 4, 64, 64, 16, 3, P, P, None) == UNSUPPORTED       # scale format
+    assert q(P, 4, 48, 48, 16, 0, P, P, None) == INVALID           # k % 32
+    assert q(P, 4, 64, 32, 8, 1, P, P, None) == INVALID            # ld < k
+    assert q(P + 4, 4, 64, 64, 8, 1, P, P, None) == INVALID        # x alignment
+    assert q(P, 4, 64, 64, 8, 1, P, P + 1, None) == INVALID        # 16-bit scales alignment
+    assert q(0, 4, 64, 64, 8, 2, P, P, None) == INVALID
+    assert q(0, 0, 64, 64, 8, 2, 0, 0, None) == OK                 # nothing to do
+
+
+def test_scaled_gemm_mx_argument_checks(L):
+    g = L.scaled_gemm_mx
+    # (M, N, K, block, sfmt, a, sa, b, sb, alpha, c, ldc, beta, out, d, ldd, stream)
+    def call(block=16, sfmt=0, K=64, a=P, sa=P, b=P, sb=P, out=BF16, d=P, ldd=128, beta=0.0, c=0):
+        return g(128, 128, K, block, sfmt, a, sa, b, sb, 1.0, c, 0, beta, out, d, ldd, None)
+    assert call(block=64) == UNSUPPORTED
+    assert call(sfmt=5) == UNSUPPORTED
+    assert call(out=9) == UNSUPPORTED
+    assert call(K=48) == INVALID
+    assert call(a=P + 8) == INVALID
+    assert call(sfmt=1, sa=P + 1) == INVALID
+    assert call(d=0) == INVALID
+    assert call(beta=1.0) == INVALID
+    assert call(block=32, sfmt=0, K=48) == INVALID        # the MXFP4 path checks too

@@ -1,0 +1,180 @@
+"""Parity of the MX variants ("Rubin FP4 GEMM deep dive": blocks of 16 or 8
+elements, section 5.3; FP16 or BF16 block scales, section 3.2) on the GPU.
+
+* mx_quantize: packed codes and scales byte-equal to the oracle's, for every
+  block size and scale format, on ragged, padded and long rows, rows of every
+  magnitude, and rows whose quotients and scales fall exactly on rounding
+  midpoints.
+* scaled_gemm_mx: D against the oracle's fp64 product of the dequantised
+  operands, max |D - D_ref| / S within the output type's tolerance, for every
+  block size and scale format, FP32 / bf16 / FP16 output, alpha / beta and
+  ragged M, N, K; and the 8192^3 shape of the MXFP4 workload on sampled
+  outputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_common import TOL, check_gemm, check_gemm_ex, from_dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SCALES = ["e8m0", "f16", "bf16"]
+
+
+def bsfp8():
+    import block_scaled_precision_fp8_amd as b
+    return b
+
+
+def inputs(seed, rows, k, kind="normal"):
+    rng = np.random.default_rng(seed)
+    if kind == "laplace":
+        return (rng.laplace(size=(rows, k)) * 1e-3).astype(np.float32)
+    x = rng.standard_normal((rows, k))
+    if kind == "rows":      # each row at its own magnitude, some all-zero rows
+        x = x * np.exp2(rng.integers(-24, 24, size=(rows, 1)))
+        x[rng.random(rows) < 0.1] = 0.0
+    return x.astype(np.float32)
+
+
+def midpoints(scale):
+    """Blocks of 8: max 6 s for every s of one binade of the scale format, the
+    rest s times the E2M1 midpoints; then amax / 6 halfway between two scale
+    values (the oracle's own pins use the same construction)."""
+    mant = {"f16": 10, "bf16": 7, "e8m0": 0}[scale]
+    rows = []
+    for j in range(2 ** mant):
+        sv = 1.0 + j * 2.0 ** -mant
+        rows.append([6 * sv] + [m * sv for m in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)])
+    if mant:
+        for j in (0, 1, 2, 3):
+            half = 1.0 + (j + 0.5) * 2.0 ** -mant
+            rows.append([6 * half, -half, 2 * half, 0.0, -3 * half, half / 4, 5 * half, -0.0])
+    x = np.array(rows, dtype=np.float64)
+    x = np.tile(x, (1, 4))                    # 32 columns
+    return x.astype(np.float32)
+
+
+def gpu_quant(x, block, scale, ld=None):
+    import torch
+    if ld is None:
+        xd = to_dev(x)
+    else:
+        buf = np.zeros((x.shape[0], ld), dtype=np.float32)
+        buf[:, : x.shape[1]] = x
+        xd = to_dev(buf)[:, : x.shape[1]]
+    p, s = bsfp8().mx_quantize(xd, block, scale)
+    torch.cuda.synchronize()
+    p, s = from_dev(p), from_dev(s)
+    if scale != "e8m0":
+        s = s.view(np.uint16)
+    return p, s
+
+
+@pytest.mark.parametrize("scale", SCALES)
+@pytest.mark.parametrize("block", [32, 16, 8])
+@pytest.mark.parametrize("rows,k,ld,kind", [(1, 32, None, "normal"), (130, 288, 300, "rows"),
+                                            (257, 4096, None, "laplace"), (7, 8192, None, "rows")])
+def test_mx_quantize_matches_oracle(block, scale, rows, k, ld, kind):
+    say(f"mx_quantize block={block} {scale} rows={rows} k={k} ld={ld} {kind}")
+    x = inputs(rows + k + block, rows, k, kind)
+    p, s = gpu_quant(x, block, scale, ld)
+    rp, rs = oracle.mx_quantize(x, block, scale)
+    assert np.array_equal(p, rp), f"{np.count_nonzero(p != rp)} code bytes differ"
+    assert np.array_equal(s, rs), f"{np.count_nonzero(s != rs)} scales differ"
+
+
+@pytest.mark.parametrize("scale", SCALES)
+@pytest.mark.parametrize("block", [32, 16, 8])
+def test_mx_quantize_midpoints_and_edges(block, scale):
+    x = midpoints(scale)
+    x[0, 8:14] = [1e-42, -0.0, 3e38, -3e38, 1e-30, 0.0]      # subnormal, -0, near FLT_MAX
+    say(f"mx_quantize midpoints block={block} {scale}")
+    p, s = gpu_quant(x, block, scale)
+    rp, rs = oracle.mx_quantize(x, block, scale)
+    assert np.array_equal(p, rp), f"{np.count_nonzero(p != rp)} code bytes differ"
+    assert np.array_equal(s, rs), f"{np.count_nonzero(s != rs)} scales differ"
+
+
+def run_gemm(qa, sa, qb, sb, block, scale, out, K, alpha=1.0, c=None, beta=0.0):
+    import torch
+    conv = (lambda t: to_dev(t.view(np.int16))) if scale != "e8m0" else to_dev
+    d = bsfp8().scaled_gemm_mx(to_dev(qa), conv(sa), to_dev(qb), conv(sb), block, scale, out,
+                               alpha, c, beta, None, K)
+    torch.cuda.synchronize()
+    return from_dev(d)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("scale", SCALES)
+@pytest.mark.parametrize("block", [16, 8, 32])
+@pytest.mark.parametrize("M,N,K", [(100, 72, 96), (256, 256, 128), (300, 260, 320), (1, 1, 32),
+                                   (513, 200, 1056)])
+def test_mx_gemm_parity(M, N, K, block, scale, out):
+    say(f"scaled_gemm_mx block={block} {scale} M={M} N={N} K={K} -> {out}")
+    a = inputs(M + 3, M, K, "normal")
+    b = inputs(N + 4, N, K, "laplace")
+    qa, sa = oracle.mx_quantize(a, block, scale)
+    qb, sb = oracle.mx_quantize(b, block, scale)
+    d = run_gemm(qa, sa, qb, sb, block, scale, out, K)
+    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, block, scale)
+    check_gemm(d, dr, sr, out, f"mx block={block} {scale} {M}x{N}x{K} {out}")
+
+
+@pytest.mark.parametrize("scale", SCALES)
+@pytest.mark.parametrize("block", [16, 8])
+def test_mx_gemm_alpha_beta(block, scale):
+    import torch
+    M, N, K = 270, 300, 192
+    a = inputs(51, M, K)
+    b = inputs(52, N, K)
+    qa, sa = oracle.mx_quantize(a, block, scale)
+    qb, sb = oracle.mx_quantize(b, block, scale)
+    c32 = np.random.default_rng(53).standard_normal((M, N)).astype(np.float32) * 20
+    say(f"scaled_gemm_mx alpha/beta block={block} {scale}")
+    d = run_gemm(qa, sa, qb, sb, block, scale, "f32", K, -0.5, torch.from_numpy(c32).cuda(), 2.0)
+    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, block, scale)
+    check_gemm_ex(d, dr, sr, -0.5, 2.0, c32.astype(np.float64), "f32", f"mx alpha/beta {block} {scale}")
+
+
+@pytest.mark.parametrize("block,scale", [(16, "e8m0"), (8, "bf16")])
+def test_mx_end_to_end(block, scale):
+    """HIP quantiser then HIP GEMM against the oracle on the same FP32 inputs."""
+    import torch
+    M, N, K = 384, 256, 1024
+    a = inputs(61, M, K)
+    b = inputs(62, N, K, "laplace")
+    b_ = bsfp8()
+    say(f"mx end to end block={block} {scale}")
+    qa, sa = b_.mx_quantize(to_dev(a), block, scale)
+    qb, sb = b_.mx_quantize(to_dev(b), block, scale)
+    d = b_.scaled_gemm_mx(qa, sa, qb, sb, block, scale, "bf16")
+    torch.cuda.synchronize()
+    rqa, rsa = oracle.mx_quantize(a, block, scale)
+    rqb, rsb = oracle.mx_quantize(b, block, scale)
+    assert np.array_equal(from_dev(qa), rqa) and np.array_equal(from_dev(qb), rqb)
+    dr, sr = oracle.gemm_mx(rqa, rsa, rqb, rsb, block, scale)
+    check_gemm(from_dev(d), dr, sr, "bf16", f"mx end to end {block} {scale}")
+
+
+@pytest.mark.parametrize("block,scale", [(16, "e8m0"), (32, "bf16")])
+def test_mx_gemm_8192_sampled(block, scale):
+    """The 8192^3 shape of the MXFP4 workload, checked on sampled outputs."""
+    w = workloads.by_name("mxfp4_8192")
+    a, b = workloads.operands(w)
+    qa, sa = oracle.mx_quantize(a, block, scale)
+    qb, sb = oracle.mx_quantize(b, block, scale)
+    say(f"scaled_gemm_mx 8192^3 block={block} {scale}")
+    d = run_gemm(qa, sa, qb, sb, block, scale, "bf16", w.K)
+    rng = np.random.default_rng(71)
+    ii = np.concatenate([rng.integers(0, w.M, 150), [0, w.M - 1, 127, 128]])
+    jj = np.concatenate([rng.integers(0, w.N, 150), [w.N - 1, 0, 128, 127]])
+    ad = oracle.dequantize_mx(qa[ii], sa[ii], block, scale)
+    bd = oracle.dequantize_mx(qb[jj], sb[jj], block, scale)
+    dr = np.sum(ad * bd, axis=1)
+    sr = np.sum(np.abs(ad * bd), axis=1)
+    err = np.abs(d[ii, jj].astype(np.float64) - dr) / sr
+    say(f"sampled max |D-Dref|/S = {err.max():.3e}")
+    assert err.max() <= TOL["bf16"]
