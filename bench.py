@@ -22,10 +22,13 @@ FP8 workloads can also be run with scales constant along K
 operand); the step then uses fp8_quantize_granular and scaled_gemm_granular.
 With --a-path online (per-tile scales) A is quantised inside the GEMM:
 fp8_quantize(B), scaled_gemm_quantize_a(A) without code output.
+The MXFP4 workload can also be run with blocks of 16 or 8 elements and with
+FP16 / BF16 block scales (--mx-block, --mx-scale): mx_quantize(A),
+mx_quantize(B), scaled_gemm_mx.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--granularity tile|row|tensor] [--a-path separate|online]
-                       [--no-cpu-baseline]
+                       [--mx-block 32|16|8] [--mx-scale e8m0|f16|bf16] [--no-cpu-baseline]
                        [--copy-calibration]
 Only one GPU is supported; --gpus N with N > 1 exits with a message.
 """
@@ -76,9 +79,11 @@ def committed_traffic(workload, source_file):
         return None, None
 
 
-def gemm_kernel_name(w, gran="tile", online=False):
+def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False):
     """The kernel scaled_gemm dispatches for this workload (mirrors the
     launchers' selection)."""
+    if mx_variant:
+        return "gemm_mx_kernel"
     if online:
         return "gemm_fp8_kernel (A quantised by quantiser waves)"
     if w.a_fmt != "mxfp4" and gran != "tile":
@@ -92,7 +97,7 @@ def gemm_kernel_name(w, gran="tile", online=False):
     return "gemm_fp8_kernel"
 
 
-def cpu_baseline(w, a, b, d_gpu, sample_rows, gran="tile"):
+def cpu_baseline(w, a, b, d_gpu, sample_rows, gran="tile", mx_block=32, mx_scale="e8m0"):
     """Time the oracle on a bounded sample: quantise all of B, `sample_rows`
     rows of A, and the product rows for that sample; extrapolate the time to
     the whole step (quantising all of A, all M rows of D).  With per-row or
@@ -127,18 +132,26 @@ def cpu_baseline(w, a, b, d_gpu, sample_rows, gran="tile"):
             "seconds_measured": round(t2 - t0, 3),
             "gpu_vs_oracle_max_err_over_S_on_sample": worst,
         }
+    mxv = w.a_fmt == "mxfp4" and (mx_block != 32 or mx_scale != "e8m0")
     t0 = time.perf_counter()
-    if w.a_fmt == "mxfp4":
+    if mxv:
+        qb, sb = oracle.mx_quantize(b, mx_block, mx_scale)
+    elif w.a_fmt == "mxfp4":
         qb, sb = oracle.mxfp4_quantize(b)
     else:
         qb, sb = oracle.fp8_quantize(b, w.b_fmt)
     t1 = time.perf_counter()
-    if w.a_fmt == "mxfp4":
+    if mxv:
+        qa, sa = oracle.mx_quantize(a[:rows], mx_block, mx_scale)
+    elif w.a_fmt == "mxfp4":
         qa, sa = oracle.mxfp4_quantize(a[:rows])
     else:
         qa, sa = oracle.fp8_quantize(a[:rows], w.a_fmt)
     t2 = time.perf_counter()
-    d_ref, s_ref = oracle.gemm_rows(w.a_fmt, qa, sa, w.b_fmt, qb, sb)
+    if mxv:
+        d_ref, s_ref = oracle.gemm_mx(qa, sa, qb, sb, mx_block, mx_scale)
+    else:
+        d_ref, s_ref = oracle.gemm_rows(w.a_fmt, qa, sa, w.b_fmt, qb, sb)
     t3 = time.perf_counter()
     scale = w.M / rows
     t_full = (t1 - t0) + (t2 - t1) * scale + (t3 - t2) * scale
@@ -194,6 +207,10 @@ def main():
     p.add_argument("--a-path", choices=["separate", "online"], default="separate",
                    help="FP8 per-tile only: online quantises A inside the GEMM "
                         "(scaled_gemm_quantize_a) instead of a separate fp8_quantize pass")
+    p.add_argument("--mx-block", type=int, choices=[32, 16, 8], default=32,
+                   help="MXFP4 only: elements per block scale")
+    p.add_argument("--mx-scale", choices=["e8m0", "f16", "bf16"], default="e8m0",
+                   help="MXFP4 only: block scale format")
     args = p.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -223,6 +240,10 @@ def main():
     if token_major and gran != "tile":
         print("bench.py: the token-major layout is quantised with per-tile scales only", file=sys.stderr)
         sys.exit(2)
+    mxv = mx and (args.mx_block != 32 or args.mx_scale != "e8m0")
+    if not mx and (args.mx_block != 32 or args.mx_scale != "e8m0"):
+        print("bench.py: --mx-block / --mx-scale apply to the MXFP4 workload", file=sys.stderr)
+        sys.exit(2)
     online = args.a_path == "online"
     if online and (mx or gran != "tile" or token_major):
         print("bench.py: --a-path online needs FP8 per-tile scales and K-contiguous operands",
@@ -238,8 +259,9 @@ def main():
     if mx:
         qa = torch.empty((w.M, w.K // 2), dtype=torch.uint8, device=dev)
         qb = torch.empty((w.N, w.K // 2), dtype=torch.uint8, device=dev)
-        sa = torch.empty((w.M, w.K // 32), dtype=torch.uint8, device=dev)
-        sb = torch.empty((w.N, w.K // 32), dtype=torch.uint8, device=dev)
+        sdt = torch.uint8 if args.mx_scale == "e8m0" else torch.int16
+        sa = torch.empty((w.M, w.K // args.mx_block), dtype=sdt, device=dev)
+        sb = torch.empty((w.N, w.K // args.mx_block), dtype=sdt, device=dev)
     else:
         qa = torch.empty((w.M, w.K), dtype=torch.uint8, device=dev)
         qb = torch.empty((w.N, w.K), dtype=torch.uint8, device=dev)
@@ -256,7 +278,10 @@ def main():
     def step(marks=None):
         if marks:
             marks[0].record(stream)
-        if mx:
+        if mxv:
+            bs.mx_quantize(a, args.mx_block, args.mx_scale, qa, sa)
+            bs.mx_quantize(b, args.mx_block, args.mx_scale, qb, sb)
+        elif mx:
             bs.mxfp4_quantize(a, qa, sa)
             bs.mxfp4_quantize(b, qb, sb)
         elif online:
@@ -276,7 +301,9 @@ def main():
             quant(b, w.b_fmt, codes=qb, scales=sb)
         if marks:
             marks[2].record(stream)
-        if online:
+        if mxv:
+            bs.scaled_gemm_mx(qa, sa, qb, sb, args.mx_block, args.mx_scale, w.out, d=d, K=w.K)
+        elif online:
             bs.scaled_gemm_quantize_a(a, qb, sb, w.a_fmt, w.b_fmt, "tile", w.out, d=d)
         elif gran != "tile":
             bs.scaled_gemm_granular(qa, sa, qb, sb, w.a_fmt, w.b_fmt, gran, gran, w.out, d=d, K=w.K)
@@ -303,17 +330,20 @@ def main():
         qb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
 
-    in_type = "fp4" if mx else "fp8"
+    in_type = "bf16" if mxv else ("fp4" if mx else "fp8")
     gemm_tflops = w.flops / (gemm_ms * 1e-3) / 1e12
     src = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc",
-                       "gemm_mxfp4.hip" if mx else ("gemm_fp8.hip" if gran == "tile" else "gemm_fp8_outer.hip"))
-    profile_tag = f"{w.name}_online" if online else (w.name if gran == "tile" else f"{w.name}_{gran}")
+                       "gemm_mx.hip" if mxv else "gemm_mxfp4.hip" if mx else
+                       ("gemm_fp8.hip" if gran == "tile" else "gemm_fp8_outer.hip"))
+    profile_tag = (f"{w.name}_b{args.mx_block}_{args.mx_scale}" if mxv else f"{w.name}_online" if online
+                   else (w.name if gran == "tile" else f"{w.name}_{gran}"))
     traffic, traffic_src = committed_traffic(profile_tag, src)
 
     # quantiser bytes: read 4 B, write 1 B (FP8) or 0.5 B (MXFP4) per element, plus scales
     def qbytes(rows):
         if mx:
-            return rows * w.K * 4 + rows * w.K // 2 + rows * (w.K // 32)
+            sbytes = 1 if args.mx_scale == "e8m0" else 2
+            return rows * w.K * 4 + rows * w.K // 2 + rows * (w.K // args.mx_block) * sbytes
         nscales = {"tile": ((rows + 127) // 128) * (w.K // 32), "row": rows, "tensor": 1}[gran]
         return rows * w.K * 4 + rows * w.K + nscales * 4
 
@@ -340,17 +370,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4e2m1" if mx else ("fp8e4m3" if w.a_fmt == w.b_fmt == "e4m3" else "fp8e5m2xe4m3"),
+        "dtype": "fp4e2m1 (dequantised to bf16)" if mxv else "fp4e2m1" if mx else ("fp8e4m3" if w.a_fmt == w.b_fmt == "e4m3" else "fp8e5m2xe4m3"),
         "data": "synthetic (seeded numpy, distributions of the workload table)",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "a_fmt": w.a_fmt,
                    "b_fmt": w.b_fmt, "out": w.out,
                    "operand_layout": "k-contiguous" if not token_major else "token-major",
-                   "scale_granularity": ("E8M0 per 32-element K block" if mx else
+                   "scale_granularity": (f"{args.mx_scale.upper()} per {args.mx_block}-element K block" if mx else
                                          {"tile": "FP32 per 128x32 tile",
                                           "row": "FP32 per row of A and per column of B",
                                           "tensor": "FP32 per tensor"}[gran]),
                    "a_path": "quantised inside the GEMM" if online else "separate quantiser",
-                   "step": ("mxfp4_quantize(A)+mxfp4_quantize(B)+scaled_gemm" if mx else
+                   "step": ("mx_quantize(A)+mx_quantize(B)+scaled_gemm_mx" if mxv else
+                            "mxfp4_quantize(A)+mxfp4_quantize(B)+scaled_gemm" if mx else
                             "fp8_quantize(B)+scaled_gemm_quantize_a(A)" if online else
                             "fp8_quantize_granular(A)+fp8_quantize_granular(B)+scaled_gemm_granular"
                             if gran != "tile" else
@@ -358,7 +389,7 @@ def main():
                             if token_major else "fp8_quantize(A)+fp8_quantize(B)+scaled_gemm")},
         "roofline": {
             "bound": "mfma",
-            "kernel": gemm_kernel_name(w, gran, online),
+            "kernel": gemm_kernel_name(w, gran, online, mxv),
             "achieved": round(gemm_tflops, 1),
             "peak": PEAK_TFLOPS[in_type],
             "unit": "TFLOP/s",
@@ -374,7 +405,8 @@ def main():
         log("cpu baseline: timing the oracle on a bounded sample ...")
         rows = int(args.cpu_sample_gflop * 1e9 / (2.0 * w.N * w.K)) // 128 * 128
         rows = max(128, min(w.M, rows))
-        result["cpu_baseline"] = cpu_baseline(w, a_host, b_host, d_host, rows, gran)
+        result["cpu_baseline"] = cpu_baseline(w, a_host, b_host, d_host, rows, gran, args.mx_block,
+                                              args.mx_scale)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

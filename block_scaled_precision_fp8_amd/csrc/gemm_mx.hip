@@ -19,8 +19,12 @@
 // t / 2 of A and of B, 32 K values (16 bytes of codes) per stage: it loads
 // the codes and their block scales for the next stage while the current one
 // is multiplied, then dequantises them into the other buffer.  LDS rows are
-// 128 bytes of bf16 (64 K), 16-byte chunk c of row R stored at c ^ (R & 7).
+// 128 bytes of bf16 (64 K), 16-byte chunk c of row R stored at
+// c ^ ((R >> 1) & 7): the 16 rows of a 16-lane read phase then cover all 16
+// groups of 4 banks.
 #include "internal.h"
+
+#include <utility>
 
 namespace bsfp8 {
 
@@ -60,9 +64,16 @@ __device__ __forceinline__ float scale_value(uint32_t bits) {
 }
 
 // The two codes of byte P of w (K 2 P, 2 P + 1), times s, into bf16 slots
-// 2 P, 2 P + 1 of hi (and the exact remainders into lo).
+// 2 P, 2 P + 1 of hi (and the exact remainders into lo).  With a power-of-two
+// s (E8M0 scales) one scaled conversion gives the exact bf16 pair directly.
 template <int P, bool SPLIT>
 __device__ __forceinline__ void dequant_pair(uint32_t w, float s, v8bf& hi, v8bf& lo) {
+    if constexpr (!SPLIT) {
+        const v2bf h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, P);
+        hi[2 * P] = h[0];
+        hi[2 * P + 1] = h[1];
+        return;
+    }
     const v2f f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, P);
     const float a = f[0] * s, b = f[1] * s;                // exact
     const __bf16 ha = static_cast<__bf16>(a), hb = static_cast<__bf16>(b);
@@ -120,46 +131,60 @@ __global__ __launch_bounds__(kThreads, SFMT == BSFP8_MX_E8M0 ? 2 : 1) void gemm_
     const bool b_ok = n0 + sr < N;
     const uint8_t* a_row = A + static_cast<int64_t>(m0 + sr) * kh;
     const uint8_t* b_row = B + static_cast<int64_t>(n0 + sr) * kh;
-    uint4 ca, cbb;
-    float sca[NB], scb[NB];
-    auto fetch = [&](int s) {
+    // this row's block scales (1 or 2 bytes each); a thread's NB scales of a
+    // stage are contiguous and aligned to their total size
+    constexpr int SB = SFMT == BSFP8_MX_E8M0 ? 1 : 2;
+    const uint8_t* sa_row = static_cast<const uint8_t*>(sA) + static_cast<int64_t>(m0 + sr) * nsc * SB;
+    const uint8_t* sb_row = static_cast<const uint8_t*>(sB) + static_cast<int64_t>(n0 + sr) * nsc * SB;
+    // NB scale fields of one load: n bits each
+    auto load_scales = [&](const uint8_t* p) -> uint64_t {
+        constexpr int bytes = NB * SB;
+        if constexpr (bytes == 1) return *p;
+        else if constexpr (bytes == 2) return *reinterpret_cast<const uint16_t*>(p);
+        else if constexpr (bytes == 4) return *reinterpret_cast<const uint32_t*>(p);
+        else return *reinterpret_cast<const uint64_t*>(p);
+    };
+    // two register slots: the codes and scales of stages s + 1 and s + 2 are
+    // in flight while stage s is multiplied
+    uint4 ca[2], cbb[2];
+    float sca[2][NB], scb[2][NB];
+    auto fetch = [&](auto SLOT, int s) {
+        constexpr int sl = SLOT;
         const int k0 = s * SK + 32 * sh;      // first K value of this thread
         const bool in_k = k0 < K;             // K is a multiple of 32: all 32 or none
-        ca = make_uint4(0, 0, 0, 0);
-        cbb = make_uint4(0, 0, 0, 0);
-        if (in_k && a_ok) ca = *reinterpret_cast<const uint4*>(a_row + k0 / 2);
-        if (in_k && b_ok) cbb = *reinterpret_cast<const uint4*>(b_row + k0 / 2);
+        ca[sl] = make_uint4(0, 0, 0, 0);
+        cbb[sl] = make_uint4(0, 0, 0, 0);
+        if (in_k && a_ok) ca[sl] = *reinterpret_cast<const uint4*>(a_row + k0 / 2);
+        if (in_k && b_ok) cbb[sl] = *reinterpret_cast<const uint4*>(b_row + k0 / 2);
+        // positions past M, N or K: scale 1 (their codes are zero)
+        uint64_t one = SFMT == BSFP8_MX_E8M0 ? 127u : SFMT == BSFP8_MX_F16 ? 0x3C00u : 0x3F80u;
+        uint64_t ones = 0;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) ones |= one << (8 * SB * j);
+        const int so = (k0 / BLOCK) * SB;
+        const uint64_t va = in_k && a_ok ? load_scales(sa_row + so) : ones;
+        const uint64_t vb = in_k && b_ok ? load_scales(sb_row + so) : ones;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            // positions past M, N or K: scale 1 (their codes are zero)
-            uint32_t ba = SFMT == BSFP8_MX_E8M0 ? 127u : SFMT == BSFP8_MX_F16 ? 0x3C00u : 0x3F80u;
-            uint32_t bb = ba;
-            const int64_t si = k0 / BLOCK + j;
-            if (in_k && a_ok) {
-                const int64_t idx = static_cast<int64_t>(m0 + sr) * nsc + si;
-                ba = SFMT == BSFP8_MX_E8M0 ? static_cast<const uint8_t*>(sA)[idx] : static_cast<const uint16_t*>(sA)[idx];
-            }
-            if (in_k && b_ok) {
-                const int64_t idx = static_cast<int64_t>(n0 + sr) * nsc + si;
-                bb = SFMT == BSFP8_MX_E8M0 ? static_cast<const uint8_t*>(sB)[idx] : static_cast<const uint16_t*>(sB)[idx];
-            }
-            sca[j] = scale_value<SFMT>(ba);
-            scb[j] = scale_value<SFMT>(bb);
+            const uint32_t mask = SB == 1 ? 0xFFu : 0xFFFFu;
+            sca[sl][j] = scale_value<SFMT>(static_cast<uint32_t>(va >> (8 * SB * j)) & mask);
+            scb[sl][j] = scale_value<SFMT>(static_cast<uint32_t>(vb >> (8 * SB * j)) & mask);
         }
     };
     // chunk c (0..7) of LDS row R of part p in buffer buf
     auto chunk_ptr = [&](int buf, int part, int R, int c) {
-        return lds + buf * L::kBuf + part * kPart + R * kRow + ((c ^ (R & 7)) << 4);
+        return lds + buf * L::kBuf + part * kPart + R * kRow + ((c ^ ((R >> 1) & 7)) << 4);
     };
-    auto stage = [&](int buf) {
+    auto stage = [&](auto SLOT, int buf) {
+        constexpr int sl = SLOT;
         v8bf hi[4], lo[4];
-        dequant32<BLOCK, SFMT, SPLIT>(ca, sca, hi, lo);
+        dequant32<BLOCK, SFMT, SPLIT>(ca[sl], sca[sl], hi, lo);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             *reinterpret_cast<v8bf*>(chunk_ptr(buf, 0, sr, 4 * sh + j)) = hi[j];
             if constexpr (SPLIT) *reinterpret_cast<v8bf*>(chunk_ptr(buf, 2, sr, 4 * sh + j)) = lo[j];
         }
-        dequant32<BLOCK, SFMT, SPLIT>(cbb, scb, hi, lo);
+        dequant32<BLOCK, SFMT, SPLIT>(cbb[sl], scb[sl], hi, lo);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             *reinterpret_cast<v8bf*>(chunk_ptr(buf, 1, sr, 4 * sh + j)) = hi[j];
@@ -181,44 +206,71 @@ __global__ __launch_bounds__(kThreads, SFMT == BSFP8_MX_E8M0 ? 2 : 1) void gemm_
         return *reinterpret_cast<const v8bf*>(chunk_ptr(buf, part, R, 2 * q + fh));
     };
 
-    fetch(0);
-    stage(0);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    fetch(I0{}, 0);
+    fetch(I1{}, 1);
+    stage(I0{}, 0);
     __syncthreads();
-    for (int s = 0; s < nst; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nst) fetch(s + 1);
-        const int nq = min(SK, K - s * SK) / 16;
-        for (int q = 0; q < nq; ++q) {
-            v8bf xa[2], xb[2];                // B rows (MFMA row operand), A rows
+    fetch(I0{}, 2);
+    // the MFMAs of K step q: B rows are the MFMA row operand, A rows the column operand
+    auto mul_step = [&](const v8bf (&xa)[2], const v8bf (&xb)[2], int buf, int q) {
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 2; ++tj)
+                acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[ti], xa[tj], acc[ti][tj], 0, 0, 0);
+        if constexpr (SPLIT) {
+            v8bf ya[2], yb[2];                // lo parts
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                yb[t] = frag(buf, 3, wn * 64 + t * 32 + fr, q);
+                ya[t] = frag(buf, 2, wm * 64 + t * 32 + fr, q);
+            }
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int tj = 0; tj < 2; ++tj) {
+                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[ti], ya[tj], acc[ti][tj], 0, 0, 0);
+                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yb[ti], xa[tj], acc[ti][tj], 0, 0, 0);
+                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yb[ti], ya[tj], acc[ti][tj], 0, 0, 0);
+                }
+        }
+    };
+    // the NQ K steps of a buffer: all fragments of a step are read before
+    // its MFMAs, and the steps are unrolled so the reads of the next overlap them
+    auto multiply = [&](auto NQ_, int buf) {
+        constexpr int NQ = NQ_;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            v8bf xa[2], xb[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 xb[t] = frag(buf, 1, wn * 64 + t * 32 + fr, q);
                 xa[t] = frag(buf, 0, wm * 64 + t * 32 + fr, q);
             }
-#pragma unroll
-            for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-                for (int tj = 0; tj < 2; ++tj)
-                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[ti], xa[tj], acc[ti][tj], 0, 0, 0);
-            if constexpr (SPLIT) {
-                v8bf ya[2], yb[2];            // lo parts
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    yb[t] = frag(buf, 3, wn * 64 + t * 32 + fr, q);
-                    ya[t] = frag(buf, 2, wm * 64 + t * 32 + fr, q);
-                }
-#pragma unroll
-                for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-                    for (int tj = 0; tj < 2; ++tj) {
-                        acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[ti], ya[tj], acc[ti][tj], 0, 0, 0);
-                        acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yb[ti], xa[tj], acc[ti][tj], 0, 0, 0);
-                        acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yb[ti], ya[tj], acc[ti][tj], 0, 0, 0);
-                    }
-            }
+            mul_step(xa, xb, buf, q);
         }
-        if (s + 1 < nst) stage(buf ^ 1);
+    };
+    // stage s: multiply buffer s % 2, dequantise stage s + 1 (slot (s + 1) % 2)
+    // into the other buffer, then refill that slot with stage s + 3
+    auto step = [&](auto PAR, int s) {
+        constexpr int par = PAR;              // s % 2
+        const int buf = par;
+        multiply(std::integral_constant<int, SK / 16>{}, buf);
+        if (s + 1 < nst) stage(std::integral_constant<int, par ^ 1>{}, buf ^ 1);
         __syncthreads();
+        if (s + 3 < nst) fetch(std::integral_constant<int, par ^ 1>{}, s + 3);
+    };
+    // full stages; K % 64 == 32 leaves a last stage of 32 K (two steps)
+    const int nfull = K / SK;
+    for (int s = 0; s < nfull; s += 2) {
+        step(I0{}, s);
+        if (s + 1 < nfull) step(I1{}, s + 1);
+    }
+    if (nfull < nst) {
+        multiply(std::integral_constant<int, 2>{}, nfull & 1);
+        __syncthreads();                      // its fragment reads end before the epilogue reuses LDS
     }
 
     // Epilogue: the FP32 tile (128 rows x 512 bytes) through LDS, then whole

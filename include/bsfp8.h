@@ -263,8 +263,8 @@ bsfp8_status mx_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, in
  * mx_quantize writes them.
  *
  * a: M x K/2 packed bytes, a_scales [M][K/block]; b: N x K/2 packed bytes
- * (the K x N column-major operand), b_scales [N][K/block]; both 16-byte
- * aligned, wide scales 2-byte aligned.  M, N >= 0; K >= 0 a multiple of 32.
+ * (the K x N column-major operand), b_scales [N][K/block]; a and b 16-byte
+ * aligned, the scale arrays 8-byte aligned.  M, N >= 0; K >= 0 a multiple of 32.
  * alpha, c, ldc, beta, out, d, ldd: as for scaled_gemm_ex.
  * block = 32 with E8M0 scales runs the block-scaled MXFP4 GEMM of
  * scaled_gemm.  Every other combination is beyond the matrix instructions'

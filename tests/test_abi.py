@@ -228,6 +228,7 @@ def test_scaled_gemm_mx_argument_checks(L):
     assert call(K=48) == INVALID
     assert call(a=P + 8) == INVALID
     assert call(sfmt=1, sa=P + 1) == INVALID
+    assert call(sfmt=0, sb=P + 4) == INVALID              # scales read 8 bytes at a time
     assert call(d=0) == INVALID
     assert call(beta=1.0) == INVALID
     assert call(block=32, sfmt=0, K=48) == INVALID        # the MXFP4 path checks too
