@@ -15,8 +15,8 @@
 // No per-block promotion is needed: the scales are inside the operands.
 //
 // Tiling: 128 x 128 output tile per workgroup, 4 waves of 64 x 64 (2 x 2 MFMA
-// tiles of 32 x 32), stages of 64 K, two LDS buffers.  Thread t stages row
-// t / 2 of A and of B, 32 K values (16 bytes of codes) per stage: it loads
+// tiles of 32 x 32), stages of 64 K, two LDS buffers.  Each thread stages one
+// row of A and of B, 32 K values (16 bytes of codes) per stage: it loads
 // the codes and their block scales for the next stage while the current one
 // is multiplied, then dequantises them into the other buffer.  LDS rows are
 // 128 bytes of bf16 (64 K), 16-byte chunk c of row R stored at
@@ -124,9 +124,12 @@ __global__ __launch_bounds__(kThreads, SFMT == BSFP8_MX_E8M0 ? 2 : 1) void gemm_
     const int kh = K >> 1;                    // code bytes per row
     const int nsc = K / BLOCK;                // scales per row
 
-    // staging role: row sr of A and B, K half sh (32 values) of each stage
-    const int sr = tid >> 1;
-    const int sh = tid & 1;
+    // staging role: row sr of A and B, K half sh (32 values) of each stage.
+    // Lanes 8 i .. 8 i + 7 of a 32-lane group take rows 2 j + (i & 1) (j = 0..7)
+    // of its 16 rows and half i >> 1, so the 8 lanes of a write phase store
+    // to 8 rows with distinct (R >> 1) & 7, i.e. 8 distinct bank groups.
+    const int sr = 16 * (tid >> 5) + 2 * (tid & 7) + ((tid >> 3) & 1);
+    const int sh = (tid >> 4) & 1;
     const bool a_ok = m0 + sr < M;
     const bool b_ok = n0 + sr < N;
     const uint8_t* a_row = A + static_cast<int64_t>(m0 + sr) * kh;
