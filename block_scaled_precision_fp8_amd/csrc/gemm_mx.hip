@@ -22,8 +22,9 @@
 // 128 bytes of bf16 (64 K), 16-byte chunk c of row R stored at
 // c ^ ((R >> 1) & 7): the 16 rows of a 16-lane read phase then cover all 16
 // groups of 4 banks.
-#include "internal.h"
+#include "big_tile.h"
 
+#include <type_traits>
 #include <utility>
 
 namespace bsfp8 {
@@ -316,10 +317,179 @@ __global__ __launch_bounds__(kThreads, SFMT == BSFP8_MX_E8M0 ? 2 : 1) void gemm_
     }
 }
 
+// Large-tile form for E8M0 scales (blocks of 16 or 8): 256 x 256 output tile,
+// 4 waves of 128 x 128 (4 x 4 MFMA tiles, accumulators in AGPRs), one
+// workgroup per CU.  Per 64-K stage each thread dequantises one row of A and
+// one of B (64 K values each) into the bf16 stage buffer (256 + 256 rows of
+// 128 bytes, chunk c of row R at c ^ ((R >> 1) & 7)); thread t takes row
+// 16 (t / 16) + 2 (t % 8) + (t / 8) % 2 so that the 8 lanes of a write phase
+// hit 8 distinct bank groups.  Half the dequantisation and half the fragment
+// reads per MFMA of the 128 x 128 form.
+constexpr int kBigRows = 256;
+constexpr int kBigPart = kBigRows * kRow;       // 32 KB
+constexpr int kBigBuf = 2 * kBigPart;           // A, B: 64 KB
+constexpr int kBigLds = 2 * kBigBuf;            // 128 KB
+
+template <int BLOCK, int OUT, bool STAGE16>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_big_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
+    constexpr int NB = SK / BLOCK;               // scales per row per stage (4 or 8 bytes)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigLds];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+    int tm, tn;
+    map_tile(blockIdx.x, tiles_m, tiles_n, 4, &tm, &tn);
+    const int m0 = tm * kBigRows;
+    const int n0 = tn * kBigRows;
+    const int nfull = K / SK;
+    const int nst = (K + SK - 1) / SK;
+    const int kh = K >> 1;
+    const int nsc = K / BLOCK;
+
+    const int sr = 16 * (tid >> 4) + 2 * (tid & 7) + ((tid >> 3) & 1);
+    const bool a_ok = m0 + sr < M;
+    const bool b_ok = n0 + sr < N;
+    const uint8_t* a_row = A + static_cast<int64_t>(m0 + sr) * kh;
+    const uint8_t* b_row = B + static_cast<int64_t>(n0 + sr) * kh;
+    const uint8_t* sa_row = sA + static_cast<int64_t>(m0 + sr) * nsc;
+    const uint8_t* sb_row = sB + static_cast<int64_t>(n0 + sr) * nsc;
+
+    // two register slots of a stage's codes (2 x 16 bytes per row) and scales
+    uint4 ca[2][2], cb[2][2];
+    uint64_t va[2], vb[2];
+    auto fetch = [&](auto SLOT, int s) {
+        constexpr int sl = SLOT;
+        const int k0 = s * SK;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bool in_k = k0 + 32 * h < K;
+            ca[sl][h] = in_k && a_ok ? *reinterpret_cast<const uint4*>(a_row + k0 / 2 + 16 * h) : make_uint4(0, 0, 0, 0);
+            cb[sl][h] = in_k && b_ok ? *reinterpret_cast<const uint4*>(b_row + k0 / 2 + 16 * h) : make_uint4(0, 0, 0, 0);
+        }
+        // the scales of each 32-K half (2 bytes for blocks of 16, 4 for 8): a
+        // row's scale array starts at a multiple of that size, not of twice
+        // it, so the halves are loaded apart; positions past M, N or K get
+        // scale 1 (their codes are zero)
+        typedef typename std::conditional<NB == 4, uint16_t, uint32_t>::type half_t;
+        constexpr uint64_t one_half = NB == 4 ? 0x7F7Full : 0x7F7F7F7Full;
+        va[sl] = 0;
+        vb[sl] = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bool in_k = k0 + 32 * h < K;
+            const half_t* pa = reinterpret_cast<const half_t*>(sa_row + k0 / BLOCK) + h;
+            const half_t* pb = reinterpret_cast<const half_t*>(sb_row + k0 / BLOCK) + h;
+            const uint64_t ha = in_k && a_ok ? static_cast<uint64_t>(*pa) : one_half;
+            const uint64_t hb = in_k && b_ok ? static_cast<uint64_t>(*pb) : one_half;
+            va[sl] |= ha << (8 * (NB / 2) * h);
+            vb[sl] |= hb << (8 * (NB / 2) * h);
+        }
+    };
+    auto chunk_ptr = [&](int buf, int part, int R, int c) {
+        return lds + buf * kBigBuf + part * kBigPart + R * kRow + ((c ^ ((R >> 1) & 7)) << 4);
+    };
+    // one row's 64 K values (codes w[0..1], scales v) into part `part`
+    auto stage_row = [&](const uint4 (&w)[2], uint64_t v, int buf, int part) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float sc[32 / BLOCK];
+#pragma unroll
+            for (int j = 0; j < 32 / BLOCK; ++j)
+                sc[j] = scale_value<BSFP8_MX_E8M0>(static_cast<uint32_t>(v >> (8 * (h * (32 / BLOCK) + j))) & 0xFFu);
+            v8bf hi[4], lo[4];
+            dequant32<BLOCK, BSFP8_MX_E8M0, false>(w[h], sc, hi, lo);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<v8bf*>(chunk_ptr(buf, part, sr, 4 * h + j)) = hi[j];
+        }
+    };
+    auto stage = [&](auto SLOT, int buf) {
+        constexpr int sl = SLOT;
+        stage_row(ca[sl], va[sl], buf, 0);
+        stage_row(cb[sl], vb[sl], buf, 1);
+    };
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    const int fr = lane & 31;
+    const int fh = lane >> 5;
+    auto frag = [&](int buf, int part, int R, int q) {
+        return *reinterpret_cast<const v8bf*>(chunk_ptr(buf, part, R, 2 * q + fh));
+    };
+    auto multiply = [&](auto NQ_, int buf) {
+        constexpr int NQ = NQ_;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            v8bf xa[4], xb[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                xb[t] = frag(buf, 1, wn * 128 + t * 32 + fr, q);
+                xa[t] = frag(buf, 0, wm * 128 + t * 32 + fr, q);
+            }
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int tj = 0; tj < 4; ++tj)
+                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[ti], xa[tj], acc[ti][tj], 0, 0, 0);
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    fetch(I0{}, 0);
+    fetch(I1{}, 1);
+    stage(I0{}, 0);
+    __syncthreads();
+    fetch(I0{}, 2);
+    auto step = [&](auto PAR, int s) {
+        constexpr int par = PAR;
+        multiply(std::integral_constant<int, SK / 16>{}, par);
+        if (s + 1 < nst) stage(std::integral_constant<int, par ^ 1>{}, par ^ 1);
+        __syncthreads();
+        if (s + 3 < nst) fetch(std::integral_constant<int, par ^ 1>{}, s + 3);
+    };
+    for (int s = 0; s < nfull; s += 2) {
+        step(I0{}, s);
+        if (s + 1 < nfull) step(I1{}, s + 1);
+    }
+    if (nfull < nst) multiply(std::integral_constant<int, 2>{}, nfull & 1);
+    // (the epilogue begins with a barrier, after which LDS is reused)
+    big_tile::NoScale pre;
+    big_tile::epilogue<OUT, STAGE16>(acc, lds, wave, lane, m0, n0, M, N, D, ldd, ep, vec_ok, pre);
+}
+
 template <int BLOCK, int SFMT, int OUT>
 hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const void* sa,
                       const uint8_t* b, const void* sb, void* d, int64_t ldd, const Epilogue& ep,
                       hipStream_t stream) {
+    if constexpr (SFMT == BSFP8_MX_E8M0 && BLOCK != 32) {
+        // the large tile wherever it still gives the chip enough workgroups
+        const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+        if (big >= 128) {
+            const int tm = static_cast<int>((M + 255) / 256), tn = static_cast<int>((N + 255) / 256);
+            const dim3 g(static_cast<uint32_t>(tm) * static_cast<uint32_t>(tn));
+            const int vec = vec16_ok(OUT, d, ldd, ep);
+            const uint8_t* sa8 = static_cast<const uint8_t*>(sa);
+            const uint8_t* sb8 = static_cast<const uint8_t*>(sb);
+            if (OUT != BSFP8_OUT_F32 && ep.beta == 0.0f)
+                hipLaunchKernelGGL((gemm_mx_big_kernel<BLOCK, OUT, OUT != BSFP8_OUT_F32>), g, dim3(kThreads), 0,
+                                   stream, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
+                                   sa8, b, sb8, d, ldd, ep, tm, tn, vec);
+            else
+                hipLaunchKernelGGL((gemm_mx_big_kernel<BLOCK, OUT, false>), g, dim3(kThreads), 0, stream,
+                                   static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, sa8, b,
+                                   sb8, d, ldd, ep, tm, tn, vec);
+            return hipGetLastError();
+        }
+    }
     const int tiles_m = static_cast<int>((M + BM - 1) / BM);
     const int tiles_n = static_cast<int>((N + BN - 1) / BN);
     const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));
