@@ -180,6 +180,8 @@ bsfp8_status scaled_gemm_mx(int64_t M, int64_t N, int64_t K, int block, bsfp8_mx
     if (K == 0) return from_hip(bsfp8::launch_fill(M, N, out, d, ldd, ep, stream));
     if (!a || !b || !a_scales || !b_scales) return BSFP8_ERR_INVALID_ARG;
     if (!aligned(a, 16) || !aligned(b, 16)) return BSFP8_ERR_INVALID_ARG;
+    // the kernels address a 256-row band of an operand with 32-bit offsets
+    if (K >= (int64_t(1) << 23)) return BSFP8_ERR_UNSUPPORTED;
     // a thread reads its block scales of a stage in one load of up to 8 bytes
     if (!aligned(a_scales, 8) || !aligned(b_scales, 8)) return BSFP8_ERR_INVALID_ARG;
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);

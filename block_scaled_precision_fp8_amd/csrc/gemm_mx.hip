@@ -131,22 +131,35 @@ __global__ __launch_bounds__(kThreads, SFMT == BSFP8_MX_E8M0 ? 2 : 1) void gemm_
     // to 8 rows with distinct (R >> 1) & 7, i.e. 8 distinct bank groups.
     const int sr = 16 * (tid >> 5) + 2 * (tid & 7) + ((tid >> 3) & 1);
     const int sh = (tid >> 4) & 1;
-    const bool a_ok = m0 + sr < M;
-    const bool b_ok = n0 + sr < N;
-    const uint8_t* a_row = A + static_cast<int64_t>(m0 + sr) * kh;
-    const uint8_t* b_row = B + static_cast<int64_t>(n0 + sr) * kh;
-    // this row's block scales (1 or 2 bytes each); a thread's NB scales of a
-    // stage are contiguous and aligned to their total size
-    constexpr int SB = SFMT == BSFP8_MX_E8M0 ? 1 : 2;
-    const uint8_t* sa_row = static_cast<const uint8_t*>(sA) + static_cast<int64_t>(m0 + sr) * nsc * SB;
-    const uint8_t* sb_row = static_cast<const uint8_t*>(sB) + static_cast<int64_t>(n0 + sr) * nsc * SB;
-    // NB scale fields of one load: n bits each
-    auto load_scales = [&](const uint8_t* p) -> uint64_t {
+    // Range-checked buffer loads, based at the tile's first row: rows past
+    // M or N and K past the end read as zero, with no branch, so the compiler
+    // waits for them only where they are used (zero scale bits are a finite
+    // scale, and they only multiply zero codes).
+    constexpr int SB = SFMT == BSFP8_MX_E8M0 ? 1 : 2;    // bytes per scale
+    const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(A + static_cast<int64_t>(m0) * kh), 0, rows_a * kh, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(B + static_cast<int64_t>(n0) * kh), 0, rows_b * kh, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(sA) + static_cast<int64_t>(m0) * nsc * SB), 0,
+        rows_a * nsc * SB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(sB) + static_cast<int64_t>(n0) * nsc * SB), 0,
+        rows_b * nsc * SB, 0x00020000);
+    constexpr uint32_t kOut = 0x80000000u;
+    const bool a_ok = sr < rows_a;
+    const bool b_ok = sr < rows_b;
+    // a thread's NB scales of a stage: NB * SB contiguous bytes, aligned to their size
+    auto load_scales = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t off) -> uint64_t {
         constexpr int bytes = NB * SB;
-        if constexpr (bytes == 1) return *p;
-        else if constexpr (bytes == 2) return *reinterpret_cast<const uint16_t*>(p);
-        else if constexpr (bytes == 4) return *reinterpret_cast<const uint32_t*>(p);
-        else return *reinterpret_cast<const uint64_t*>(p);
+        if constexpr (bytes == 1) return __builtin_amdgcn_raw_buffer_load_b8(rs, static_cast<int>(off), 0, 0);
+        else if constexpr (bytes == 2) return __builtin_amdgcn_raw_buffer_load_b16(rs, static_cast<int>(off), 0, 0);
+        else if constexpr (bytes == 4) return __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(off), 0, 0);
+        else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, static_cast<int>(off), 0, 0);
+            return static_cast<uint64_t>(v[0]) | (static_cast<uint64_t>(v[1]) << 32);
+        }
     };
     // two register slots: the codes and scales of stages s + 1 and s + 2 are
     // in flight while stage s is multiplied
@@ -156,18 +169,15 @@ __global__ __launch_bounds__(kThreads, SFMT == BSFP8_MX_E8M0 ? 2 : 1) void gemm_
         constexpr int sl = SLOT;
         const int k0 = s * SK + 32 * sh;      // first K value of this thread
         const bool in_k = k0 < K;             // K is a multiple of 32: all 32 or none
-        ca[sl] = make_uint4(0, 0, 0, 0);
-        cbb[sl] = make_uint4(0, 0, 0, 0);
-        if (in_k && a_ok) ca[sl] = *reinterpret_cast<const uint4*>(a_row + k0 / 2);
-        if (in_k && b_ok) cbb[sl] = *reinterpret_cast<const uint4*>(b_row + k0 / 2);
-        // positions past M, N or K: scale 1 (their codes are zero)
-        uint64_t one = SFMT == BSFP8_MX_E8M0 ? 127u : SFMT == BSFP8_MX_F16 ? 0x3C00u : 0x3F80u;
-        uint64_t ones = 0;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) ones |= one << (8 * SB * j);
-        const int so = (k0 / BLOCK) * SB;
-        const uint64_t va = in_k && a_ok ? load_scales(sa_row + so) : ones;
-        const uint64_t vb = in_k && b_ok ? load_scales(sb_row + so) : ones;
+        const uint32_t oa = in_k && a_ok ? static_cast<uint32_t>(sr * kh + k0 / 2) : kOut;
+        const uint32_t ob = in_k && b_ok ? static_cast<uint32_t>(sr * kh + k0 / 2) : kOut;
+        const auto wa = __builtin_amdgcn_raw_buffer_load_b128(rs_a, static_cast<int>(oa), 0, 0);
+        const auto wb = __builtin_amdgcn_raw_buffer_load_b128(rs_b, static_cast<int>(ob), 0, 0);
+        ca[sl] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+        cbb[sl] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+        const uint32_t so = static_cast<uint32_t>((k0 / BLOCK) * SB);
+        const uint64_t va = load_scales(rs_sa, in_k && a_ok ? static_cast<uint32_t>(sr * nsc * SB) + so : kOut);
+        const uint64_t vb = load_scales(rs_sb, in_k && b_ok ? static_cast<uint32_t>(sr * nsc * SB) + so : kOut);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const uint32_t mask = SB == 1 ? 0xFFu : 0xFFFFu;
@@ -353,12 +363,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_big_kernel(
     const int nsc = K / BLOCK;
 
     const int sr = 16 * (tid >> 4) + 2 * (tid & 7) + ((tid >> 3) & 1);
-    const bool a_ok = m0 + sr < M;
-    const bool b_ok = n0 + sr < N;
-    const uint8_t* a_row = A + static_cast<int64_t>(m0 + sr) * kh;
-    const uint8_t* b_row = B + static_cast<int64_t>(n0 + sr) * kh;
-    const uint8_t* sa_row = sA + static_cast<int64_t>(m0 + sr) * nsc;
-    const uint8_t* sb_row = sB + static_cast<int64_t>(n0 + sr) * nsc;
+    // Range-checked buffer loads, based at the tile's first row: rows past
+    // M or N and K past the end read as zero (an out-of-range offset), with
+    // no branch, so the compiler waits for them only where they are used.
+    // A zero E8M0 byte is the finite scale 2^-127 and multiplies zero codes.
+    const int rows_a = min(kBigRows, M - m0), rows_b = min(kBigRows, N - n0);
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(A + static_cast<int64_t>(m0) * kh), 0, rows_a * kh, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(B + static_cast<int64_t>(n0) * kh), 0, rows_b * kh, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sA + static_cast<int64_t>(m0) * nsc), 0, rows_a * nsc, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sB + static_cast<int64_t>(n0) * nsc), 0, rows_b * nsc, 0x00020000);
+    constexpr uint32_t kOut = 0x80000000u;
+    const bool a_ok = sr < rows_a;
+    const bool b_ok = sr < rows_b;
 
     // two register slots of a stage's codes (2 x 16 bytes per row) and scales
     uint4 ca[2][2], cb[2][2];
@@ -369,24 +389,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_big_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool in_k = k0 + 32 * h < K;
-            ca[sl][h] = in_k && a_ok ? *reinterpret_cast<const uint4*>(a_row + k0 / 2 + 16 * h) : make_uint4(0, 0, 0, 0);
-            cb[sl][h] = in_k && b_ok ? *reinterpret_cast<const uint4*>(b_row + k0 / 2 + 16 * h) : make_uint4(0, 0, 0, 0);
+            const uint32_t oa = in_k && a_ok ? static_cast<uint32_t>(sr * kh + k0 / 2 + 16 * h) : kOut;
+            const uint32_t ob = in_k && b_ok ? static_cast<uint32_t>(sr * kh + k0 / 2 + 16 * h) : kOut;
+            const auto wa = __builtin_amdgcn_raw_buffer_load_b128(rs_a, static_cast<int>(oa), 0, 0);
+            const auto wb = __builtin_amdgcn_raw_buffer_load_b128(rs_b, static_cast<int>(ob), 0, 0);
+            ca[sl][h] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+            cb[sl][h] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
         }
-        // the scales of each 32-K half (2 bytes for blocks of 16, 4 for 8): a
-        // row's scale array starts at a multiple of that size, not of twice
-        // it, so the halves are loaded apart; positions past M, N or K get
-        // scale 1 (their codes are zero)
-        typedef typename std::conditional<NB == 4, uint16_t, uint32_t>::type half_t;
-        constexpr uint64_t one_half = NB == 4 ? 0x7F7Full : 0x7F7F7F7Full;
+        // the scales of each 32-K half (2 bytes for blocks of 16, 4 for 8),
+        // loaded apart: a row's scales start at a multiple of that size only
         va[sl] = 0;
         vb[sl] = 0;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool in_k = k0 + 32 * h < K;
-            const half_t* pa = reinterpret_cast<const half_t*>(sa_row + k0 / BLOCK) + h;
-            const half_t* pb = reinterpret_cast<const half_t*>(sb_row + k0 / BLOCK) + h;
-            const uint64_t ha = in_k && a_ok ? static_cast<uint64_t>(*pa) : one_half;
-            const uint64_t hb = in_k && b_ok ? static_cast<uint64_t>(*pb) : one_half;
+            const int so = k0 / BLOCK + h * (NB / 2);
+            const uint32_t oa = in_k && a_ok ? static_cast<uint32_t>(sr * nsc + so) : kOut;
+            const uint32_t ob = in_k && b_ok ? static_cast<uint32_t>(sr * nsc + so) : kOut;
+            uint64_t ha, hb;
+            if constexpr (NB == 4) {
+                ha = __builtin_amdgcn_raw_buffer_load_b16(rs_sa, static_cast<int>(oa), 0, 0);
+                hb = __builtin_amdgcn_raw_buffer_load_b16(rs_sb, static_cast<int>(ob), 0, 0);
+            } else {
+                ha = __builtin_amdgcn_raw_buffer_load_b32(rs_sa, static_cast<int>(oa), 0, 0);
+                hb = __builtin_amdgcn_raw_buffer_load_b32(rs_sb, static_cast<int>(ob), 0, 0);
+            }
             va[sl] |= ha << (8 * (NB / 2) * h);
             vb[sl] |= hb << (8 * (NB / 2) * h);
         }
@@ -415,52 +442,100 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_big_kernel(
         stage_row(cb[sl], vb[sl], buf, 1);
     };
 
+    // Fragment reads and MFMAs are ordered inline assembly (the scheme of the
+    // large MXFP4 kernel): the 8 fragment reads of the next 16-K step are
+    // issued between the 16 MFMAs of the current one, and each step starts
+    // with an explicit lgkmcnt wait.  Stage s + 1 is dequantised during steps
+    // 0..2 of stage s into the other buffer (free since the previous barrier);
+    // the barrier before step 3 publishes it, and step 3 reads its first
+    // fragments.
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((big_tile::lds_byte*)lds));
+    const int fr = lane & 31;
+    const int fh = lane >> 5;
+    const int sw = (fr >> 1) & 7;
+    uint32_t rd_a[2][4], rd_b[2][4];
+#pragma unroll
+    for (int bf = 0; bf < 2; ++bf)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t pos = static_cast<uint32_t>(((2 * q + fh) ^ sw) << 4);
+            rd_a[bf][q] = lds0 + bf * kBigBuf + (wm * 128 + fr) * kRow + pos;
+            rd_b[bf][q] = lds0 + bf * kBigBuf + kBigPart + (wn * 128 + fr) * kRow + pos;
+        }
+    struct Frag { big_tile::u32x4 x[4], y[4]; };    // x: B rows (MFMA row operand), y: A rows
+    Frag frg[2];
+    auto read_frags = [&](Frag& g, uint32_t ra, uint32_t rb) {
+        big_tile::static_for<4>([&](auto t) {
+            big_tile::lds_read16<t * 32 * kRow>(g.x[t], rb);
+            big_tile::lds_read16<t * 32 * kRow>(g.y[t], ra);
+        });
+    };
     v16f acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
-    const int fr = lane & 31;
-    const int fh = lane >> 5;
-    auto frag = [&](int buf, int part, int R, int q) {
-        return *reinterpret_cast<const v8bf*>(chunk_ptr(buf, part, R, 2 * q + fh));
-    };
-    auto multiply = [&](auto NQ_, int buf) {
-        constexpr int NQ = NQ_;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            v8bf xa[4], xb[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                xb[t] = frag(buf, 1, wn * 128 + t * 32 + fr, q);
-                xa[t] = frag(buf, 0, wm * 128 + t * 32 + fr, q);
+    // the 16 MFMAs of one step on f, with the 8 reads of the next step into g
+    auto kstep = [&](const Frag& f, Frag& g, uint32_t ra, uint32_t rb) {
+        big_tile::static_for<16>([&](auto J) {
+            constexpr int j = J;
+            constexpr int ti = j >> 2, tj = j & 3;
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+a"(acc[ti][tj]) : "v"(f.x[ti]), "v"(f.y[tj]));
+            if constexpr (j < 8) {
+                constexpr int t = j >> 1;
+                if constexpr (j & 1) big_tile::lds_read16<t * 32 * kRow>(g.y[t], ra);
+                else big_tile::lds_read16<t * 32 * kRow>(g.x[t], rb);
             }
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                for (int tj = 0; tj < 4; ++tj)
-                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[ti], xa[tj], acc[ti][tj], 0, 0, 0);
-        }
+        });
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     fetch(I0{}, 0);
     fetch(I1{}, 1);
     stage(I0{}, 0);
-    __syncthreads();
+    big_tile::lds_wait_barrier();
+    read_frags(frg[0], rd_a[0][0], rd_b[0][0]);
     fetch(I0{}, 2);
     auto step = [&](auto PAR, int s) {
-        constexpr int par = PAR;
-        multiply(std::integral_constant<int, SK / 16>{}, par);
-        if (s + 1 < nst) stage(std::integral_constant<int, par ^ 1>{}, par ^ 1);
-        __syncthreads();
-        if (s + 3 < nst) fetch(std::integral_constant<int, par ^ 1>{}, s + 3);
+        constexpr int par = PAR;              // s % 2 = this stage's buffer
+        constexpr int nb = par ^ 1;
+        const bool more = s + 1 < nst;
+        big_tile::lds_wait();
+        kstep(frg[0], frg[1], rd_a[par][1], rd_b[par][1]);
+        if (more) stage_row(ca[nb], va[nb], nb, 0);
+        big_tile::lds_wait();
+        kstep(frg[1], frg[0], rd_a[par][2], rd_b[par][2]);
+        if (more) stage_row(cb[nb], vb[nb], nb, 1);
+        big_tile::lds_wait();
+        kstep(frg[0], frg[1], rd_a[par][3], rd_b[par][3]);
+        big_tile::lds_wait_barrier();         // stage s + 1 published; buffer par is free after step 3's reads
+        kstep(frg[1], frg[0], rd_a[nb][0], rd_b[nb][0]);
+        if (s + 3 < nst) fetch(std::integral_constant<int, nb>{}, s + 3);
     };
-    for (int s = 0; s < nfull; s += 2) {
+    // pairs of stages with no branch around either (a conditional second step
+    // made the compiler copy all 256 accumulators at the loop's join)
+    int s = 0;
+    for (; s + 1 < nfull; s += 2) {
         step(I0{}, s);
-        if (s + 1 < nfull) step(I1{}, s + 1);
+        step(I1{}, s + 1);
     }
-    if (nfull < nst) multiply(std::integral_constant<int, 2>{}, nfull & 1);
+    if (s < nfull) step(I0{}, s);
+    if (nfull < nst) {
+        // the last 32 K: its first fragments are in frg[0]
+        const int pb = nfull & 1;
+        big_tile::lds_wait();
+        kstep(frg[0], frg[1], rd_a[pb][1], rd_b[pb][1]);
+        big_tile::lds_wait();
+        kstep(frg[1], frg[0], rd_a[pb][1], rd_b[pb][1]);   // (its reads are not used)
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // MFMA results must settle before the accumulation registers are read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                   "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]),
+                   "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
+                   "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
     // (the epilogue begins with a barrier, after which LDS is reused)
     big_tile::NoScale pre;
     big_tile::epilogue<OUT, STAGE16>(acc, lds, wave, lane, m0, n0, M, N, D, ldd, ep, vec_ok, pre);
