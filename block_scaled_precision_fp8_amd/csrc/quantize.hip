@@ -203,122 +203,163 @@ __global__ __launch_bounds__(kThreads) void fp8_quantize_t_kernel(
     }
 }
 
+// Rows in chunks of up to 4096 values, 16 per lane of a wave: lane l holds
+// values 256 i + 4 l .. 256 i + 4 l + 3 (i = 0..15) of the chunk, so each load
+// instruction reads 1 KB in lane order.  The loads are range-checked buffer
+// loads over the chunk: values at or past the row's end read as zero with no
+// branch, so all 16 are in flight together (a conditional load compiles to a
+// branch that waits for the loads before it).  Stores past the end are dropped
+// the same way.
+constexpr int kChunk = 4096;
+constexpr int kCachePolicyNT = 2;             // non-temporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// values [c0, min(c0 + 4096, n)) of row xr
+template <bool NT>
+__device__ __forceinline__ void load_chunk(const float* xr, int64_t c0, int64_t n, int lane, float4 (&v)[16]) {
+    const __amdgpu_buffer_rsrc_t rs = span_rsrc(xr + c0, 4 * min(n - c0, static_cast<int64_t>(kChunk)));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, (i * 64 + lane) * 16, 0, NT ? kCachePolicyNT : 0);
+        v[i] = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                           __uint_as_float(w[3]));
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void store_chunk(uint8_t* cr, int64_t c0, int64_t n, int lane, const Fp8Quotient& qt,
+                                            const float4 (&v)[16]) {
+    const __amdgpu_buffer_rsrc_t rs = span_rsrc(cr + c0, min(n - c0, static_cast<int64_t>(kChunk)));
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        __builtin_amdgcn_raw_buffer_store_b32(fp8_codes4<FMT>(qt, v[i]), rs, (i * 64 + lane) * 4, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max(float a) {
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    a = fmaxf(a, __shfl_xor(a, 4));
+    a = fmaxf(a, __shfl_xor(a, 8));
+    a = fmaxf(a, __shfl_xor(a, 16));
+    return fmaxf(a, __shfl_xor(a, 32));
+}
+
+__device__ __forceinline__ float chunk_max(const float4 (&v)[16]) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, abs_max4(v[i]));
+    return a;
+}
+
 // Per-row scales ("Why grind FP8 GEMM on CDNA4", section 3.3 weighs per-row,
 // per-column and per-tensor scales against per-tile ones): one wave per row,
-// amax reduced across the wave, s = fl32(amax / F), then the codes.  Rows of up
-// to 4096 elements stay in registers between the two steps; longer rows are
+// amax reduced across the wave, s = fl32(amax / F), then the codes.  A row of
+// up to 4096 values stays in registers between the two steps; longer rows are
 // read twice (the second time mostly from cache).  The per-row scales of a B
 // operand stored N x K are its per-column scales.
-template <int FMT, bool INREG>
+template <int FMT, bool LONG>
 __global__ __launch_bounds__(kThreads) void fp8_quantize_rows_kernel(
     const float* __restrict__ x, int64_t rows, int64_t k, int64_t ld,
     uint8_t* __restrict__ codes, float* __restrict__ scales) {
     constexpr float F = FMT == BSFP8_E4M3 ? 448.0f : 57344.0f;
     const int lane = threadIdx.x & 63;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    // wave-uniform, so the buffer resources built from it stay in scalar registers
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= rows) return;                    // the whole wave leaves together
     const float* xr = x + row * ld;
     uint8_t* cr = codes + row * k;
-    auto wave_max = [](float a) {
-        a = fmaxf(a, __shfl_xor(a, 1));
-        a = fmaxf(a, __shfl_xor(a, 2));
-        a = fmaxf(a, __shfl_xor(a, 4));
-        a = fmaxf(a, __shfl_xor(a, 8));
-        a = fmaxf(a, __shfl_xor(a, 16));
-        return fmaxf(a, __shfl_xor(a, 32));
-    };
+    float4 v[16];
     float amax = 0.0f;
-    if constexpr (INREG) {
-        float4 v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t c = (static_cast<int64_t>(i) * 64 + lane) * 4;
-            v[i] = c < k ? load_once(xr + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            amax = fmaxf(amax, abs_max4(v[i]));
-        }
-        amax = wave_max(amax);
-        float s = amax / F;
-        if (s == 0.0f) s = 1.0f;
-        if (lane == 0) scales[row] = s;
-        const Fp8Quotient qt(s);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t c = (static_cast<int64_t>(i) * 64 + lane) * 4;
-            if (c < k) *reinterpret_cast<uint32_t*>(cr + c) = fp8_codes4<FMT>(qt, v[i]);
-        }
+    if constexpr (!LONG) {
+        load_chunk<true>(xr, 0, k, lane, v);
+        amax = chunk_max(v);
     } else {
-        for (int64_t c = lane * 4; c < k; c += 256)
-            amax = fmaxf(amax, abs_max4(*reinterpret_cast<const float4*>(xr + c)));
-        amax = wave_max(amax);
-        float s = amax / F;
-        if (s == 0.0f) s = 1.0f;
-        if (lane == 0) scales[row] = s;
-        const Fp8Quotient qt(s);
-        for (int64_t c = lane * 4; c < k; c += 256)
-            *reinterpret_cast<uint32_t*>(cr + c) = fp8_codes4<FMT>(qt, load_once(xr + c));
+        for (int64_t c0 = 0; c0 < k; c0 += kChunk) {
+            load_chunk<false>(xr, c0, k, lane, v);
+            amax = fmaxf(amax, chunk_max(v));
+        }
+    }
+    amax = wave_max(amax);
+    float s = amax / F;
+    if (s == 0.0f) s = 1.0f;
+    if (lane == 0) scales[row] = s;
+    const Fp8Quotient qt(s);
+    if constexpr (!LONG) {
+        store_chunk<FMT>(cr, 0, k, lane, qt, v);
+    } else {
+        for (int64_t c0 = 0; c0 < k; c0 += kChunk) {
+            load_chunk<false>(xr, c0, k, lane, v);
+            store_chunk<FMT>(cr, c0, k, lane, qt, v);
+        }
     }
 }
 
-// Per-tensor scale, in four launches on one stream: the scale word is
-// cleared, every workgroup folds its maximum |x| into it with one atomic
-// maximum on the FP32 bit pattern (non-negative floats order like their bits),
-// the codes are computed from s = fl32(amax / F), and the word is replaced by s.
-__global__ __launch_bounds__(64) void clear_word_kernel(uint32_t* word) {
-    if (threadIdx.x == 0) *word = 0u;
-}
+// Per-tensor scale, in three launches on one stream: every workgroup of the
+// first reduces the maximum |x| of its rows into one partial maximum; one
+// workgroup then reduces the partials and stores s = fl32(amax / F); the last
+// launch writes the codes.  The partials are kept in the code buffer, which
+// the last launch overwrites in full (it holds at least 32 bytes per row, and
+// there is one 4-byte partial per workgroup of at least 4 rows), so no
+// workspace is needed and nothing has to be cleared first.
+constexpr int kMaxPartials = 2048;
 
-// One wave per row, as in the per-row kernel; each workgroup folds the
-// maximum of its four rows into the word with one atomic.
+// One wave per row, as in the per-row kernel, striding over the rows.  These
+// loads are ordinary ones, so the second pass over x finds much of it in cache.
 __global__ __launch_bounds__(kThreads) void amax_kernel(const float* __restrict__ x, int64_t rows,
-                                                        int64_t k, int64_t ld, uint32_t* word) {
+                                                        int64_t k, int64_t ld, float* partial) {
     __shared__ float red[4];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     float amax = 0.0f;
-    if (row < rows) {
+    for (int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave; row < rows;
+         row += static_cast<int64_t>(gridDim.x) * 4) {
         const float* xr = x + row * ld;
-        for (int64_t c = lane * 4; c < k; c += 256)
-            amax = fmaxf(amax, abs_max4(*reinterpret_cast<const float4*>(xr + c)));
+        float4 v[16];
+        for (int64_t c0 = 0; c0 < k; c0 += kChunk) {
+            load_chunk<false>(xr, c0, k, lane, v);
+            amax = fmaxf(amax, chunk_max(v));
+        }
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
-    amax = fmaxf(amax, __shfl_xor(amax, 8));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax = wave_max(amax);
     if (lane == 0) red[wave] = amax;
     __syncthreads();
-    if (threadIdx.x == 0)
-        atomicMax(word, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+    if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 template <int FMT>
-__device__ __forceinline__ float tensor_scale(const uint32_t* word) {
+__global__ __launch_bounds__(kThreads) void tensor_scale_kernel(const float* partial, int n, float* scale) {
     constexpr float F = FMT == BSFP8_E4M3 ? 448.0f : 57344.0f;
-    float s = __uint_as_float(*word) / F;
-    return s == 0.0f ? 1.0f : s;
+    __shared__ float red[4];
+    float amax = 0.0f;
+    for (int i = threadIdx.x; i < n; i += kThreads) amax = fmaxf(amax, partial[i]);
+    amax = wave_max(amax);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) / F;
+        if (s == 0.0f) s = 1.0f;
+        *scale = s;
+    }
 }
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void fp8_quantize_tensor_kernel(
-    const float* __restrict__ x, int64_t rows, int64_t k, int64_t ld, const uint32_t* word,
+    const float* __restrict__ x, int64_t rows, int64_t k, int64_t ld, const float* scale,
     uint8_t* __restrict__ codes) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    // wave-uniform, so the buffer resources built from it stay in scalar registers
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= rows) return;                    // the whole wave leaves together
-    const Fp8Quotient qt(tensor_scale<FMT>(word));
+    const Fp8Quotient qt(*scale);
     const float* xr = x + row * ld;
     uint8_t* cr = codes + row * k;
-    for (int64_t c = lane * 4; c < k; c += 256)
-        *reinterpret_cast<uint32_t*>(cr + c) = fp8_codes4<FMT>(qt, load_once(xr + c));
-}
-
-template <int FMT>
-__global__ __launch_bounds__(64) void tensor_scale_kernel(uint32_t* word) {
-    if (threadIdx.x == 0) {
-        const float s = tensor_scale<FMT>(word);
-        *word = __float_as_uint(s);
+    float4 v[16];
+    for (int64_t c0 = 0; c0 < k; c0 += kChunk) {
+        load_chunk<true>(xr, c0, k, lane, v);
+        store_chunk<FMT>(cr, c0, k, lane, qt, v);
     }
 }
 
@@ -501,12 +542,14 @@ hipError_t launch_fp8_quantize_t(const float* x, int64_t k, int64_t rows, int64_
 hipError_t launch_fp8_quantize_rows(const float* x, int64_t rows, int64_t k, int64_t ld, int fmt,
                                     uint8_t* codes, float* scales, hipStream_t stream) {
     const dim3 grid(static_cast<uint32_t>((rows + 3) / 4));
-    const bool inreg = k <= 4096;
+    // separate kernels: the loop over long rows would raise the register use
+    // (and lower the occupancy) of the common one
+    const bool long_rows = k > kChunk;
     if (fmt == BSFP8_E4M3) {
-        if (inreg) hipLaunchKernelGGL((fp8_quantize_rows_kernel<BSFP8_E4M3, true>), grid, dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales);
+        if (long_rows) hipLaunchKernelGGL((fp8_quantize_rows_kernel<BSFP8_E4M3, true>), grid, dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales);
         else hipLaunchKernelGGL((fp8_quantize_rows_kernel<BSFP8_E4M3, false>), grid, dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales);
     } else {
-        if (inreg) hipLaunchKernelGGL((fp8_quantize_rows_kernel<BSFP8_E5M2, true>), grid, dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales);
+        if (long_rows) hipLaunchKernelGGL((fp8_quantize_rows_kernel<BSFP8_E5M2, true>), grid, dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales);
         else hipLaunchKernelGGL((fp8_quantize_rows_kernel<BSFP8_E5M2, false>), grid, dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales);
     }
     return hipGetLastError();
@@ -514,16 +557,17 @@ hipError_t launch_fp8_quantize_rows(const float* x, int64_t rows, int64_t k, int
 
 hipError_t launch_fp8_quantize_tensor(const float* x, int64_t rows, int64_t k, int64_t ld, int fmt,
                                       uint8_t* codes, float* scales, hipStream_t stream) {
-    uint32_t* word = reinterpret_cast<uint32_t*>(scales);
-    const dim3 grid(static_cast<uint32_t>((rows + 3) / 4));
-    hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, stream, word);
-    hipLaunchKernelGGL(amax_kernel, grid, dim3(kThreads), 0, stream, x, rows, k, ld, word);
+    const int64_t wgs = (rows + 3) / 4;
+    const int parts = static_cast<int>(min(wgs, static_cast<int64_t>(kMaxPartials)));
+    float* partial = reinterpret_cast<float*>(codes);     // rows * k >= 32 * rows bytes
+    hipLaunchKernelGGL(amax_kernel, dim3(parts), dim3(kThreads), 0, stream, x, rows, k, ld, partial);
+    const dim3 grid(static_cast<uint32_t>(wgs));
     if (fmt == BSFP8_E4M3) {
-        hipLaunchKernelGGL(fp8_quantize_tensor_kernel<BSFP8_E4M3>, grid, dim3(kThreads), 0, stream, x, rows, k, ld, word, codes);
-        hipLaunchKernelGGL(tensor_scale_kernel<BSFP8_E4M3>, dim3(1), dim3(64), 0, stream, word);
+        hipLaunchKernelGGL(tensor_scale_kernel<BSFP8_E4M3>, dim3(1), dim3(kThreads), 0, stream, partial, parts, scales);
+        hipLaunchKernelGGL(fp8_quantize_tensor_kernel<BSFP8_E4M3>, grid, dim3(kThreads), 0, stream, x, rows, k, ld, scales, codes);
     } else {
-        hipLaunchKernelGGL(fp8_quantize_tensor_kernel<BSFP8_E5M2>, grid, dim3(kThreads), 0, stream, x, rows, k, ld, word, codes);
-        hipLaunchKernelGGL(tensor_scale_kernel<BSFP8_E5M2>, dim3(1), dim3(64), 0, stream, word);
+        hipLaunchKernelGGL(tensor_scale_kernel<BSFP8_E5M2>, dim3(1), dim3(kThreads), 0, stream, partial, parts, scales);
+        hipLaunchKernelGGL(fp8_quantize_tensor_kernel<BSFP8_E5M2>, grid, dim3(kThreads), 0, stream, x, rows, k, ld, scales, codes);
     }
     return hipGetLastError();
 }

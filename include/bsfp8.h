@@ -197,8 +197,9 @@ typedef enum {
  * Per scale group (tile, row or whole operand): amax = max |x|, s = amax / F
  * rounded to FP32 (s = 1 when that is zero), code = saturating round-to-
  * nearest-even of (x / s rounded to FP32).  Bit-exact.  rows == 0 or k == 0
- * writes nothing.  BSFP8_GRAN_TENSOR uses scales[0] as its working word
- * between its launches, so concurrent reads of scales[0] race with the call.
+ * writes nothing.  BSFP8_GRAN_TENSOR runs three launches and keeps partial
+ * maxima in the codes buffer between them, so reads of codes or scales[0]
+ * that overlap the call race with it.
  */
 bsfp8_status fp8_quantize_granular(const float* x, int64_t rows, int64_t k, int64_t ld,
                                    bsfp8_granularity g, bsfp8_format fmt, uint8_t* codes,
@@ -269,8 +270,9 @@ bsfp8_status mx_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, in
  * block = 32 with E8M0 scales runs the block-scaled MXFP4 GEMM of
  * scaled_gemm.  Every other combination is beyond the matrix instructions'
  * block scaling (one E8M0 scale per 32 K values): its operands are
- * dequantised exactly to bf16 (a wide scale as an exact bf16 pair) and
- * multiplied with FP32 accumulation.  Accuracy as for scaled_gemm_ex.
+ * dequantised exactly to bf16 (a wide scale as an exact bf16 pair hi + lo) and
+ * multiplied with FP32 accumulation; 16-bit outputs leave out the lo * lo
+ * products (below 2^-16 of hi * hi).  Accuracy as for scaled_gemm_ex.
  */
 bsfp8_status scaled_gemm_mx(int64_t M, int64_t N, int64_t K, int block, bsfp8_mx_scale sfmt,
                             const void* a, const void* a_scales, const void* b,

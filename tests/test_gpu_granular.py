@@ -56,6 +56,7 @@ def inputs(seed, rows, k, kind="normal"):
 @pytest.mark.parametrize("rows,k,ld,kind", [
     (1, 32, None, "normal"), (3, 64, 96, "normal"), (130, 288, None, "wide"),
     (257, 4096, None, "laplace"), (5, 8192, None, "wide"), (64, 4128, None, "normal"),
+    (9, 12320, 12352, "wide"), (6, 4064, 4100, "normal"),
 ])
 def test_quantize_granular_matches_oracle(gran, fmt, rows, k, ld, kind):
     say(f"fp8_quantize_granular {gran} {fmt} rows={rows} k={k} ld={ld} {kind}")
