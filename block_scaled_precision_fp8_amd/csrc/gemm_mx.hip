@@ -78,14 +78,14 @@ __device__ __forceinline__ void dequant_pair(uint32_t w, float s, v8bf& hi, v8bf
         return;
     }
     const v2f f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, P);
-    const float a = f[0] * s, b = f[1] * s;                // exact
-    const __bf16 ha = static_cast<__bf16>(a), hb = static_cast<__bf16>(b);
-    hi[2 * P] = ha;
-    hi[2 * P + 1] = hb;
-    if constexpr (SPLIT) {
-        lo[2 * P] = static_cast<__bf16>(a - static_cast<float>(ha));   // exact
-        lo[2 * P + 1] = static_cast<__bf16>(b - static_cast<float>(hb));
-    }
+    const v2f v = f * s;                                   // exact
+    const v2bf h = __builtin_convertvector(v, v2bf);       // one packed RNE conversion
+    const v2f r = v - __builtin_convertvector(h, v2f);     // exact remainders
+    const v2bf l = __builtin_convertvector(r, v2bf);       // exact
+    hi[2 * P] = h[0];
+    hi[2 * P + 1] = h[1];
+    lo[2 * P] = l[0];
+    lo[2 * P + 1] = l[1];
 }
 
 // 32 codes (16 bytes, K order, low nibble first) of one row and their block
@@ -546,10 +546,250 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_big_kernel(
     big_tile::epilogue<OUT, STAGE16>(acc, lds, wave, lane, m0, n0, M, N, D, ldd, ep, vec_ok, pre);
 }
 
+// Large-tile form for FP16 / BF16 block scales: 256 x 256 output tile, 4 waves
+// of 128 x 128 (accumulators in AGPRs), one workgroup per CU, as the E8M0
+// form, but with stages of 32 K so that the hi and lo parts of both operands
+// (4 parts of 256 rows x 64 bytes) fit twice in LDS.  Row R keeps 16-byte chunk
+// c at c ^ ((R >> 2) & 3): the 16 rows of a fragment-read phase and the 8
+// consecutive rows of a staging-write phase then hit distinct bank groups.
+// Thread t stages row t of A and of B.
+//
+// Each stage is two K steps of 16, with one barrier between them.  The first
+// step multiplies while it reads the second step's fragments and dequantises
+// the B rows of the next stage into the other buffer; the barrier publishes
+// that stage and frees this one's buffer; the second step multiplies while it
+// reads the next stage's first fragments and dequantises the A rows of the
+// stage after next into the freed buffer.  A wave issues in order, so the
+// conversion overlaps the matrix core only where it sits between MFMAs: one
+// pair of values every KINDS MFMAs.  A and B codes are fetched separately,
+// each two stages before use.  Stages past the last one are dequantised from
+// zeros (range-checked loads past K) and never multiplied.
+constexpr int kSRow = 64;                      // bytes per LDS row: 32 bf16
+constexpr int kSPart = kBigRows * kSRow;       // 16 KB
+constexpr int kSBuf = 4 * kSPart;              // A hi, A lo, B hi, B lo: 64 KB
+static_assert(2 * kSBuf == kBigLds, "two stage buffers fill the epilogue's LDS");
+
+template <int BLOCK, int SFMT, int OUT, bool STAGE16>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_split_big_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
+    constexpr int NB = 32 / BLOCK;               // scales per row per stage
+    constexpr int KINDS = OUT == BSFP8_OUT_F32 ? 4 : 3;   // hi*hi, hi*lo, lo*hi (, lo*lo)
+    constexpr int NMF = 16 * KINDS;              // MFMAs per K step
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigLds];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+    int tm, tn;
+    map_tile(blockIdx.x, tiles_m, tiles_n, 4, &tm, &tn);
+    const int m0 = tm * kBigRows;
+    const int n0 = tn * kBigRows;
+    const int nst = K / 32;                      // K is a multiple of 32
+    const int kh = K >> 1;
+    const int nsc = K / BLOCK;
+
+    // Range-checked buffer loads based at the tile's first row: rows past M
+    // or N and K past the end read as zero, with no branch.  Zero scale bits
+    // are the scale 0, and they only multiply zero codes.
+    const int rows_a = min(kBigRows, M - m0), rows_b = min(kBigRows, N - n0);
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(A + static_cast<int64_t>(m0) * kh), 0, rows_a * kh, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(B + static_cast<int64_t>(n0) * kh), 0, rows_b * kh, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sA + static_cast<int64_t>(m0) * nsc * 2), 0, rows_a * nsc * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sB + static_cast<int64_t>(n0) * nsc * 2), 0, rows_b * nsc * 2, 0x00020000);
+    constexpr uint32_t kOut = 0x80000000u;
+    const bool a_ok = tid < rows_a;
+    const bool b_ok = tid < rows_b;
+
+    // two register slots per operand of a stage's codes (16 bytes of the row)
+    // and scales (2 NB bytes, aligned to their size); stage t uses slot t % 2
+    uint4 cw[2][2];                              // [operand][slot]
+    uint64_t sv[2][2];
+    auto fetch = [&](auto OP, auto SLOT, int s) {
+        constexpr int op = OP, sl = SLOT;
+        const __amdgpu_buffer_rsrc_t& rs = op == 0 ? rs_a : rs_b;
+        const __amdgpu_buffer_rsrc_t& rss = op == 0 ? rs_sa : rs_sb;
+        const bool ok = (op == 0 ? a_ok : b_ok) && s * 32 < K;
+        const uint32_t oc = ok ? static_cast<uint32_t>(tid * kh + s * 16) : kOut;
+        const uint32_t os = ok ? static_cast<uint32_t>(tid * nsc * 2 + (s * 32 / BLOCK) * 2) : kOut;
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(oc), 0, 0);
+        cw[op][sl] = make_uint4(w[0], w[1], w[2], w[3]);
+        if constexpr (NB == 1) sv[op][sl] = __builtin_amdgcn_raw_buffer_load_b16(rss, static_cast<int>(os), 0, 0);
+        else if constexpr (NB == 2) sv[op][sl] = __builtin_amdgcn_raw_buffer_load_b32(rss, static_cast<int>(os), 0, 0);
+        else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rss, static_cast<int>(os), 0, 0);
+            sv[op][sl] = static_cast<uint64_t>(v[0]) | (static_cast<uint64_t>(v[1]) << 32);
+        }
+    };
+
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((big_tile::lds_byte*)lds));
+    // staging writes: chunk c of row tid of buffer 0 (buffer 1 is kSBuf further)
+    const int wkey = (tid >> 2) & 3;
+    uint32_t wr[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) wr[c] = lds0 + tid * kSRow + ((c ^ wkey) << 4);
+    // piece p (0..15) of the staging of one row: values 2 p, 2 p + 1 of operand
+    // OP from slot SL; the fourth piece of a chunk writes its hi and lo parts
+    // to buffer BF
+    big_tile::u32x4 chi, clo;                    // a chunk's hi and lo bf16 pairs
+    auto piece = [&](auto OP, auto SL, auto BF, auto Pp) {
+        constexpr int op = OP, sl = SL, bf = BF, p = Pp;
+        constexpr int c = p >> 2;
+        const uint4& w4 = cw[op][sl];
+        uint32_t w = c == 0 ? w4.x : c == 1 ? w4.y : c == 2 ? w4.z : w4.w;
+        uint32_t sb = static_cast<uint32_t>(sv[op][sl] >> (16 * ((8 * c) / BLOCK))) & 0xFFFFu;
+        // pinned to this point of the MFMA sequence: its inputs are taken
+        // here and its results are required here, so the compiler can neither
+        // gather the pieces into one burst nor delay them to the write
+        asm volatile("" : "+v"(w), "+v"(sb));
+        const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, p & 3) * scale_value<SFMT>(sb);  // exact
+        const v2bf h = __builtin_convertvector(v, v2bf);                          // RNE
+        const v2bf l = __builtin_convertvector(v - __builtin_convertvector(h, v2f), v2bf);   // exact
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h), lb = __builtin_bit_cast(uint32_t, l);
+        asm volatile("" : : "v"(hb), "v"(lb));
+        chi[p & 3] = hb;
+        clo[p & 3] = lb;
+        if constexpr ((p & 3) == 3) {
+            const uint32_t addr = wr[c] + bf * kSBuf;
+            big_tile::lds_write16<op * 2 * kSPart>(addr, chi);
+            big_tile::lds_write16<op * 2 * kSPart + kSPart>(addr, clo);
+        }
+    };
+    auto stage_row = [&](auto OP, auto SL, auto BF) {
+        big_tile::static_for<16>([&](auto Pp) { piece(OP, SL, BF, Pp); });
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // fragment reads: lane half h of step q reads chunk 2 q + h of its row
+    const int fr = lane & 31;
+    const int fh = lane >> 5;
+    const int rkey = (fr >> 2) & 3;
+    uint32_t rd_a[2][2], rd_b[2][2];
+#pragma unroll
+    for (int bf = 0; bf < 2; ++bf)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t pos = static_cast<uint32_t>(((2 * q + fh) ^ rkey) << 4);
+            rd_a[bf][q] = lds0 + bf * kSBuf + (wm * 128 + fr) * kSRow + pos;
+            rd_b[bf][q] = lds0 + bf * kSBuf + 2 * kSPart + (wn * 128 + fr) * kSRow + pos;
+        }
+    // x: B rows (the MFMA row operand), y: A rows; h / l: hi / lo parts
+    struct Frag { big_tile::u32x4 xh[4], yh[4], xl[4], yl[4]; };
+    Frag frg[2];
+    // read r (0..15) of a step.  The order keeps the first four away from the
+    // registers the previous step's last MFMAs read, and puts each fragment
+    // well before its first use in the next step.
+    auto read = [&](auto Rr, Frag& g, uint32_t ra, uint32_t rb) {
+        constexpr int r = Rr;
+        constexpr int t = r < 8 ? r & 3 : r < 11 ? r - 8 : r < 15 ? r - 11 : 3;
+        constexpr int kLo = kSPart;
+        if constexpr (r < 4) big_tile::lds_read16<t * 32 * kSRow>(g.xh[t], rb);
+        else if constexpr (r < 8) {
+            if constexpr (KINDS == 3) big_tile::lds_read16<kLo + t * 32 * kSRow>(g.yl[t], ra);
+            else big_tile::lds_read16<t * 32 * kSRow>(g.yh[t], ra);
+        } else if constexpr (r < 11 || r == 15) big_tile::lds_read16<kLo + t * 32 * kSRow>(g.xl[t], rb);
+        else {
+            if constexpr (KINDS == 3) big_tile::lds_read16<t * 32 * kSRow>(g.yh[t], ra);
+            else big_tile::lds_read16<kLo + t * 32 * kSRow>(g.yl[t], ra);
+        }
+    };
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    // the NMF MFMAs of one step on f, kind by kind; the 16 reads of the next
+    // step into g, one every KINDS MFMAs; the 16 staging pieces of one row of
+    // operand OP (slot SL) into buffer BF, one every KINDS MFMAs
+    auto kstep = [&](auto OP, auto SL, auto BF, const Frag& f, Frag& g, uint32_t ra, uint32_t rb) {
+        big_tile::static_for<NMF>([&](auto J) {
+            constexpr int j = J;
+            constexpr int kind = j / 16, ti = (j % 16) >> 2, tj = j & 3;
+            const big_tile::u32x4& x = kind == 0 || kind == 1 ? f.xh[ti] : f.xl[ti];
+            const big_tile::u32x4& y = kind == 0 || kind == 2 ? f.yh[tj] : f.yl[tj];
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[ti][tj]) : "v"(x), "v"(y));
+            if constexpr (j % KINDS == 0) read(std::integral_constant<int, j / KINDS>{}, g, ra, rb);
+            if constexpr (j % KINDS == 1) piece(OP, SL, BF, std::integral_constant<int, j / KINDS>{});
+        });
+    };
+
+    // prologue: stage 0 whole and the A rows of stage 1 dequantised, the
+    // next codes of each slot in flight
+    fetch(I0{}, I0{}, 0);
+    fetch(I1{}, I0{}, 0);
+    fetch(I0{}, I1{}, 1);
+    fetch(I1{}, I1{}, 1);
+    stage_row(I0{}, I0{}, I0{});
+    stage_row(I1{}, I0{}, I0{});
+    stage_row(I0{}, I1{}, I1{});
+    fetch(I0{}, I0{}, 2);
+    fetch(I1{}, I0{}, 2);
+    fetch(I0{}, I1{}, 3);
+    big_tile::lds_wait_barrier();
+    big_tile::static_for<16>([&](auto Rr) { read(Rr, frg[0], rd_a[0][0], rd_b[0][0]); });
+    // stage s: buffer PAR = s % 2 holds it
+    auto stage = [&](auto PAR, int s) {
+        constexpr int par = PAR;
+        using P = std::integral_constant<int, par>;
+        using Q = std::integral_constant<int, par ^ 1>;
+        big_tile::lds_wait();
+        kstep(I1{}, Q{}, Q{}, frg[0], frg[1], rd_a[par][1], rd_b[par][1]);   // B rows of stage s + 1
+        fetch(I1{}, Q{}, s + 3);
+        big_tile::lds_wait_barrier();         // stage s + 1 published; buffer par is free
+        kstep(I0{}, P{}, P{}, frg[1], frg[0], rd_a[par ^ 1][0], rd_b[par ^ 1][0]);   // A rows of stage s + 2
+        fetch(I0{}, P{}, s + 4);
+    };
+    // pairs of stages with no branch around either (see the E8M0 form)
+    int s = 0;
+    for (; s + 1 < nst; s += 2) {
+        stage(I0{}, s);
+        stage(I1{}, s + 1);
+    }
+    if (s < nst) stage(I0{}, s);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // MFMA results must settle before the accumulation registers are read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                   "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]),
+                   "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
+                   "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
+    // (the epilogue begins with a barrier, after which LDS is reused)
+    big_tile::NoScale pre;
+    big_tile::epilogue<OUT, STAGE16>(acc, lds, wave, lane, m0, n0, M, N, D, ldd, ep, vec_ok, pre);
+}
+
 template <int BLOCK, int SFMT, int OUT>
 hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const void* sa,
                       const uint8_t* b, const void* sb, void* d, int64_t ldd, const Epilogue& ep,
                       hipStream_t stream) {
+    if constexpr (SFMT != BSFP8_MX_E8M0) {
+        // the large tile wherever it still gives the chip enough workgroups
+        const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+        if (big >= 128) {
+            const int tm = static_cast<int>((M + 255) / 256), tn = static_cast<int>((N + 255) / 256);
+            const dim3 g(static_cast<uint32_t>(tm) * static_cast<uint32_t>(tn));
+            const int vec = vec16_ok(OUT, d, ldd, ep);
+            const uint8_t* sa8 = static_cast<const uint8_t*>(sa);
+            const uint8_t* sb8 = static_cast<const uint8_t*>(sb);
+            if (OUT != BSFP8_OUT_F32 && ep.beta == 0.0f)
+                hipLaunchKernelGGL((gemm_mx_split_big_kernel<BLOCK, SFMT, OUT, OUT != BSFP8_OUT_F32>), g,
+                                   dim3(kThreads), 0, stream, static_cast<int>(M), static_cast<int>(N),
+                                   static_cast<int>(K), a, sa8, b, sb8, d, ldd, ep, tm, tn, vec);
+            else
+                hipLaunchKernelGGL((gemm_mx_split_big_kernel<BLOCK, SFMT, OUT, false>), g, dim3(kThreads), 0,
+                                   stream, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
+                                   sa8, b, sb8, d, ldd, ep, tm, tn, vec);
+            return hipGetLastError();
+        }
+    }
     if constexpr (SFMT == BSFP8_MX_E8M0 && BLOCK != 32) {
         // the large tile wherever it still gives the chip enough workgroups
         const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);

@@ -8,8 +8,9 @@ elements, section 5.3; FP16 or BF16 block scales, section 3.2) on the GPU.
 * scaled_gemm_mx: D against the oracle's fp64 product of the dequantised
   operands, max |D - D_ref| / S within the output type's tolerance, for every
   block size and scale format, FP32 / bf16 / FP16 output, alpha / beta and
-  ragged M, N, K, on both the 128 x 128 and the 256 x 256 kernel; and the
-  8192^3 shape of the MXFP4 workload on sampled outputs.
+  ragged M, N, K, on the 128 x 128 kernel and both 256 x 256 kernels (E8M0;
+  FP16 / BF16 scales); and the 8192^3 shape of the MXFP4 workload on sampled
+  outputs.
 """
 import numpy as np
 import pytest
@@ -139,36 +140,47 @@ def test_mx_gemm_alpha_beta(block, scale):
     check_gemm_ex(d, dr, sr, -0.5, 2.0, c32.astype(np.float64), "f32", f"mx alpha/beta {block} {scale}")
 
 
+LARGE = [(16, "e8m0"), (8, "e8m0"), (32, "f16"), (16, "f16"), (8, "f16"),
+         (32, "bf16"), (16, "bf16"), (8, "bf16")]
+
+
 @pytest.mark.parametrize("out", ["bf16", "f32", "f16"])
-@pytest.mark.parametrize("block", [16, 8])
+@pytest.mark.parametrize("block,scale", LARGE)
 @pytest.mark.parametrize("M,N,K", [(4100, 2049, 160), (2304, 3840, 512)])
-def test_mx_gemm_large_tile_parity(M, N, K, block, out):
-    """Shapes with at least 128 tiles of 256 x 256 take the large-tile kernel
-    (E8M0 blocks of 16 or 8): ragged M and N, K % 64 == 32, all outputs."""
-    say(f"scaled_gemm_mx large tile block={block} M={M} N={N} K={K} -> {out}")
+def test_mx_gemm_large_tile_parity(M, N, K, block, scale, out):
+    """Shapes with at least 128 tiles of 256 x 256 take the large-tile kernels
+    (E8M0 blocks of 16 or 8; FP16 / BF16 scales with any block): ragged M
+    and N, K % 64 == 32, all outputs."""
+    say(f"scaled_gemm_mx large tile block={block} {scale} M={M} N={N} K={K} -> {out}")
     a = inputs(M + K, M, K, "normal")
     b = inputs(N + K, N, K, "laplace")
-    qa, sa = oracle.mx_quantize(a, block, "e8m0")
-    qb, sb = oracle.mx_quantize(b, block, "e8m0")
-    d = run_gemm(qa, sa, qb, sb, block, "e8m0", out, K)
-    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, block, "e8m0")
-    check_gemm(d, dr, sr, out, f"mx large tile {block} {M}x{N}x{K} {out}")
+    qa, sa = oracle.mx_quantize(a, block, scale)
+    qb, sb = oracle.mx_quantize(b, block, scale)
+    d = run_gemm(qa, sa, qb, sb, block, scale, out, K)
+    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, block, scale)
+    check_gemm(d, dr, sr, out, f"mx large tile {block} {scale} {M}x{N}x{K} {out}")
 
 
-@pytest.mark.parametrize("block", [16, 8])
-def test_mx_gemm_large_tile_alpha_beta(block):
+@pytest.mark.parametrize("block,scale", [(16, "e8m0"), (8, "e8m0"), (16, "f16"), (8, "bf16")])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_mx_gemm_large_tile_alpha_beta(block, scale, out):
     import torch
     M, N, K = 2304, 3840, 224
     a = inputs(81, M, K)
     b = inputs(82, N, K)
-    qa, sa = oracle.mx_quantize(a, block, "e8m0")
-    qb, sb = oracle.mx_quantize(b, block, "e8m0")
-    c16 = torch.from_numpy(np.random.default_rng(83).standard_normal((M, N)).astype(np.float32) * 20).to(torch.bfloat16)
-    say(f"scaled_gemm_mx large tile alpha/beta block={block}")
-    d = run_gemm(qa, sa, qb, sb, block, "e8m0", "bf16", K, 0.75, c16.cuda(), -1.5)
-    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, block, "e8m0")
-    check_gemm_ex(d, dr, sr, 0.75, -1.5, c16.float().numpy().astype(np.float64), "bf16",
-                  f"mx large tile alpha/beta {block}")
+    qa, sa = oracle.mx_quantize(a, block, scale)
+    qb, sb = oracle.mx_quantize(b, block, scale)
+    c32 = np.random.default_rng(83).standard_normal((M, N)).astype(np.float32) * 20
+    if out == "bf16":
+        c = torch.from_numpy(c32).to(torch.bfloat16)
+        cref = c.float().numpy().astype(np.float64)
+    else:
+        c = torch.from_numpy(c32)
+        cref = c32.astype(np.float64)
+    say(f"scaled_gemm_mx large tile alpha/beta block={block} {scale} -> {out}")
+    d = run_gemm(qa, sa, qb, sb, block, scale, out, K, 0.75, c.cuda(), -1.5)
+    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, block, scale)
+    check_gemm_ex(d, dr, sr, 0.75, -1.5, cref, out, f"mx large tile alpha/beta {block} {scale} {out}")
 
 
 @pytest.mark.parametrize("block,scale", [(16, "e8m0"), (8, "bf16")])
