@@ -423,28 +423,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_big_kernel(
             vb[sl] |= hb << (8 * (NB / 2) * h);
         }
     };
-    auto chunk_ptr = [&](int buf, int part, int R, int c) {
-        return lds + buf * kBigBuf + part * kBigPart + R * kRow + ((c ^ ((R >> 1) & 7)) << 4);
-    };
-    // one row's 64 K values (codes w[0..1], scales v) into part `part`
-    auto stage_row = [&](const uint4 (&w)[2], uint64_t v, int buf, int part) {
+    // Staging, in pieces placed between the MFMAs of a K step: piece p (0..31)
+    // converts values 2 p, 2 p + 1 of this thread's row of operand OP (slot
+    // SL), 64-K half p / 16, chunk (p / 4) % 4, with its block's E8M0 scale;
+    // the fourth piece of a chunk writes it to row sr of part OP of buffer BF
+    // (chunk c of row R at c ^ ((R >> 1) & 7)).
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((big_tile::lds_byte*)lds));
+    uint32_t wr[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float sc[32 / BLOCK];
-#pragma unroll
-            for (int j = 0; j < 32 / BLOCK; ++j)
-                sc[j] = scale_value<BSFP8_MX_E8M0>(static_cast<uint32_t>(v >> (8 * (h * (32 / BLOCK) + j))) & 0xFFu);
-            v8bf hi[4], lo[4];
-            dequant32<BLOCK, BSFP8_MX_E8M0, false>(w[h], sc, hi, lo);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<v8bf*>(chunk_ptr(buf, part, sr, 4 * h + j)) = hi[j];
+    for (int c = 0; c < 8; ++c) wr[c] = lds0 + sr * kRow + ((c ^ ((sr >> 1) & 7)) << 4);
+    big_tile::u32x4 chunk;
+    uint32_t cwd;                                // the chunk's code word and scale,
+    float csc;                                   // taken at its first piece
+    auto piece = [&](auto OP, auto SL, auto BF, auto Pp) {
+        constexpr int op = OP, sl = SL, bf = BF, p = Pp;
+        constexpr int h = p >> 4, j = (p >> 2) & 3, c = 4 * h + j;
+        if constexpr ((p & 3) == 0) {
+            const uint4& w4 = op == 0 ? ca[sl][h] : cb[sl][h];
+            cwd = j == 0 ? w4.x : j == 1 ? w4.y : j == 2 ? w4.z : w4.w;
+            csc = scale_value<BSFP8_MX_E8M0>(
+                static_cast<uint32_t>((op == 0 ? va[sl] : vb[sl]) >> (8 * ((32 * h + 8 * j) / BLOCK))) & 0xFFu);
+            // the chunk's work is pinned to this point of the MFMA sequence
+            asm volatile("" : "+v"(cwd), "+v"(csc));
         }
+        const v2bf pr = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cwd, csc, p & 3);
+        const uint32_t pb = __builtin_bit_cast(uint32_t, pr);
+        asm volatile("" : : "v"(pb));            // and each pair is done here
+        chunk[p & 3] = pb;
+        if constexpr ((p & 3) == 3) big_tile::lds_write16<op * kBigPart>(wr[c] + bf * kBigBuf, chunk);
     };
-    auto stage = [&](auto SLOT, int buf) {
-        constexpr int sl = SLOT;
-        stage_row(ca[sl], va[sl], buf, 0);
-        stage_row(cb[sl], vb[sl], buf, 1);
+    auto stage_row = [&](auto OP, auto SL, auto BF) {
+        big_tile::static_for<32>([&](auto Pp) { piece(OP, SL, BF, Pp); });
     };
 
     // Fragment reads and MFMAs are ordered inline assembly (the scheme of the
@@ -454,7 +463,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_big_kernel(
     // 0..2 of stage s into the other buffer (free since the previous barrier);
     // the barrier before step 3 publishes it, and step 3 reads its first
     // fragments.
-    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((big_tile::lds_byte*)lds));
     const int fr = lane & 31;
     const int fh = lane >> 5;
     const int sw = (fr >> 1) & 7;
@@ -481,7 +489,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_big_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
     // the 16 MFMAs of one step on f, with the 8 reads of the next step into g
-    auto kstep = [&](const Frag& f, Frag& g, uint32_t ra, uint32_t rb) {
+    // and, with DEQ, the 32 staging pieces of operand OP's row of slot SL
+    // into buffer BF, two after each MFMA
+    auto kstep = [&](auto DEQ, auto OP, auto SL, const Frag& f, Frag& g, uint32_t ra, uint32_t rb) {
         big_tile::static_for<16>([&](auto J) {
             constexpr int j = J;
             constexpr int ti = j >> 2, tj = j & 3;
@@ -492,31 +502,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_big_kernel(
                 if constexpr (j & 1) big_tile::lds_read16<t * 32 * kRow>(g.y[t], ra);
                 else big_tile::lds_read16<t * 32 * kRow>(g.x[t], rb);
             }
+            if constexpr (DEQ) {
+                piece(OP, SL, SL, std::integral_constant<int, 2 * j>{});
+                piece(OP, SL, SL, std::integral_constant<int, 2 * j + 1>{});
+            }
         });
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     fetch(I0{}, 0);
     fetch(I1{}, 1);
-    stage(I0{}, 0);
+    stage_row(I0{}, I0{}, I0{});
+    stage_row(I1{}, I0{}, I0{});
     big_tile::lds_wait_barrier();
     read_frags(frg[0], rd_a[0][0], rd_b[0][0]);
     fetch(I0{}, 2);
+    // Stage s + 1 (slot and buffer s % 2 ^ 1) is dequantised during steps 0
+    // and 1 of stage s, also after the last stage, from zeros: that buffer
+    // was last read before the previous barrier.
     auto step = [&](auto PAR, int s) {
         constexpr int par = PAR;              // s % 2 = this stage's buffer
         constexpr int nb = par ^ 1;
-        const bool more = s + 1 < nst;
+        using NB_ = std::integral_constant<int, nb>;
         big_tile::lds_wait();
-        kstep(frg[0], frg[1], rd_a[par][1], rd_b[par][1]);
-        if (more) stage_row(ca[nb], va[nb], nb, 0);
+        kstep(std::true_type{}, I0{}, NB_{}, frg[0], frg[1], rd_a[par][1], rd_b[par][1]);
         big_tile::lds_wait();
-        kstep(frg[1], frg[0], rd_a[par][2], rd_b[par][2]);
-        if (more) stage_row(cb[nb], vb[nb], nb, 1);
+        kstep(std::true_type{}, I1{}, NB_{}, frg[1], frg[0], rd_a[par][2], rd_b[par][2]);
         big_tile::lds_wait();
-        kstep(frg[0], frg[1], rd_a[par][3], rd_b[par][3]);
+        kstep(std::false_type{}, I0{}, NB_{}, frg[0], frg[1], rd_a[par][3], rd_b[par][3]);
         big_tile::lds_wait_barrier();         // stage s + 1 published; buffer par is free after step 3's reads
-        kstep(frg[1], frg[0], rd_a[nb][0], rd_b[nb][0]);
-        if (s + 3 < nst) fetch(std::integral_constant<int, nb>{}, s + 3);
+        kstep(std::false_type{}, I0{}, NB_{}, frg[1], frg[0], rd_a[nb][0], rd_b[nb][0]);
+        if (s + 3 < nst) fetch(NB_{}, s + 3);
     };
     // pairs of stages with no branch around either (a conditional second step
     // made the compiler copy all 256 accumulators at the loop's join)
@@ -530,9 +546,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_big_kernel(
         // the last 32 K: its first fragments are in frg[0]
         const int pb = nfull & 1;
         big_tile::lds_wait();
-        kstep(frg[0], frg[1], rd_a[pb][1], rd_b[pb][1]);
+        kstep(std::false_type{}, I0{}, I0{}, frg[0], frg[1], rd_a[pb][1], rd_b[pb][1]);
         big_tile::lds_wait();
-        kstep(frg[1], frg[0], rd_a[pb][1], rd_b[pb][1]);   // (its reads are not used)
+        kstep(std::false_type{}, I0{}, I0{}, frg[1], frg[0], rd_a[pb][1], rd_b[pb][1]);   // (its reads are not used)
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     // MFMA results must settle before the accumulation registers are read
@@ -639,17 +655,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_split_big_kernel(
     // OP from slot SL; the fourth piece of a chunk writes its hi and lo parts
     // to buffer BF
     big_tile::u32x4 chi, clo;                    // a chunk's hi and lo bf16 pairs
+    uint32_t cwd;                                // the chunk's code word and scale,
+    float csc;                                   // taken at its first piece
     auto piece = [&](auto OP, auto SL, auto BF, auto Pp) {
         constexpr int op = OP, sl = SL, bf = BF, p = Pp;
         constexpr int c = p >> 2;
-        const uint4& w4 = cw[op][sl];
-        uint32_t w = c == 0 ? w4.x : c == 1 ? w4.y : c == 2 ? w4.z : w4.w;
-        uint32_t sb = static_cast<uint32_t>(sv[op][sl] >> (16 * ((8 * c) / BLOCK))) & 0xFFFFu;
-        // pinned to this point of the MFMA sequence: its inputs are taken
-        // here and its results are required here, so the compiler can neither
-        // gather the pieces into one burst nor delay them to the write
-        asm volatile("" : "+v"(w), "+v"(sb));
-        const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, p & 3) * scale_value<SFMT>(sb);  // exact
+        if constexpr ((p & 3) == 0) {
+            const uint4& w4 = cw[op][sl];
+            cwd = c == 0 ? w4.x : c == 1 ? w4.y : c == 2 ? w4.z : w4.w;
+            csc = scale_value<SFMT>(static_cast<uint32_t>(sv[op][sl] >> (16 * ((8 * c) / BLOCK))) & 0xFFFFu);
+            // the chunk's work is pinned to this point of the MFMA sequence
+            // (and each pair's results are required below), so the compiler
+            // can neither gather the pieces into one burst nor delay them
+            asm volatile("" : "+v"(cwd), "+v"(csc));
+        }
+        const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cwd, 1.0f, p & 3) * csc;  // exact
         const v2bf h = __builtin_convertvector(v, v2bf);                          // RNE
         const v2bf l = __builtin_convertvector(v - __builtin_convertvector(h, v2f), v2bf);   // exact
         const uint32_t hb = __builtin_bit_cast(uint32_t, h), lb = __builtin_bit_cast(uint32_t, l);
