@@ -146,11 +146,13 @@ LARGE = [(16, "e8m0"), (8, "e8m0"), (32, "f16"), (16, "f16"), (8, "f16"),
 
 @pytest.mark.parametrize("out", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("block,scale", LARGE)
-@pytest.mark.parametrize("M,N,K", [(4100, 2049, 160), (2304, 3840, 512)])
+@pytest.mark.parametrize("M,N,K", [(4100, 2049, 160), (2304, 3840, 512), (2304, 3840, 32),
+                                   (2304, 3840, 64)])
 def test_mx_gemm_large_tile_parity(M, N, K, block, scale, out):
     """Shapes with at least 128 tiles of 256 x 256 take the large-tile kernels
     (E8M0 blocks of 16 or 8; FP16 / BF16 scales with any block): ragged M
-    and N, K % 64 == 32, all outputs."""
+    and N, K % 64 == 32, all outputs, and K of one or two 32-K blocks (the
+    pipelines' shortest runs)."""
     say(f"scaled_gemm_mx large tile block={block} {scale} M={M} N={N} K={K} -> {out}")
     a = inputs(M + K, M, K, "normal")
     b = inputs(N + K, N, K, "laplace")
