@@ -203,12 +203,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_kernel(
 // accumulation registers), one workgroup per CU.  A K step of 64 reads 8
 // fragments of 1 KB per wave for 16 MFMAs, half the LDS traffic per FLOP of
 // the 128 x 128 tiling; the 256-wide edge halves the L2 traffic per FLOP.
-// Codes and E8M0 scales arrive through buffer loads (rows past the matrix
-// edge read as zero) one stage ahead of use.
+// Codes go straight from global memory to LDS (direct loads, rows past the
+// matrix edge read as zero) one stage ahead of use; the E8M0 scales arrive in
+// registers by buffer loads, also one stage ahead.
 // ---------------------------------------------------------------------------
-constexpr int kBigOperandBytes = 256 * kStride;
-constexpr int kBigStageBytes = 2 * kBigOperandBytes;
-constexpr int kBigLdsBytes = 2 * kBigStageBytes;     // 147456 bytes
 
 // E2M1 x E2M1 MFMA with E8M0 block scales; byte SEL of each scale register is used.
 template <int SEL>
