@@ -177,6 +177,8 @@ def test_workload_end_to_end(name):
     (("mxfp4", "mxfp4"), 2048, 2048, 768),
     (("e4m3", "e4m3"), 2088, 2072, 512),       # large-tile FP8 path, ragged edges
     (("e5m2", "e4m3"), 2048, 2080, 384),
+    (("e4m3", "e4m3"), 4100, 2049, 160),       # 4 rows in the last tile row, K % 128 = 32
+    (("e5m2", "e4m3"), 4224, 2048, 384),
 ])
 def test_medium_ragged_large_tile_kernels(fmts, M, N, K, out):
     """Shapes big enough for the large-tile kernels, with partial edge tiles,
@@ -193,6 +195,7 @@ _TORCH_DT = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
     (("e5m2", "e4m3"), 2088, 2072, 512),     # FP8 kernel, ragged edges
     (("mxfp4", "mxfp4"), 130, 260, 288),      # small MXFP4 kernel
     (("mxfp4", "mxfp4"), 2088, 2072, 512),    # 256 x 256 MXFP4 kernel
+    (("e4m3", "e4m3"), 4100, 2049, 160),      # FP8 kernel, larger ragged shape
 ])
 def test_alpha_beta_epilogue(fmts, M, N, K, out):
     """D = alpha A B + beta C through scaled_gemm_ex, C in the output type;
