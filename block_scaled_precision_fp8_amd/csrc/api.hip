@@ -147,6 +147,8 @@ bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K, bsfp8_format 
     if (!aligned(a_scales, 4) || !aligned(b_scales, 4)) return BSFP8_ERR_INVALID_ARG;
     const float* sa = static_cast<const float*>(a_scales);
     const float* sb = static_cast<const float*>(b_scales);
+    // the per-tile kernel addresses a 128-row band of an operand with 32-bit offsets
+    if (path == 0 && K >= (int64_t(1) << 24)) return BSFP8_ERR_UNSUPPORTED;
     if (path == 0)
         return from_hip(bsfp8::launch_gemm_fp8(M, N, K, a_fmt, a8, sa, b_fmt, b8, sb, out, d, ldd, ep,
                                                stream, tensor_mask));

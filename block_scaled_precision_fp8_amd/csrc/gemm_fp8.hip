@@ -310,15 +310,19 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
         }
     }
 
-    // direct loads: instruction i (0..3) of wave w fills rows 32 i + 8 w .. + 7
+    // direct loads: instruction i (0..3) of wave w fills rows 32 i + 8 w .. + 7.
+    // The buffer resources start at the tile's first row and cover its rows,
+    // so every offset stays below 128 K < 2^31 (K < 2^24) however large the
+    // operand, and rows past M or N fail the range check and read as zero.
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(A), 0, QA ? 0 : M * K, 0x00020000);
+        const_cast<uint8_t*>(A) + (QA ? 0 : static_cast<int64_t>(m0) * K), 0,
+        QA ? 0 : min(BM, M - m0) * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(B), 0, N * K, 0x00020000);
+        const_cast<uint8_t*>(B) + static_cast<int64_t>(n0) * K, 0, min(BN, N - n0) * K, 0x00020000);
     const int drow = 8 * wave + (lane >> 3);
     const int dchunk = (lane & 7) ^ ((drow >> 1) & 7);
-    const uint32_t dma_a = static_cast<uint32_t>(m0 + drow) * K + dchunk * 16;
-    const uint32_t dma_b = static_cast<uint32_t>(n0 + drow) * K + dchunk * 16;
+    const uint32_t dma_a = static_cast<uint32_t>(drow) * K + dchunk * 16;
+    const uint32_t dma_b = static_cast<uint32_t>(drow) * K + dchunk * 16;
     const uint32_t row_step = 32u * static_cast<uint32_t>(K);
     // direct loads of a stage: A (without QA) and B, alternating
     auto dma_one = [&](auto J, int stage, int buf) {

@@ -131,7 +131,10 @@ bsfp8_status mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
  *       the output traffic).
  * d:    M x N row-major, leading dimension ldd >= N (elements), aligned to
  *       its element size.
- * a, b must be 16-byte aligned.  K = 0 writes zeros.
+ * a, b must be 16-byte aligned.  K = 0 writes zeros.  FP8 operands need
+ * K < 2^24 (the kernel addresses a 128-row band of an operand with 32-bit
+ * offsets); larger K returns BSFP8_ERR_UNSUPPORTED.  M and N are limited only
+ * by the 2^31 - 1 bound on each dimension and on the number of 128 x 128 tiles.
  *
  * Accuracy: with S = sum_k |a_k b_k| (dequantised operands), every output
  * satisfies |D - exact| <= 2^-19 S for FP32 output and <= 2^-7 S for bf16 and
@@ -216,7 +219,8 @@ bsfp8_status fp8_quantize_granular(const float* x, int64_t rows, int64_t k, int6
  *   FP8, TILE with TILE or TENSOR: the product of the two K block scales
  *     multiplies each 32-wide K block's partial sum, as in scaled_gemm.
  *   MXFP4: MX32 on both sides (as scaled_gemm).
- * Other combinations (TILE with ROW) return BSFP8_ERR_UNSUPPORTED.
+ * Other combinations (TILE with ROW) return BSFP8_ERR_UNSUPPORTED, and so
+ * does K >= 2^23 with both FP8 scales constant along K.
  * Accuracy as for scaled_gemm_ex.
  */
 bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K,
@@ -265,7 +269,8 @@ bsfp8_status mx_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, in
  *
  * a: M x K/2 packed bytes, a_scales [M][K/block]; b: N x K/2 packed bytes
  * (the K x N column-major operand), b_scales [N][K/block]; a and b 16-byte
- * aligned, the scale arrays 8-byte aligned.  M, N >= 0; K >= 0 a multiple of 32.
+ * aligned, the scale arrays 8-byte aligned.  M, N >= 0; K >= 0 a multiple of
+ * 32, below 2^23 unless block == 32 with E8M0 scales (BSFP8_ERR_UNSUPPORTED).
  * alpha, c, ldc, beta, out, d, ldd: as for scaled_gemm_ex.
  * block = 32 with E8M0 scales runs the block-scaled MXFP4 GEMM of
  * scaled_gemm.  Every other combination is beyond the matrix instructions'

@@ -109,6 +109,8 @@ def test_scaled_gemm_argument_checks(L):
     assert g(128, 128, 64, E4M3, P, P, E4M3, P, P, 5, P, 128, None) == UNSUPPORTED
     assert g(0, 128, 64, E4M3, 0, 0, E4M3, 0, 0, BF16, 0, 128, None) == OK      # empty
     assert g(128, 0, 64, E4M3, 0, 0, E4M3, 0, 0, F32, 0, 0, None) == OK
+    # FP8: a 128-row band of an operand must fit 32-bit offsets (K < 2^24)
+    assert g(128, 128, 1 << 24, E4M3, P, P, E4M3, P, P, BF16, P, 128, None) == UNSUPPORTED
 
 
 

@@ -242,3 +242,38 @@ def test_k_zero_writes_beta_c(out):
     torch.cuda.synchronize()
     expect = (-2.0 * c.float()).to(dt)   # one FP32 product, then the output rounding
     assert torch.equal(d, expect)
+
+
+def test_fp8_operand_beyond_32bit_offsets():
+    """An A operand larger than 2^32 bytes: 2^19 + 96 rows of 8192 E4M3 codes
+    (4.3 GB), generated on the device.  Outputs in rows past the first 2^32
+    bytes of A, and in the first and last rows, against the oracle on a
+    sub-problem that holds just the sampled rows (each at the start of its own
+    128-row tile, with that tile's scales)."""
+    import torch
+    M, N, K = (1 << 19) + 96, 256, 8192
+    say(f"scaled_gemm with A of {M * K / 2**30:.2f} GiB ({M}x{N}x{K})")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    # random codes with exponent bit 3 cleared: every value finite (no 0x7F / 0xFF)
+    qa = torch.randint(0, 256, (M, K), dtype=torch.uint8, device="cuda", generator=g)
+    qa &= 0xF7
+    qb = torch.randint(0, 256, (N, K), dtype=torch.uint8, device="cuda", generator=g) & 0xF7
+    sa = torch.rand(((M + 127) // 128, K // 32), device="cuda", generator=g) + 0.5
+    sb = torch.rand(((N + 127) // 128, K // 32), device="cuda", generator=g) + 0.5
+    d = bsfp8().scaled_gemm(qa, sa, qb, sb, "e4m3", "e4m3", "bf16")
+    torch.cuda.synchronize()
+    first_past = (1 << 32) // K                      # first row that starts past 2^32 bytes
+    rng = np.random.default_rng(8)
+    ii = np.unique(np.concatenate([[0, 1, first_past - 1, first_past, first_past + 1, M - 1, M - 2],
+                                   rng.integers(first_past, M, 25)]))
+    jj = rng.integers(0, N, ii.size)
+    jj[-1] = N - 1
+    rows = qa[torch.from_numpy(ii).cuda()].cpu().numpy()
+    srows = sa[torch.from_numpy(ii // 128).cuda()].cpu().numpy()
+    del qa
+    sub = np.zeros((128 * ii.size, K), dtype=np.uint8)
+    sub[0::128] = rows
+    dr, sr = oracle.gemm_points("e4m3", sub, srows, "e4m3", from_dev(qb), from_dev(sb),
+                                128 * np.arange(ii.size), jj)
+    got = from_dev(d[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()])
+    check_gemm(got, dr, sr, "bf16", "A beyond 2^32 bytes")
