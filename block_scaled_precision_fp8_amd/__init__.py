@@ -9,10 +9,16 @@ raises, and a non-OK status raises ``RuntimeError``.
 Functions (same names as the C ABI):
   fp8_quantize(x, fmt="e4m3", tile_rows=128) -> (codes, scales)
   fp8_quantize_transposed(x, fmt="e4m3", tile_rows=128) -> (codes of x^T, scales)
+  fp8_quantize_granular(x, fmt="e4m3", granularity="tile"|"row"|"tensor") -> (codes, scales)
   mxfp4_quantize(x) -> (packed, scales)
+  mx_quantize(x, block=32|16|8, scale="e8m0"|"f16"|"bf16") -> (packed, scales)
   scaled_gemm(a, a_scales, b, b_scales, a_fmt, b_fmt, out="bf16", d=None) -> d
   scaled_gemm_ex(a, a_scales, b, b_scales, a_fmt, b_fmt, out="bf16", alpha=1.0,
                  c=None, beta=0.0, d=None) -> d = alpha A B + beta C
+  scaled_gemm_granular(..., a_gran, b_gran, ...) -> d (scales per tile, row or tensor)
+  scaled_gemm_mx(a, a_scales, b, b_scales, block, scale, out="bf16", ...) -> d
+  scaled_gemm_quantize_a(x, b, b_scales, ...) -> d (A quantised inside the GEMM;
+                 optionally also its codes and scales)
 """
 from __future__ import annotations
 
