@@ -581,10 +581,115 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
     }
 }
 
+// Skinny form (few output rows, so few 128 x 128 tiles: the two-pass kernel
+// would keep only a handful of CUs streaming B).  One workgroup per 32 x 32
+// output tile, N / 32 of them per 32 rows; its four waves split the K blocks
+// into four contiguous ranges and each computes the tile's partial sum over
+// its range with the same per-block product and promotion as the main kernel
+// (tile_product, acc = fma(sigma_kb, P_kb, acc)).  Fragments go from global
+// memory straight to registers in the MFMA layout (lane (r, h) loads the 16
+// codes K 16 h .. 16 h + 15 of row r of a block), kDepth blocks ahead, with
+// range-checked buffer loads: rows past M or N and blocks past the wave's
+// range read as zero and their sigma is zero.  The four partial sums are
+// added in a fixed order through LDS, so the result does not depend on
+// timing; wave 0 writes the tile.
+constexpr int kSkinnyDepth = 8;              // blocks in flight per wave
+constexpr int64_t kSkinnyMaxM = 64;          // rows up to which the skinny form is used
+
+template <int AF, int BF, int OUT>
+__global__ __launch_bounds__(kThreads, 2) void gemm_fp8_skinny_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
+    const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D,
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok, int tensor_mask) {
+    __shared__ v16f part[3][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Workgroups go to the 8 XCDs round-robin by launch index.  The row tiles
+    // of one column tile are launched 8 apart, so they run on the same XCD at
+    // about the same time and read that tile's B rows through one L2.  The
+    // column tiles are padded to a multiple of 8; padding workgroups exit.
+    const int grp = static_cast<int>(blockIdx.x) / (8 * tiles_m);
+    const int rem = static_cast<int>(blockIdx.x) - grp * 8 * tiles_m;
+    const int tm = rem >> 3, tn = grp * 8 + (rem & 7);
+    if (tn >= tiles_n) return;
+    const int m0 = tm * 32, n0 = tn * 32;
+    const int nkb = K >> 5;
+    const int per = (nkb + 3) >> 2;
+    const int kb0 = min(wave * per, nkb), kb1 = min(kb0 + per, nkb);
+
+    // operand rows of this tile (the resources start at its first row, so
+    // offsets stay below 32 K)
+    const int rows_a = min(32, M - m0), rows_b = min(32, N - n0);
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(A) + static_cast<int64_t>(m0) * K, 0, rows_a * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(B) + static_cast<int64_t>(n0) * K, 0, rows_b * K, 0x00020000);
+    const int r = lane & 31, h = lane >> 5;
+    const uint32_t off0 = static_cast<uint32_t>(r * K + 16 * h);
+    // sigma of block kb (zero past the wave's range)
+    const bool a_tensor = (tensor_mask & 1) != 0, b_tensor = (tensor_mask & 2) != 0;
+    const float* sa_row = sA + (a_tensor ? 0 : static_cast<int64_t>(m0 >> 7) * nkb);
+    const float* sb_row = sB + (b_tensor ? 0 : static_cast<int64_t>(n0 >> 7) * nkb);
+    auto sigma = [&](int kb) {
+        if (kb >= kb1) return 0.0f;
+        return (a_tensor ? sa_row[0] : sa_row[kb]) * (b_tensor ? sb_row[0] : sb_row[kb]);
+    };
+    // slot j: the fragments and sigma of one block, fetched kSkinnyDepth blocks ahead
+    u32x4 xa[kSkinnyDepth], xb[kSkinnyDepth];
+    float sg[kSkinnyDepth];
+    auto fetch = [&](auto SLOT, int kb) {
+        constexpr int j = SLOT;
+        const uint32_t o = kb < kb1 ? off0 + static_cast<uint32_t>(kb) * 32u : 0x80000000u;
+        const auto wa = __builtin_amdgcn_raw_buffer_load_b128(rs_a, static_cast<int>(o), 0, 0);
+        const auto wb = __builtin_amdgcn_raw_buffer_load_b128(rs_b, static_cast<int>(o), 0, 0);
+        xa[j] = u32x4{wa[0], wa[1], wa[2], wa[3]};
+        xb[j] = u32x4{wb[0], wb[1], wb[2], wb[3]};
+        sg[j] = sigma(kb);
+    };
+    v16f acc = v16f{};
+    static_for<kSkinnyDepth>([&](auto J) { fetch(J, kb0 + J); });
+    for (int kb = kb0; kb < kb1; kb += kSkinnyDepth) {
+        static_for<kSkinnyDepth>([&](auto J) {
+            constexpr int j = J;
+            const float sgj = sg[j];
+            const v16f p = tile_product<AF, BF, OUT>(xb[j], xa[j]);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = fmaf(sgj, p[e], acc[e]);
+            fetch(J, kb + j + kSkinnyDepth);
+        });
+    }
+    if (wave > 0) part[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    // the partial sums of waves 1, 2, 3, added in that order
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        const v16f q = part[w][lane];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] += q[e];
+    }
+    // lane (r, h) holds row m0 + r, columns n0 + 8 q + 4 h + e in acc[4 q + e]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float a4[4] = {acc[4 * q + 0], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        finish_row_chunk<OUT, 4>(D, ldd, ep, m0 + r, n0 + 8 * q + 4 * h, M, N, vec_ok, a4);
+    }
+}
+
 template <int AF, int BF, int OUT, bool QA>
 hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
                       const uint8_t* b, const float* sb, void* d, int64_t ldd,
                       const Epilogue& ep, int tensor_mask, const OnlineA& qa, hipStream_t stream) {
+    if constexpr (!QA) {
+        if (M <= kSkinnyMaxM) {
+            const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
+            const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
+            hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, OUT>), dim3(wgs), dim3(kThreads), 0,
+                               stream, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, sa,
+                               b, sb, d, ldd, ep, tm, tn, vec16_ok(OUT, d, ldd, ep), tensor_mask);
+            return hipGetLastError();
+        }
+    }
     const int tiles_m = static_cast<int>((M + BM - 1) / BM);
     const int tiles_n = static_cast<int>((N + BN - 1) / BN);
     const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));

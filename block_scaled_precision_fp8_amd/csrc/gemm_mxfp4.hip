@@ -431,11 +431,103 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     big_tile::epilogue<OUT, STAGE16>(acc, lds, wave, lane, m0, n0, M, N, D, ldd, ep, vec_ok, none);
 }
 
+// Skinny form (up to kSkinnyMaxM rows), as the FP8 one: one workgroup per
+// 32 x 32 output tile, the four waves split the 64-K steps into contiguous
+// ranges, fragments and scale bytes go from global memory straight to
+// registers kDepth steps ahead (lane (r, h) takes the 16 packed bytes and the
+// E8M0 byte of block 2 t + h of row r), and the partial sums are added in a
+// fixed order through LDS.  Blocks past K or past the wave's range read as
+// zero codes with a zero scale byte (2^-127), which contribute nothing.
+constexpr int kSkinnyDepth = 8;
+constexpr int64_t kSkinnyMaxM = 64;
+
+template <int OUT>
+__global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_skinny_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
+    __shared__ v16f part[3][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Workgroups go to the 8 XCDs round-robin by launch index.  The row tiles
+    // of one column tile are launched 8 apart, so they run on the same XCD at
+    // about the same time and read that tile's B rows through one L2.  The
+    // column tiles are padded to a multiple of 8; padding workgroups exit.
+    const int grp = static_cast<int>(blockIdx.x) / (8 * tiles_m);
+    const int rem = static_cast<int>(blockIdx.x) - grp * 8 * tiles_m;
+    const int tm = rem >> 3, tn = grp * 8 + (rem & 7);
+    if (tn >= tiles_n) return;
+    const int m0 = tm * 32, n0 = tn * 32;
+    const int kbytes = K >> 1, nkb = K >> 5;
+    const int nsteps = (nkb + 1) >> 1;          // 64-K steps; the last may hold one block
+    const int per = (nsteps + 3) >> 2;
+    const int t0 = min(wave * per, nsteps), t1 = min(t0 + per, nsteps);
+
+    const int rows_a = min(32, M - m0), rows_b = min(32, N - n0);
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(A) + static_cast<int64_t>(m0) * kbytes, 0, rows_a * kbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(B) + static_cast<int64_t>(n0) * kbytes, 0, rows_b * kbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sA) + static_cast<int64_t>(m0) * nkb, 0, rows_a * nkb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sB) + static_cast<int64_t>(n0) * nkb, 0, rows_b * nkb, 0x00020000);
+    const int r = lane & 31, h = lane >> 5;
+    constexpr uint32_t kOut = 0x80000000u;
+    uint4 xa[kSkinnyDepth], xb[kSkinnyDepth];
+    uint32_t ea[kSkinnyDepth], eb[kSkinnyDepth];
+    auto fetch = [&](auto SLOT, int t) {
+        constexpr int j = SLOT;
+        const int blk = 2 * t + h;
+        const bool ok = t < t1 && blk < nkb;
+        const uint32_t oc = ok ? static_cast<uint32_t>(r * kbytes + 16 * blk) : kOut;
+        const uint32_t os = ok ? static_cast<uint32_t>(r * nkb + blk) : kOut;
+        const auto wa = __builtin_amdgcn_raw_buffer_load_b128(rs_a, static_cast<int>(oc), 0, 0);
+        const auto wb = __builtin_amdgcn_raw_buffer_load_b128(rs_b, static_cast<int>(oc), 0, 0);
+        xa[j] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+        xb[j] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+        ea[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_sa, static_cast<int>(os), 0, 0);
+        eb[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_sb, static_cast<int>(os), 0, 0);
+    };
+    v16f acc = v16f{};
+    static_for<kSkinnyDepth>([&](auto J) { fetch(J, t0 + J); });
+    for (int t = t0; t < t1; t += kSkinnyDepth) {
+        static_for<kSkinnyDepth>([&](auto J) {
+            constexpr int j = J;
+            acc = mfma_fp4(xb[j], xa[j], eb[j], ea[j], acc);   // B rows are the row operand
+            fetch(J, t + j + kSkinnyDepth);
+        });
+    }
+    if (wave > 0) part[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        const v16f q = part[w][lane];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] += q[e];
+    }
+    // lane (r, h) holds row m0 + r, columns n0 + 8 q + 4 h + e in acc[4 q + e]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float a4[4] = {acc[4 * q + 0], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        finish_row_chunk<OUT, 4>(D, ldd, ep, m0 + r, n0 + 8 * q + 4 * h, M, N, vec_ok, a4);
+    }
+}
+
 template <int OUT>
 hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* a_scales,
                       const uint8_t* b, const uint8_t* b_scales, void* d, int64_t ldd,
                       const Epilogue& ep, hipStream_t stream) {
     const int vec = vec16_ok(OUT, d, ldd, ep);
+    if (M <= kSkinnyMaxM) {
+        const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
+        const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
+        hipLaunchKernelGGL(gemm_mxfp4_skinny_kernel<OUT>, dim3(wgs), dim3(kThreads), 0, stream,
+                           static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, a_scales, b,
+                           b_scales, d, ldd, ep, tm, tn, vec);
+        return hipGetLastError();
+    }
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
     const bool fits32 = M * (K / 2) < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31);
     if (K % 256 == 0 && big_tiles >= kBigTileThreshold && fits32) {

@@ -79,6 +79,17 @@ def test_dot_examples_fp32_output_exact():
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fmts", [("e4m3", "e4m3"), ("e5m2", "e4m3")])
+@pytest.mark.parametrize("M,N,K", [(1, 257, 32), (33, 1000, 4128), (64, 4096, 8192), (17, 96, 96),
+                                   (64, 130, 1024)])
+def test_fp8_skinny(M, N, K, fmts, out):
+    """Up to 64 rows: the skinny kernel (32 x 32 tiles, K blocks split over four
+    waves and summed in a fixed order).  K = 32 leaves three waves without a
+    block; 129 blocks split 33 / 33 / 33 / 30; ragged N."""
+    full_check(M, N, K, fmts[0], fmts[1], out, seed=M + N + K, label="skinny")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("fmts", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"),
                                   ("e5m2", "e5m2")])
 @pytest.mark.parametrize("M,N,K", [(200, 328, 96), (1, 1, 32), (129, 255, 64),
@@ -92,6 +103,16 @@ def test_fp8_small_ragged(M, N, K, fmts, out):
                                    (256, 256, 512), (130, 260, 288), (64, 64, 2080)])
 def test_mxfp4_small_ragged(M, N, K, out):
     full_check(M, N, K, "mxfp4", "mxfp4", out, seed=M * 5 + N + K, label="small mxfp4")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("M,N,K", [(1, 257, 32), (33, 1000, 4128), (64, 4096, 8192), (17, 96, 96),
+                                   (48, 130, 2080)])
+def test_mxfp4_skinny(M, N, K, out):
+    """Up to 64 rows: the skinny MXFP4 kernel (32 x 32 tiles, the 64-K steps
+    split over four waves and summed in a fixed order).  K % 64 == 32 leaves a
+    last step with one block; K = 32 leaves three waves without a step."""
+    full_check(M, N, K, "mxfp4", "mxfp4", out, seed=M * 7 + N + K, label="skinny mxfp4")
 
 
 def test_degenerate_shapes():
@@ -196,6 +217,8 @@ _TORCH_DT = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
     (("mxfp4", "mxfp4"), 130, 260, 288),      # small MXFP4 kernel
     (("mxfp4", "mxfp4"), 2088, 2072, 512),    # 256 x 256 MXFP4 kernel
     (("e4m3", "e4m3"), 4100, 2049, 160),      # FP8 kernel, larger ragged shape
+    (("e5m2", "e4m3"), 40, 300, 480),         # skinny FP8 kernel
+    (("mxfp4", "mxfp4"), 40, 300, 480),       # skinny MXFP4 kernel
 ])
 def test_alpha_beta_epilogue(fmts, M, N, K, out):
     """D = alpha A B + beta C through scaled_gemm_ex, C in the output type;

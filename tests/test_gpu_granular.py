@@ -96,7 +96,7 @@ COMBOS = [("row", "row"), ("row", "tensor"), ("tensor", "row"), ("tensor", "tens
 
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("ga,gb", COMBOS)
-@pytest.mark.parametrize("M,N,K", [(100, 72, 96), (256, 256, 64), (300, 260, 320), (1, 1, 32),
+@pytest.mark.parametrize("M,N,K", [(100, 72, 96), (256, 256, 64), (300, 260, 320), (1, 1, 32), (48, 300, 640),
                                    (513, 200, 1056)])
 def test_granular_gemm_parity(ga, gb, M, N, K, out):
     say(f"scaled_gemm_granular {ga}x{gb} M={M} N={N} K={K} -> {out}")
