@@ -88,6 +88,8 @@ def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False):
         return "gemm_fp8_kernel (A quantised by quantiser waves)"
     if w.a_fmt != "mxfp4" and gran != "tile":
         return "gemm_fp8_outer_kernel"
+    if w.M <= 64:
+        return "gemm_mxfp4_skinny_kernel" if w.a_fmt == "mxfp4" else "gemm_fp8_skinny_kernel"
     if w.a_fmt == "mxfp4":
         big_tiles = ((w.M + 255) // 256) * ((w.N + 255) // 256)
         fits32 = w.M * (w.K // 2) < 2**31 and w.N * (w.K // 2) < 2**31
@@ -95,6 +97,18 @@ def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False):
             return "gemm_mxfp4_big_kernel"
         return "gemm_mxfp4_kernel"
     return "gemm_fp8_kernel"
+
+
+def gemm_bytes(w, gran="tile", mx_block=32, mx_scale="e8m0", mx=False):
+    """Algorithmic HBM bytes of one GEMM launch: the codes of A and B, their
+    scales, and D (each read or written once)."""
+    out_b = 4 if w.out == "f32" else 2
+    if mx:
+        sbytes = 1 if mx_scale == "e8m0" else 2
+        return (w.M + w.N) * (w.K // 2 + (w.K // mx_block) * sbytes) + w.M * w.N * out_b
+    nsc = {"tile": lambda r: ((r + 127) // 128) * (w.K // 32), "row": lambda r: r,
+           "tensor": lambda r: 1}[gran]
+    return (w.M + w.N) * w.K + (nsc(w.M) + nsc(w.N)) * 4 + w.M * w.N * out_b
 
 
 def cpu_baseline(w, a, b, d_gpu, sample_rows, gran="tile", mx_block=32, mx_scale="e8m0"):
@@ -347,6 +361,21 @@ def main():
         nscales = {"tile": ((rows + 127) // 128) * (w.K // 32), "row": rows, "tensor": 1}[gran]
         return rows * w.K * 4 + rows * w.K + nscales * 4
 
+    # The GEMM's bound: HBM when its arithmetic intensity (FLOP per algorithmic
+    # byte: codes of A and B, their scales, D) is below the ridge point
+    # peak FLOP/s / peak bytes/s, the matrix cores otherwise.
+    gbytes = gemm_bytes(w, gran, args.mx_block, args.mx_scale, mx)
+    if w.flops / gbytes < PEAK_TFLOPS[in_type] * 1e12 / (HBM_GBPS * 1e9):
+        gemm_gbps = gbytes / (gemm_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": gemm_kernel_name(w, gran, online, mxv),
+                    "achieved": round(gemm_gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
+                    "frac": round(gemm_gbps / HBM_GBPS, 4), "algorithmic_bytes": gbytes}
+    else:
+        roofline = {"bound": "mfma", "kernel": gemm_kernel_name(w, gran, online, mxv),
+                    "achieved": round(gemm_tflops, 1), "peak": PEAK_TFLOPS[in_type], "unit": "TFLOP/s",
+                    "frac": round(gemm_tflops / PEAK_TFLOPS[in_type], 4)}
+    roofline.update({"traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": traffic_src})
+
     kernels = {
         "scaled_gemm_ms": round(gemm_ms, 4),
         "scaled_gemm_tflops": round(gemm_tflops, 1),
@@ -387,17 +416,7 @@ def main():
                             if gran != "tile" else
                             "fp8_quantize_transposed(G)+fp8_quantize_transposed(X)+scaled_gemm"
                             if token_major else "fp8_quantize(A)+fp8_quantize(B)+scaled_gemm")},
-        "roofline": {
-            "bound": "mfma",
-            "kernel": gemm_kernel_name(w, gran, online, mxv),
-            "achieved": round(gemm_tflops, 1),
-            "peak": PEAK_TFLOPS[in_type],
-            "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / PEAK_TFLOPS[in_type], 4),
-            "traffic": traffic,
-            "traffic_unit": "bytes per launch",
-            "traffic_source": traffic_src,
-        },
+        "roofline": roofline,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

@@ -138,8 +138,8 @@ def test_degenerate_shapes():
 
 
 def _points(M, N, rng, n=3000):
-    ii = np.concatenate([np.arange(128), rng.integers(0, M, n), [M - 1] * 4])
-    jj = np.concatenate([rng.integers(0, N, 128), rng.integers(0, N, n), [0, 1, N - 2, N - 1]])
+    ii = np.concatenate([np.arange(min(128, M)), rng.integers(0, M, n), [M - 1] * 4])
+    jj = np.concatenate([rng.integers(0, N, min(128, M)), rng.integers(0, N, n), [0, 1, N - 2, N - 1]])
     return ii.astype(np.int64), jj.astype(np.int64)
 
 

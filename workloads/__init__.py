@@ -16,8 +16,11 @@ CDNA4 compares precisions at, section 5.4, and the size of the MXFP4 host
 example in the Rubin FP4 GEMM article, section 4.4), a Transformer
 feed-forward shape (the motivation in section 1.1 of the CDNA4 article), a
 weight-gradient shape with E5M2 gradients (section 2.2 of the same article
-assigns E5M2 to gradients), and an MXFP4 square case.  They are synthetic
-stand-ins; no dataset or trained weights are involved.
+assigns E5M2 to gradients), and an MXFP4 square case.  Two more are
+decode-shaped (16 tokens against an 8192 x 8192 weight, FP8 and MXFP4): their
+GEMM streams the weight once and is bound by HBM bandwidth, not by the matrix
+cores.  They are synthetic stand-ins; no dataset or trained weights are
+involved.
 """
 from __future__ import annotations
 
@@ -77,6 +80,12 @@ WORKLOADS = [
     Workload(5, "mxfp4_8192", 8192, 8192, 8192, "mxfp4", "mxfp4", "bf16",
              ("normal", 1.0), ("normal", 1.0),
              "A, B ~N(0,1); E2M1 in 32-wide K blocks with E8M0 scales; bf16 output"),
+    Workload(6, "skinny_e4m3_16x8192x8192", 16, 8192, 8192, "e4m3", "e4m3", "bf16",
+             ("normal", 1.0), ("normal", 0.02),
+             "16 tokens ~N(0,1) against weights ~N(0,0.02); 128x32 tiles; bf16 output; HBM-bound"),
+    Workload(7, "skinny_mxfp4_16x8192x8192", 16, 8192, 8192, "mxfp4", "mxfp4", "bf16",
+             ("normal", 1.0), ("normal", 0.02),
+             "16 tokens ~N(0,1) against weights ~N(0,0.02); E2M1 with E8M0 scales; bf16 output; HBM-bound"),
 ]
 
 
