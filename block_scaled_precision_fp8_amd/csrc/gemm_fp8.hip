@@ -593,14 +593,19 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
 // range read as zero and their sigma is zero.  The four partial sums are
 // added in a fixed order through LDS, so the result does not depend on
 // timing; wave 0 writes the tile.
+// OUTER: scales constant along K (per row of A or per tensor, per column of B
+// or per tensor; a_step / b_step are 1 or 0): the blocks are summed unscaled
+// and the scale product multiplies the sum once, at write-back, as in the
+// K-constant kernel.
 constexpr int kSkinnyDepth = 8;              // blocks in flight per wave
 constexpr int64_t kSkinnyMaxM = 64;          // rows up to which the skinny form is used
 
-template <int AF, int BF, int OUT>
+template <int AF, int BF, int OUT, bool OUTER>
 __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_skinny_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
     const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D,
-    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok, int tensor_mask) {
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok, int tensor_mask, int a_step,
+    int b_step) {
     __shared__ v16f part[3][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -632,6 +637,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_skinny_kernel(
     const float* sb_row = sB + (b_tensor ? 0 : static_cast<int64_t>(n0 >> 7) * nkb);
     auto sigma = [&](int kb) {
         if (kb >= kb1) return 0.0f;
+        if constexpr (OUTER) return 1.0f;
         return (a_tensor ? sa_row[0] : sa_row[kb]) * (b_tensor ? sb_row[0] : sb_row[kb]);
     };
     // slot j: the fragments and sigma of one block, fetched kSkinnyDepth blocks ahead
@@ -669,11 +675,42 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_skinny_kernel(
         for (int e = 0; e < 16; ++e) acc[e] += q[e];
     }
     // lane (r, h) holds row m0 + r, columns n0 + 8 q + 4 h + e in acc[4 q + e]
+    float s_m = 1.0f;
+    if constexpr (OUTER) s_m = sA[static_cast<int64_t>(min(m0 + r, M - 1)) * a_step];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const float a4[4] = {acc[4 * q + 0], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        float a4[4] = {acc[4 * q + 0], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        if constexpr (OUTER) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = min(n0 + 8 * q + 4 * h + e, N - 1);
+                a4[e] = (s_m * sB[static_cast<int64_t>(n) * b_step]) * a4[e];
+            }
+        }
         finish_row_chunk<OUT, 4>(D, ldd, ep, m0 + r, n0 + 8 * q + 4 * h, M, N, vec_ok, a4);
     }
+}
+
+// The skinny form for scales constant along K (called by the K-constant GEMM's
+// launcher for up to kSkinnyMaxM rows).
+template <int AF, int BF>
+hipError_t launch_skinny_outer_typed(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
+                                     int a_step, const uint8_t* b, const float* sb, int b_step, int out,
+                                     void* d, int64_t ldd, const Epilogue& ep, hipStream_t stream) {
+    const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
+    const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
+    const int vec = vec16_ok(out, d, ldd, ep);
+    const int Mi = static_cast<int>(M), Ni = static_cast<int>(N), Ki = static_cast<int>(K);
+    if (out == BSFP8_OUT_F32)
+        hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, BSFP8_OUT_F32, true>), dim3(wgs), dim3(kThreads), 0,
+                           stream, Mi, Ni, Ki, a, sa, b, sb, d, ldd, ep, tm, tn, vec, 0, a_step, b_step);
+    else if (out == BSFP8_OUT_BF16)
+        hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, BSFP8_OUT_BF16, true>), dim3(wgs), dim3(kThreads), 0,
+                           stream, Mi, Ni, Ki, a, sa, b, sb, d, ldd, ep, tm, tn, vec, 0, a_step, b_step);
+    else
+        hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, BSFP8_OUT_F16, true>), dim3(wgs), dim3(kThreads), 0,
+                           stream, Mi, Ni, Ki, a, sa, b, sb, d, ldd, ep, tm, tn, vec, 0, a_step, b_step);
+    return hipGetLastError();
 }
 
 template <int AF, int BF, int OUT, bool QA>
@@ -684,9 +721,9 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const f
         if (M <= kSkinnyMaxM) {
             const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
             const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
-            hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, OUT>), dim3(wgs), dim3(kThreads), 0,
+            hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, OUT, false>), dim3(wgs), dim3(kThreads), 0,
                                stream, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, sa,
-                               b, sb, d, ldd, ep, tm, tn, vec16_ok(OUT, d, ldd, ep), tensor_mask);
+                               b, sb, d, ldd, ep, tm, tn, vec16_ok(OUT, d, ldd, ep), tensor_mask, 0, 0);
             return hipGetLastError();
         }
     }
@@ -733,6 +770,21 @@ hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, int a_fmt, const uin
     const OnlineA none{nullptr, 0, nullptr, nullptr};
     return launch_formats<false>(M, N, K, a_fmt, a, a_scales, b_fmt, b, b_scales, out, d, ldd, ep,
                                  tensor_mask, none, stream);
+}
+
+bool skinny_outer_fits(int64_t M) { return M <= kSkinnyMaxM; }
+
+hipError_t launch_gemm_fp8_skinny_outer(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,
+                                        const float* a_scales, int a_step, int b_fmt, const uint8_t* b,
+                                        const float* b_scales, int b_step, int out, void* d, int64_t ldd,
+                                        const Epilogue& ep, hipStream_t stream) {
+    if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E4M3)
+        return launch_skinny_outer_typed<BSFP8_E4M3, BSFP8_E4M3>(M, N, K, a, a_scales, a_step, b, b_scales, b_step, out, d, ldd, ep, stream);
+    if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E5M2)
+        return launch_skinny_outer_typed<BSFP8_E4M3, BSFP8_E5M2>(M, N, K, a, a_scales, a_step, b, b_scales, b_step, out, d, ldd, ep, stream);
+    if (a_fmt == BSFP8_E5M2 && b_fmt == BSFP8_E4M3)
+        return launch_skinny_outer_typed<BSFP8_E5M2, BSFP8_E4M3>(M, N, K, a, a_scales, a_step, b, b_scales, b_step, out, d, ldd, ep, stream);
+    return launch_skinny_outer_typed<BSFP8_E5M2, BSFP8_E5M2>(M, N, K, a, a_scales, a_step, b, b_scales, b_step, out, d, ldd, ep, stream);
 }
 
 hipError_t launch_gemm_fp8_online_a(int64_t M, int64_t N, int64_t K, int a_fmt, const OnlineA& qa,

@@ -324,6 +324,10 @@ hipError_t launch_gemm_fp8_outer(int64_t M, int64_t N, int64_t K, int a_fmt, con
                                  const float* a_scales, int a_step, int b_fmt, const uint8_t* b,
                                  const float* b_scales, int b_step, int out, void* d, int64_t ldd,
                                  const Epilogue& ep, hipStream_t stream) {
+    // few rows: the skinny per-tile kernel streams B with far more workgroups
+    if (skinny_outer_fits(M))
+        return launch_gemm_fp8_skinny_outer(M, N, K, a_fmt, a, a_scales, a_step, b_fmt, b, b_scales, b_step,
+                                            out, d, ldd, ep, stream);
     if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E4M3)
         return launch_typed<BSFP8_E4M3, BSFP8_E4M3>(M, N, K, a, a_scales, a_step, b, b_scales, b_step, out, d, ldd, ep, stream);
     if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E5M2)

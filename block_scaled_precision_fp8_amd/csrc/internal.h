@@ -41,6 +41,12 @@ hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, int a_fmt, const uin
                            const Epilogue& ep, hipStream_t stream, int tensor_mask = 0);
 // FP8 operands whose scales are constant along K: a_scales[m * a_step] and
 // b_scales[n * b_step] (step 1 for per-row scales, 0 for one per tensor).
+// The skinny per-tile GEMM in its K-constant-scales form (up to 64 rows).
+bool skinny_outer_fits(int64_t M);
+hipError_t launch_gemm_fp8_skinny_outer(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,
+                                        const float* a_scales, int a_step, int b_fmt, const uint8_t* b,
+                                        const float* b_scales, int b_step, int out, void* d, int64_t ldd,
+                                        const Epilogue& ep, hipStream_t stream);
 hipError_t launch_gemm_fp8_outer(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,
                                  const float* a_scales, int a_step, int b_fmt, const uint8_t* b,
                                  const float* b_scales, int b_step, int out, void* d, int64_t ldd,

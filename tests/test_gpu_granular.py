@@ -97,6 +97,7 @@ COMBOS = [("row", "row"), ("row", "tensor"), ("tensor", "row"), ("tensor", "tens
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("ga,gb", COMBOS)
 @pytest.mark.parametrize("M,N,K", [(100, 72, 96), (256, 256, 64), (300, 260, 320), (1, 1, 32), (48, 300, 640),
+                                   (16, 2050, 4128),
                                    (513, 200, 1056)])
 def test_granular_gemm_parity(ga, gb, M, N, K, out):
     say(f"scaled_gemm_granular {ga}x{gb} M={M} N={N} K={K} -> {out}")
@@ -126,9 +127,9 @@ def test_granular_gemm_formats(fmts):
 
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("ga,gb", [("row", "row"), ("tile", "tensor")])
-def test_granular_alpha_beta(ga, gb, out):
+@pytest.mark.parametrize("M,N,K", [(270, 300, 192), (40, 300, 640)])   # the second: skinny kernel
+def test_granular_alpha_beta(ga, gb, out, M, N, K):
     import torch
-    M, N, K = 270, 300, 192
     a = inputs(21, M, K)
     b = inputs(22, N, K)
     qa, sa = oracle.fp8_quantize_granular(a, "e4m3", ga)
