@@ -88,7 +88,7 @@ def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False):
         return "gemm_fp8_kernel (A quantised by quantiser waves)"
     if w.a_fmt != "mxfp4" and gran != "tile":
         return "gemm_fp8_outer_kernel"
-    if w.M <= 64:
+    if w.M <= 64 or ((w.M + 127) // 128) * ((w.N + 127) // 128) < 32:
         return "gemm_mxfp4_skinny_kernel" if w.a_fmt == "mxfp4" else "gemm_fp8_skinny_kernel"
     if w.a_fmt == "mxfp4":
         big_tiles = ((w.M + 255) // 256) * ((w.N + 255) // 256)

@@ -599,6 +599,7 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
 // K-constant kernel.
 constexpr int kSkinnyDepth = 8;              // blocks in flight per wave
 constexpr int64_t kSkinnyMaxM = 64;          // rows up to which the skinny form is used
+constexpr int64_t kSkinnyMaxTiles = 32;      // ... and 128 x 128 tiles below which it is too
 
 template <int AF, int BF, int OUT, bool OUTER>
 __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_skinny_kernel(
@@ -718,7 +719,7 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const f
                       const uint8_t* b, const float* sb, void* d, int64_t ldd,
                       const Epilogue& ep, int tensor_mask, const OnlineA& qa, hipStream_t stream) {
     if constexpr (!QA) {
-        if (M <= kSkinnyMaxM) {
+        if (M <= kSkinnyMaxM || ((M + 127) / 128) * ((N + 127) / 128) < kSkinnyMaxTiles) {
             const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
             const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
             hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, OUT, false>), dim3(wgs), dim3(kThreads), 0,

@@ -440,6 +440,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
 // zero codes with a zero scale byte (2^-127), which contribute nothing.
 constexpr int kSkinnyDepth = 8;
 constexpr int64_t kSkinnyMaxM = 64;
+constexpr int64_t kSkinnyMaxTiles = 32;      // 128 x 128 tiles below which the skinny form is used too
 
 template <int OUT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_skinny_kernel(
@@ -520,7 +521,7 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const u
                       const uint8_t* b, const uint8_t* b_scales, void* d, int64_t ldd,
                       const Epilogue& ep, hipStream_t stream) {
     const int vec = vec16_ok(OUT, d, ldd, ep);
-    if (M <= kSkinnyMaxM) {
+    if (M <= kSkinnyMaxM || ((M + 127) / 128) * ((N + 127) / 128) < kSkinnyMaxTiles) {
         const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
         const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
         hipLaunchKernelGGL(gemm_mxfp4_skinny_kernel<OUT>, dim3(wgs), dim3(kThreads), 0, stream,
