@@ -82,13 +82,14 @@ def committed_traffic(workload, source_file):
 def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False):
     """The kernel scaled_gemm dispatches for this workload (mirrors the
     launchers' selection)."""
+    skinny = w.M <= 64 or ((w.M + 127) // 128) * ((w.N + 127) // 128) < 32
     if mx_variant:
-        return "gemm_mx_kernel"
+        return "gemm_mx_skinny_kernel" if skinny else "gemm_mx_kernel"
     if online:
         return "gemm_fp8_kernel (A quantised by quantiser waves)"
     if w.a_fmt != "mxfp4" and gran != "tile":
         return "gemm_fp8_outer_kernel"
-    if w.M <= 64 or ((w.M + 127) // 128) * ((w.N + 127) // 128) < 32:
+    if skinny:
         return "gemm_mxfp4_skinny_kernel" if w.a_fmt == "mxfp4" else "gemm_fp8_skinny_kernel"
     if w.a_fmt == "mxfp4":
         big_tiles = ((w.M + 255) // 256) * ((w.N + 255) // 256)

@@ -786,10 +786,151 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_split_big_kernel(
     big_tile::epilogue<OUT, STAGE16>(acc, lds, wave, lane, m0, n0, M, N, D, ldd, ep, vec_ok, pre);
 }
 
+template <int... I, typename F>
+__device__ __forceinline__ void static_for_mx_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for_mx(F&& f) {
+    static_for_mx_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Skinny form (up to 64 rows, or fewer than 32 tiles of 128 x 128): one
+// workgroup per 32 x 32 output tile whose four waves split the 32-K blocks into
+// contiguous ranges, as the skinny FP8 and MXFP4 kernels do.  No LDS staging:
+// lane (r, h) loads the 8 packed bytes of K 16 h .. 16 h + 15 of block kb of
+// row r (and their one or two block scales), dequantises them in registers and
+// feeds two bf16 MFMAs (K 16 h .. + 7 in the first, the rest in the second).
+// Every lane of A and of B uses this same assignment of K to MFMA slots, so
+// each dot product is unchanged.  Wide scales use the hi / lo split (three
+// products, four for FP32 output).  Blocks past the wave's range read as zero.
+constexpr int kMxSkinnyDepth = 8;
+constexpr int64_t kMxSkinnyMaxM = 64;
+constexpr int64_t kMxSkinnyMaxTiles = 32;
+
+template <int BLOCK, int SFMT, int OUT>
+__global__ __launch_bounds__(kThreads, 2) void gemm_mx_skinny_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
+    constexpr bool SPLIT = SFMT != BSFP8_MX_E8M0;
+    constexpr int SB = SPLIT ? 2 : 1;                     // bytes per scale
+    constexpr int NS = BLOCK == 8 ? 2 : 1;                // scales per lane per block
+    __shared__ v16f part[3][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // the row tiles of a column tile are launched 8 apart (the same XCD)
+    const int grp = static_cast<int>(blockIdx.x) / (8 * tiles_m);
+    const int rem = static_cast<int>(blockIdx.x) - grp * 8 * tiles_m;
+    const int tm = rem >> 3, tn = grp * 8 + (rem & 7);
+    if (tn >= tiles_n) return;
+    const int m0 = tm * 32, n0 = tn * 32;
+    const int kh = K >> 1, nkb = K >> 5, nsc = K / BLOCK;
+    const int per = (nkb + 3) >> 2;
+    const int kb0 = min(wave * per, nkb), kb1 = min(kb0 + per, nkb);
+
+    const int rows_a = min(32, M - m0), rows_b = min(32, N - n0);
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(A) + static_cast<int64_t>(m0) * kh, 0, rows_a * kh, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(B) + static_cast<int64_t>(n0) * kh, 0, rows_b * kh, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sA) + static_cast<int64_t>(m0) * nsc * SB, 0, rows_a * nsc * SB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sB) + static_cast<int64_t>(n0) * nsc * SB, 0, rows_b * nsc * SB, 0x00020000);
+    const int r = lane & 31, h = lane >> 5;
+    constexpr uint32_t kOut = 0x80000000u;
+    // the scale index of this lane's first value of block kb
+    auto sidx = [&](int kb) { return (32 * kb + 16 * h) / BLOCK; };
+    uint2 ca[kMxSkinnyDepth], cb[kMxSkinnyDepth];
+    uint32_t va[kMxSkinnyDepth], vb[kMxSkinnyDepth];   // NS scales of SB bytes
+    auto fetch = [&](auto SLOT, int kb) {
+        constexpr int j = SLOT;
+        const bool ok = kb < kb1;
+        const uint32_t oc = ok ? static_cast<uint32_t>(r * kh + 16 * kb + 8 * h) : kOut;
+        const uint32_t os = ok ? static_cast<uint32_t>((r * nsc + sidx(kb)) * SB) : kOut;
+        const auto wa = __builtin_amdgcn_raw_buffer_load_b64(rs_a, static_cast<int>(oc), 0, 0);
+        const auto wb = __builtin_amdgcn_raw_buffer_load_b64(rs_b, static_cast<int>(oc), 0, 0);
+        ca[j] = make_uint2(wa[0], wa[1]);
+        cb[j] = make_uint2(wb[0], wb[1]);
+        if constexpr (NS * SB == 1) {
+            va[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_sa, static_cast<int>(os), 0, 0);
+            vb[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_sb, static_cast<int>(os), 0, 0);
+        } else if constexpr (NS * SB == 2) {
+            va[j] = __builtin_amdgcn_raw_buffer_load_b16(rs_sa, static_cast<int>(os), 0, 0);
+            vb[j] = __builtin_amdgcn_raw_buffer_load_b16(rs_sb, static_cast<int>(os), 0, 0);
+        } else {
+            va[j] = __builtin_amdgcn_raw_buffer_load_b32(rs_sa, static_cast<int>(os), 0, 0);
+            vb[j] = __builtin_amdgcn_raw_buffer_load_b32(rs_sb, static_cast<int>(os), 0, 0);
+        }
+    };
+    // 16 codes (two words, K order) with their scale(s) -> bf16 hi (and lo),
+    // 8 values per MFMA step
+    auto dequant = [&](const uint2& w, uint32_t v, v8bf (&hi)[2], v8bf (&lo)[2]) {
+        constexpr uint32_t mask = SB == 1 ? 0xFFu : 0xFFFFu;
+        const float s0 = scale_value<SFMT>(v & mask);
+        const float s1 = NS == 2 ? scale_value<SFMT>((v >> (8 * SB)) & mask) : s0;
+        dequant_pair<0, SPLIT>(w.x, s0, hi[0], lo[0]);
+        dequant_pair<1, SPLIT>(w.x, s0, hi[0], lo[0]);
+        dequant_pair<2, SPLIT>(w.x, s0, hi[0], lo[0]);
+        dequant_pair<3, SPLIT>(w.x, s0, hi[0], lo[0]);
+        dequant_pair<0, SPLIT>(w.y, s1, hi[1], lo[1]);
+        dequant_pair<1, SPLIT>(w.y, s1, hi[1], lo[1]);
+        dequant_pair<2, SPLIT>(w.y, s1, hi[1], lo[1]);
+        dequant_pair<3, SPLIT>(w.y, s1, hi[1], lo[1]);
+    };
+    v16f acc = v16f{};
+    static_for_mx<kMxSkinnyDepth>([&](auto J) { fetch(J, kb0 + J); });
+    for (int kb = kb0; kb < kb1; kb += kMxSkinnyDepth) {
+        static_for_mx<kMxSkinnyDepth>([&](auto J) {
+            constexpr int j = J;
+            v8bf ah[2], al[2], bh[2], bl[2];
+            dequant(ca[j], va[j], ah, al);
+            dequant(cb[j], vb[j], bh, bl);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                // B rows are the MFMA row operand, A rows the column operand
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[q], ah[q], acc, 0, 0, 0);
+                if constexpr (SPLIT) {
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[q], al[q], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[q], ah[q], acc, 0, 0, 0);
+                    if constexpr (OUT == BSFP8_OUT_F32)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[q], al[q], acc, 0, 0, 0);
+                }
+            }
+            fetch(J, kb + j + kMxSkinnyDepth);
+        });
+    }
+    if (wave > 0) part[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        const v16f q = part[w][lane];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] += q[e];
+    }
+    // lane (r, h) holds row m0 + r, columns n0 + 8 q + 4 h + e in acc[4 q + e]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float a4[4] = {acc[4 * q + 0], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        finish_row_chunk<OUT, 4>(D, ldd, ep, m0 + r, n0 + 8 * q + 4 * h, M, N, vec_ok, a4);
+    }
+}
+
 template <int BLOCK, int SFMT, int OUT>
 hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const void* sa,
                       const uint8_t* b, const void* sb, void* d, int64_t ldd, const Epilogue& ep,
                       hipStream_t stream) {
+    if (M <= kMxSkinnyMaxM || ((M + 127) / 128) * ((N + 127) / 128) < kMxSkinnyMaxTiles) {
+        const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
+        const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
+        hipLaunchKernelGGL((gemm_mx_skinny_kernel<BLOCK, SFMT, OUT>), dim3(wgs), dim3(kThreads), 0, stream,
+                           static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
+                           static_cast<const uint8_t*>(sa), b, static_cast<const uint8_t*>(sb), d, ldd, ep,
+                           tm, tn, vec16_ok(OUT, d, ldd, ep));
+        return hipGetLastError();
+    }
     if constexpr (SFMT != BSFP8_MX_E8M0) {
         // the large tile wherever it still gives the chip enough workgroups
         const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);

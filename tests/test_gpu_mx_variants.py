@@ -8,9 +8,9 @@ elements, section 5.3; FP16 or BF16 block scales, section 3.2) on the GPU.
 * scaled_gemm_mx: D against the oracle's fp64 product of the dequantised
   operands, max |D - D_ref| / S within the output type's tolerance, for every
   block size and scale format, FP32 / bf16 / FP16 output, alpha / beta and
-  ragged M, N, K, on the 128 x 128 kernel and both 256 x 256 kernels (E8M0;
-  FP16 / BF16 scales); and the 8192^3 shape of the MXFP4 workload on sampled
-  outputs.
+  ragged M, N, K, on the skinny kernel (up to 64 rows or few tiles), the
+  128 x 128 kernel and both 256 x 256 kernels (E8M0; FP16 / BF16 scales);
+  and the 8192^3 shape of the MXFP4 workload on sampled outputs.
 """
 import numpy as np
 import pytest
@@ -112,8 +112,10 @@ def run_gemm(qa, sa, qb, sb, block, scale, out, K, alpha=1.0, c=None, beta=0.0):
 @pytest.mark.parametrize("scale", SCALES)
 @pytest.mark.parametrize("block", [16, 8, 32])
 @pytest.mark.parametrize("M,N,K", [(100, 72, 96), (256, 256, 128), (300, 260, 320), (1, 1, 32),
-                                   (513, 200, 1056)])
+                                   (513, 200, 1056), (1000, 600, 96), (700, 1030, 320)])
 def test_mx_gemm_parity(M, N, K, block, scale, out):
+    """Shapes with fewer than 32 tiles of 128 x 128 take the skinny kernel, the
+    last two (40 and 54 tiles, M > 64) the 128 x 128 kernel."""
     say(f"scaled_gemm_mx block={block} {scale} M={M} N={N} K={K} -> {out}")
     a = inputs(M + 3, M, K, "normal")
     b = inputs(N + 4, N, K, "laplace")
@@ -138,6 +140,47 @@ def test_mx_gemm_alpha_beta(block, scale):
     d = run_gemm(qa, sa, qb, sb, block, scale, "f32", K, -0.5, torch.from_numpy(c32).cuda(), 2.0)
     dr, sr = oracle.gemm_mx(qa, sa, qb, sb, block, scale)
     check_gemm_ex(d, dr, sr, -0.5, 2.0, c32.astype(np.float64), "f32", f"mx alpha/beta {block} {scale}")
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("block,scale", [(16, "e8m0"), (8, "e8m0"), (32, "f16"), (16, "bf16"),
+                                         (8, "f16"), (8, "bf16")])
+@pytest.mark.parametrize("M,N,K", [(16, 1000, 4096), (1, 520, 416), (33, 300, 32), (64, 2100, 1568),
+                                   (50, 64, 8192)])
+def test_mx_gemm_skinny_parity(M, N, K, block, scale, out):
+    """Up to 64 rows: the skinny kernel, whose four waves split the 32-K blocks
+    (K = 32: three waves idle; K = 416: ranges of 4, 4, 4 and 1 blocks; long K:
+    several rounds of its 8-deep prefetch), ragged M and N."""
+    say(f"scaled_gemm_mx skinny block={block} {scale} M={M} N={N} K={K} -> {out}")
+    a = inputs(M + K + 5, M, K, "normal")
+    b = inputs(N + K + 6, N, K, "laplace")
+    qa, sa = oracle.mx_quantize(a, block, scale)
+    qb, sb = oracle.mx_quantize(b, block, scale)
+    d = run_gemm(qa, sa, qb, sb, block, scale, out, K)
+    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, block, scale)
+    check_gemm(d, dr, sr, out, f"mx skinny {block} {scale} {M}x{N}x{K} {out}")
+
+
+@pytest.mark.parametrize("block,scale", [(16, "e8m0"), (8, "bf16")])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_mx_gemm_skinny_alpha_beta(block, scale, out):
+    import torch
+    M, N, K = 40, 700, 640
+    a = inputs(91, M, K)
+    b = inputs(92, N, K)
+    qa, sa = oracle.mx_quantize(a, block, scale)
+    qb, sb = oracle.mx_quantize(b, block, scale)
+    c32 = np.random.default_rng(93).standard_normal((M, N)).astype(np.float32) * 20
+    if out == "bf16":
+        c = torch.from_numpy(c32).to(torch.bfloat16)
+        cref = c.float().numpy().astype(np.float64)
+    else:
+        c = torch.from_numpy(c32)
+        cref = c32.astype(np.float64)
+    say(f"scaled_gemm_mx skinny alpha/beta block={block} {scale} -> {out}")
+    d = run_gemm(qa, sa, qb, sb, block, scale, out, K, 1.25, c.cuda(), 0.5)
+    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, block, scale)
+    check_gemm_ex(d, dr, sr, 1.25, 0.5, cref, out, f"mx skinny alpha/beta {block} {scale} {out}")
 
 
 LARGE = [(16, "e8m0"), (8, "e8m0"), (32, "f16"), (16, "f16"), (8, "f16"),
