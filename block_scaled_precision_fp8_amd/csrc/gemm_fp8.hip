@@ -598,16 +598,17 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
 // and the scale product multiplies the sum once, at write-back, as in the
 // K-constant kernel.
 constexpr int kSkinnyDepth = 8;              // blocks in flight per wave
+constexpr int kSkinnyWaves = 4;              // waves per workgroup, splitting K
 constexpr int64_t kSkinnyMaxM = 64;          // rows up to which the skinny form is used
 constexpr int64_t kSkinnyMaxTiles = 32;      // ... and 128 x 128 tiles below which it is too
 
 template <int AF, int BF, int OUT, bool OUTER>
-__global__ __launch_bounds__(kThreads, 2) void gemm_fp8_skinny_kernel(
+__global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_fp8_skinny_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
     const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D,
     int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok, int tensor_mask, int a_step,
     int b_step) {
-    __shared__ v16f part[3][64];
+    __shared__ v16f part[kSkinnyWaves - 1][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Workgroups go to the 8 XCDs round-robin by launch index.  The row tiles
@@ -620,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_skinny_kernel(
     if (tn >= tiles_n) return;
     const int m0 = tm * 32, n0 = tn * 32;
     const int nkb = K >> 5;
-    const int per = (nkb + 3) >> 2;
+    const int per = (nkb + kSkinnyWaves - 1) / kSkinnyWaves;
     const int kb0 = min(wave * per, nkb), kb1 = min(kb0 + per, nkb);
 
     // operand rows of this tile (the resources start at its first row, so
@@ -668,9 +669,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_fp8_skinny_kernel(
     if (wave > 0) part[wave - 1][lane] = acc;
     __syncthreads();
     if (wave != 0) return;
-    // the partial sums of waves 1, 2, 3, added in that order
+    // the partial sums of waves 1, 2, ..., added in that order
 #pragma unroll
-    for (int w = 0; w < 3; ++w) {
+    for (int w = 0; w < kSkinnyWaves - 1; ++w) {
         const v16f q = part[w][lane];
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] += q[e];
@@ -703,13 +704,13 @@ hipError_t launch_skinny_outer_typed(int64_t M, int64_t N, int64_t K, const uint
     const int vec = vec16_ok(out, d, ldd, ep);
     const int Mi = static_cast<int>(M), Ni = static_cast<int>(N), Ki = static_cast<int>(K);
     if (out == BSFP8_OUT_F32)
-        hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, BSFP8_OUT_F32, true>), dim3(wgs), dim3(kThreads), 0,
+        hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, BSFP8_OUT_F32, true>), dim3(wgs), dim3(64 * kSkinnyWaves), 0,
                            stream, Mi, Ni, Ki, a, sa, b, sb, d, ldd, ep, tm, tn, vec, 0, a_step, b_step);
     else if (out == BSFP8_OUT_BF16)
-        hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, BSFP8_OUT_BF16, true>), dim3(wgs), dim3(kThreads), 0,
+        hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, BSFP8_OUT_BF16, true>), dim3(wgs), dim3(64 * kSkinnyWaves), 0,
                            stream, Mi, Ni, Ki, a, sa, b, sb, d, ldd, ep, tm, tn, vec, 0, a_step, b_step);
     else
-        hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, BSFP8_OUT_F16, true>), dim3(wgs), dim3(kThreads), 0,
+        hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, BSFP8_OUT_F16, true>), dim3(wgs), dim3(64 * kSkinnyWaves), 0,
                            stream, Mi, Ni, Ki, a, sa, b, sb, d, ldd, ep, tm, tn, vec, 0, a_step, b_step);
     return hipGetLastError();
 }
@@ -722,7 +723,7 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const f
         if (M <= kSkinnyMaxM || ((M + 127) / 128) * ((N + 127) / 128) < kSkinnyMaxTiles) {
             const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
             const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
-            hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, OUT, false>), dim3(wgs), dim3(kThreads), 0,
+            hipLaunchKernelGGL((gemm_fp8_skinny_kernel<AF, BF, OUT, false>), dim3(wgs), dim3(64 * kSkinnyWaves), 0,
                                stream, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, sa,
                                b, sb, d, ldd, ep, tm, tn, vec16_ok(OUT, d, ldd, ep), tensor_mask, 0, 0);
             return hipGetLastError();

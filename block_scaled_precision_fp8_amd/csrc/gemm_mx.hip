@@ -804,19 +804,20 @@ __device__ __forceinline__ void static_for_mx(F&& f) {
 // Every lane of A and of B uses this same assignment of K to MFMA slots, so
 // each dot product is unchanged.  Wide scales use the hi / lo split (three
 // products, four for FP32 output).  Blocks past the wave's range read as zero.
-constexpr int kMxSkinnyDepth = 8;
+constexpr int kMxSkinnyDepth = 8;           // 32-K blocks in flight per wave
+constexpr int kMxSkinnyWaves = 4;           // waves per workgroup, splitting K
 constexpr int64_t kMxSkinnyMaxM = 64;
 constexpr int64_t kMxSkinnyMaxTiles = 32;
 
 template <int BLOCK, int SFMT, int OUT>
-__global__ __launch_bounds__(kThreads, 2) void gemm_mx_skinny_kernel(
+__global__ __launch_bounds__(64 * kMxSkinnyWaves, 8 / kMxSkinnyWaves) void gemm_mx_skinny_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
     int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
     constexpr bool SPLIT = SFMT != BSFP8_MX_E8M0;
     constexpr int SB = SPLIT ? 2 : 1;                     // bytes per scale
     constexpr int NS = BLOCK == 8 ? 2 : 1;                // scales per lane per block
-    __shared__ v16f part[3][64];
+    __shared__ v16f part[kMxSkinnyWaves - 1][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // the row tiles of a column tile are launched 8 apart (the same XCD)
@@ -826,7 +827,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mx_skinny_kernel(
     if (tn >= tiles_n) return;
     const int m0 = tm * 32, n0 = tn * 32;
     const int kh = K >> 1, nkb = K >> 5, nsc = K / BLOCK;
-    const int per = (nkb + 3) >> 2;
+    const int per = (nkb + kMxSkinnyWaves - 1) / kMxSkinnyWaves;
     const int kb0 = min(wave * per, nkb), kb1 = min(kb0 + per, nkb);
 
     const int rows_a = min(32, M - m0), rows_b = min(32, N - n0);
@@ -905,7 +906,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mx_skinny_kernel(
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
-    for (int w = 0; w < 3; ++w) {
+    for (int w = 0; w < kMxSkinnyWaves - 1; ++w) {
         const v16f q = part[w][lane];
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] += q[e];
@@ -925,7 +926,7 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const v
     if (M <= kMxSkinnyMaxM || ((M + 127) / 128) * ((N + 127) / 128) < kMxSkinnyMaxTiles) {
         const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
         const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
-        hipLaunchKernelGGL((gemm_mx_skinny_kernel<BLOCK, SFMT, OUT>), dim3(wgs), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL((gemm_mx_skinny_kernel<BLOCK, SFMT, OUT>), dim3(wgs), dim3(64 * kMxSkinnyWaves), 0, stream,
                            static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
                            static_cast<const uint8_t*>(sa), b, static_cast<const uint8_t*>(sb), d, ldd, ep,
                            tm, tn, vec16_ok(OUT, d, ldd, ep));

@@ -438,16 +438,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
 // E8M0 byte of block 2 t + h of row r), and the partial sums are added in a
 // fixed order through LDS.  Blocks past K or past the wave's range read as
 // zero codes with a zero scale byte (2^-127), which contribute nothing.
-constexpr int kSkinnyDepth = 8;
+constexpr int kSkinnyDepth = 8;              // 64-K steps in flight per wave
+constexpr int kSkinnyWaves = 4;              // waves per workgroup, splitting K
 constexpr int64_t kSkinnyMaxM = 64;
 constexpr int64_t kSkinnyMaxTiles = 32;      // 128 x 128 tiles below which the skinny form is used too
 
 template <int OUT>
-__global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_skinny_kernel(
+__global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_mxfp4_skinny_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
     int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
-    __shared__ v16f part[3][64];
+    __shared__ v16f part[kSkinnyWaves - 1][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Workgroups go to the 8 XCDs round-robin by launch index.  The row tiles
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_skinny_kernel(
     const int m0 = tm * 32, n0 = tn * 32;
     const int kbytes = K >> 1, nkb = K >> 5;
     const int nsteps = (nkb + 1) >> 1;          // 64-K steps; the last may hold one block
-    const int per = (nsteps + 3) >> 2;
+    const int per = (nsteps + kSkinnyWaves - 1) / kSkinnyWaves;
     const int t0 = min(wave * per, nsteps), t1 = min(t0 + per, nsteps);
 
     const int rows_a = min(32, M - m0), rows_b = min(32, N - n0);
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_skinny_kernel(
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
-    for (int w = 0; w < 3; ++w) {
+    for (int w = 0; w < kSkinnyWaves - 1; ++w) {
         const v16f q = part[w][lane];
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] += q[e];
@@ -524,7 +525,7 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const u
     if (M <= kSkinnyMaxM || ((M + 127) / 128) * ((N + 127) / 128) < kSkinnyMaxTiles) {
         const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
         const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
-        hipLaunchKernelGGL(gemm_mxfp4_skinny_kernel<OUT>, dim3(wgs), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL(gemm_mxfp4_skinny_kernel<OUT>, dim3(wgs), dim3(64 * kSkinnyWaves), 0, stream,
                            static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, a_scales, b,
                            b_scales, d, ldd, ep, tm, tn, vec);
         return hipGetLastError();

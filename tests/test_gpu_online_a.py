@@ -178,10 +178,12 @@ def test_online_a_without_code_output_and_degenerate_sizes():
 def test_online_a_matches_quantise_then_gemm_bitwise():
     """Consistency of the two HIP paths (not a parity check; the oracle tests
     above are): the same codes go through the same accumulation, so D is the
-    same bits as fp8_quantize followed by scaled_gemm."""
+    same bits as fp8_quantize followed by scaled_gemm.  The shape has 36 tiles
+    of 128 x 128, so scaled_gemm takes the 128 x 128 kernel as well (below 32
+    tiles it takes the skinny kernel, whose K split sums in another order)."""
     import torch
     b_ = bsfp8()
-    M, N, K = 384, 512, 1184
+    M, N, K = 768, 768, 1184
     x = to_dev(inputs(111, M, K, "tiles"))
     qb, sb = b_operand(112, N, K, "e4m3", kind="normal")
     qbd, sbd = to_dev(qb), to_dev(sb)
