@@ -583,21 +583,22 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
 
 // Skinny form (few output rows, so few 128 x 128 tiles: the two-pass kernel
 // would keep only a handful of CUs streaming B).  One workgroup per 32 x 32
-// output tile, N / 32 of them per 32 rows; its four waves split the K blocks
-// into four contiguous ranges and each computes the tile's partial sum over
-// its range with the same per-block product and promotion as the main kernel
-// (tile_product, acc = fma(sigma_kb, P_kb, acc)).  Fragments go from global
-// memory straight to registers in the MFMA layout (lane (r, h) loads the 16
-// codes K 16 h .. 16 h + 15 of row r of a block), kDepth blocks ahead, with
-// range-checked buffer loads: rows past M or N and blocks past the wave's
-// range read as zero and their sigma is zero.  The four partial sums are
+// output tile, N / 32 of them per 32 rows; its four waves split K into four
+// contiguous ranges of 4-block chunks and each computes the tile's partial sum
+// over its range with the same per-block product and promotion as the main
+// kernel (tile_product, acc = fma(sigma_kb, P_kb, acc)).  Each load
+// instruction reads whole 128-byte row segments (8 rows x 128 bytes), which
+// pass through the wave's own LDS area into the MFMA layout (lane (r, h) takes
+// the 16 codes K 16 h .. 16 h + 15 of row r of a block); kDepth chunks are in
+// flight.  Range-checked buffer loads: rows past M or N and blocks past the
+// wave's range read as zero and their sigma is zero.  The four partial sums are
 // added in a fixed order through LDS, so the result does not depend on
 // timing; wave 0 writes the tile.
 // OUTER: scales constant along K (per row of A or per tensor, per column of B
 // or per tensor; a_step / b_step are 1 or 0): the blocks are summed unscaled
 // and the scale product multiplies the sum once, at write-back, as in the
 // K-constant kernel.
-constexpr int kSkinnyDepth = 8;              // blocks in flight per wave
+constexpr int kSkinnyDepth = 2;              // chunks of 4 blocks in flight per wave
 constexpr int kSkinnyWaves = 4;              // waves per workgroup, splitting K
 constexpr int64_t kSkinnyMaxM = 64;          // rows up to which the skinny form is used
 constexpr int64_t kSkinnyMaxTiles = 32;      // ... and 128 x 128 tiles below which it is too
@@ -609,6 +610,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_fp8_
     int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok, int tensor_mask, int a_step,
     int b_step) {
     __shared__ v16f part[kSkinnyWaves - 1][64];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kSkinnyWaves][2][32 * 128];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Workgroups go to the 8 XCDs round-robin by launch index.  The row tiles
@@ -621,8 +623,12 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_fp8_
     if (tn >= tiles_n) return;
     const int m0 = tm * 32, n0 = tn * 32;
     const int nkb = K >> 5;
-    const int per = (nkb + kSkinnyWaves - 1) / kSkinnyWaves;
-    const int kb0 = min(wave * per, nkb), kb1 = min(kb0 + per, nkb);
+    // K is split into chunks of 4 blocks (128 bytes of each row); each wave
+    // takes a contiguous range of chunks
+    const int nch = (nkb + 3) >> 2;
+    const int cper = (nch + kSkinnyWaves - 1) / kSkinnyWaves;
+    const int c0 = min(wave * cper, nch), c1 = min(c0 + cper, nch);
+    const int kb1 = min(4 * c1, nkb);
 
     // operand rows of this tile (the resources start at its first row, so
     // offsets stay below 32 K)
@@ -632,7 +638,6 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_fp8_
     const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(B) + static_cast<int64_t>(n0) * K, 0, rows_b * K, 0x00020000);
     const int r = lane & 31, h = lane >> 5;
-    const uint32_t off0 = static_cast<uint32_t>(r * K + 16 * h);
     // sigma of block kb (zero past the wave's range)
     const bool a_tensor = (tensor_mask & 1) != 0, b_tensor = (tensor_mask & 2) != 0;
     const float* sa_row = sA + (a_tensor ? 0 : static_cast<int64_t>(m0 >> 7) * nkb);
@@ -642,28 +647,50 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_fp8_
         if constexpr (OUTER) return 1.0f;
         return (a_tensor ? sa_row[0] : sa_row[kb]) * (b_tensor ? sb_row[0] : sb_row[kb]);
     };
-    // slot j: the fragments and sigma of one block, fetched kSkinnyDepth blocks ahead
-    u32x4 xa[kSkinnyDepth], xb[kSkinnyDepth];
-    float sg[kSkinnyDepth];
-    auto fetch = [&](auto SLOT, int kb) {
+    // Loads read whole 128-byte row segments: lane l takes 16-byte piece l & 7
+    // of row (l >> 3) + 8 i, so each instruction covers 8 rows x 128 bytes.
+    // The wave stages the chunk in its own LDS area (piece g of row R at
+    // g ^ (R & 7)) and reads the MFMA fragments back: lane (r, h) takes bytes
+    // 32 b + 16 h .. + 15 of row r for block b of the chunk.
+    const int lr = lane >> 3, lg = lane & 7;
+    uint8_t* st_a = stage[wave][0];
+    uint8_t* st_b = stage[wave][1];
+    u32x4 ga[kSkinnyDepth][4], gb[kSkinnyDepth][4];
+    auto fetch = [&](auto SLOT, int c) {
         constexpr int j = SLOT;
-        const uint32_t o = kb < kb1 ? off0 + static_cast<uint32_t>(kb) * 32u : 0x80000000u;
-        const auto wa = __builtin_amdgcn_raw_buffer_load_b128(rs_a, static_cast<int>(o), 0, 0);
-        const auto wb = __builtin_amdgcn_raw_buffer_load_b128(rs_b, static_cast<int>(o), 0, 0);
-        xa[j] = u32x4{wa[0], wa[1], wa[2], wa[3]};
-        xb[j] = u32x4{wb[0], wb[1], wb[2], wb[3]};
-        sg[j] = sigma(kb);
+        const bool ok = c < c1 && 4 * c + (lg >> 1) < nkb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t o = ok ? static_cast<uint32_t>((lr + 8 * i) * K + 128 * c + 16 * lg) : 0x80000000u;
+            const auto wa = __builtin_amdgcn_raw_buffer_load_b128(rs_a, static_cast<int>(o), 0, 0);
+            const auto wb = __builtin_amdgcn_raw_buffer_load_b128(rs_b, static_cast<int>(o), 0, 0);
+            ga[j][i] = u32x4{wa[0], wa[1], wa[2], wa[3]};
+            gb[j][i] = u32x4{wb[0], wb[1], wb[2], wb[3]};
+        }
     };
     v16f acc = v16f{};
-    static_for<kSkinnyDepth>([&](auto J) { fetch(J, kb0 + J); });
-    for (int kb = kb0; kb < kb1; kb += kSkinnyDepth) {
+    static_for<kSkinnyDepth>([&](auto J) { fetch(J, c0 + J); });
+    for (int c = c0; c < c1; c += kSkinnyDepth) {
         static_for<kSkinnyDepth>([&](auto J) {
             constexpr int j = J;
-            const float sgj = sg[j];
-            const v16f p = tile_product<AF, BF, OUT>(xb[j], xa[j]);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[e] = fmaf(sgj, p[e], acc[e]);
-            fetch(J, kb + j + kSkinnyDepth);
+            for (int i = 0; i < 4; ++i) {
+                const int row = lr + 8 * i;
+                const int pos = row * 128 + 16 * (lg ^ (row & 7));
+                *reinterpret_cast<u32x4*>(st_a + pos) = ga[j][i];
+                *reinterpret_cast<u32x4*>(st_b + pos) = gb[j][i];
+            }
+            fetch(J, c + j + kSkinnyDepth);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int pos = r * 128 + 16 * ((2 * b + h) ^ (r & 7));
+                const u32x4 xa = *reinterpret_cast<const u32x4*>(st_a + pos);
+                const u32x4 xb = *reinterpret_cast<const u32x4*>(st_b + pos);
+                const float sgb = sigma(4 * (c + j) + b);
+                const v16f p = tile_product<AF, BF, OUT>(xb, xa);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[e] = fmaf(sgb, p[e], acc[e]);
+            }
         });
     }
     if (wave > 0) part[wave - 1][lane] = acc;

@@ -796,15 +796,17 @@ __device__ __forceinline__ void static_for_mx(F&& f) {
 }
 
 // Skinny form (up to 64 rows, or fewer than 32 tiles of 128 x 128): one
-// workgroup per 32 x 32 output tile whose four waves split the 32-K blocks into
-// contiguous ranges, as the skinny FP8 and MXFP4 kernels do.  No LDS staging:
-// lane (r, h) loads the 8 packed bytes of K 16 h .. 16 h + 15 of block kb of
-// row r (and their one or two block scales), dequantises them in registers and
-// feeds two bf16 MFMAs (K 16 h .. + 7 in the first, the rest in the second).
+// workgroup per 32 x 32 output tile whose four waves split K into contiguous
+// ranges of 8-block chunks, as the skinny FP8 and MXFP4 kernels do.  Codes are
+// loaded as whole 128-byte row segments and pass through the wave's own LDS
+// area; lane (r, h) then takes the 8 packed bytes of K 16 h .. 16 h + 15 of
+// block kb of row r (and loads their one or two block scales), dequantises
+// them in registers and feeds two bf16 MFMAs (K 16 h .. + 7 in the first, the
+// rest in the second).
 // Every lane of A and of B uses this same assignment of K to MFMA slots, so
 // each dot product is unchanged.  Wide scales use the hi / lo split (three
 // products, four for FP32 output).  Blocks past the wave's range read as zero.
-constexpr int kMxSkinnyDepth = 8;           // 32-K blocks in flight per wave
+constexpr int kMxSkinnyDepth = 2;           // chunks of 8 blocks in flight per wave
 constexpr int kMxSkinnyWaves = 4;           // waves per workgroup, splitting K
 constexpr int64_t kMxSkinnyMaxM = 64;
 constexpr int64_t kMxSkinnyMaxTiles = 32;
@@ -818,6 +820,7 @@ __global__ __launch_bounds__(64 * kMxSkinnyWaves, 8 / kMxSkinnyWaves) void gemm_
     constexpr int SB = SPLIT ? 2 : 1;                     // bytes per scale
     constexpr int NS = BLOCK == 8 ? 2 : 1;                // scales per lane per block
     __shared__ v16f part[kMxSkinnyWaves - 1][64];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kMxSkinnyWaves][2][32 * 128];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // the row tiles of a column tile are launched 8 apart (the same XCD)
@@ -827,8 +830,11 @@ __global__ __launch_bounds__(64 * kMxSkinnyWaves, 8 / kMxSkinnyWaves) void gemm_
     if (tn >= tiles_n) return;
     const int m0 = tm * 32, n0 = tn * 32;
     const int kh = K >> 1, nkb = K >> 5, nsc = K / BLOCK;
-    const int per = (nkb + kMxSkinnyWaves - 1) / kMxSkinnyWaves;
-    const int kb0 = min(wave * per, nkb), kb1 = min(kb0 + per, nkb);
+    // K is split into chunks of 8 blocks (128 bytes of each row); each wave
+    // takes a contiguous range of chunks
+    const int nch = (nkb + 7) >> 3;
+    const int cper = (nch + kMxSkinnyWaves - 1) / kMxSkinnyWaves;
+    const int c0 = min(wave * cper, nch), c1 = min(c0 + cper, nch);
 
     const int rows_a = min(32, M - m0), rows_b = min(32, N - n0);
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
@@ -841,28 +847,44 @@ __global__ __launch_bounds__(64 * kMxSkinnyWaves, 8 / kMxSkinnyWaves) void gemm_
         const_cast<uint8_t*>(sB) + static_cast<int64_t>(n0) * nsc * SB, 0, rows_b * nsc * SB, 0x00020000);
     const int r = lane & 31, h = lane >> 5;
     constexpr uint32_t kOut = 0x80000000u;
+    // Code loads read whole 128-byte row segments: lane l takes 16-byte piece
+    // l & 7 (block 8 c + (l & 7)) of row (l >> 3) + 8 i.  The wave stages the
+    // chunk in its own LDS area (piece g of row R at g ^ (R & 7)); for block b
+    // of the chunk lane (r, h) reads back the 8 bytes of K 16 h .. 16 h + 15
+    // of row r and loads their scale(s) itself.
+    const int lr = lane >> 3, lg = lane & 7;
+    uint8_t* st_a = stage[wave][0];
+    uint8_t* st_b = stage[wave][1];
     // the scale index of this lane's first value of block kb
     auto sidx = [&](int kb) { return (32 * kb + 16 * h) / BLOCK; };
-    uint2 ca[kMxSkinnyDepth], cb[kMxSkinnyDepth];
-    uint32_t va[kMxSkinnyDepth], vb[kMxSkinnyDepth];   // NS scales of SB bytes
-    auto fetch = [&](auto SLOT, int kb) {
+    uint4 ga[kMxSkinnyDepth][4], gb[kMxSkinnyDepth][4];
+    uint32_t va[kMxSkinnyDepth][8], vb[kMxSkinnyDepth][8];   // NS scales of SB bytes per block
+    auto fetch = [&](auto SLOT, int c) {
         constexpr int j = SLOT;
-        const bool ok = kb < kb1;
-        const uint32_t oc = ok ? static_cast<uint32_t>(r * kh + 16 * kb + 8 * h) : kOut;
-        const uint32_t os = ok ? static_cast<uint32_t>((r * nsc + sidx(kb)) * SB) : kOut;
-        const auto wa = __builtin_amdgcn_raw_buffer_load_b64(rs_a, static_cast<int>(oc), 0, 0);
-        const auto wb = __builtin_amdgcn_raw_buffer_load_b64(rs_b, static_cast<int>(oc), 0, 0);
-        ca[j] = make_uint2(wa[0], wa[1]);
-        cb[j] = make_uint2(wb[0], wb[1]);
-        if constexpr (NS * SB == 1) {
-            va[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_sa, static_cast<int>(os), 0, 0);
-            vb[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_sb, static_cast<int>(os), 0, 0);
-        } else if constexpr (NS * SB == 2) {
-            va[j] = __builtin_amdgcn_raw_buffer_load_b16(rs_sa, static_cast<int>(os), 0, 0);
-            vb[j] = __builtin_amdgcn_raw_buffer_load_b16(rs_sb, static_cast<int>(os), 0, 0);
-        } else {
-            va[j] = __builtin_amdgcn_raw_buffer_load_b32(rs_sa, static_cast<int>(os), 0, 0);
-            vb[j] = __builtin_amdgcn_raw_buffer_load_b32(rs_sb, static_cast<int>(os), 0, 0);
+        const bool cok = c < c1;
+        const bool ok = cok && 8 * c + lg < nkb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t o = ok ? static_cast<uint32_t>((lr + 8 * i) * kh + 128 * c + 16 * lg) : kOut;
+            const auto wa = __builtin_amdgcn_raw_buffer_load_b128(rs_a, static_cast<int>(o), 0, 0);
+            const auto wb = __builtin_amdgcn_raw_buffer_load_b128(rs_b, static_cast<int>(o), 0, 0);
+            ga[j][i] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+            gb[j][i] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+        }
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const int kb = 8 * c + b;
+            const uint32_t os = cok && kb < nkb ? static_cast<uint32_t>((r * nsc + sidx(kb)) * SB) : kOut;
+            if constexpr (NS * SB == 1) {
+                va[j][b] = __builtin_amdgcn_raw_buffer_load_b8(rs_sa, static_cast<int>(os), 0, 0);
+                vb[j][b] = __builtin_amdgcn_raw_buffer_load_b8(rs_sb, static_cast<int>(os), 0, 0);
+            } else if constexpr (NS * SB == 2) {
+                va[j][b] = __builtin_amdgcn_raw_buffer_load_b16(rs_sa, static_cast<int>(os), 0, 0);
+                vb[j][b] = __builtin_amdgcn_raw_buffer_load_b16(rs_sb, static_cast<int>(os), 0, 0);
+            } else {
+                va[j][b] = __builtin_amdgcn_raw_buffer_load_b32(rs_sa, static_cast<int>(os), 0, 0);
+                vb[j][b] = __builtin_amdgcn_raw_buffer_load_b32(rs_sb, static_cast<int>(os), 0, 0);
+            }
         }
     };
     // 16 codes (two words, K order) with their scale(s) -> bf16 hi (and lo),
@@ -881,25 +903,44 @@ __global__ __launch_bounds__(64 * kMxSkinnyWaves, 8 / kMxSkinnyWaves) void gemm_
         dequant_pair<3, SPLIT>(w.y, s1, hi[1], lo[1]);
     };
     v16f acc = v16f{};
-    static_for_mx<kMxSkinnyDepth>([&](auto J) { fetch(J, kb0 + J); });
-    for (int kb = kb0; kb < kb1; kb += kMxSkinnyDepth) {
+    static_for_mx<kMxSkinnyDepth>([&](auto J) { fetch(J, c0 + J); });
+    for (int c = c0; c < c1; c += kMxSkinnyDepth) {
         static_for_mx<kMxSkinnyDepth>([&](auto J) {
             constexpr int j = J;
-            v8bf ah[2], al[2], bh[2], bl[2];
-            dequant(ca[j], va[j], ah, al);
-            dequant(cb[j], vb[j], bh, bl);
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                // B rows are the MFMA row operand, A rows the column operand
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[q], ah[q], acc, 0, 0, 0);
-                if constexpr (SPLIT) {
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[q], al[q], acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[q], ah[q], acc, 0, 0, 0);
-                    if constexpr (OUT == BSFP8_OUT_F32)
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[q], al[q], acc, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const int row = lr + 8 * i;
+                const int pos = row * 128 + 16 * (lg ^ (row & 7));
+                *reinterpret_cast<uint4*>(st_a + pos) = ga[j][i];
+                *reinterpret_cast<uint4*>(st_b + pos) = gb[j][i];
+            }
+            uint32_t sa8[8], sb8[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                sa8[b] = va[j][b];
+                sb8[b] = vb[j][b];
+            }
+            fetch(J, c + j + kMxSkinnyDepth);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const int pos = r * 128 + 16 * (b ^ (r & 7)) + 8 * h;
+                const uint2 wa = *reinterpret_cast<const uint2*>(st_a + pos);
+                const uint2 wb = *reinterpret_cast<const uint2*>(st_b + pos);
+                v8bf ah[2], al[2], bh[2], bl[2];
+                dequant(wa, sa8[b], ah, al);
+                dequant(wb, sb8[b], bh, bl);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    // B rows are the MFMA row operand, A rows the column operand
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[q], ah[q], acc, 0, 0, 0);
+                    if constexpr (SPLIT) {
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bh[q], al[q], acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[q], ah[q], acc, 0, 0, 0);
+                        if constexpr (OUT == BSFP8_OUT_F32)
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bl[q], al[q], acc, 0, 0, 0);
+                    }
                 }
             }
-            fetch(J, kb + j + kMxSkinnyDepth);
         });
     }
     if (wave > 0) part[wave - 1][lane] = acc;

@@ -432,13 +432,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
 }
 
 // Skinny form (up to kSkinnyMaxM rows), as the FP8 one: one workgroup per
-// 32 x 32 output tile, the four waves split the 64-K steps into contiguous
-// ranges, fragments and scale bytes go from global memory straight to
-// registers kDepth steps ahead (lane (r, h) takes the 16 packed bytes and the
-// E8M0 byte of block 2 t + h of row r), and the partial sums are added in a
-// fixed order through LDS.  Blocks past K or past the wave's range read as
-// zero codes with a zero scale byte (2^-127), which contribute nothing.
-constexpr int kSkinnyDepth = 8;              // 64-K steps in flight per wave
+// 32 x 32 output tile, the four waves split K into contiguous ranges of
+// 8-block chunks, codes are loaded as whole 128-byte row segments and staged
+// through LDS into the MFMA layout (lane (r, h) takes the 16 packed bytes and
+// the E8M0 byte of block 2 s + h of row r for 64-K step s), and the partial
+// sums are added in a fixed order through LDS.  Blocks past K or past the
+// wave's range read as zero codes with a zero scale byte (2^-127), which
+// contribute nothing.
+constexpr int kSkinnyDepth = 2;              // chunks of 8 blocks in flight per wave
 constexpr int kSkinnyWaves = 4;              // waves per workgroup, splitting K
 constexpr int64_t kSkinnyMaxM = 64;
 constexpr int64_t kSkinnyMaxTiles = 32;      // 128 x 128 tiles below which the skinny form is used too
@@ -449,6 +450,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_mxfp
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
     int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
     __shared__ v16f part[kSkinnyWaves - 1][64];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kSkinnyWaves][2][32 * 128];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Workgroups go to the 8 XCDs round-robin by launch index.  The row tiles
@@ -461,9 +463,11 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_mxfp
     if (tn >= tiles_n) return;
     const int m0 = tm * 32, n0 = tn * 32;
     const int kbytes = K >> 1, nkb = K >> 5;
-    const int nsteps = (nkb + 1) >> 1;          // 64-K steps; the last may hold one block
-    const int per = (nsteps + kSkinnyWaves - 1) / kSkinnyWaves;
-    const int t0 = min(wave * per, nsteps), t1 = min(t0 + per, nsteps);
+    // K is split into chunks of 8 blocks (128 bytes of each row); each wave
+    // takes a contiguous range of chunks
+    const int nch = (nkb + 7) >> 3;
+    const int cper = (nch + kSkinnyWaves - 1) / kSkinnyWaves;
+    const int c0 = min(wave * cper, nch), c1 = min(c0 + cper, nch);
 
     const int rows_a = min(32, M - m0), rows_b = min(32, N - n0);
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
@@ -476,28 +480,62 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_mxfp
         const_cast<uint8_t*>(sB) + static_cast<int64_t>(n0) * nkb, 0, rows_b * nkb, 0x00020000);
     const int r = lane & 31, h = lane >> 5;
     constexpr uint32_t kOut = 0x80000000u;
-    uint4 xa[kSkinnyDepth], xb[kSkinnyDepth];
-    uint32_t ea[kSkinnyDepth], eb[kSkinnyDepth];
-    auto fetch = [&](auto SLOT, int t) {
+    // Code loads read whole 128-byte row segments: lane l takes 16-byte piece
+    // l & 7 (block 8 c + (l & 7)) of row (l >> 3) + 8 i.  The wave stages the
+    // chunk in its own LDS area (piece g of row R at g ^ (R & 7)) and reads the
+    // fragments back: for step s of the chunk lane (r, h) takes block
+    // 8 c + 2 s + h of row r, with its E8M0 byte.
+    const int lr = lane >> 3, lg = lane & 7;
+    uint8_t* st_a = stage[wave][0];
+    uint8_t* st_b = stage[wave][1];
+    uint4 ga[kSkinnyDepth][4], gb[kSkinnyDepth][4];
+    uint32_t ea[kSkinnyDepth][4], eb[kSkinnyDepth][4];
+    auto fetch = [&](auto SLOT, int c) {
         constexpr int j = SLOT;
-        const int blk = 2 * t + h;
-        const bool ok = t < t1 && blk < nkb;
-        const uint32_t oc = ok ? static_cast<uint32_t>(r * kbytes + 16 * blk) : kOut;
-        const uint32_t os = ok ? static_cast<uint32_t>(r * nkb + blk) : kOut;
-        const auto wa = __builtin_amdgcn_raw_buffer_load_b128(rs_a, static_cast<int>(oc), 0, 0);
-        const auto wb = __builtin_amdgcn_raw_buffer_load_b128(rs_b, static_cast<int>(oc), 0, 0);
-        xa[j] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
-        xb[j] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
-        ea[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_sa, static_cast<int>(os), 0, 0);
-        eb[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_sb, static_cast<int>(os), 0, 0);
+        const bool cok = c < c1;
+        const bool ok = cok && 8 * c + lg < nkb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t o = ok ? static_cast<uint32_t>((lr + 8 * i) * kbytes + 128 * c + 16 * lg) : kOut;
+            const auto wa = __builtin_amdgcn_raw_buffer_load_b128(rs_a, static_cast<int>(o), 0, 0);
+            const auto wb = __builtin_amdgcn_raw_buffer_load_b128(rs_b, static_cast<int>(o), 0, 0);
+            ga[j][i] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+            gb[j][i] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int blk = 8 * c + 2 * st + h;
+            const uint32_t os = cok && blk < nkb ? static_cast<uint32_t>(r * nkb + blk) : kOut;
+            ea[j][st] = __builtin_amdgcn_raw_buffer_load_b8(rs_sa, static_cast<int>(os), 0, 0);
+            eb[j][st] = __builtin_amdgcn_raw_buffer_load_b8(rs_sb, static_cast<int>(os), 0, 0);
+        }
     };
     v16f acc = v16f{};
-    static_for<kSkinnyDepth>([&](auto J) { fetch(J, t0 + J); });
-    for (int t = t0; t < t1; t += kSkinnyDepth) {
+    static_for<kSkinnyDepth>([&](auto J) { fetch(J, c0 + J); });
+    for (int c = c0; c < c1; c += kSkinnyDepth) {
         static_for<kSkinnyDepth>([&](auto J) {
             constexpr int j = J;
-            acc = mfma_fp4(xb[j], xa[j], eb[j], ea[j], acc);   // B rows are the row operand
-            fetch(J, t + j + kSkinnyDepth);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = lr + 8 * i;
+                const int pos = row * 128 + 16 * (lg ^ (row & 7));
+                *reinterpret_cast<uint4*>(st_a + pos) = ga[j][i];
+                *reinterpret_cast<uint4*>(st_b + pos) = gb[j][i];
+            }
+            uint32_t sa4[4], sb4[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                sa4[st] = ea[j][st];
+                sb4[st] = eb[j][st];
+            }
+            fetch(J, c + j + kSkinnyDepth);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int pos = r * 128 + 16 * ((2 * st + h) ^ (r & 7));
+                const uint4 xa = *reinterpret_cast<const uint4*>(st_a + pos);
+                const uint4 xb = *reinterpret_cast<const uint4*>(st_b + pos);
+                acc = mfma_fp4(xb, xa, sb4[st], sa4[st], acc);   // B rows are the row operand
+            }
         });
     }
     if (wave > 0) part[wave - 1][lane] = acc;
