@@ -83,9 +83,11 @@ def test_dot_examples_fp32_output_exact():
 @pytest.mark.parametrize("M,N,K", [(1, 257, 32), (33, 1000, 4128), (64, 4096, 8192), (17, 96, 96),
                                    (64, 130, 1024)])
 def test_fp8_skinny(M, N, K, fmts, out):
-    """Up to 64 rows: the skinny kernel (32 x 32 tiles, K blocks split over four
-    waves and summed in a fixed order).  K = 32 leaves three waves without a
-    block; 129 blocks split 33 / 33 / 33 / 30; ragged N."""
+    """Up to 64 rows: the skinny kernel (32 x 32 tiles; K split over four waves
+    in chunks of 4 blocks, 128 bytes of a row, and summed in a fixed order).
+    K = 32 leaves three waves without a block; K = 96 gives wave 0 one partial
+    chunk; 129 blocks split 36 / 36 / 36 / 21, the last chunk holding one
+    block; ragged N."""
     full_check(M, N, K, fmts[0], fmts[1], out, seed=M + N + K, label="skinny")
 
 
@@ -109,9 +111,10 @@ def test_mxfp4_small_ragged(M, N, K, out):
 @pytest.mark.parametrize("M,N,K", [(1, 257, 32), (33, 1000, 4128), (64, 4096, 8192), (17, 96, 96),
                                    (48, 130, 2080)])
 def test_mxfp4_skinny(M, N, K, out):
-    """Up to 64 rows: the skinny MXFP4 kernel (32 x 32 tiles, the 64-K steps
-    split over four waves and summed in a fixed order).  K % 64 == 32 leaves a
-    last step with one block; K = 32 leaves three waves without a step."""
+    """Up to 64 rows: the skinny MXFP4 kernel (32 x 32 tiles; K split over four
+    waves in chunks of 8 blocks, 128 bytes of a row, and summed in a fixed
+    order).  129 blocks split 40 / 40 / 40 / 9 and 65 blocks 24 / 24 / 17, each
+    with a last chunk of one block; K = 32 leaves three waves without a block."""
     full_check(M, N, K, "mxfp4", "mxfp4", out, seed=M * 7 + N + K, label="skinny mxfp4")
 
 

@@ -148,9 +148,10 @@ def test_mx_gemm_alpha_beta(block, scale):
 @pytest.mark.parametrize("M,N,K", [(16, 1000, 4096), (1, 520, 416), (33, 300, 32), (64, 2100, 1568),
                                    (50, 64, 8192)])
 def test_mx_gemm_skinny_parity(M, N, K, block, scale, out):
-    """Up to 64 rows: the skinny kernel, whose four waves split the 32-K blocks
-    (K = 32: three waves idle; K = 416: ranges of 4, 4, 4 and 1 blocks; long K:
-    several rounds of its 8-deep prefetch), ragged M and N."""
+    """Up to 64 rows: the skinny kernel, whose four waves split K in chunks of
+    8 blocks (K = 32: three waves idle; K = 416: 8 and 5 blocks on two waves;
+    K = 1568: 16 / 16 / 16 / 1; long K: several rounds of its two-chunk
+    prefetch), ragged M and N."""
     say(f"scaled_gemm_mx skinny block={block} {scale} M={M} N={N} K={K} -> {out}")
     a = inputs(M + K + 5, M, K, "normal")
     b = inputs(N + K + 6, N, K, "laplace")
