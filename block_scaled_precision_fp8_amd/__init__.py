@@ -8,6 +8,7 @@ raises, and a non-OK status raises ``RuntimeError``.
 
 Functions (same names as the C ABI):
   fp8_quantize(x, fmt="e4m3", tile_rows=128) -> (codes, scales)
+  fp8_quantize_pair(a, b, a_fmt="e4m3", b_fmt="e4m3") -> (a_codes, a_scales, b_codes, b_scales)
   fp8_quantize_transposed(x, fmt="e4m3", tile_rows=128) -> (codes of x^T, scales)
   fp8_quantize_granular(x, fmt="e4m3", granularity="tile"|"row"|"tensor") -> (codes, scales)
   mxfp4_quantize(x) -> (packed, scales)
@@ -54,6 +55,8 @@ def lib() -> ctypes.CDLL:
     i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     L.fp8_quantize.argtypes = [vp, i64, i64, i64, c_int, c_int, vp, vp, vp]
     L.fp8_quantize.restype = c_int
+    L.fp8_quantize_pair.argtypes = [vp, i64, i64, c_int, vp, vp, vp, i64, i64, c_int, vp, vp, i64, vp]
+    L.fp8_quantize_pair.restype = c_int
     L.fp8_quantize_transposed.argtypes = [vp, i64, i64, i64, c_int, c_int, vp, vp, vp]
     L.fp8_quantize_transposed.restype = c_int
     L.mxfp4_quantize.argtypes = [vp, i64, i64, i64, vp, vp, vp]
@@ -117,6 +120,38 @@ def fp8_quantize(x, fmt: str = "e4m3", tile_rows: int = FP8_TILE_ROWS,
                             FORMATS[fmt], _dev_ptr(codes), _dev_ptr(scales), _stream(x))
     _check(st, "fp8_quantize")
     return codes, scales
+
+
+def fp8_quantize_pair(a, b, a_fmt: str = "e4m3", b_fmt: str = "e4m3", a_codes=None, a_scales=None,
+                      b_codes=None, b_scales=None):
+    """fp8_quantize of A (M x K) and B (N x K, the N x K storage of a K x N
+    operand) in one launch; returns (a_codes, a_scales, b_codes, b_scales),
+    byte-for-byte what two fp8_quantize calls give."""
+    import torch
+    for t in (a, b):
+        if t.dtype != torch.float32 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("a and b must be 2-D float32 CUDA tensors with unit column stride")
+    if a.shape[1] != b.shape[1] or a.device != b.device:
+        raise ValueError("a and b must have the same K and device")
+    k = a.shape[1]
+
+    def outs(x, codes, scales):
+        rows = x.shape[0]
+        if codes is None:
+            codes = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+        if scales is None:
+            scales = torch.empty(((rows + FP8_TILE_ROWS - 1) // FP8_TILE_ROWS, (k + 31) // 32),
+                                 dtype=torch.float32, device=x.device)
+        return codes, scales
+
+    a_codes, a_scales = outs(a, a_codes, a_scales)
+    b_codes, b_scales = outs(b, b_codes, b_scales)
+    ld = lambda x: x.stride(0) if x.shape[0] > 1 else k
+    st = lib().fp8_quantize_pair(_dev_ptr(a), a.shape[0], ld(a), FORMATS[a_fmt], _dev_ptr(a_codes),
+                                 _dev_ptr(a_scales), _dev_ptr(b), b.shape[0], ld(b), FORMATS[b_fmt],
+                                 _dev_ptr(b_codes), _dev_ptr(b_scales), k, _stream(a))
+    _check(st, "fp8_quantize_pair")
+    return a_codes, a_scales, b_codes, b_scales
 
 
 

@@ -37,6 +37,28 @@ bsfp8_status fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, i
     return from_hip(bsfp8::launch_fp8_quantize(x, rows, k, ld, fmt, codes, scales, stream));
 }
 
+bsfp8_status fp8_quantize_pair(const float* a, int64_t a_rows, int64_t a_ld, bsfp8_format a_fmt,
+                               uint8_t* a_codes, float* a_scales, const float* b, int64_t b_rows,
+                               int64_t b_ld, bsfp8_format b_fmt, uint8_t* b_codes, float* b_scales,
+                               int64_t k, hipStream_t stream) {
+    if (!is_fp8(a_fmt) || !is_fp8(b_fmt)) return BSFP8_ERR_UNSUPPORTED;
+    if (a_rows < 0 || b_rows < 0 || k < 0 || a_ld < k || b_ld < k || (k % 32) != 0)
+        return BSFP8_ERR_INVALID_ARG;
+    if (k == 0) return BSFP8_OK;
+    if (a_rows == 0) a = nullptr;
+    if (b_rows == 0) b = nullptr;
+    if (a_rows > 0 && (!a || !a_codes || !a_scales || !aligned(a, 16) || (a_ld % 4) != 0 ||
+                       !aligned(a_codes, 4) || !aligned(a_scales, 4)))
+        return BSFP8_ERR_INVALID_ARG;
+    if (b_rows > 0 && (!b || !b_codes || !b_scales || !aligned(b, 16) || (b_ld % 4) != 0 ||
+                       !aligned(b_codes, 4) || !aligned(b_scales, 4)))
+        return BSFP8_ERR_INVALID_ARG;
+    const int64_t ncb = (k + 127) / 128;
+    if (((a_rows + 127) / 128 + (b_rows + 127) / 128) * ncb > kI32Max) return BSFP8_ERR_INVALID_ARG;
+    return from_hip(bsfp8::launch_fp8_quantize_pair(a, a_rows, a_ld, a_fmt, a_codes, a_scales, b, b_rows,
+                                                    b_ld, b_fmt, b_codes, b_scales, k, stream));
+}
+
 bsfp8_status fp8_quantize_transposed(const float* x, int64_t k, int64_t rows, int64_t ld,
                                      int tile_rows, bsfp8_format fmt, uint8_t* codes,
                                      float* scales, hipStream_t stream) {

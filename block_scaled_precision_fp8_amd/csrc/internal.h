@@ -13,6 +13,10 @@ namespace bsfp8 {
 // layer and returns the launch status.
 hipError_t launch_fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, int fmt,
                                uint8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_fp8_quantize_pair(const float* a, int64_t rows_a, int64_t lda, int fmt_a,
+                                    uint8_t* codes_a, float* scales_a, const float* b, int64_t rows_b,
+                                    int64_t ldb, int fmt_b, uint8_t* codes_b, float* scales_b, int64_t k,
+                                    hipStream_t stream);
 hipError_t launch_fp8_quantize_t(const float* x, int64_t k, int64_t rows, int64_t ld, int fmt,
                                  uint8_t* codes, float* scales, hipStream_t stream);
 hipError_t launch_fp8_quantize_rows(const float* x, int64_t rows, int64_t k, int64_t ld, int fmt,

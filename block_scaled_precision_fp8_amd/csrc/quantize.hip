@@ -35,13 +35,11 @@ __device__ __forceinline__ float4 load_once(const float* p) {
 // wave reads two full 512-byte row segments per load instruction and every
 // thread's 64 values belong to a single tile (chunk / 8).
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void fp8_quantize_kernel(
-    const float* __restrict__ x, int64_t rows, int64_t k, int64_t ld,
-    uint8_t* __restrict__ codes, float* __restrict__ scales, int64_t ncol_blocks) {
+__device__ __forceinline__ void quantize_block(const float* __restrict__ x, int64_t rows, int64_t k,
+                                               int64_t ld, uint8_t* __restrict__ codes,
+                                               float* __restrict__ scales, int64_t ncol_blocks,
+                                               int64_t bid, float (*red)[4]) {
     constexpr float F = FMT == BSFP8_E4M3 ? 448.0f : 57344.0f;
-    __shared__ float red[4][4];
-
-    const int64_t bid = blockIdx.x;
     const int64_t rt = bid / ncol_blocks;
     const int64_t cb = bid - rt * ncol_blocks;
     const int tid = threadIdx.x;
@@ -92,6 +90,31 @@ __global__ __launch_bounds__(kThreads) void fp8_quantize_kernel(
         if (!(col_ok && r < rows)) continue;
         *reinterpret_cast<uint32_t*>(codes + r * k + col) = fp8_codes4<FMT>(qt, v[i]);
     }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void fp8_quantize_kernel(
+    const float* __restrict__ x, int64_t rows, int64_t k, int64_t ld,
+    uint8_t* __restrict__ codes, float* __restrict__ scales, int64_t ncol_blocks) {
+    __shared__ float red[4][4];
+    quantize_block<FMT>(x, rows, k, ld, codes, scales, ncol_blocks, blockIdx.x, red);
+}
+
+// Two operands with the same K in one launch (the A and B of one GEMM): the
+// first blocks_a workgroups take A's 128 x 128 blocks, the rest B's.  Each
+// workgroup does exactly what fp8_quantize_kernel does for its block.
+template <int FA, int FB>
+__global__ __launch_bounds__(kThreads) void fp8_quantize_pair_kernel(
+    const float* __restrict__ xa, int64_t rows_a, int64_t lda, uint8_t* __restrict__ codes_a,
+    float* __restrict__ scales_a, int64_t blocks_a, const float* __restrict__ xb, int64_t rows_b,
+    int64_t ldb, uint8_t* __restrict__ codes_b, float* __restrict__ scales_b, int64_t k,
+    int64_t ncol_blocks) {
+    __shared__ float red[4][4];
+    const int64_t bid = blockIdx.x;
+    if (bid < blocks_a)
+        quantize_block<FA>(xa, rows_a, k, lda, codes_a, scales_a, ncol_blocks, bid, red);
+    else
+        quantize_block<FB>(xb, rows_b, k, ldb, codes_b, scales_b, ncol_blocks, bid - blocks_a, red);
 }
 
 // Transposing variant: x is k x rows row-major (for example a gradient or an
@@ -521,6 +544,30 @@ hipError_t launch_fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t 
     else
         hipLaunchKernelGGL(fp8_quantize_kernel<BSFP8_E5M2>, dim3(static_cast<uint32_t>(blocks)),
                            dim3(kThreads), 0, stream, x, rows, k, ld, codes, scales, ncb);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize_pair(const float* a, int64_t rows_a, int64_t lda, int fmt_a,
+                                    uint8_t* codes_a, float* scales_a, const float* b, int64_t rows_b,
+                                    int64_t ldb, int fmt_b, uint8_t* codes_b, float* scales_b, int64_t k,
+                                    hipStream_t stream) {
+    const int64_t ncb = (k + 127) / 128;
+    const int64_t blocks_a = (rows_a + 127) / 128 * ncb;
+    const int64_t blocks = blocks_a + (rows_b + 127) / 128 * ncb;
+    if (blocks == 0) return hipSuccess;
+    const dim3 g(static_cast<uint32_t>(blocks));
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, g, dim3(kThreads), 0, stream, a, rows_a, lda, codes_a, scales_a,
+                           blocks_a, b, rows_b, ldb, codes_b, scales_b, k, ncb);
+    };
+    if (fmt_a == BSFP8_E4M3 && fmt_b == BSFP8_E4M3)
+        go(fp8_quantize_pair_kernel<BSFP8_E4M3, BSFP8_E4M3>);
+    else if (fmt_a == BSFP8_E4M3)
+        go(fp8_quantize_pair_kernel<BSFP8_E4M3, BSFP8_E5M2>);
+    else if (fmt_b == BSFP8_E4M3)
+        go(fp8_quantize_pair_kernel<BSFP8_E5M2, BSFP8_E4M3>);
+    else
+        go(fp8_quantize_pair_kernel<BSFP8_E5M2, BSFP8_E5M2>);
     return hipGetLastError();
 }
 

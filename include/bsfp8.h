@@ -74,6 +74,23 @@ bsfp8_status fp8_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, i
                           bsfp8_format fmt, uint8_t* codes, float* scales, hipStream_t stream);
 
 /*
+ * fp8_quantize_pair -- fp8_quantize of the two operands of one GEMM, A
+ * (a_rows x k) and B (b_rows x k, N x K storage), in a single launch
+ * ([CDNA4-FP8] sections 3.3 and 4.2; 128 x 32 tiles as fp8_quantize).
+ *
+ * Each operand takes the arguments, layout, alignment and ownership rules of
+ * fp8_quantize for its side (x, ld, fmt, codes, scales), with one shared k.
+ * The outputs are byte-for-byte those of two fp8_quantize calls.  Either side
+ * may have 0 rows (its pointers are then ignored).  Errors as fp8_quantize;
+ * nothing is launched unless both sides pass the checks.  The two sides'
+ * buffers must not overlap.
+ */
+bsfp8_status fp8_quantize_pair(const float* a, int64_t a_rows, int64_t a_ld, bsfp8_format a_fmt,
+                               uint8_t* a_codes, float* a_scales, const float* b, int64_t b_rows,
+                               int64_t b_ld, bsfp8_format b_fmt, uint8_t* b_codes, float* b_scales,
+                               int64_t k, hipStream_t stream);
+
+/*
  * fp8_quantize_transposed -- per-tile FP8 quantisation of x^T, for operands
  * stored the other way round, such as the gradient G and activation X of a
  * weight-gradient product dW = G^T X ([CDNA4-FP8] section 3.3's per-tile

@@ -241,3 +241,47 @@ def test_workload_operands_transposed_full_size():
     a, b = workloads.operands(w)
     assert_fp8_t_equal(a, w.a_fmt, label=f"{w.name} A from G")
     assert_fp8_t_equal(b, w.b_fmt, label=f"{w.name} B from X")
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
+@pytest.mark.parametrize("ra,rb,k,lda", [(300, 130, 288, 300), (0, 257, 160, None), (129, 0, 96, None),
+                                         (1, 1, 32, None), (640, 1100, 1024, 1028)])
+def test_fp8_quantize_pair(fa, fb, ra, rb, k, lda):
+    """fp8_quantize_pair: A's and B's codes and scales byte-equal to the
+    oracle's (and so to two fp8_quantize calls), ragged rows, a padded A, an
+    empty side, mixed formats."""
+    import torch
+    b_ = bsfp8()
+    rng = np.random.default_rng(ra * 7 + rb * 3 + k)
+    x = (rng.standard_normal((ra, k)) * np.exp2(rng.integers(-20, 20, size=(ra, 1)))).astype(np.float32)
+    y = rng.laplace(size=(rb, k)).astype(np.float32)
+    if lda is None:
+        xd = to_dev(x) if ra else torch.empty((0, k), dtype=torch.float32, device="cuda")
+    else:
+        buf = np.zeros((ra, lda), dtype=np.float32)
+        buf[:, :k] = x
+        xd = to_dev(buf)[:, :k]
+    yd = to_dev(y) if rb else torch.empty((0, k), dtype=torch.float32, device="cuda")
+    say(f"fp8_quantize_pair {fa} {fb} A {ra}x{k} ld={lda} B {rb}x{k}")
+    qa, sa, qb, sb = b_.fp8_quantize_pair(xd, yd, fa, fb)
+    torch.cuda.synchronize()
+    for rows, xx, fmt, q, s in ((ra, x, fa, qa, sa), (rb, y, fb, qb, sb)):
+        if rows == 0:
+            continue
+        rq, rs = oracle.fp8_quantize(xx, fmt)
+        assert np.array_equal(from_dev(q), rq), f"{np.count_nonzero(from_dev(q) != rq)} codes differ"
+        assert np.array_equal(from_dev(s), rs), "scales differ"
+
+
+def test_fp8_quantize_pair_square_4096():
+    """The two 4096 x 4096 operands of the square workload in one launch,
+    byte-equal to the oracle."""
+    import torch
+    w = workloads.by_name("square_e4m3_4096")
+    a, b = workloads.operands(w)
+    say("fp8_quantize_pair square 4096")
+    qa, sa, qb, sb = bsfp8().fp8_quantize_pair(to_dev(a), to_dev(b), w.a_fmt, w.b_fmt)
+    torch.cuda.synchronize()
+    for x, fmt, q, s in ((a, w.a_fmt, qa, sa), (b, w.b_fmt, qb, sb)):
+        rq, rs = oracle.fp8_quantize(x, fmt)
+        assert np.array_equal(from_dev(q), rq) and np.array_equal(from_dev(s), rs)
