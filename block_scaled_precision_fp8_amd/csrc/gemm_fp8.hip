@@ -44,6 +44,7 @@
 //  * The output tile leaves through LDS, so every store writes whole rows.
 #include "fp8_codec.h"
 
+#include <type_traits>
 #include <utility>
 
 namespace bsfp8 {
@@ -324,21 +325,33 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
     const uint32_t dma_a = static_cast<uint32_t>(drow) * K + dchunk * 16;
     const uint32_t dma_b = static_cast<uint32_t>(drow) * K + dchunk * 16;
     const uint32_t row_step = 32u * static_cast<uint32_t>(K);
-    // direct loads of a stage: A (without QA) and B, alternating
-    auto dma_one = [&](auto J, int stage, int buf) {
+    // direct loads of a stage: A (without QA) and B, alternating.  The stage's
+    // K offset rides in the scalar offset, which the range check does not
+    // cover.  A full stage lies inside every row; in a partial last stage (K
+    // not a multiple of 128) the chunks at or past K are CHECKED: they get an
+    // out-of-range VGPR offset and read as zero without touching memory.
+    const int kend = K - dchunk * 16;       // chunk at stage offset so is inside K iff so < kend
+    auto dma_one = [&](auto J, int stage, int buf, auto CHECKED) {
         constexpr int j = J;
         constexpr int i = j >> 1;
         const int so = min(stage, last) * 128;
         if constexpr ((j & 1) == 0) {
-            if constexpr (!QA)
+            if constexpr (!QA) {
+                uint32_t vo = dma_a + i * row_step;
+                if constexpr (CHECKED) vo = so < kend ? vo : 0x80000000u;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs_a, (lds_void*)(lds + buf * kDStage + (32 * i + 8 * wave) * kDRow), 16,
-                    dma_a + i * row_step, so, 0, 0);
+                    rs_a, (lds_void*)(lds + buf * kDStage + (32 * i + 8 * wave) * kDRow), 16, vo, so, 0, 0);
+            }
         } else {
+            uint32_t vo = dma_b + i * row_step;
+            if constexpr (CHECKED) vo = so < kend ? vo : 0x80000000u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs_b, (lds_void*)(lds + buf * kDStage + kDOperand + (32 * i + 8 * wave) * kDRow), 16,
-                dma_b + i * row_step, so, 0, 0);
+                rs_b, (lds_void*)(lds + buf * kDStage + kDOperand + (32 * i + 8 * wave) * kDRow), 16, vo, so,
+                0, 0);
         }
+    };
+    auto dma_stage = [&](int stage, int buf, auto CHECKED) {
+        static_for<8>([&](auto J) { dma_one(J, stage, buf, CHECKED); });
     };
 
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
@@ -376,17 +389,31 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
         return (a_tensor ? sa0 : __uint_as_float(a_bits)) * (b_tensor ? sb0 : __uint_as_float(b_bits));
     };
     u32x4 nsa = u32x4{}, nsb;
-    // The stage offset goes in the scalar offset, which the range check does
-    // not cover; a per-tensor side keeps it at zero so that its loads stay
-    // inside the one-float array (the rest of the 16 bytes reads as zero).
-    auto load_scales = [&](int stage) {
+    // A full stage's four scales lie inside the tile row, and the stage offset
+    // rides in the scalar offset.  In a partial last stage (K / 32 not a
+    // multiple of 4) the four scales would reach past the row, and for the
+    // last tile row past the array: CHECKED loads put the stage offset in the
+    // range-checked VGPR offset instead, and a dwordx4 load is checked per
+    // dword, so the scales past the array read as zero without touching
+    // memory.  A per-tensor side keeps its offset at zero: its load covers the
+    // one-float array and three dwords that read as zero.
+    auto load_scales = [&](int stage, auto CHECKED) {
         const int so = min(stage, last) * 16;
         const int so_sa = a_tensor ? 0 : so;
         const int so_sb = b_tensor ? 0 : so;
-        if constexpr (!QA)
-            asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsa) : "v"(so_a), "s"(rs_sa), "s"(so_sa) : "memory");
-        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsb) : "v"(so_b), "s"(rs_sb), "s"(so_sb) : "memory");
+        if constexpr (CHECKED) {
+            const uint32_t va = so_a + so_sa, vb = so_b + so_sb;
+            if constexpr (!QA)
+                asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(nsa) : "v"(va), "s"(rs_sa) : "memory");
+            asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(nsb) : "v"(vb), "s"(rs_sb) : "memory");
+        } else {
+            if constexpr (!QA)
+                asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsa) : "v"(so_a), "s"(rs_sa), "s"(so_sa) : "memory");
+            asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(nsb) : "v"(so_b), "s"(rs_sb), "s"(so_sb) : "memory");
+        }
     };
+    constexpr std::true_type kChecked{};
+    constexpr std::false_type kUnchecked{};
 
     v16f acc[2][2];
 #pragma unroll
@@ -395,8 +422,9 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
         for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
     u32x4 fx[2][2], fy[2][2];    // [set][t]
 
-    static_for<8>([&](auto J) { dma_one(J, 0, 0); });
-    load_scales(0);
+    // the prologue's loads are checked (stage 0 or 1 may be the partial one)
+    dma_stage(0, 0, kChecked);
+    load_scales(0, kChecked);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // with QA, a second barrier: stage 0's A codes and scales are in LDS
@@ -405,11 +433,13 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
         lds_read16<t * 32 * kDRow>(fx[0][t], rd_b[0][0]);
         lds_read16<t * 32 * kDRow>(fy[0][t], rd_a[0][0]);
     });
-    static_for<8>([&](auto J) { dma_one(J, 1, 1); });
+    dma_stage(1, 1, kChecked);
 
-    // full stages run unconditionally; a partial last stage (K not a multiple
-    // of 128) is finished by the tail below
-    for (int s = 0; s < nfull; ++s) {
+    // Full stages run unconditionally; a partial last stage (K not a multiple
+    // of 128) is finished by the tail below.  A stage loads the scales of the
+    // next stage and the codes of the one after; only the last two full stages
+    // can load the partial stage, so only they run the checked loads.
+    auto run_stage = [&](int s, auto CHECKED) {
         const int cb = s & 1;
         // this stage's scales: issued one stage ago, followed by the direct
         // loads of the next stage (8 of them, 4 with QA)
@@ -423,7 +453,7 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
             if constexpr (QA) sig[k] = sa_lds[cb][k] * (b_tensor ? sb0 : __uint_as_float(cbv[k]));
             else sig[k] = sigma(ca[k], cbv[k]);
         }
-        load_scales(s + 1);
+        load_scales(s + 1, CHECKED);
 
         auto block = [&](auto KB) {
             constexpr int kb = KB;
@@ -445,7 +475,7 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
                 lds_read16<t * 32 * kDRow>(fx[(kb + 1) & 1][t], rb ? rd_b[1][nkb_] : rd_b[0][nkb_]);
                 lds_read16<t * 32 * kDRow>(fy[(kb + 1) & 1][t], rb ? rd_a[1][nkb_] : rd_a[0][nkb_]);
             });
-            if constexpr (kb == 3) static_for<8>([&](auto J) { dma_one(J, s + 2, cb); });
+            if constexpr (kb == 3) dma_stage(s + 2, cb, CHECKED);
             // the MFMAs below may only start after the prefetch is issued
             asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(g[0]), "+v"(g[1]));
             {
@@ -466,7 +496,11 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
         block(std::integral_constant<int, 1>{});
         block(std::integral_constant<int, 2>{});
         block(std::integral_constant<int, 3>{});
-    }
+    };
+    const int nfast = nfull < nst ? max(0, nfull - 2) : nfull;
+    int s0 = 0;
+    for (; s0 < nfast; ++s0) run_stage(s0, kUnchecked);
+    for (; s0 < nfull; ++s0) run_stage(s0, kChecked);
     if (nfull < nst) {
         // partial stage: its data and block-0 fragments are already in place
         const int cb = nfull & 1;

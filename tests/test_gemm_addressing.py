@@ -1,0 +1,135 @@
+"""Host-side replay of the per-tile FP8 GEMM's buffer addressing (CPU).
+
+gemm_fp8_kernel (csrc/gemm_fp8.hip) loads its operands and scales with raw
+buffer loads: a VGPR offset that the hardware range-checks against the
+resource's size (per dword for multi-dword loads) and a scalar offset that it
+does not check.  A partial last K stage ("Why grind FP8 GEMM on CDNA4",
+section 5.3: edge tiles must not read past the matrix) is where an unchecked
+scalar stage offset could reach past the end of an operand or a scale array.
+
+These tests replay, in Python, the offsets the kernel computes for every
+load of the edge tiles, apply the range check, and assert that no byte past
+the caller's buffers (A: M x K, B: N x K, scales: ceil(rows / 128) x K / 32
+floats) is touched, for ragged K.  The replay follows the kernel's launch
+order: the prologue loads stages 0 and 1 (checked), full stage s loads the
+scales of stage s + 1 and the codes of stage s + 2 (both clamped to the last
+stage), and only the last two full stages use the checked forms when a
+partial stage exists.  A second run with the checked forms switched off (the
+kernel's earlier addressing) must find the overrun, which shows the replay
+can see one.
+"""
+import pytest
+
+OOB = 0x80000000
+
+
+def _stages(K):
+    nkb = K // 32
+    nst = (nkb + 3) // 4
+    nfull = nkb // 4
+    nfast = max(0, nfull - 2) if nfull < nst else nfull
+    return nkb, nst, nfull, nfast
+
+
+def _load_schedule(K, fixed=True):
+    """(stage, checked) of every code-load group and every scale load, in order."""
+    nkb, nst, nfull, nfast = _stages(K)
+    codes = [(0, True), (1, True)]
+    scales = [(0, True)]
+    for s in range(nfull):
+        checked = fixed and s >= nfast
+        scales.append((s + 1, checked))
+        codes.append((s + 2, checked))
+    if not fixed:
+        codes = [(st, False) for st, _ in codes]
+        scales = [(st, False) for st, _ in scales]
+    return codes, scales
+
+
+def _touch(voff, soff, nbytes, records):
+    """Bytes touched by a raw buffer load of nbytes (range check per dword on
+    the VGPR offset), relative to the resource base; empty when checked out."""
+    out = []
+    for j in range(0, nbytes, 4):
+        v = (voff + j) & 0xFFFFFFFF
+        if v < records:
+            out.append(v + soff + 3)
+    return out
+
+
+def max_code_byte(rows, K, fixed=True):
+    """Largest byte offset of an operand (rows x K codes) that the direct loads touch."""
+    nkb, nst, nfull, nfast = _stages(K)
+    last = nst - 1
+    codes, _ = _load_schedule(K, fixed)
+    tiles = (rows + 127) // 128
+    worst = -1
+    for t in {0, tiles - 1}:
+        r0 = t * 128
+        rows_here = min(128, rows - r0)
+        records = rows_here * K
+        for wave in range(4):
+            for lane in range(64):
+                drow = 8 * wave + (lane >> 3)
+                dchunk = (lane & 7) ^ ((drow >> 1) & 7)
+                dma = drow * K + dchunk * 16
+                kend = K - dchunk * 16
+                for stage, checked in codes:
+                    so = min(stage, last) * 128
+                    for i in range(4):
+                        vo = dma + i * 32 * K
+                        if checked and not so < kend:
+                            vo = OOB
+                        for b in _touch(vo, so, 16, records):
+                            worst = max(worst, r0 * K + b)
+    return worst
+
+
+def max_scale_byte(rows, K, fixed=True, tensor=False):
+    """Largest byte offset of a scale array that the scale loads touch."""
+    nkb, nst, nfull, nfast = _stages(K)
+    last = nst - 1
+    _, scales = _load_schedule(K, fixed)
+    tiles = (rows + 127) // 128
+    records = 4 if tensor else tiles * nkb * 4
+    worst = -1
+    for t in {0, tiles - 1}:
+        base_v = 0 if tensor else t * nkb * 4
+        for stage, checked in scales:
+            so = 0 if tensor else min(stage, last) * 16
+            if checked:
+                touched = _touch(base_v + so, 0, 16, records)
+            else:
+                touched = _touch(base_v, so, 16, records)
+            worst = max([worst, *touched])
+    return worst
+
+
+RAGGED_K = [32, 64, 96, 128, 160, 288, 4000, 4096]
+ROWS = [128, 1000, 4096, 4100]
+
+
+@pytest.mark.parametrize("K", RAGGED_K)
+@pytest.mark.parametrize("rows", ROWS)
+def test_code_loads_stay_inside_operand(rows, K):
+    assert max_code_byte(rows, K) < rows * K
+
+
+@pytest.mark.parametrize("K", RAGGED_K)
+@pytest.mark.parametrize("rows", ROWS)
+def test_scale_loads_stay_inside_scale_array(rows, K):
+    nscale_bytes = ((rows + 127) // 128) * (K // 32) * 4
+    assert max_scale_byte(rows, K) < nscale_bytes
+    assert max_scale_byte(rows, K, tensor=True) < 4
+
+
+@pytest.mark.parametrize("K", [160, 288, 4000])
+def test_replay_finds_the_unchecked_overrun(K):
+    # the earlier addressing (stage offset unchecked in every stage) reads past
+    # the last row of the operand and past the scale array when K is ragged
+    # and the partial stage is not the first (with one stage, K = 96, the
+    # stage offset is zero and the range check alone keeps the loads inside)
+    rows = 1000
+    assert max_code_byte(rows, K, fixed=False) >= rows * K
+    if (K // 32) % 4:
+        assert max_scale_byte(rows, K, fixed=False) >= ((rows + 127) // 128) * (K // 32) * 4
