@@ -146,25 +146,40 @@ def _points(M, N, rng, n=3000):
     return ii.astype(np.int64), jj.astype(np.int64)
 
 
+def _row_tiles(M, every):
+    """Rows of every `every`-th 128-row tile of D, plus the last row."""
+    rows = [np.arange(t, min(t + 128, M)) for t in range(0, M, 128 * every)]
+    return np.unique(np.concatenate(rows + [np.array([M - 1])]))
+
+
 @pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
 def test_workload_full_size(name):
     """Every workload at its full size, in the launch configuration the benchmark
-    times: whole tiny product; sampled outputs (a full 128-row tile's worth of
-    points plus random ones and the corners) for the large ones."""
+    times, compared with the oracle on whole rows of D: all of D for the small,
+    decode-shaped and 4096-cube workloads, every 8th 128-row tile (all columns)
+    plus the last row for the feed-forward, weight-gradient and MXFP4 ones."""
     w = workloads.by_name(name)
     a, b = workloads.operands(w)
     qa, sa = oracle_quant(a, w.a_fmt)
     qb, sb = oracle_quant(b, w.b_fmt)
     say(f"{name}: oracle codes ready; GPU scaled_gemm {w.M}x{w.N}x{w.K} -> {w.out}")
     d = run_gpu_gemm(qa, sa, qb, sb, w.a_fmt, w.b_fmt, w.out, w.K)
-    if w.M * w.N <= 256 * 256:
+    every = 1 if w.M * w.N * w.K <= 4096 ** 3 else 8
+    rows = _row_tiles(w.M, every)
+    say(f"{name}: oracle on {rows.size} of {w.M} rows (every {every} row tiles)")
+    if every == 1:
         dr, sr = oracle.gemm_rows(w.a_fmt, qa, sa, w.b_fmt, qb, sb)
-        check_gemm(d, dr, sr, w.out, name)
     else:
-        rng = np.random.default_rng(w.index)
-        ii, jj = _points(w.M, w.N, rng)
-        dr, sr = oracle.gemm_points(w.a_fmt, qa, sa, w.b_fmt, qb, sb, ii, jj)
-        check_gemm(d[ii, jj], dr, sr, w.out, name)
+        # the oracle on those rows: tile-aligned slices keep their tile's scales
+        parts = []
+        for t in range(0, w.M, 128 * every):
+            r1 = min(t + 128, w.M)
+            parts.append(oracle.gemm_rows(w.a_fmt, qa, sa, w.b_fmt, qb, sb, t, r1))
+        if (w.M - 1) // 128 % every:
+            parts.append(oracle.gemm_rows(w.a_fmt, qa, sa, w.b_fmt, qb, sb, w.M - 1, w.M))
+        dr = np.concatenate([p[0] for p in parts])
+        sr = np.concatenate([p[1] for p in parts])
+    check_gemm(d[rows], dr, sr, w.out, name)
 
 
 @pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
@@ -303,3 +318,75 @@ def test_fp8_operand_beyond_32bit_offsets():
                                 128 * np.arange(ii.size), jj)
     got = from_dev(d[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()])
     check_gemm(got, dr, sr, "bf16", "A beyond 2^32 bytes")
+
+
+# ---------------------------------------------------------------- guard bands
+_GUARD_CASES = [
+    # (a_fmt, b_fmt, M, N, K, kernel exercised)
+    ("e4m3", "e4m3", 1000, 4100, 288, "per-tile FP8, ragged edges and a partial K stage"),
+    ("e5m2", "e4m3", 40, 300, 480, "skinny FP8"),
+    ("mxfp4", "mxfp4", 2088, 2072, 512, "256 x 256 MXFP4"),
+    ("mxfp4", "mxfp4", 130, 260, 288, "128 x 128 MXFP4"),
+    ("mxfp4", "mxfp4", 40, 300, 480, "skinny MXFP4"),
+]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("a_fmt,b_fmt,M,N,K,what", _GUARD_CASES)
+def test_strided_d_guard_band(a_fmt, b_fmt, M, N, K, what, out):
+    """D written into rows of N + 64 elements (ldd > N), inside a buffer
+    pre-filled with a canary: every output is checked against the oracle and
+    the 64 columns past N of every row, and two rows past M, must still hold
+    the canary (masked edge stores write nothing outside the M x N window)."""
+    import torch
+    from gpu_common import guarded, untouched
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out]
+    say(f"guard band: {what} M={M} N={N} K={K} {a_fmt}x{b_fmt} -> {out}, ldd = N + 64")
+    a = workloads.normal(M + K, M, K)
+    b = workloads.normal(N + K, N, K)
+    qa, sa = oracle_quant(a, a_fmt)
+    qb, sb = oracle_quant(b, b_fmt)
+    buf, d = guarded((M, N), dt, extra_cols=64, extra_rows=2, tail=64)
+    assert d.stride(0) == N + 64
+    bsfp8().scaled_gemm(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), a_fmt, b_fmt, out, d=d, K=K)
+    torch.cuda.synchronize()
+    assert untouched(buf, (M, N), extra_cols=64, extra_rows=2, tail=64), f"{what}: write outside D"
+    dr, sr = oracle.gemm_rows(a_fmt, qa, sa, b_fmt, qb, sb)
+    check_gemm(from_dev(d), dr, sr, out, f"guard band {what}")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_strided_d_guard_band_alpha_beta(out):
+    """The alpha / beta epilogue with ldd = ldc = N + 64 (C read from, and D
+    written into, strided rows), both inside canary-filled buffers."""
+    import torch
+    from gpu_common import guarded, untouched
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[out]
+    M, N, K = 1000, 4100, 160
+    say(f"guard band alpha/beta M={M} N={N} K={K} -> {out}")
+    a = workloads.normal(3, M, K)
+    b = workloads.normal(4, N, K)
+    c = workloads.normal(5, M, N)
+    qa, sa = oracle.fp8_quantize(a, "e4m3")
+    qb, sb = oracle.fp8_quantize(b, "e4m3")
+    dbuf, d = guarded((M, N), dt, extra_cols=64, extra_rows=1)
+    cbuf, cv = guarded((M, N), dt, extra_cols=64, extra_rows=1)
+    cv.copy_(torch.from_numpy(c).to(dt).cuda())
+    c_used = cv.float().cpu().numpy()
+    bsfp8().scaled_gemm_ex(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), "e4m3", "e4m3", out,
+                           alpha=0.5, c=cv, beta=-1.25, d=d, K=K)
+    torch.cuda.synchronize()
+    assert untouched(dbuf, (M, N), extra_cols=64, extra_rows=1), "write outside D"
+    assert untouched(cbuf, (M, N), extra_cols=64, extra_rows=1), "write into C's guard band"
+    dr, sr = oracle.gemm_rows("e4m3", qa, sa, "e4m3", qb, sb)
+    check_gemm_ex(from_dev(d), dr, sr, 0.5, -1.25, c_used, out, "guard band alpha/beta")
+
+
+@pytest.mark.parametrize("M,N,K", [(1000, 4100, 288), (1000, 4100, 4000), (640, 4608, 224),
+                                   (4100, 2049, 96)])
+def test_per_tile_ragged_k(M, N, K):
+    """The per-tile FP8 kernel with K not a multiple of 128: the partial last
+    stage (1 to 3 blocks) is loaded with range-checked offsets, so the chunks
+    and scales past K read as zero; the whole product is compared."""
+    for out in ("f32", "bf16"):
+        full_check(M, N, K, "e4m3", "e4m3", out, seed=M + 3 * N + K, label=f"ragged K {K}")

@@ -285,3 +285,86 @@ def test_fp8_quantize_pair_square_4096():
     for x, fmt, q, s in ((a, w.a_fmt, qa, sa), (b, w.b_fmt, qb, sb)):
         rq, rs = oracle.fp8_quantize(x, fmt)
         assert np.array_equal(from_dev(q), rq) and np.array_equal(from_dev(s), rs)
+
+
+# ---------------------------------------------------------------- guard bands
+@pytest.mark.parametrize("rows,k", [(200, 96), (1, 32), (129, 4128), (4100, 160)])
+def test_quantiser_guard_bands(rows, k):
+    """Codes and scales written into buffers with a canary tail of 256
+    elements after them (the scale arrays of ragged shapes end mid-tile): every
+    quantiser writes exactly its output and nothing past it, and the output is
+    byte-equal to the oracle's."""
+    import torch
+    from gpu_common import guarded, untouched
+    b = bsfp8()
+    rng = np.random.default_rng(rows + k)
+    x = (rng.standard_normal((rows, k)) * 3).astype(np.float32)
+    xd = to_dev(x)
+    T = 256
+    ntile = (rows + 127) // 128
+
+    say(f"guard bands fp8_quantize {rows}x{k}")
+    cb, codes = guarded((rows, k), torch.uint8, tail=T)
+    sbuf, scales = guarded((ntile * (k // 32),), torch.float32, tail=T)
+    b.fp8_quantize(xd, "e4m3", codes=codes, scales=scales.view(ntile, k // 32))
+    torch.cuda.synchronize()
+    assert untouched(cb, (rows, k), tail=T) and untouched(sbuf, (ntile * (k // 32),), tail=T)
+    rc, rs = oracle.fp8_quantize(x, "e4m3")
+    assert np.array_equal(from_dev(codes), rc) and np.array_equal(from_dev(scales).reshape(rs.shape), rs)
+
+    say(f"guard bands fp8_quantize_pair {rows}x{k} with {rows + 5}x{k}")
+    x2 = (rng.standard_normal((rows + 5, k))).astype(np.float32)
+    nt2 = (rows + 5 + 127) // 128
+    cb1, c1 = guarded((rows, k), torch.uint8, tail=T)
+    sb1, s1 = guarded((ntile * (k // 32),), torch.float32, tail=T)
+    cb2, c2 = guarded((rows + 5, k), torch.uint8, tail=T)
+    sb2, s2 = guarded((nt2 * (k // 32),), torch.float32, tail=T)
+    b.fp8_quantize_pair(xd, to_dev(x2), "e4m3", "e5m2", c1, s1.view(ntile, k // 32), c2,
+                        s2.view(nt2, k // 32))
+    torch.cuda.synchronize()
+    assert untouched(cb1, (rows, k), tail=T) and untouched(sb1, (ntile * (k // 32),), tail=T)
+    assert untouched(cb2, (rows + 5, k), tail=T) and untouched(sb2, (nt2 * (k // 32),), tail=T)
+    r2c, r2s = oracle.fp8_quantize(x2, "e5m2")
+    assert np.array_equal(from_dev(c1), rc) and np.array_equal(from_dev(c2), r2c)
+    assert np.array_equal(from_dev(s2).reshape(r2s.shape), r2s)
+
+    say(f"guard bands fp8_quantize_transposed {rows}x{k}")
+    cbt, ct = guarded((rows, k), torch.uint8, tail=T)
+    sbt, st = guarded((ntile * (k // 32),), torch.float32, tail=T)
+    ldt = (rows + 3) // 4 * 4      # x^T stored k x rows, rows padded to 16 bytes
+    xt = np.zeros((k, ldt), dtype=np.float32)
+    xt[:, :rows] = x.T
+    b.fp8_quantize_transposed(to_dev(xt)[:, :rows], "e4m3", codes=ct,
+                              scales=st.view(ntile, k // 32))
+    torch.cuda.synchronize()
+    assert untouched(cbt, (rows, k), tail=T) and untouched(sbt, (ntile * (k // 32),), tail=T)
+    assert np.array_equal(from_dev(ct), rc)
+
+    for gran, ns in (("row", rows), ("tensor", 1)):
+        say(f"guard bands fp8_quantize_granular {gran} {rows}x{k}")
+        cbg, cg = guarded((rows, k), torch.uint8, tail=T)
+        sbg, sg = guarded((ns,), torch.float32, tail=T)
+        b.fp8_quantize_granular(xd, "e4m3", gran, codes=cg, scales=sg)
+        torch.cuda.synchronize()
+        assert untouched(cbg, (rows, k), tail=T) and untouched(sbg, (ns,), tail=T)
+        gc, gs = oracle.fp8_quantize_granular(x, "e4m3", gran)
+        assert np.array_equal(from_dev(cg), gc) and np.array_equal(from_dev(sg).reshape(gs.shape), gs)
+
+    say(f"guard bands mxfp4_quantize {rows}x{k}")
+    pbm, pm = guarded((rows, k // 2), torch.uint8, tail=T)
+    sbm, sm = guarded((rows * (k // 32),), torch.uint8, tail=T)
+    b.mxfp4_quantize(xd, packed=pm, scales=sm.view(rows, k // 32))
+    torch.cuda.synchronize()
+    assert untouched(pbm, (rows, k // 2), tail=T) and untouched(sbm, (rows * (k // 32),), tail=T)
+    mp, ms = oracle.mxfp4_quantize(x)
+    assert np.array_equal(from_dev(pm), mp) and np.array_equal(from_dev(sm).reshape(ms.shape), ms)
+
+    say(f"guard bands mx_quantize block 8 bf16 {rows}x{k}")
+    pbx, px = guarded((rows, k // 2), torch.uint8, tail=T)
+    sbx, sx = guarded((rows * (k // 8),), torch.int16, tail=T)
+    b.mx_quantize(xd, 8, "bf16", packed=px, scales=sx.view(rows, k // 8))
+    torch.cuda.synchronize()
+    assert untouched(pbx, (rows, k // 2), tail=T) and untouched(sbx, (rows * (k // 8),), tail=T)
+    xp, xs = oracle.mx_quantize(x, 8, "bf16")
+    assert np.array_equal(from_dev(px), xp)
+    assert np.array_equal(from_dev(sx).view(np.uint16).reshape(xs.shape), xs)
