@@ -162,6 +162,9 @@ bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K, bsfp8_format 
     if (tiles > kI32Max) return BSFP8_ERR_INVALID_ARG;
     const uint8_t* a8 = static_cast<const uint8_t*>(a);
     const uint8_t* b8 = static_cast<const uint8_t*>(b);
+    // the MXFP4 kernels address a 32-row band of an operand (the skinny
+    // kernel's tile) with 32-bit byte offsets: 32 K / 2 < 2^31
+    if (path == 2 && K >= (int64_t(1) << 26)) return BSFP8_ERR_UNSUPPORTED;
     if (path == 2)
         return from_hip(bsfp8::launch_gemm_mxfp4(M, N, K, a8, static_cast<const uint8_t*>(a_scales), b8,
                                                  static_cast<const uint8_t*>(b_scales), out, d, ldd, ep,

@@ -150,7 +150,8 @@ bsfp8_status mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_t ld,
  *       its element size.
  * a, b must be 16-byte aligned.  K = 0 writes zeros.  FP8 operands need
  * K < 2^24 (the kernel addresses a 128-row band of an operand with 32-bit
- * offsets); larger K returns BSFP8_ERR_UNSUPPORTED.  M and N are limited only
+ * offsets) and MXFP4 operands K < 2^26 (a 32-row band); larger K returns
+ * BSFP8_ERR_UNSUPPORTED.  M and N are limited only
  * by the 2^31 - 1 bound on each dimension and on the number of 128 x 128 tiles.
  *
  * Accuracy: with S = sum_k |a_k b_k| (dequantised operands), every output
@@ -338,7 +339,14 @@ bsfp8_status scaled_gemm_quantize_a(int64_t M, int64_t N, int64_t K, const float
                                     void* d, int64_t ldd, uint8_t* a_codes, float* a_scales,
                                     hipStream_t stream);
 
-/* Human-readable name of a status code (static storage). */
+/*
+ * bsfp8_status_string -- the name of a status code ("BSFP8_OK", ...;
+ * "BSFP8_ERR_UNKNOWN" for a value that is not a bsfp8_status), in static
+ * storage owned by the library; never NULL.  The status values follow the
+ * check-then-run flow of the CUTLASS GEMM interface in [RUBIN-FP4] section
+ * 3.4 (can_implement, then initialize and run): every argument check happens
+ * before anything runs, and a rejected call reports why instead of running.
+ */
 const char* bsfp8_status_string(bsfp8_status s);
 
 /* Library version, (major << 16) | minor. */

@@ -30,7 +30,8 @@ def L():
 
 def test_header_declares_the_three_calls():
     names = declared_functions()
-    for n in ("fp8_quantize", "fp8_quantize_transposed", "fp8_quantize_granular", "mxfp4_quantize",
+    for n in ("fp8_quantize", "fp8_quantize_pair", "fp8_quantize_transposed", "fp8_quantize_granular",
+              "mxfp4_quantize",
               "scaled_gemm", "scaled_gemm_ex", "scaled_gemm_granular", "scaled_gemm_quantize_a",
               "mx_quantize", "scaled_gemm_mx",
               "bsfp8_status_string",
@@ -68,6 +69,37 @@ def test_fp8_quantize_argument_checks(L):
     assert q(P, 128, 64, 64, 128, 7, P, P, None) == UNSUPPORTED
     assert q(0, 0, 64, 64, 128, E4M3, 0, 0, None) == OK             # empty: nothing to do
     assert q(0, 128, 0, 0, 128, E4M3, 0, 0, None) == OK
+
+
+def test_fp8_quantize_pair_argument_checks(L):
+    # (a, a_rows, a_ld, a_fmt, a_codes, a_scales, b, b_rows, b_ld, b_fmt, b_codes, b_scales, k, stream)
+    q = L.fp8_quantize_pair
+    ok = (P, 128, 64, E4M3, P, P, P, 256, 64, E5M2, P, P, 64, None)
+
+    def call(**kw):
+        names = ["a", "a_rows", "a_ld", "a_fmt", "a_codes", "a_scales", "b", "b_rows", "b_ld",
+                 "b_fmt", "b_codes", "b_scales", "k", "stream"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return q(*[args[n] for n in names])
+
+    assert call(k=48, a_ld=48, b_ld=48) == INVALID            # k % 32
+    assert call(a_ld=32) == INVALID                            # a_ld < k
+    assert call(b_ld=32) == INVALID                            # b_ld < k
+    assert call(a_ld=66) == INVALID                            # a_ld % 4
+    assert call(a=0) == INVALID                                # null a, non-empty side
+    assert call(b_codes=0) == INVALID                          # null codes, non-empty side
+    assert call(b_scales=0) == INVALID                         # null scales, non-empty side
+    assert call(a=P + 4) == INVALID                            # a not 16-byte aligned
+    assert call(a_codes=P + 2) == INVALID                      # codes not 4-byte aligned
+    assert call(b_scales=P + 2) == INVALID                     # scales not 4-byte aligned
+    assert call(a_rows=-1) == INVALID
+    assert call(a_fmt=MXFP4) == UNSUPPORTED
+    assert call(b_fmt=9) == UNSUPPORTED
+    # a side with no rows ignores its pointers: nothing is launched for it, and
+    # with both sides empty (or k = 0) nothing at all
+    assert call(a_rows=0, b_rows=0, a=0, a_codes=0, a_scales=0, b=0, b_codes=0, b_scales=0) == OK
+    assert call(k=0, a=0, b=0, a_codes=0, b_codes=0, a_scales=0, b_scales=0) == OK
 
 
 def test_fp8_quantize_transposed_argument_checks(L):
@@ -111,6 +143,9 @@ def test_scaled_gemm_argument_checks(L):
     assert g(128, 0, 64, E4M3, 0, 0, E4M3, 0, 0, F32, 0, 0, None) == OK
     # FP8: a 128-row band of an operand must fit 32-bit offsets (K < 2^24)
     assert g(128, 128, 1 << 24, E4M3, P, P, E4M3, P, P, BF16, P, 128, None) == UNSUPPORTED
+    # MXFP4: a 32-row band must fit 32-bit byte offsets (K < 2^26)
+    assert g(64, 128, 1 << 26, MXFP4, P, P, MXFP4, P, P, BF16, P, 128, None) == UNSUPPORTED
+    assert g(64, 128, (1 << 26) + 32, MXFP4, P, P, MXFP4, P, P, BF16, P, 128, None) == UNSUPPORTED
 
 
 
