@@ -11,8 +11,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsfp8.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["api.hip", "quantize.hip", "gemm_fp8.hip", "gemm_fp8_outer.hip", "gemm_mxfp4.hip",
-           "gemm_mx.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm_fp8.hip", "gemm_fp8_big.hip", "gemm_fp8_outer.hip",
+           "gemm_mxfp4.hip", "gemm_mx.hip"]
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:

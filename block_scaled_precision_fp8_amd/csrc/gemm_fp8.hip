@@ -421,6 +421,16 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
     u32x4 fx[2][2], fy[2][2];    // [set][t]
+    // the last tile's product of the previous block, promoted during the next
+    // block (a zero product with a zero scale before the first)
+    v16f pend = v16f{};
+    float pend_sig = 0.0f;
+    auto promote = [](v16f& a, float sg, const v16f& p) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r] = fmaf(sg, p[r], a[r]);
+    };
+    // MFMA instructions per 32-wide block of the wave's four 32 x 32 tiles
+    constexpr int kMfmaPerBlock = 8;
 
     // the prologue's loads are checked (stage 0 or 1 may be the partial one)
     dma_stage(0, 0, kChecked);
@@ -478,19 +488,26 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
             if constexpr (kb == 3) dma_stage(s + 2, cb, CHECKED);
             // the MFMAs below may only start after the prefetch is issued
             asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(g[0]), "+v"(g[1]));
-            {
-                const float sig_kb = sig[kb];
+            // Software-pipelined promotion: each tile's product is promoted
+            // while the next tile's MFMAs run (the last tile's, while the
+            // next block's first MFMAs run), one MFMA then 8 FMAs, so that the
+            // matrix core and the VALU work at the same time.  Every
+            // accumulator still receives its blocks in K order.
+            const float sig_kb = sig[kb];
+            const v16f p0 = tile_product<AF, BF, OUT>(f[0], g[0]);
+            promote(acc[1][1], pend_sig, pend);
+            const v16f p1 = tile_product<AF, BF, OUT>(f[0], g[1]);
+            promote(acc[0][0], sig_kb, p0);
+            const v16f p2 = tile_product<AF, BF, OUT>(f[1], g[0]);
+            promote(acc[0][1], sig_kb, p1);
+            pend = tile_product<AF, BF, OUT>(f[1], g[1]);
+            promote(acc[1][0], sig_kb, p2);
+            pend_sig = sig_kb;
 #pragma unroll
-                for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-                    for (int tj = 0; tj < 2; ++tj) {
-                        const v16f p = tile_product<AF, BF, OUT>(f[ti], g[tj]);
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[ti][tj][r] = fmaf(sig_kb, p[r], acc[ti][tj][r]);
-                    }
+            for (int i = 0; i < kMfmaPerBlock; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 64 / kMfmaPerBlock, 0);  // then its FMAs
             }
-            // close the block: its promotions finish before the next block's reads
-            asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]));
         };
         block(std::integral_constant<int, 0>{});
         block(std::integral_constant<int, 1>{});
@@ -501,6 +518,8 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
     int s0 = 0;
     for (; s0 < nfast; ++s0) run_stage(s0, kUnchecked);
     for (; s0 < nfull; ++s0) run_stage(s0, kChecked);
+    // the last full block's pending tile
+    promote(acc[1][1], pend_sig, pend);
     if (nfull < nst) {
         // partial stage: its data and block-0 fragments are already in place
         const int cb = nfull & 1;
@@ -815,6 +834,11 @@ hipError_t launch_formats(int64_t M, int64_t N, int64_t K, int a_fmt, const uint
                           const float* a_scales, int b_fmt, const uint8_t* b, const float* b_scales,
                           int out, void* d, int64_t ldd, const Epilogue& ep, int tensor_mask,
                           const OnlineA& qa, hipStream_t stream) {
+    // problems with enough 256 x 256 tiles take the large-tile kernel (half the
+    // L2-to-LDS bytes per FLOP); the others the 128 x 128 or skinny kernels
+    if (!QA && M > kSkinnyMaxM && gemm_fp8_big_fits(M, N, K))
+        return launch_gemm_fp8_big(M, N, K, a_fmt, a, a_scales, b_fmt, b, b_scales, out, d, ldd, ep,
+                                   tensor_mask, stream);
     if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E4M3)
         return launch_typed<BSFP8_E4M3, BSFP8_E4M3, QA>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, tensor_mask, qa, stream);
     if (a_fmt == BSFP8_E4M3 && b_fmt == BSFP8_E5M2)

@@ -43,6 +43,13 @@ hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, int a_fmt, const uin
                            const float* a_scales, int b_fmt, const uint8_t* b,
                            const float* b_scales, int out, void* d, int64_t ldd,
                            const Epilogue& ep, hipStream_t stream, int tensor_mask = 0);
+// The 256 x 256-tile form of the per-tile FP8 GEMM (same arithmetic, no
+// online A); fits when the problem has enough 256 x 256 tiles to fill the chip.
+bool gemm_fp8_big_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_fp8_big(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,
+                               const float* a_scales, int b_fmt, const uint8_t* b,
+                               const float* b_scales, int out, void* d, int64_t ldd,
+                               const Epilogue& ep, int tensor_mask, hipStream_t stream);
 // FP8 operands whose scales are constant along K: a_scales[m * a_step] and
 // b_scales[n * b_step] (step 1 for per-row scales, 0 for one per tensor).
 // The skinny per-tile GEMM in its K-constant-scales form (up to 64 rows).

@@ -390,3 +390,46 @@ def test_per_tile_ragged_k(M, N, K):
     and scales past K read as zero; the whole product is compared."""
     for out in ("f32", "bf16"):
         full_check(M, N, K, "e4m3", "e4m3", out, seed=M + 3 * N + K, label=f"ragged K {K}")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("fmts,M,N,K", [
+    (("e4m3", "e4m3"), 3000, 4200, 288),      # ragged M and N, a partial K stage of one block
+    (("e5m2", "e4m3"), 4096, 3136, 224),      # a partial stage of three blocks only
+    (("e4m3", "e5m2"), 3584, 3584, 640),      # five full stages (odd count)
+])
+def test_big_tile_kernel(fmts, M, N, K, out):
+    """Shapes with at least 192 tiles of 256 x 256 run the large-tile per-tile
+    kernel (8 waves of 64 x 128); whole D against the oracle."""
+    full_check(M, N, K, fmts[0], fmts[1], out, seed=M + 5 * N + K, label="big tile")
+
+
+def test_big_tile_kernel_long_ragged_k():
+    full_check(3000, 4200, 4000, "e4m3", "e4m3", "bf16", seed=77, label="big tile K = 4000")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_big_tile_kernel_guard_band_alpha_beta(out):
+    """The large-tile kernel's general epilogue (alpha, beta * C) with D and C
+    in strided rows inside canary-filled buffers."""
+    import torch
+    from gpu_common import guarded, untouched
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[out]
+    M, N, K = 3000, 4200, 160
+    say(f"big tile guard band alpha/beta M={M} N={N} K={K} -> {out}")
+    a = workloads.normal(13, M, K)
+    b = workloads.normal(14, N, K)
+    c = workloads.normal(15, M, N)
+    qa, sa = oracle.fp8_quantize(a, "e4m3")
+    qb, sb = oracle.fp8_quantize(b, "e4m3")
+    dbuf, d = guarded((M, N), dt, extra_cols=64, extra_rows=1)
+    cbuf, cv = guarded((M, N), dt, extra_cols=64, extra_rows=1)
+    cv.copy_(torch.from_numpy(c).to(dt).cuda())
+    c_used = cv.float().cpu().numpy()
+    bsfp8().scaled_gemm_ex(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), "e4m3", "e4m3", out,
+                           alpha=-1.5, c=cv, beta=0.75, d=d, K=K)
+    torch.cuda.synchronize()
+    assert untouched(dbuf, (M, N), extra_cols=64, extra_rows=1), "write outside D"
+    assert untouched(cbuf, (M, N), extra_cols=64, extra_rows=1), "write into C's guard band"
+    dr, sr = oracle.gemm_rows("e4m3", qa, sa, "e4m3", qb, sb)
+    check_gemm_ex(from_dev(d), dr, sr, -1.5, 0.75, c_used, out, "big tile guard band alpha/beta")

@@ -189,3 +189,19 @@ def test_square_4096_row_column_scales_sampled():
     err = np.abs(d[ii, jj].astype(np.float64) - dr) / sr
     say(f"sampled max |D-Dref|/S = {err.max():.3e}")
     assert err.max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("ga,gb", [("tile", "tensor"), ("tensor", "tile")])
+def test_granular_large_tile_kernel(ga, gb, out):
+    """Per-tile with per-tensor scales on a shape with enough 256 x 256 tiles
+    for the large-tile per-tile kernel (ragged M and N, a partial K stage)."""
+    M, N, K = 3000, 4200, 160
+    say(f"scaled_gemm_granular {ga}x{gb} M={M} N={N} K={K} -> {out} (large-tile kernel)")
+    a = inputs(31, M, K)
+    b = inputs(32, N, K, "laplace")
+    qa, sa = oracle.fp8_quantize_granular(a, "e4m3", ga)
+    qb, sb = oracle.fp8_quantize_granular(b, "e5m2", gb)
+    d = run_gemm(qa, sa, ga, qb, sb, gb, "e4m3", "e5m2", out, K)
+    dr, sr = oracle.gemm_granular("e4m3", qa, sa, ga, "e5m2", qb, sb, gb)
+    check_gemm(d, dr, sr, out, f"{ga}x{gb} {M}x{N}x{K} {out} large tile")
