@@ -151,3 +151,106 @@ def dot_values(instr, xs, ys, cs, sa=None, sb=None):
     fa, fb, K = INSTR[instr]
     pad = lambda rows: [list(r) + [0.0] * (K - len(r)) for r in rows]
     return dot(instr, pack_operand(fa, pad(xs), K), pack_operand(fb, pad(ys), K), cs, sa, sb)
+
+
+# ---------------------------------------------------------------- issue rates
+# rate_probe.hip: instruction and pattern selectors of mfma_rate_launch
+R_FP8_K16, R_SCALE_FP8_K64, R_SCALE_FP4_K64, R_BF16_K16, R_FP8_16X16X32 = range(5)
+RATE_NAMES = {
+    R_FP8_K16: "v_mfma_f32_32x32x16_fp8_fp8",
+    R_SCALE_FP8_K64: "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3)",
+    R_SCALE_FP4_K64: "v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1)",
+    R_BF16_K16: "v_mfma_f32_32x32x16_bf16",
+    R_FP8_16X16X32: "v_mfma_f32_16x16x32_fp8_fp8",
+}
+P_CHAINS, P_PROMOTE, P_INTERLEAVE = 0, 1, 2
+PATTERN_NAMES = {P_CHAINS: "independent chains", P_PROMOTE: "per-block promotion",
+                 P_INTERLEAVE: "per-block promotion, interleaved"}
+
+
+def _rate_lib():
+    L = lib()
+    if not hasattr(L, "_rate_declared"):
+        vp = ctypes.c_void_p
+        L.mfma_rate_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_float, vp, vp, vp, vp]
+        L.mfma_rate_launch.restype = ctypes.c_int
+        L.mfma_rate_flops_per_iter.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.mfma_rate_flops_per_iter.restype = ctypes.c_double
+        L._rate_declared = True
+    return L
+
+
+RATE_SRC_DWORDS = 9216
+
+
+def rate_operands(instr, data, seed=7):
+    """RATE_SRC_DWORDS dwords of operand registers: random valid codes of the
+    instruction's element format, or zeros."""
+    n = RATE_SRC_DWORDS
+    if data == "zero":
+        return np.zeros(n, dtype=np.uint32)
+    g = np.random.Generator(np.random.PCG64(seed))
+    if instr == R_BF16_K16:
+        v = g.standard_normal(2 * n).astype(np.float32).view(np.uint32) >> 16
+        return (v[0::2] | (v[1::2] << 16)).astype(np.uint32)
+    if instr == R_SCALE_FP4_K64:
+        return g.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+    codes = g.integers(0, 256, size=4 * n, dtype=np.int64)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E      # no E4M3 NaN
+    return codes.astype(np.uint8).view(np.uint32).copy()
+
+
+def rate(instr, pattern=P_CHAINS, data="random", waves_per_simd=2, iters=20000, cus=None,
+         repeats=3, device="cuda:0"):
+    """Sustained rate of one pattern over the whole chip.
+
+    Launches cus * waves_per_simd workgroups of four waves (one per SIMD) and
+    returns a dict: TFLOP/s of the matrix work from the kernel's HIP-event time
+    (median of `repeats` launches after one warm-up), the shader clock from the
+    waves' s_memtime / s_memrealtime ratio (median over waves, GHz), and the
+    shader cycles per instruction that ratio implies."""
+    import torch
+
+    dev = torch.device(device)
+    if cus is None:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nwg = cus * waves_per_simd
+    src = torch.from_numpy(rate_operands(instr, data).view(np.int32).copy()).to(dev)
+    times = torch.zeros(2 * nwg * 4, dtype=torch.int64, device=dev)
+    sink = torch.zeros(nwg * 4 * 64, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    L = _rate_lib()
+    fl = L.mfma_rate_flops_per_iter(instr, pattern)
+    if fl <= 0:
+        raise ValueError("unknown instruction or pattern")
+    ms = []
+    for r in range(repeats + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = L.mfma_rate_launch(instr, pattern, nwg, iters, 1.0, src.data_ptr(), times.data_ptr(),
+                                sink.data_ptr(), stream.cuda_stream)
+        e1.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"mfma_rate_launch returned {rc}")
+        torch.cuda.synchronize(dev)
+        if r > 0:
+            ms.append(e0.elapsed_time(e1))
+    t = times.cpu().numpy().reshape(-1, 2).astype(np.float64)
+    ghz = float(np.median(t[:, 0] / np.maximum(t[:, 1], 1) * 0.1))
+    ms_med = float(np.median(ms))
+    total = fl * iters * nwg * 4
+    instr_per_iter = 4 if pattern == P_CHAINS else 4 * (4 if instr == R_FP8_16X16X32 else
+                                                       2 if instr in (R_FP8_K16, R_BF16_K16) else 1)
+    # shader cycles per instruction per SIMD, from the chip-wide rate at the
+    # measured clock (the waves of one SIMD do not start and end together, so
+    # their own loop times overstate the overlap)
+    tflops = total / (ms_med * 1e-3) / 1e12
+    flop_per_instr = fl / instr_per_iter
+    cyc_per_instr = flop_per_instr / (tflops * 1e12 / (cus * 4 * ghz * 1e9)) if tflops > 0 else 0.0
+    return {
+        "instr": RATE_NAMES[instr], "pattern": PATTERN_NAMES[pattern], "data": data,
+        "waves_per_simd": waves_per_simd, "workgroups": nwg, "iters": iters,
+        "ms": round(ms_med, 4), "tflops": round(tflops, 1),
+        "sclk_ghz": round(ghz, 3), "shader_cycles_per_instr_per_simd": round(cyc_per_instr, 2),
+    }
