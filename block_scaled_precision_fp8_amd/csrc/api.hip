@@ -142,10 +142,12 @@ bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K, bsfp8_format 
         if (a_g != BSFP8_GRAN_TILE && b_g != BSFP8_GRAN_TILE) {
             path = 1;
         } else {
-            // per-tile scales on one side: the other side may be per tile or per tensor
-            if (a_g == BSFP8_GRAN_ROW || b_g == BSFP8_GRAN_ROW) return BSFP8_ERR_UNSUPPORTED;
+            // per-tile scales on one side: the other side's scale is per tile or
+            // per tensor (in the K block product), or per row (a unit scale in the
+            // product, and the row's scale on the FP32 sum at write-back)
             path = 0;
-            tensor_mask = (a_g == BSFP8_GRAN_TENSOR ? 1 : 0) | (b_g == BSFP8_GRAN_TENSOR ? 2 : 0);
+            tensor_mask = (a_g == BSFP8_GRAN_TENSOR ? 1 : 0) | (b_g == BSFP8_GRAN_TENSOR ? 2 : 0) |
+                          (a_g == BSFP8_GRAN_ROW ? 1 | 4 : 0) | (b_g == BSFP8_GRAN_ROW ? 2 | 8 : 0);
         }
     }
     if (M < 0 || N < 0 || K < 0 || (K % 32) != 0) return BSFP8_ERR_INVALID_ARG;
@@ -154,9 +156,13 @@ bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K, bsfp8_format 
     const uintptr_t es = out == BSFP8_OUT_F32 ? 4 : 2;
     if (!d || ldd < N || !aligned(d, es)) return BSFP8_ERR_INVALID_ARG;
     if (beta != 0.0f && (!c || ldc < N || !aligned(c, es))) return BSFP8_ERR_INVALID_ARG;
-    const bsfp8::Epilogue ep{alpha, beta, beta != 0.0f ? c : nullptr, beta != 0.0f ? ldc : 0};
+    bsfp8::Epilogue ep{alpha, beta, beta != 0.0f ? c : nullptr, beta != 0.0f ? ldc : 0};
     if (K == 0) return from_hip(bsfp8::launch_fill(M, N, out, d, ldd, ep, stream));
     if (!a || !b || !a_scales || !b_scales) return BSFP8_ERR_INVALID_ARG;
+    if (path == 0) {
+        if (tensor_mask & 4) ep.row_scale = static_cast<const float*>(a_scales);
+        if (tensor_mask & 8) ep.col_scale = static_cast<const float*>(b_scales);
+    }
     if (!aligned(a, 16) || !aligned(b, 16)) return BSFP8_ERR_INVALID_ARG;
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles > kI32Max) return BSFP8_ERR_INVALID_ARG;

@@ -382,9 +382,10 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
         const_cast<float*>(sB), 0, b_tensor ? 4 : static_cast<int>(tiles_n) * nkb * 4, 0x00020000);
     const uint32_t so_a = a_tensor ? 0u : static_cast<uint32_t>(tm) * nkb * 4;
     const uint32_t so_b = b_tensor ? 0u : static_cast<uint32_t>(tn) * nkb * 4;
+    // (bit 2 / bit 3: that side's scales are per row and applied at write-back)
     float sa0 = 0.0f;
-    if constexpr (!QA) sa0 = sA[0];
-    const float sb0 = sB[0];
+    if constexpr (!QA) sa0 = (tensor_mask & 4) ? 1.0f : sA[0];
+    const float sb0 = (tensor_mask & 8) ? 1.0f : sB[0];
     auto sigma = [&](uint32_t a_bits, uint32_t b_bits) {
         return (a_tensor ? sa0 : __uint_as_float(a_bits)) * (b_tensor ? sb0 : __uint_as_float(b_bits));
     };
@@ -566,7 +567,7 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
     // bank conflicts.
     __syncthreads();
     if constexpr (OUT != BSFP8_OUT_F32) {
-        if (ep.beta == 0.0f) {
+        if (ep.beta == 0.0f && !ep.row_scale && !ep.col_scale) {
             // 16-bit output without C: alpha * acc converted while staged
             // (128 rows x 256 bytes), a store covers 4 rows
 #pragma unroll
@@ -698,7 +699,10 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_fp8_
     auto sigma = [&](int kb) {
         if (kb >= kb1) return 0.0f;
         if constexpr (OUTER) return 1.0f;
-        return (a_tensor ? sa_row[0] : sa_row[kb]) * (b_tensor ? sb_row[0] : sb_row[kb]);
+        // (bit 2 / bit 3: that side's scales are per row and applied at write-back)
+        const float sa = (tensor_mask & 4) ? 1.0f : a_tensor ? sa_row[0] : sa_row[kb];
+        const float sb = (tensor_mask & 8) ? 1.0f : b_tensor ? sb_row[0] : sb_row[kb];
+        return sa * sb;
     };
     // Loads read whole 128-byte row segments: lane l takes 16-byte piece l & 7
     // of row (l >> 3) + 8 i, so each instruction covers 8 rows x 128 bytes.

@@ -166,11 +166,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     // few VALU instructions per stage but keeps the stage one basic block
     auto dma_stage = [&](int stage, int buf, bool checked) {
         const int so = min(stage, last) * 128;
-        const bool in_k = !checked || so < kend;
+        // bit 31 set puts every chunk at or past K out of range; the empty asm
+        // keeps the compiler from turning the select into a branch per load
+        uint32_t oob = (!checked || so < kend) ? 0u : 0x80000000u;
+        asm volatile("" : "+v"(oob));
         static_for<8>([&](auto J) {
             constexpr int j = J;
             constexpr int i = j >> 1;
-            const uint32_t vo = in_k ? dma + i * row_step : 0x80000000u;
+            const uint32_t vo = (dma + i * row_step) | oob;
             lds_void* dst = (lds_void*)(lds + (j & 1) * kBOffset + buf * kOperand + (64 * i + 8 * wave) * kRow);
             __builtin_amdgcn_raw_ptr_buffer_load_lds((j & 1) ? rs_b : rs_a, dst, 16, vo, so, 0, 0);
         });
@@ -211,8 +214,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
         const_cast<float*>(sB), 0, b_tensor ? 4 : st_n * nkb * 4, 0x00020000);
     const uint32_t so_a = a_tensor ? 0u : static_cast<uint32_t>(2 * tm + (wm >> 1)) * nkb * 4;
     const uint32_t so_b = b_tensor ? 0u : static_cast<uint32_t>(2 * tn + wn) * nkb * 4;
-    const float sa0 = sA[0];
-    const float sb0 = sB[0];
+    // bit 2 (bit 3): that side's scales are per row, applied at write-back
+    const float sa0 = (tensor_mask & 4) ? 1.0f : sA[0];
+    const float sb0 = (tensor_mask & 8) ? 1.0f : sB[0];
     u32x4 nsa, nsb;
     // A full stage's four scales lie inside the tile row (stage offset in the
     // scalar offset); a partial last stage's would reach past it, so CHECKED
@@ -243,14 +247,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     u32x4 fa[2][2], fb[2];      // fa[set][t]
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+    // stage 0, its scales and stage 1 all in flight before the first wait
+    // (vmcnt counts in issue order: stage 0 and the scales are in once at
+    // most stage 1's 8 direct loads are outstanding)
     dma_stage(0, 0, true);
     load_scales(nsa, nsb, 0, true);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    dma_stage(1, 1, true);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     read_a(fa[0][0], 0, I0{}, I0{});
     read_a(fa[0][1], 0, I0{}, I1{});
     read_b(fb[0], 0, I0{}, I0{});
-    dma_stage(1, 1, true);
 
     // One stage (4 blocks of 4 groups) in LDS buffer CB (compile time); it
     // loads the scales of the next stage and the codes of the one after,
@@ -371,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     // scattered writes and the row reads free of bank conflicts.
     __syncthreads();
     if constexpr (OUT != BSFP8_OUT_F32) {
-        if (ep.beta == 0.0f) {
+        if (ep.beta == 0.0f && !ep.row_scale && !ep.col_scale) {
             // 16-bit output without C: alpha * acc converted while staged,
             // 256 rows x 512 bytes = the whole 128 KB in one pass
 #pragma unroll

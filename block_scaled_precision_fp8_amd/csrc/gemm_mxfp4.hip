@@ -357,17 +357,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     struct Frag { u32x4 x[4], y[4]; };
     Frag fr[2];
 
-    // Prologue: stage 0 into buffer 0, its first fragments into registers, and
-    // stage 1 on its way into buffer 1.
+    // Prologue: stage 0 into buffer 0 and stage 1 into buffer 1 both in flight
+    // before the first wait (vmcnt counts in issue order: stage 0 and its
+    // scales are in once at most stage 1's 16 direct loads are outstanding),
+    // then stage 0's first fragments into registers.
     dma_stage(0, 0);
     load_scales(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    dma_stage(1, 1);
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     lds_wait_barrier();
     static_for<4>([&](auto t) {
         lds_read16<t * 32 * kDmaRowBytes>(fr[0].x[t], rd_b[0][0]);
         lds_read16<t * 32 * kDmaRowBytes>(fr[0].y[t], rd_a[0][0]);
     });
-    dma_stage(1, 1);
 
     for (int s = 0; s < nst; ++s) {
         const int cb = s & 1;

@@ -29,16 +29,22 @@ hipError_t launch_mxfp4_quantize(const float* x, int64_t rows, int64_t k, int64_
 hipError_t launch_mx_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, int block,
                               int sfmt, uint8_t* packed, void* scales, hipStream_t stream);
 // The GEMM epilogue: D = alpha * (A B) + beta * C, C of D's element type.
-// beta == 0 means C is not read (c may be null).
+// beta == 0 means C is not read (c may be null).  row_scale (col_scale), when
+// set, multiplies output row m (column n) by row_scale[m] (col_scale[n]): the
+// per-row scales of an operand whose other side has per-tile scales, applied
+// to the FP32 sum at write-back (only finish_row_chunk applies them).
 struct Epilogue {
     float alpha;
     float beta;
     const void* c;
     int64_t ldc;
+    const float* row_scale = nullptr;
+    const float* col_scale = nullptr;
 };
 
 // Per-tile FP8 scales; bit 0 (bit 1) of tensor_mask marks a_scales (b_scales)
-// as one scale for the whole operand instead.
+// as one scale for the whole operand instead, and bit 2 (bit 3) with it makes
+// that scale 1 (the operand's per-row scales ride in the epilogue).
 hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, int a_fmt, const uint8_t* a,
                            const float* a_scales, int b_fmt, const uint8_t* b,
                            const float* b_scales, int out, void* d, int64_t ldd,
@@ -116,15 +122,24 @@ __device__ __forceinline__ float from_half_bits(uint16_t h) {
 }
 
 // Finish NV (4 or 8) consecutive outputs D[m][n .. n+NV-1]: v = alpha * acc
-// (+ beta * C), converted to the output type; masked at the edges, one
+// (times the row and column scales when set) (+ beta * C), converted to the output type; masked at the edges, one
 // 16-byte store when vec allows (NV = 4 for FP32, 8 for 16-bit outputs).
 template <int OUT, int NV>
 __device__ __forceinline__ void finish_row_chunk(void* D, int64_t ldd, const Epilogue& ep, int m,
                                                  int n, int M, int N, int vec, const float* acc) {
     if (m >= M) return;
     float v[NV];
+    if (ep.row_scale || ep.col_scale) {
+        const float rs = ep.row_scale ? ep.row_scale[m] : 1.0f;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = ep.alpha * acc[j];
+        for (int j = 0; j < NV; ++j) {
+            const float cs = ep.col_scale && n + j < N ? ep.col_scale[n + j] : 1.0f;
+            v[j] = ep.alpha * ((rs * cs) * acc[j]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[j] = ep.alpha * acc[j];
+    }
     const bool full = vec && n + NV <= N;
     if (ep.beta != 0.0f) {
         if constexpr (OUT == BSFP8_OUT_F32) {

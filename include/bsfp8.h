@@ -236,9 +236,13 @@ bsfp8_status fp8_quantize_granular(const float* x, int64_t rows, int64_t k, int6
  *     product multiplies the FP32 sum over all of K once, at write-back.
  *   FP8, TILE with TILE or TENSOR: the product of the two K block scales
  *     multiplies each 32-wide K block's partial sum, as in scaled_gemm.
+ *   FP8, TILE with ROW (either side): the TILE side's K block scale
+ *     multiplies each K block's partial sum, and the ROW side's scale (of the
+ *     output row for A, of the output column for B) multiplies the FP32 sum
+ *     over K at write-back.
  *   MXFP4: MX32 on both sides (as scaled_gemm).
- * Other combinations (TILE with ROW) return BSFP8_ERR_UNSUPPORTED, and so
- * does K >= 2^23 with both FP8 scales constant along K.
+ * Other combinations return BSFP8_ERR_UNSUPPORTED, and so does K >= 2^23
+ * with both FP8 scales constant along K.
  * Accuracy as for scaled_gemm_ex.
  */
 bsfp8_status scaled_gemm_granular(int64_t M, int64_t N, int64_t K,

@@ -198,8 +198,9 @@ def test_scaled_gemm_granular_argument_checks(L):
     # (M, N, K, af, a, sa, ag, bf, b, sb, bg, alpha, c, ldc, beta, out, d, ldd, stream)
     def call(ag, bg, af=E4M3, bf=E4M3, K=64, out=BF16):
         return g(128, 128, K, af, P, P, ag, bf, P, P, bg, 1.0, 0, 0, 0.0, out, P, 128, None)
-    assert call(TILE, ROW) == UNSUPPORTED          # per-row with per-tile: not built
-    assert call(ROW, TILE) == UNSUPPORTED
+    # per-row with per-tile scales is accepted: a bad K is what it rejects
+    assert call(TILE, ROW, K=48) == INVALID
+    assert call(ROW, TILE, K=48) == INVALID
     assert call(TILE, MX32) == UNSUPPORTED         # E8M0 blocks with FP8 operands
     assert call(MX32, MX32, af=MXFP4, bf=E4M3) == UNSUPPORTED
     assert call(TILE, TILE, af=MXFP4, bf=MXFP4) == UNSUPPORTED

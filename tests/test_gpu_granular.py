@@ -91,7 +91,7 @@ def run_gemm(qa, sa, ga, qb, sb, gb, a_fmt, b_fmt, out, K, alpha=1.0, c=None, be
 
 
 COMBOS = [("row", "row"), ("row", "tensor"), ("tensor", "row"), ("tensor", "tensor"),
-          ("tile", "tensor"), ("tensor", "tile")]
+          ("tile", "tensor"), ("tensor", "tile"), ("tile", "row"), ("row", "tile")]
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
@@ -126,7 +126,7 @@ def test_granular_gemm_formats(fmts):
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("ga,gb", [("row", "row"), ("tile", "tensor")])
+@pytest.mark.parametrize("ga,gb", [("row", "row"), ("tile", "tensor"), ("tile", "row"), ("row", "tile")])
 @pytest.mark.parametrize("M,N,K", [(270, 300, 192), (40, 300, 640)])   # the second: skinny kernel
 def test_granular_alpha_beta(ga, gb, out, M, N, K):
     import torch
@@ -192,10 +192,11 @@ def test_square_4096_row_column_scales_sampled():
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-@pytest.mark.parametrize("ga,gb", [("tile", "tensor"), ("tensor", "tile")])
+@pytest.mark.parametrize("ga,gb", [("tile", "tensor"), ("tensor", "tile"), ("tile", "row"), ("row", "tile")])
 def test_granular_large_tile_kernel(ga, gb, out):
-    """Per-tile with per-tensor scales on a shape with enough 256 x 256 tiles
-    for the large-tile per-tile kernel (ragged M and N, a partial K stage)."""
+    """Per-tile with per-tensor or per-row scales on a shape with enough
+    256 x 256 tiles for the large-tile per-tile kernel (ragged M and N, a
+    partial K stage)."""
     M, N, K = 3000, 4200, 160
     say(f"scaled_gemm_granular {ga}x{gb} M={M} N={N} K={K} -> {out} (large-tile kernel)")
     a = inputs(31, M, K)
