@@ -558,7 +558,12 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
                 }
         }
     }
+    // the last stage's scale loads and fragment reads may have no consumer:
+    // naming them after the wait keeps their registers from being reused
+    // while they are in flight
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("" :: "v"(nsa), "v"(nsb), "v"(fx[0][0]), "v"(fx[0][1]), "v"(fx[1][0]), "v"(fx[1][1]),
+                       "v"(fy[0][0]), "v"(fy[0][1]), "v"(fy[1][0]), "v"(fy[1][1]));
 
     // Epilogue through LDS (free now): the tile is written in the MFMA layout
     // and read back by rows, so that each 64-lane store covers whole output

@@ -370,7 +370,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
             });
         }
     }
+    // the last stage's scale loads and fragment reads may have no consumer:
+    // naming them after the wait keeps their registers from being reused
+    // while they are in flight
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("" :: "v"(nsa), "v"(nsb), "v"(fa[0][0]), "v"(fa[0][1]), "v"(fa[1][0]), "v"(fa[1][1]),
+                       "v"(fb[0]), "v"(fb[1]));
 
     // Epilogue through LDS (free now): acc[ti][tj][4 q + e] is tile element
     // (wm 64 + 32 tj + lane % 32, wn 128 + 32 ti + 8 q + 4 (lane / 32) + e).

@@ -273,8 +273,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_outer_kernel(
             }
         });
     }
-    // no direct load may still be writing LDS when the epilogue reuses it
+    // no direct load may still be writing LDS when the epilogue reuses it, and
+    // the last step's fragment reads, which have no consumer, are named after
+    // the wait so that their registers are not reused while in flight
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        asm volatile("" :: "v"(fr[q].xl[0]), "v"(fr[q].xl[1]), "v"(fr[q].xl[2]), "v"(fr[q].xl[3]),
+                           "v"(fr[q].xh[0]), "v"(fr[q].xh[1]), "v"(fr[q].xh[2]), "v"(fr[q].xh[3]));
+        asm volatile("" :: "v"(fr[q].yl[0]), "v"(fr[q].yl[1]), "v"(fr[q].yl[2]), "v"(fr[q].yl[3]),
+                           "v"(fr[q].yh[0]), "v"(fr[q].yh[1]), "v"(fr[q].yh[2]), "v"(fr[q].yh[3]));
+    }
     // MFMA results must settle before the accumulation registers are read.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),

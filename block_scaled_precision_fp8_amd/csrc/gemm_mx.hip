@@ -550,7 +550,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_big_kernel(
         big_tile::lds_wait();
         kstep(std::false_type{}, I0{}, I0{}, frg[1], frg[0], rd_a[pb][1], rd_b[pb][1]);   // (its reads are not used)
     }
+    // the last step's fragment reads have no consumer: naming them after the
+    // wait keeps their registers from being reused while they are in flight
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        asm volatile("" :: "v"(frg[q].x[0]), "v"(frg[q].x[1]), "v"(frg[q].x[2]), "v"(frg[q].x[3]),
+                           "v"(frg[q].y[0]), "v"(frg[q].y[1]), "v"(frg[q].y[2]), "v"(frg[q].y[3]));
     // MFMA results must settle before the accumulation registers are read
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
@@ -774,7 +780,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_split_big_kernel(
         stage(I1{}, s + 1);
     }
     if (s < nst) stage(I0{}, s);
+    // the last step's fragment reads have no consumer: naming them after the
+    // wait keeps their registers from being reused while they are in flight
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        asm volatile("" :: "v"(frg[q].xh[0]), "v"(frg[q].xh[1]), "v"(frg[q].xh[2]), "v"(frg[q].xh[3]),
+                           "v"(frg[q].yh[0]), "v"(frg[q].yh[1]), "v"(frg[q].yh[2]), "v"(frg[q].yh[3]));
+        asm volatile("" :: "v"(frg[q].xl[0]), "v"(frg[q].xl[1]), "v"(frg[q].xl[2]), "v"(frg[q].xl[3]),
+                           "v"(frg[q].yl[0]), "v"(frg[q].yl[1]), "v"(frg[q].yl[2]), "v"(frg[q].yl[3]));
+    }
     // MFMA results must settle before the accumulation registers are read
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),

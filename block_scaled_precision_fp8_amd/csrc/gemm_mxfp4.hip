@@ -337,6 +337,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     // no register-writing loads in the main loop: the waits for them (and for
     // the direct loads) are the explicit vmcnt waits below.
     u32x2 nsa[4], nsb[4];
+    auto load_scale = [](u32x2& dst, uint32_t vo, int so, __amdgpu_buffer_rsrc_t rs) {
+        asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen" : "=v"(dst) : "v"(vo), "s"(rs), "s"(so) : "memory");
+    };
+    // scale load q (0..7: A row q / 2 for even q, B row q / 2 for odd q) of a stage
+    auto scale_one = [&](int stage, int q) {
+        const int so = min(stage, last) * 8;
+        const int t = q >> 1;
+        if (q & 1)
+            load_scale(nsb[t], soff_b + t * srow_step, so, rs_sb);
+        else
+            load_scale(nsa[t], soff_a + t * srow_step, so, rs_sa);
+    };
     auto load_scales = [&](int stage) {
         const int so = min(stage, last) * 8;
 #pragma unroll
@@ -379,13 +391,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         uint32_t wa[4], wb[4];
         gather_scales(wa[0], wa[1], wa[2], wa[3], nsa[0], nsa[1], nsa[2], nsa[3], perm_sel);
         gather_scales(wb[0], wb[1], wb[2], wb[3], nsb[0], nsb[1], nsb[2], nsb[3], perm_sel);
-        load_scales(s + 1);
 
         // One K step (64 K values): 16 MFMAs on fragment set KS & 1 with the 8
-        // fragment reads of the next step in their shadows.  Step 3 follows the
-        // barrier that publishes stage s + 1: it reads that stage's first
-        // fragments and starts the direct loads of stage s + 2 into this
-        // stage's buffer, which no wave reads any more.
+        // fragment reads of the next step in their shadows.  Step 0 loads the
+        // scales of stage s + 1, one after each of its last 8 MFMAs (with one
+        // wave per SIMD, a burst of loads between two MFMAs leaves the matrix
+        // core idle until the loads issue).  Step 3 follows the barrier that
+        // publishes stage s + 1: it reads that stage's first fragments and
+        // starts the direct loads of stage s + 2 into this stage's buffer,
+        // which no wave reads any more.
         auto kstep = [&](auto KS) {
             constexpr int ks = KS;
             constexpr int nks = (ks + 1) & 3;
@@ -405,6 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
                     else
                         lds_read16<t * 32 * kDmaRowBytes>(g.x[t], rb_addr);
                 }
+                if constexpr (ks == 0 && j >= 8) scale_one(s + 1, j - 8);
                 if constexpr (ks == 3) dma_one(J, s + 2, cb);
             });
         };
@@ -420,8 +435,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         lds_wait_barrier();
         kstep(std::integral_constant<int, 3>{});
     }
-    // no direct load may still be writing LDS when the workgroup ends
+    // no direct load may still be writing LDS when the workgroup ends, and no
+    // register load may still be in flight when its register is reused: the
+    // last stage's scale loads and fragment reads have no consumer, so they
+    // are named after the wait to keep their registers
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("" :: "v"(fr[0].x[0]), "v"(fr[0].x[1]), "v"(fr[0].x[2]), "v"(fr[0].x[3]),
+                       "v"(fr[0].y[0]), "v"(fr[0].y[1]), "v"(fr[0].y[2]), "v"(fr[0].y[3]));
+    asm volatile("" :: "v"(fr[1].x[0]), "v"(fr[1].x[1]), "v"(fr[1].x[2]), "v"(fr[1].x[3]),
+                       "v"(fr[1].y[0]), "v"(fr[1].y[1]), "v"(fr[1].y[2]), "v"(fr[1].y[3]));
+    asm volatile("" :: "v"(nsa[0]), "v"(nsa[1]), "v"(nsa[2]), "v"(nsa[3]),
+                       "v"(nsb[0]), "v"(nsb[1]), "v"(nsb[2]), "v"(nsb[3]));
     // MFMA results must settle before the accumulation registers are read.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
