@@ -457,6 +457,279 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     big_tile::epilogue<OUT, STAGE16>(acc, lds, wave, lane, m0, n0, M, N, D, ldd, ep, vec_ok, none);
 }
 
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+// Large-tile variant for K a multiple of 32 but not of 256: the same tile and
+// MFMAs as gemm_mxfp4_big_kernel, with K staged in a ring of four 128-K
+// buffers.  Chunks (32-element blocks) past K load as zero through
+// range-checked offsets, and so do their scale bytes (a scale row of K / 32
+// bytes need not start on a 4-byte boundary: each row's 8 bytes of a 256-K step
+// are cut out of an aligned 12-byte load).  Every load is spread over the K
+// steps, at most one memory instruction after each MFMA.  On K a multiple of
+// 256 this form measured 10% slower than the two-buffer kernel (8192^3), which
+// therefore keeps those.
+//
+// Ring LDS layout: 4 buffers of 32 KB, each A then B, 256 rows of 64
+// bytes (unpadded, so that direct loads can fill them).  Row R keeps its
+// 16-byte chunk g at position g ^ ((R >> 2) & 3): the 16 lanes of a
+// fragment-read phase (16 consecutive rows, one chunk) then hit 16 distinct
+// 4-bank groups.
+constexpr int kRingRow = 64;
+constexpr int kRingOperand = 256 * kRingRow;           // 16 KB
+constexpr int kRingBuffer = 2 * kRingOperand;          // 32 KB
+constexpr int kRingLds = 4 * kRingBuffer;              // 128 KB
+
+// STAGE16: 16-bit output with beta == 0, converted while staged (one pass).
+// It is a template parameter rather than a branch on beta so that each
+// instantiation holds only one epilogue: with both, the 256 live accumulators
+// at the branch spilled to scratch.
+template <int OUT, bool STAGE16>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_ring_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
+    int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRingLds];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+
+    int tm, tn;
+    map_tile(blockIdx.x, tiles_m, tiles_n, 8, &tm, &tn);
+    const int m0 = tm * 256;
+    const int n0 = tn * 256;
+    const int kbytes = K >> 1;
+    const int nkb = K >> 5;
+    const int nh = (nkb + 3) >> 2;       // 128-K buffers, the last one partial
+    const int nss = (nkb + 7) >> 3;      // 256-K scale steps
+    const int nrounds = (nh + 3) >> 2;   // trips around the 4-buffer ring
+
+    // Direct loads: load i (0..3) of wave w fills LDS rows 64 w + 16 i .. + 15
+    // of one operand in one buffer (1 KB, 16 bytes per lane in lane order);
+    // lane l takes row 64 w + 16 i + l / 4 and the global chunk that belongs
+    // at position l % 4, whose swizzle (row >> 2) & 3 = (l >> 4) & 3 is the
+    // same for every i and w.  The row is in the range-checked VGPR offset
+    // (rows past the matrix edge load zeros), the buffer's K offset in the
+    // scalar offset; a chunk past K (block 4 h + chunk >= K / 32) gets an
+    // out-of-range VGPR offset.
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(A), 0, M * kbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(B), 0, N * kbytes, 0x00020000);
+    const int drow = 64 * wave + (lane >> 2);
+    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint32_t dma_a = static_cast<uint32_t>(m0 + drow) * kbytes + dchunk * 16;
+    const uint32_t dma_b = static_cast<uint32_t>(n0 + drow) * kbytes + dchunk * 16;
+    const uint32_t row16 = 16u * static_cast<uint32_t>(kbytes);
+    // load I (0..3 A, 4..7 B) of K buffer h into ring buffer BUF
+    auto dma_one = [&](auto I, auto BUF, int h) {
+        constexpr int q = I;
+        constexpr int buf = BUF;
+        constexpr int i = q & 3;
+        uint32_t oob = 4 * h + dchunk < nkb ? 0u : 0x80000000u;
+        asm volatile("" : "+v"(oob));
+        const uint32_t vo = ((q < 4 ? dma_a : dma_b) + i * row16) | oob;
+        lds_void* dst = (lds_void*)(lds + buf * kRingBuffer + (q < 4 ? 0 : kRingOperand) +
+                                    (64 * wave + 16 * i) * kRingRow);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 4 ? rs_a : rs_b, dst, 16, vo, h * kRingRow, 0, 0);
+    };
+
+    // Fragment reads: lane (frag_row r, half h) reads chunk 2 q + h of rows
+    // wm*128 + 32 t + r (A) and wn*128 + 32 t + r (B) for K step q (0, 1) of
+    // a buffer; t and the buffer are immediate offsets from one of two bases
+    // (buffers 0, 1 and buffers 2, 3), so that they stay below 64 KB.
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte*)lds));
+    const int frag_row = lane & 31;
+    const int half = lane >> 5;
+    const int sw = (frag_row >> 2) & 3;
+    uint32_t rd_a[2][2], rd_b[2][2];     // [hi][q]
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t pos = static_cast<uint32_t>(((2 * q + half) ^ sw) * 16);
+            rd_a[hi][q] = lds0 + hi * 2 * kRingBuffer + (wm * 128 + frag_row) * kRingRow + pos;
+            rd_b[hi][q] = lds0 + hi * 2 * kRingBuffer + kRingOperand + (wn * 128 + frag_row) * kRingRow + pos;
+        }
+
+    // Scales: this lane feeds rows wm*128 + 32 t + frag_row of A and
+    // wn*128 + 32 t + frag_row of B; 256 K cover 8 scale bytes of a row, at
+    // byte offset row * K / 32 + 8 S.  The 12 bytes from the dword below it are
+    // loaded (the whole offset range-checked: rows past the edge and steps past
+    // K read as zero) and the 8 cut out with v_alignbyte; bytes of blocks past
+    // K are cleared.
+    const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sA), 0, M * nkb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(sB), 0, N * nkb, 0x00020000);
+    const uint32_t soff_a = static_cast<uint32_t>(m0 + wm * 128 + frag_row) * nkb;
+    const uint32_t soff_b = static_cast<uint32_t>(n0 + wn * 128 + frag_row) * nkb;
+    // (the byte shift of row t, (soff + t * srow_step) & 3, is recomputed where
+    // it is used rather than kept in registers)
+    const uint32_t srow_step = 32u * static_cast<uint32_t>(nkb);
+    const uint32_t perm_sel = 0x06040200u + 0x01010101u * static_cast<uint32_t>(half);
+    u32x3 nsa[2][4], nsb[2][4];     // [256-K step parity][t]
+    auto scale_ld = [](u32x3& dst, uint32_t vo, __amdgpu_buffer_rsrc_t rs) {
+        asm volatile("buffer_load_dwordx3 %0, %1, %2, 0 offen" : "=v"(dst) : "v"(vo), "s"(rs) : "memory");
+    };
+    // the scale load of row t (A for OP 0, B for OP 1) for 256-K step S into set SET
+    auto scale_one = [&](auto OP, auto SET, int t, int S) {
+        uint32_t vo = ((OP ? soff_b : soff_a) + t * srow_step + S * 8) & ~3u;
+        vo = S < nss ? vo : 0x80000000u;
+        asm volatile("" : "+v"(vo));
+        if constexpr (OP)
+            scale_ld(nsb[SET][t], vo, rs_sb);
+        else
+            scale_ld(nsa[SET][t], vo, rs_sa);
+    };
+    // the 8 scale bytes of a row out of its 12 loaded bytes
+    auto cut8 = [](const u32x3& w, uint32_t sh) {
+        return u32x2{__builtin_amdgcn_alignbyte(w.y, w.x, sh), __builtin_amdgcn_alignbyte(w.z, w.y, sh)};
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto scales_all = [&](auto SET, int S) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            scale_one(I0{}, SET, t, S);
+            scale_one(I1{}, SET, t, S);
+        }
+    };
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+    struct Frag { u32x4 x[4], y[4]; };
+    Frag fr[2];
+
+    // Prologue: buffers 0, 1, 2 and the A half of buffer 3 in flight, with the
+    // scales of the first two 256-K steps; then buffer 0's first fragments.
+    // (vmcnt counts in issue order: buffer 0 and the first scales are in once
+    // at most the 28 loads issued after them are outstanding.)
+    static_for<8>([&](auto I) { dma_one(I, I0{}, 0); });
+    scales_all(I0{}, 0);
+    static_for<8>([&](auto I) { dma_one(I, I1{}, 1); });
+    static_for<8>([&](auto I) { dma_one(I, std::integral_constant<int, 2>{}, 2); });
+    scales_all(I1{}, 1);
+    static_for<4>([&](auto I) { dma_one(I, std::integral_constant<int, 3>{}, 3); });
+    asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
+    lds_wait_barrier();
+    static_for<4>([&](auto t) {
+        lds_read16<t * 32 * kRingRow>(fr[0].x[t], rd_b[0][0]);
+        lds_read16<t * 32 * kRingRow>(fr[0].y[t], rd_a[0][0]);
+    });
+
+    // Round r visits ring buffers 0..3 = K buffers h = 4 r .. 4 r + 3, two K
+    // steps each.  In the first K step of buffer h the B half of buffer h + 3
+    // is loaded (its ring slot, h - 1's, is free since the barrier inside
+    // h - 1), in the second the A half of buffer h + 4 (into h's own slot, free
+    // since the barrier just before); each K step also loads two scale rows of
+    // the 256-K step two ahead.  Per K step the loads issue in the order 4
+    // direct loads, 2 scale loads, so that:
+    //  * the barrier inside buffer h (publishing buffer h + 1, whose B half
+    //    was issued 4 K steps earlier) may leave 2 + 4 * 6 = 26 loads in flight;
+    //  * the scales of a 256-K step, whose last loads were issued in the last
+    //    K step two steps back, are in once at most 4 * 6 = 24 are.
+    uint32_t wa[4], wb[4];
+    for (int r = 0; r < nrounds; ++r) {
+        static_for<4>([&](auto BUF) {
+            constexpr int b = BUF;
+            constexpr int set = b >> 1;          // parity of the 256-K step
+            const int h = 4 * r + b;
+            if constexpr ((b & 1) == 0) {
+                const int S = h >> 1;
+                asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+                u32x3 ra[4], rb3[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) { ra[t] = nsa[set][t]; rb3[t] = nsb[set][t]; }
+                asm volatile("" : "+v"(ra[0]), "+v"(ra[1]), "+v"(ra[2]), "+v"(ra[3]),
+                                  "+v"(rb3[0]), "+v"(rb3[1]), "+v"(rb3[2]), "+v"(rb3[3]));
+                // bytes of blocks at or past K / 32 (the last step's) are cleared
+                const int vb = nkb - 8 * S;
+                const uint32_t mlo = vb >= 4 ? 0xFFFFFFFFu : vb <= 0 ? 0u : (1u << (8 * vb)) - 1u;
+                const uint32_t mhi = vb >= 8 ? 0xFFFFFFFFu : vb <= 4 ? 0u : (1u << (8 * (vb - 4))) - 1u;
+                u32x2 ca[4], cbv[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    ca[t] = cut8(ra[t], (soff_a + t * srow_step) & 3u);
+                    cbv[t] = cut8(rb3[t], (soff_b + t * srow_step) & 3u);
+                    ca[t].x &= mlo; ca[t].y &= mhi;
+                    cbv[t].x &= mlo; cbv[t].y &= mhi;
+                }
+                gather_scales(wa[0], wa[1], wa[2], wa[3], ca[0], ca[1], ca[2], ca[3], perm_sel);
+                gather_scales(wb[0], wb[1], wb[2], wb[3], cbv[0], cbv[1], cbv[2], cbv[3], perm_sel);
+            }
+            static_for<2>([&](auto Q) {
+                constexpr int q = Q;
+                constexpr int k = 2 * b + q;             // K step within the round
+                constexpr int ks = 2 * (b & 1) + q;      // K step within the 256-K step
+                constexpr int nb = q == 0 ? b : (b + 1) & 3;
+                constexpr int nq = q ^ 1;
+                const Frag& f = fr[k & 1];
+                Frag& g = fr[(k + 1) & 1];
+                const uint32_t ra = rd_a[nb >> 1][nq];
+                const uint32_t rb = rd_b[nb >> 1][nq];
+                constexpr int boff = (nb & 1) * kRingBuffer;
+                if constexpr (q == 0) lds_wait();
+                static_for<16>([&](auto J) {
+                    constexpr int j = J;
+                    constexpr int ti = j >> 2, tj = j & 3;
+                    mfma_fp4_sel<ks>(acc[ti][tj], f.x[ti], f.y[tj], wb[ti], wa[tj]);
+                    if constexpr ((j & 1) == 0) {
+                        constexpr int t = j >> 2;
+                        if constexpr ((j & 2) == 0)
+                            lds_read16<boff + t * 32 * kRingRow>(g.x[t], rb);
+                        else
+                            lds_read16<boff + t * 32 * kRingRow>(g.y[t], ra);
+                    } else if constexpr (j < 8) {
+                        constexpr int i = j >> 1;
+                        if constexpr (q == 0)
+                            dma_one(std::integral_constant<int, 4 + i>{}, std::integral_constant<int, (b + 3) & 3>{}, h + 3);
+                        else
+                            dma_one(std::integral_constant<int, i>{}, std::integral_constant<int, b>{}, h + 4);
+                    } else if constexpr (j == 9) {
+                        scale_one(I0{}, std::integral_constant<int, set>{}, ks, (h >> 1) + 2);
+                    } else if constexpr (j == 11) {
+                        scale_one(I1{}, std::integral_constant<int, set>{}, ks, (h >> 1) + 2);
+                    }
+                });
+                if constexpr (q == 0) {
+                    // buffer h + 1 has landed; publish it (and free buffer h)
+                    asm volatile("s_waitcnt vmcnt(26)" ::: "memory");
+                    lds_wait_barrier();
+                }
+            });
+        });
+    }
+    // no direct load may still be writing LDS when the workgroup ends, and no
+    // register load may still be in flight when its register is reused: the
+    // last K step's fragment reads and the scale loads past the end have no
+    // consumer, so they are named after the wait to keep their registers
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("" :: "v"(fr[0].x[0]), "v"(fr[0].x[1]), "v"(fr[0].x[2]), "v"(fr[0].x[3]),
+                       "v"(fr[0].y[0]), "v"(fr[0].y[1]), "v"(fr[0].y[2]), "v"(fr[0].y[3]));
+    asm volatile("" :: "v"(fr[1].x[0]), "v"(fr[1].x[1]), "v"(fr[1].x[2]), "v"(fr[1].x[3]),
+                       "v"(fr[1].y[0]), "v"(fr[1].y[1]), "v"(fr[1].y[2]), "v"(fr[1].y[3]));
+    asm volatile("" :: "v"(nsa[0][0]), "v"(nsa[0][1]), "v"(nsa[0][2]), "v"(nsa[0][3]),
+                       "v"(nsa[1][0]), "v"(nsa[1][1]), "v"(nsa[1][2]), "v"(nsa[1][3]));
+    asm volatile("" :: "v"(nsb[0][0]), "v"(nsb[0][1]), "v"(nsb[0][2]), "v"(nsb[0][3]),
+                       "v"(nsb[1][0]), "v"(nsb[1][1]), "v"(nsb[1][2]), "v"(nsb[1][3]));
+    // MFMA results must settle before the accumulation registers are read.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                   "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]),
+                   "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
+                   "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
+
+    NoScale none;
+    big_tile::epilogue<OUT, STAGE16>(acc, lds, wave, lane, m0, n0, M, N, D, ldd, ep, vec_ok, none);
+}
+
 // Skinny form (up to kSkinnyMaxM rows), as the FP8 one: one workgroup per
 // 32 x 32 output tile, the four waves split K into contiguous ranges of
 // 8-block chunks, codes are loaded as whole 128-byte row segments and staged
@@ -596,20 +869,29 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const u
     }
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
     const bool fits32 = M * (K / 2) < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31);
-    if (K % 256 == 0 && big_tiles >= kBigTileThreshold && fits32) {
+    if (big_tiles >= kBigTileThreshold && fits32) {
         const int tm = static_cast<int>((M + 255) / 256), tn = static_cast<int>((N + 255) / 256);
         const dim3 g(static_cast<uint32_t>(tm) * static_cast<uint32_t>(tn));
+        const int Mi = static_cast<int>(M), Ni = static_cast<int>(N), Ki = static_cast<int>(K);
+        // K a multiple of 256: the two-buffer kernel; other K: the ring of 128-K buffers
+        const bool two = K % 256 == 0;
         if constexpr (OUT != BSFP8_OUT_F32) {
             if (ep.beta == 0.0f) {
-                hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, true>), g, dim3(kThreads), 0, stream,
-                                   static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
-                                   a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
+                if (two)
+                    hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, true>), g, dim3(kThreads), 0, stream,
+                                       Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
+                else
+                    hipLaunchKernelGGL((gemm_mxfp4_ring_kernel<OUT, true>), g, dim3(kThreads), 0, stream,
+                                       Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
                 return hipGetLastError();
             }
         }
-        hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, false>), g, dim3(kThreads), 0, stream,
-                           static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a,
-                           a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
+        if (two)
+            hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, false>), g, dim3(kThreads), 0, stream,
+                               Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
+        else
+            hipLaunchKernelGGL((gemm_mxfp4_ring_kernel<OUT, false>), g, dim3(kThreads), 0, stream,
+                               Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
         return hipGetLastError();
     }
     const int tiles_m = static_cast<int>((M + BM - 1) / BM);

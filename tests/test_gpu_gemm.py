@@ -214,6 +214,10 @@ def test_workload_end_to_end(name):
 @pytest.mark.parametrize("fmts,M,N,K", [
     (("mxfp4", "mxfp4"), 2088, 2072, 512),     # 256 x 256 MXFP4 kernel, ragged edges
     (("mxfp4", "mxfp4"), 2048, 2048, 768),
+    (("mxfp4", "mxfp4"), 2088, 2072, 640),     # 256 x 256 ring kernel: K % 256 = 128
+    (("mxfp4", "mxfp4"), 2056, 2048, 544),     # ring kernel: K / 32 = 17, scale rows unaligned
+    (("mxfp4", "mxfp4"), 2048, 2304, 96),      # ring kernel: one partial 128-K buffer
+    (("mxfp4", "mxfp4"), 2048, 2080, 1056),    # ring kernel: a partial last trip around the ring
     (("e4m3", "e4m3"), 2088, 2072, 512),       # large-tile FP8 path, ragged edges
     (("e5m2", "e4m3"), 2048, 2080, 384),
     (("e4m3", "e4m3"), 4100, 2049, 160),       # 4 rows in the last tile row, K % 128 = 32
@@ -326,6 +330,7 @@ _GUARD_CASES = [
     ("e4m3", "e4m3", 1000, 4100, 288, "per-tile FP8, ragged edges and a partial K stage"),
     ("e5m2", "e4m3", 40, 300, 480, "skinny FP8"),
     ("mxfp4", "mxfp4", 2088, 2072, 512, "256 x 256 MXFP4"),
+    ("mxfp4", "mxfp4", 2088, 2072, 544, "256 x 256 MXFP4 ring, ragged K"),
     ("mxfp4", "mxfp4", 130, 260, 288, "128 x 128 MXFP4"),
     ("mxfp4", "mxfp4", 40, 300, 480, "skinny MXFP4"),
 ]
