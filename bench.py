@@ -138,8 +138,8 @@ def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False):
     if w.a_fmt == "mxfp4":
         big_tiles = ((w.M + 255) // 256) * ((w.N + 255) // 256)
         fits32 = w.M * (w.K // 2) < 2**31 and w.N * (w.K // 2) < 2**31
-        if w.K % 256 == 0 and big_tiles >= 64 and fits32:
-            return "gemm_mxfp4_big_kernel"
+        if big_tiles >= 64 and fits32:
+            return "gemm_mxfp4_big_kernel" if w.K % 256 == 0 else "gemm_mxfp4_ring_kernel"
         return "gemm_mxfp4_kernel"
     big_tiles = ((w.M + 255) // 256) * ((w.N + 255) // 256)
     if w.K < 2**23 and big_tiles >= 192:
