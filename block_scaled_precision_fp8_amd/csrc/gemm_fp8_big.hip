@@ -162,21 +162,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     const uint32_t dma = static_cast<uint32_t>(drow) * K + dchunk * 16;
     const uint32_t row_step = 64u * static_cast<uint32_t>(K);
     const int kend = K - dchunk * 16;
-    // checked: a partial last stage may be among the loads; the select costs a
-    // few VALU instructions per stage but keeps the stage one basic block
-    auto dma_stage = [&](int stage, int buf, bool checked) {
+    // Load J (0..7) of a stage: A for even J, B for odd, rows 64 (J / 2) + ...
+    // checked: the stage may be the partial last one; the select costs a few
+    // VALU instructions but keeps the stage one basic block.
+    auto dma_one = [&](auto J, int stage, int buf, bool checked) {
+        constexpr int j = J;
+        constexpr int i = j >> 1;
         const int so = min(stage, last) * 128;
         // bit 31 set puts every chunk at or past K out of range; the empty asm
         // keeps the compiler from turning the select into a branch per load
         uint32_t oob = (!checked || so < kend) ? 0u : 0x80000000u;
         asm volatile("" : "+v"(oob));
-        static_for<8>([&](auto J) {
-            constexpr int j = J;
-            constexpr int i = j >> 1;
-            const uint32_t vo = (dma + i * row_step) | oob;
-            lds_void* dst = (lds_void*)(lds + (j & 1) * kBOffset + buf * kOperand + (64 * i + 8 * wave) * kRow);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds((j & 1) ? rs_b : rs_a, dst, 16, vo, so, 0, 0);
-        });
+        const uint32_t vo = (dma + i * row_step) | oob;
+        lds_void* dst = (lds_void*)(lds + (j & 1) * kBOffset + buf * kOperand + (64 * i + 8 * wave) * kRow);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((j & 1) ? rs_b : rs_a, dst, 16, vo, so, 0, 0);
     };
 
     // Fragment reads: lane (frag_row r, half h) reads 16-byte chunk 2 kb + h
@@ -247,28 +246,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     u32x4 fa[2][2], fb[2];      // fa[set][t]
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    // stage 0, its scales and stage 1 all in flight before the first wait
-    // (vmcnt counts in issue order: stage 0 and the scales are in once at
-    // most stage 1's 8 direct loads are outstanding)
-    dma_stage(0, 0, true);
+    // stage 0 and its scales; stage s + 1 is loaded during stage s
+    static_for<8>([&](auto J) { dma_one(J, 0, 0, true); });
     load_scales(nsa, nsb, 0, true);
-    dma_stage(1, 1, true);
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     read_a(fa[0][0], 0, I0{}, I0{});
     read_a(fa[0][1], 0, I0{}, I1{});
     read_b(fb[0], 0, I0{}, I0{});
 
     // One stage (4 blocks of 4 groups) in LDS buffer CB (compile time); it
-    // loads the scales of the next stage and the codes of the one after,
-    // checked in the last two full stages (the only ones that can load a
-    // partial stage).  Group g multiplies B tile g with both A tiles, the
-    // tiles (g, 0) and (g, 1), while the VALU promotes the tile before each.
+    // loads the next stage's scales at its top and the next stage's codes into
+    // the other buffer, one direct load in each group of blocks 0 and 1 (a
+    // burst of loads between MFMAs holds a wave's MFMAs back; the other
+    // buffer is free since the last stage's barrier), checked in the last full
+    // stage (the only one that can load a partial stage).  Group g multiplies
+    // B tile g with both A tiles, the tiles (g, 0) and (g, 1), while the VALU
+    // promotes the tile before each.
     auto run_stage = [&](int s, auto CB, bool checked) {
         constexpr int cb = CB;
-        // this stage's scales: issued one stage ago, followed by the 8 direct
-        // loads of the next stage
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        // this stage's scales were loaded during the last stage, whose barrier
+        // waited for every load
+
         u32x4 ca = nsa, cbv = nsb;
         asm volatile("" : "+v"(ca), "+v"(cbv));
         float sig[4];
@@ -284,10 +283,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
                 constexpr int g = G;
                 u32x4& bcur = fb[g & 1];
                 if constexpr (kb == 3 && g == 3) {
-                    // the next stage's direct loads are in (only its two scale
-                    // loads may be outstanding); after the barrier every wave
-                    // is done with this stage's buffer
-                    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+                    // the next stage's codes and scales are in; after the
+                    // barrier every wave is done with this stage's buffer
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
                 } else {
                     lds_wait();
@@ -304,8 +302,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
                     read_a(fa[as ^ 1][0], 0, std::integral_constant<int, cb ^ 1>{}, I0{});
                     read_a(fa[as ^ 1][1], 0, std::integral_constant<int, cb ^ 1>{}, I1{});
                     read_b(fb[0], 0, std::integral_constant<int, cb ^ 1>{}, I0{});
-                    dma_stage(s + 2, cb, checked);
                 }
+                if constexpr (kb < 2) dma_one(std::integral_constant<int, 4 * kb + g>{}, s + 1, cb ^ 1, checked);
                 // tile (g, 0) while the previous tile is promoted, then tile
                 // (g, 1) while (g, 0) is
                 v16f& prev = acc[g == 0 ? 3 : g - 1][1];
@@ -328,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
             pend_sig = sg;
         });
     };
-    const int nfast = nfull < nst ? max(0, nfull - 2) : nfull;
+    const int nfast = nfull < nst ? nfull - 1 : nfull;
     int s0 = 0;
     for (; s0 + 1 < nfull; s0 += 2) {
         run_stage(s0, std::integral_constant<int, 0>{}, s0 >= nfast);
@@ -340,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     if (nfull < nst) {
         // partial stage (1 to 3 blocks) in buffer nfull % 2: its scales and
         // block 0's A and first B fragments are already loaded (set 0)
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         u32x4 ca = nsa, cbv = nsb;
         asm volatile("" : "+v"(ca), "+v"(cbv));
         const int nk = nkb - 4 * nfull;

@@ -133,3 +133,80 @@ def test_replay_finds_the_unchecked_overrun(K):
     assert max_code_byte(rows, K, fixed=False) >= rows * K
     if (K // 32) % 4:
         assert max_scale_byte(rows, K, fixed=False) >= ((rows + 127) // 128) * (K // 32) * 4
+
+
+# ---------------------------------------------------------------- large tiles
+# gemm_fp8_big_kernel (csrc/gemm_fp8_big.hip): 256-row operand bands, 8 waves;
+# load j (0..7) of wave w covers rows 64 (j / 2) + 8 w + lane / 8 of A (even j)
+# or B (odd j).  Stage 0 is loaded (checked) before the loop; full stage s loads
+# the codes and scales of stage s + 1 (clamped to the last stage), checked in
+# the last full stage when a partial stage follows.
+def _big_schedule(K, fixed=True):
+    nkb, nst, nfull, _ = _stages(K)
+    nfast = nfull - 1 if nfull < nst else nfull
+    loads = [(0, True)] + [(s + 1, fixed and s >= nfast) for s in range(nfull)]
+    if not fixed:
+        loads = [(st, False) for st, _ in loads]
+    return loads
+
+
+def max_code_byte_big(rows, K, fixed=True):
+    nkb, nst, _, _ = _stages(K)
+    last = nst - 1
+    tiles = (rows + 255) // 256
+    worst = -1
+    for t in {0, tiles - 1}:
+        r0 = t * 256
+        records = min(256, rows - r0) * K
+        for wave in range(8):
+            for lane in range(64):
+                drow = 8 * wave + (lane >> 3)
+                dchunk = (lane & 7) ^ ((drow >> 1) & 7)
+                dma = drow * K + dchunk * 16
+                kend = K - dchunk * 16
+                for stage, checked in _big_schedule(K, fixed):
+                    so = min(stage, last) * 128
+                    for i in range(4):
+                        vo = dma + i * 64 * K
+                        if checked and not so < kend:
+                            vo |= OOB
+                        for b in _touch(vo, so, 16, records):
+                            worst = max(worst, r0 * K + b)
+    return worst
+
+
+def max_scale_byte_big(rows, K, fixed=True):
+    nkb, nst, _, _ = _stages(K)
+    last = nst - 1
+    st_rows = (rows + 127) // 128
+    records = st_rows * nkb * 4
+    worst = -1
+    for t in {0, (rows + 255) // 256 - 1}:
+        for half in (0, 1):
+            so_a = (2 * t + half) * nkb * 4
+            for stage, checked in _big_schedule(K, fixed):
+                so = min(stage, last) * 16
+                if checked:
+                    touched = _touch(so_a + so, 0, 16, records)
+                else:
+                    touched = _touch(so_a, so, 16, records)
+                worst = max([worst, *touched])
+    return worst
+
+
+@pytest.mark.parametrize("K", RAGGED_K)
+@pytest.mark.parametrize("rows", ROWS)
+def test_big_tile_code_loads_stay_inside_operand(rows, K):
+    assert max_code_byte_big(rows, K) < rows * K
+
+
+@pytest.mark.parametrize("K", RAGGED_K)
+@pytest.mark.parametrize("rows", ROWS)
+def test_big_tile_scale_loads_stay_inside_scale_array(rows, K):
+    assert max_scale_byte_big(rows, K) < ((rows + 127) // 128) * (K // 32) * 4
+
+
+@pytest.mark.parametrize("K", [160, 288, 4000])
+def test_big_tile_replay_finds_the_unchecked_overrun(K):
+    rows = 1000
+    assert max_code_byte_big(rows, K, fixed=False) >= rows * K
