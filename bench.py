@@ -316,7 +316,7 @@ def main():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-gflop", type=float, default=150.0,
+    p.add_argument("--cpu-sample-gflop", type=float, default=650.0,
                    help="oracle product work to time (whole 128-row tiles spread over A)")
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--mfma-rates", action="store_true",
