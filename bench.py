@@ -128,7 +128,11 @@ def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False):
     launchers' selection)."""
     skinny = w.M <= 64 or ((w.M + 127) // 128) * ((w.N + 127) // 128) < 32
     if mx_variant:
-        return "gemm_mx_skinny_kernel" if skinny else "gemm_mx_kernel"
+        if skinny:
+            return "gemm_mx_skinny_kernel"
+        if ((w.M + 255) // 256) * ((w.N + 255) // 256) >= 128:
+            return "gemm_mx_split_big_kernel" if mx_variant == "wide" else "gemm_mx_big_kernel"
+        return "gemm_mx_kernel"
     if online:
         return "gemm_fp8_kernel (A quantised by quantiser waves)"
     if w.a_fmt != "mxfp4" and gran != "tile":
@@ -371,6 +375,7 @@ def main():
         print("bench.py: the token-major layout is quantised with per-tile scales only", file=sys.stderr)
         sys.exit(2)
     mxv = mx and (args.mx_block != 32 or args.mx_scale != "e8m0")
+    mx_kind = ("wide" if args.mx_scale != "e8m0" else "e8m0") if mxv else False
     if not mx and (args.mx_block != 32 or args.mx_scale != "e8m0"):
         print("bench.py: --mx-block / --mx-scale apply to the MXFP4 workload", file=sys.stderr)
         sys.exit(2)
@@ -493,7 +498,7 @@ def main():
 
     in_type = "bf16" if mxv else ("fp4" if mx else "fp8")
     gemm_tflops = w.flops / (gemm_ms * 1e-3) / 1e12
-    kname = gemm_kernel_name(w, gran, online, mxv)
+    kname = gemm_kernel_name(w, gran, online, mx_kind)
     src = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc",
                        "gemm_mx.hip" if mxv else "gemm_mxfp4.hip" if mx else
                        "gemm_fp8_big.hip" if kname == "gemm_fp8_big_kernel" else
@@ -517,11 +522,11 @@ def main():
     gbytes = gemm_bytes(w, gran, args.mx_block, args.mx_scale, mx)
     if w.flops / gbytes < PEAK_TFLOPS[in_type] * 1e12 / (HBM_GBPS * 1e9):
         gemm_gbps = gbytes / (gemm_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "kernel": gemm_kernel_name(w, gran, online, mxv),
+        roofline = {"bound": "hbm", "kernel": gemm_kernel_name(w, gran, online, mx_kind),
                     "achieved": round(gemm_gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
                     "frac": round(gemm_gbps / HBM_GBPS, 4), "algorithmic_bytes": gbytes}
     else:
-        roofline = {"bound": "mfma", "kernel": gemm_kernel_name(w, gran, online, mxv),
+        roofline = {"bound": "mfma", "kernel": gemm_kernel_name(w, gran, online, mx_kind),
                     "achieved": round(gemm_tflops, 1), "peak": PEAK_TFLOPS[in_type], "unit": "TFLOP/s",
                     "frac": round(gemm_tflops / PEAK_TFLOPS[in_type], 4),
                     "algorithmic_flops": w.flops}
