@@ -222,6 +222,10 @@ __device__ __forceinline__ void mfma_fp4_sel(v16f& acc, const u32x4& x, const u3
 // 2 ks + half of the stage's 8 blocks) into byte ks of one register.  The
 // trailing wait states cover the VALU-write to MFMA-read dependency.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int OFF>
+__device__ __forceinline__ void lds_read8(u32x2& v, uint32_t addr) {
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
 __device__ __forceinline__ void gather_scales(uint32_t& w0, uint32_t& w1, uint32_t& w2, uint32_t& w3,
                                               const u32x2& s0, const u32x2& s1, const u32x2& s2,
                                               const u32x2& s3, uint32_t sel) {
@@ -246,6 +250,12 @@ constexpr int kDmaOperandBytes = 256 * kDmaRowBytes;     // 32 KB
 constexpr int kDmaStageBytes = 2 * kDmaOperandBytes;     // 64 KB
 constexpr int kDmaLdsBytes = 2 * kDmaStageBytes;         // 128 KB
 typedef __attribute__((address_space(3))) void lds_void;
+// The large-tile kernel's scales go through LDS as well, after the codes: a
+// period of 4 stages (1024 K) takes 32 scale bytes of each of the tile's 256
+// A rows and 256 B rows, 16 KB, in two buffers (160 KB of LDS in all).
+constexpr int kScalePeriodBytes = 16 * 1024;
+constexpr int kScaleLdsOffset = kDmaLdsBytes;
+constexpr int kBigLdsBytes = kDmaLdsBytes + 2 * kScalePeriodBytes;
 
 // STAGE16: 16-bit output with beta == 0, converted while staged (one pass).
 // It is a template parameter rather than a branch on beta so that each
@@ -256,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
     int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kDmaLdsBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigLdsBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -324,40 +334,58 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         }
 
     // Scales: this lane feeds rows wm*128 + 32 t + frag_row of A and
-    // wn*128 + 32 t + frag_row of B; a stage covers 8 scale blocks per row.
+    // wn*128 + 32 t + frag_row of B; a stage covers 8 scale blocks (bytes) per
+    // row.  A scale row of K / 32 bytes holds a whole 16-byte load only every
+    // few rows, and a load into registers of one lane's 8 bytes touches 32 rows
+    // (32 cache lines) per instruction, which holds the single wave per SIMD
+    // back for long.  So the scales are staged in LDS by direct loads of 32
+    // rows x 32 bytes (a period of 4 stages), one per wave and stage, a period
+    // ahead of use, and read with ds_read_b64.  Load j (0..15) of a period
+    // covers operand j / 8 (A, then B), rows 32 (j % 8) .. + 31 of the tile;
+    // lane l brings 16 bytes, half l / 32 of the period's 32 bytes of row
+    // l % 32, and lands at (l / 32) * 512 + (l % 32) * 16 of the load's 1 KB.
+    // Offsets are range-checked (VGPR offset only): rows past M or N and bytes
+    // past the scale array read as zero, bytes past a row's end read the next
+    // row and are never used.
     const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(sA), 0, M * nkb, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(sB), 0, N * nkb, 0x00020000);
-    const uint32_t soff_a = static_cast<uint32_t>(m0 + wm * 128 + frag_row) * nkb;
-    const uint32_t soff_b = static_cast<uint32_t>(n0 + wn * 128 + frag_row) * nkb;
     const uint32_t srow_step = 32u * static_cast<uint32_t>(nkb);
+    const int lastp = (nst - 1) >> 2;
+    // this wave's loads q = 0..3 of a period are j = 4 wave + q: operand
+    // wave / 2, rows 128 (wave % 2) + 32 q + lane % 32
+    const uint32_t sdma = static_cast<uint32_t>((wave < 2 ? m0 : n0) + 128 * (wave & 1) + (lane & 31)) * nkb +
+                          (lane >> 5) * 16;
+    auto scale_dma = [&](int period, int q) {
+        const uint32_t vo = sdma + q * srow_step + min(period, lastp) * 32;
+        lds_void* dst = (lds_void*)(lds + kScaleLdsOffset + (period & 1) * kScalePeriodBytes +
+                                    (4 * wave + q) * 1024);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 2 ? rs_sa : rs_sb, dst, 16, vo, 0, 0, 0);
+    };
+    // reads of a stage's scales: A tile t is load j = 4 wm + t, B tile t is
+    // j = 8 + 4 wn + t; the stage's buffer, half and 8-byte word are added per
+    // stage, t is an immediate offset
+    const uint32_t srd_a = lds0 + kScaleLdsOffset + (4 * wm) * 1024 + frag_row * 16;
+    const uint32_t srd_b = lds0 + kScaleLdsOffset + (8 + 4 * wn) * 1024 + frag_row * 16;
     const uint32_t perm_sel = 0x06040200u + 0x01010101u * static_cast<uint32_t>(half);
-    // Scale loads are issued as assembly as well, so that the compiler tracks
-    // no register-writing loads in the main loop: the waits for them (and for
-    // the direct loads) are the explicit vmcnt waits below.
     u32x2 nsa[4], nsb[4];
-    auto load_scale = [](u32x2& dst, uint32_t vo, int so, __amdgpu_buffer_rsrc_t rs) {
-        asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen" : "=v"(dst) : "v"(vo), "s"(rs), "s"(so) : "memory");
+    auto read_scales = [&](int stage) {
+        const uint32_t so = ((stage >> 2) & 1) * kScalePeriodBytes + ((stage >> 1) & 1) * 512 + (stage & 1) * 8;
+        const uint32_t ra = srd_a + so, rb = srd_b + so;
+        static_for<4>([&](auto T) {
+            constexpr int t = T;
+            lds_read8<t * 1024>(nsa[t], ra);
+            lds_read8<t * 1024>(nsb[t], rb);
+        });
     };
-    // scale load q (0..7: A row q / 2 for even q, B row q / 2 for odd q) of a stage
-    auto scale_one = [&](int stage, int q) {
-        const int so = min(stage, last) * 8;
-        const int t = q >> 1;
-        if (q & 1)
-            load_scale(nsb[t], soff_b + t * srow_step, so, rs_sb);
+    // scale read T (0..7: A tile T / 2 for even T, B tile T / 2 for odd T) of a stage
+    auto read_scale_one = [&](uint32_t ra, uint32_t rb, auto T) {
+        constexpr int t = T;
+        if constexpr (t & 1)
+            lds_read8<(t >> 1) * 1024>(nsb[t >> 1], rb);
         else
-            load_scale(nsa[t], soff_a + t * srow_step, so, rs_sa);
-    };
-    auto load_scales = [&](int stage) {
-        const int so = min(stage, last) * 8;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
-                         : "=v"(nsa[t]) : "v"(soff_a + t * srow_step), "s"(rs_sa), "s"(so) : "memory");
-            asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
-                         : "=v"(nsb[t]) : "v"(soff_b + t * srow_step), "s"(rs_sb), "s"(so) : "memory");
-        }
+            lds_read8<(t >> 1) * 1024>(nsa[t >> 1], ra);
     };
 
     v16f acc[4][4];
@@ -369,12 +397,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     struct Frag { u32x4 x[4], y[4]; };
     Frag fr[2];
 
-    // Prologue: stage 0 into buffer 0 and stage 1 into buffer 1 both in flight
-    // before the first wait (vmcnt counts in issue order: stage 0 and its
-    // scales are in once at most stage 1's 16 direct loads are outstanding),
-    // then stage 0's first fragments into registers.
+    // Prologue: stage 0 into buffer 0, the first period's scales and stage 1
+    // into buffer 1 all in flight before the first wait (vmcnt counts in issue
+    // order: stage 0 and the scales are in once at most stage 1's 16 direct
+    // loads are outstanding), then stage 0's first fragments and scales into
+    // registers.
     dma_stage(0, 0);
-    load_scales(0);
+    static_for<4>([&](auto q) { scale_dma(0, q); });
     dma_stage(1, 1);
     asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     lds_wait_barrier();
@@ -382,24 +411,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         lds_read16<t * 32 * kDmaRowBytes>(fr[0].x[t], rd_b[0][0]);
         lds_read16<t * 32 * kDmaRowBytes>(fr[0].y[t], rd_a[0][0]);
     });
+    read_scales(0);
 
     for (int s = 0; s < nst; ++s) {
         const int cb = s & 1;
-        // this stage's scales were loaded one stage ago; only the 16 direct
-        // loads issued since may still be in flight
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        // this stage's scales and first fragments were read during the last
+        // stage's step 3 (or the prologue)
+        lds_wait();
         uint32_t wa[4], wb[4];
         gather_scales(wa[0], wa[1], wa[2], wa[3], nsa[0], nsa[1], nsa[2], nsa[3], perm_sel);
         gather_scales(wb[0], wb[1], wb[2], wb[3], nsb[0], nsb[1], nsb[2], nsb[3], perm_sel);
+        // stage s + 1's scale reads (step 3): its buffer, half and word
+        const int s1 = s + 1;
+        const uint32_t sso = ((s1 >> 2) & 1) * kScalePeriodBytes + ((s1 >> 1) & 1) * 512 + (s1 & 1) * 8;
+        const uint32_t sra = srd_a + sso, srb = srd_b + sso;
 
         // One K step (64 K values): 16 MFMAs on fragment set KS & 1 with the 8
-        // fragment reads of the next step in their shadows.  Step 0 loads the
-        // scales of stage s + 1, one after each of its last 8 MFMAs (with one
-        // wave per SIMD, a burst of loads between two MFMAs leaves the matrix
-        // core idle until the loads issue).  Step 3 follows the barrier that
-        // publishes stage s + 1: it reads that stage's first fragments and
-        // starts the direct loads of stage s + 2 into this stage's buffer,
-        // which no wave reads any more.
+        // fragment reads of the next step in their shadows.  Step 0 issues this
+        // wave's share of the next period's scales (one direct load after its
+        // ninth MFMA: with one wave per SIMD, a burst of loads between two
+        // MFMAs leaves the matrix core idle until the loads issue).  Step 3
+        // follows the barrier that publishes stage s + 1: it reads that
+        // stage's first fragments and scales and starts the direct loads of
+        // stage s + 2 into this stage's buffer, which no wave reads any more.
         auto kstep = [&](auto KS) {
             constexpr int ks = KS;
             constexpr int nks = (ks + 1) & 3;
@@ -418,20 +452,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
                         lds_read16<t * 32 * kDmaRowBytes>(g.y[t], ra_addr);
                     else
                         lds_read16<t * 32 * kDmaRowBytes>(g.x[t], rb_addr);
+                } else if constexpr (ks == 3) {
+                    read_scale_one(sra, srb, std::integral_constant<int, j - 8>{});
                 }
-                if constexpr (ks == 0 && j >= 8) scale_one(s + 1, j - 8);
+                if constexpr (ks == 0 && j == 8) scale_dma((s >> 2) + 1, s & 3);
                 if constexpr (ks == 3) dma_one(J, s + 2, cb);
             });
         };
-        lds_wait();
         kstep(std::integral_constant<int, 0>{});
         lds_wait();
         kstep(std::integral_constant<int, 1>{});
         lds_wait();
         kstep(std::integral_constant<int, 2>{});
-        // stage s + 1 has landed (only the 8 scale loads issued since may be
-        // outstanding); publish it
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        // stage s + 1 has landed, and so has this stage's scale load: publish
+        // them (the last reads of the scale buffer that the next period's
+        // loads refill were waited for before an earlier barrier)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_wait_barrier();
         kstep(std::integral_constant<int, 3>{});
     }

@@ -213,7 +213,9 @@ def test_workload_end_to_end(name):
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("fmts,M,N,K", [
     (("mxfp4", "mxfp4"), 2088, 2072, 512),     # 256 x 256 MXFP4 kernel, ragged edges
-    (("mxfp4", "mxfp4"), 2048, 2048, 768),
+    (("mxfp4", "mxfp4"), 2048, 2048, 768),     # scales: one partial 4-stage period, rows 8-byte aligned
+    (("mxfp4", "mxfp4"), 2056, 2048, 1280),    # scales: a second period of one stage
+    (("mxfp4", "mxfp4"), 2048, 2064, 2304),    # scales: two full periods and one stage
     (("mxfp4", "mxfp4"), 2088, 2072, 640),     # 256 x 256 ring kernel: K % 256 = 128
     (("mxfp4", "mxfp4"), 2056, 2048, 544),     # ring kernel: K / 32 = 17, scale rows unaligned
     (("mxfp4", "mxfp4"), 2048, 2304, 96),      # ring kernel: one partial 128-K buffer
