@@ -204,8 +204,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_kernel(
 // fragments of 1 KB per wave for 16 MFMAs, half the LDS traffic per FLOP of
 // the 128 x 128 tiling; the 256-wide edge halves the L2 traffic per FLOP.
 // Codes go straight from global memory to LDS (direct loads, rows past the
-// matrix edge read as zero) one stage ahead of use; the E8M0 scales arrive in
-// registers by buffer loads, also one stage ahead.
+// matrix edge read as zero) one stage ahead of use; the E8M0 scales go the
+// same way a period of 4 stages ahead, into 32 KB of LDS beside the codes.
 // ---------------------------------------------------------------------------
 
 // E2M1 x E2M1 MFMA with E8M0 block scales; byte SEL of each scale register is used.
@@ -397,15 +397,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     struct Frag { u32x4 x[4], y[4]; };
     Frag fr[2];
 
-    // Prologue: stage 0 into buffer 0, the first period's scales and stage 1
+    // Prologue: stage 0 into buffer 0, the first period's scales and the
+    // first half of stage 1 (loads 0..7; stage 0's step 0 issues the rest)
     // into buffer 1 all in flight before the first wait (vmcnt counts in issue
-    // order: stage 0 and the scales are in once at most stage 1's 16 direct
+    // order: stage 0 and the scales are in once at most stage 1's 8 direct
     // loads are outstanding), then stage 0's first fragments and scales into
     // registers.
     dma_stage(0, 0);
     static_for<4>([&](auto q) { scale_dma(0, q); });
-    dma_stage(1, 1);
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    static_for<8>([&](auto J) { dma_one(J, 1, 1); });
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     lds_wait_barrier();
     static_for<4>([&](auto t) {
         lds_read16<t * 32 * kDmaRowBytes>(fr[0].x[t], rd_b[0][0]);
@@ -427,13 +428,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         const uint32_t sra = srd_a + sso, srb = srd_b + sso;
 
         // One K step (64 K values): 16 MFMAs on fragment set KS & 1 with the 8
-        // fragment reads of the next step in their shadows.  Step 0 issues this
-        // wave's share of the next period's scales (one direct load after its
-        // ninth MFMA: with one wave per SIMD, a burst of loads between two
-        // MFMAs leaves the matrix core idle until the loads issue).  Step 3
-        // follows the barrier that publishes stage s + 1: it reads that
-        // stage's first fragments and scales and starts the direct loads of
-        // stage s + 2 into this stage's buffer, which no wave reads any more.
+        // fragment reads of the next step in their shadows.  Step 3 follows
+        // the barrier that publishes stage s + 1: it reads that stage's first
+        // fragments and scales and issues the first 8 direct loads of stage
+        // s + 2 into this stage's buffer, which no wave reads any more; step 0
+        // of the next stage issues the other 8, and this wave's share of the
+        // next period's scales.  With one wave per SIMD, a memory instruction
+        // between two MFMAs holds the matrix core until it issues, and the
+        // loads back up once they ask more of L2 than it delivers to a CU: one
+        // direct load after every second MFMA, over two steps, keeps a stage's
+        // 64 KB under that rate (16 loads in one step measured 5-7% slower).
         auto kstep = [&](auto KS) {
             constexpr int ks = KS;
             constexpr int nks = (ks + 1) & 3;
@@ -456,7 +460,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
                     read_scale_one(sra, srb, std::integral_constant<int, j - 8>{});
                 }
                 if constexpr (ks == 0 && j == 8) scale_dma((s >> 2) + 1, s & 3);
-                if constexpr (ks == 3) dma_one(J, s + 2, cb);
+                if constexpr (ks == 3 && (j & 1)) dma_one(std::integral_constant<int, (j >> 1)>{}, s + 2, cb);
+                if constexpr (ks == 0 && (j & 1))
+                    dma_one(std::integral_constant<int, (8 + (j >> 1))>{}, s + 1, cb ^ 1);
             });
         };
         kstep(std::integral_constant<int, 0>{});
@@ -464,9 +470,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         kstep(std::integral_constant<int, 1>{});
         lds_wait();
         kstep(std::integral_constant<int, 2>{});
-        // stage s + 1 has landed, and so has this stage's scale load: publish
-        // them (the last reads of the scale buffer that the next period's
-        // loads refill were waited for before an earlier barrier)
+        // stage s + 1 has landed (its second half was issued in step 0), and
+        // so has this stage's scale load: publish them (the last reads of the
+        // scale buffer that the next period's loads refill were waited for
+        // before an earlier barrier)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_wait_barrier();
         kstep(std::integral_constant<int, 3>{});
