@@ -141,6 +141,19 @@ __device__ __forceinline__ v16f tile_product(const u32x4& x, const u32x4& y) {
     }
     return p;
 }
+// Half H of tile_product for 16-bit outputs: the instruction over K 16 H ..
+// 16 H + 15 of the block, accumulating into p.
+template <int AF, int BF, int H>
+__device__ __forceinline__ v16f product_half(const u32x4& x, const u32x4& y, v16f p) {
+    const uint64_t xv = static_cast<uint64_t>(x[2 * H]) | (static_cast<uint64_t>(x[2 * H + 1]) << 32);
+    const uint64_t yv = static_cast<uint64_t>(y[2 * H]) | (static_cast<uint64_t>(y[2 * H + 1]) << 32);
+    return mfma_codes<AF, BF>(xv, yv, p);
+}
+template <int H>
+__device__ __forceinline__ void promote_half(v16f& a, float sg, const v16f& p) {
+#pragma unroll
+    for (int r = 8 * H; r < 8 * H + 8; ++r) a[r] = fmaf(sg, p[r], a[r]);
+}
 
 // QA: the A operand arrives in FP32 and is quantised inside the kernel on its
 // way to LDS ("Why grind FP8 GEMM on CDNA4", section 4.2 converts and scales
@@ -495,20 +508,46 @@ __global__ __launch_bounds__(QA ? kQThreads : kThreads, QA ? 1 : 2) void gemm_fp
             // matrix core and the VALU work at the same time.  Every
             // accumulator still receives its blocks in K order.
             const float sig_kb = sig[kb];
-            const v16f p0 = tile_product<AF, BF, OUT>(f[0], g[0]);
-            promote(acc[1][1], pend_sig, pend);
-            const v16f p1 = tile_product<AF, BF, OUT>(f[0], g[1]);
-            promote(acc[0][0], sig_kb, p0);
-            const v16f p2 = tile_product<AF, BF, OUT>(f[1], g[0]);
-            promote(acc[0][1], sig_kb, p1);
-            pend = tile_product<AF, BF, OUT>(f[1], g[1]);
-            promote(acc[1][0], sig_kb, p2);
-            pend_sig = sig_kb;
+            if constexpr (OUT == BSFP8_OUT_F32) {
+                const v16f p0 = tile_product<AF, BF, OUT>(f[0], g[0]);
+                promote(acc[1][1], pend_sig, pend);
+                const v16f p1 = tile_product<AF, BF, OUT>(f[0], g[1]);
+                promote(acc[0][0], sig_kb, p0);
+                const v16f p2 = tile_product<AF, BF, OUT>(f[1], g[0]);
+                promote(acc[0][1], sig_kb, p1);
+                pend = tile_product<AF, BF, OUT>(f[1], g[1]);
+                promote(acc[1][0], sig_kb, p2);
 #pragma unroll
-            for (int i = 0; i < kMfmaPerBlock; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 64 / kMfmaPerBlock, 0);  // then its FMAs
+                for (int i = 0; i < kMfmaPerBlock; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 64 / kMfmaPerBlock, 0);  // then its FMAs
+                }
+            } else {
+                // the same order fixed by scheduling barriers: left free, the
+                // compiler placed FMAs right behind the MFMA whose result they
+                // read, holding the wave's next MFMA back
+                // tile product q of x, y while the previous tile's product pp
+                // is promoted into pa
+                auto tile_slots = [&](v16f& q, const u32x4& x, const u32x4& y, v16f& pa, float ps,
+                                      const v16f& pp) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    q = product_half<AF, BF, 0>(x, y, v16f{});
+                    __builtin_amdgcn_sched_barrier(0);
+                    promote_half<0>(pa, ps, pp);
+                    __builtin_amdgcn_sched_barrier(0);
+                    q = product_half<AF, BF, 1>(x, y, q);
+                    __builtin_amdgcn_sched_barrier(0);
+                    promote_half<1>(pa, ps, pp);
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                v16f q0, q1, q2, q3;
+                tile_slots(q0, f[0], g[0], acc[1][1], pend_sig, pend);
+                tile_slots(q1, f[0], g[1], acc[0][0], sig_kb, q0);
+                tile_slots(q2, f[1], g[0], acc[0][1], sig_kb, q1);
+                tile_slots(q3, f[1], g[1], acc[1][0], sig_kb, q2);
+                pend = q3;
             }
+            pend_sig = sig_kb;
         };
         block(std::integral_constant<int, 0>{});
         block(std::integral_constant<int, 1>{});

@@ -116,6 +116,19 @@ __device__ __forceinline__ void promote(v16f& a, float sg, const v16f& p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) a[r] = fmaf(sg, p[r], a[r]);
 }
+template <int H>
+__device__ __forceinline__ void promote_half(v16f& a, float sg, const v16f& p) {
+#pragma unroll
+    for (int r = 8 * H; r < 8 * H + 8; ++r) a[r] = fmaf(sg, p[r], a[r]);
+}
+// Half H of tile_product: the instruction over K 16 H .. 16 H + 15 of the block.
+template <int AF, int BF, int OUT, int H>
+__device__ __forceinline__ v16f product_half(const u32x4& x, const u32x4& y, v16f p) {
+    static_assert(OUT != BSFP8_OUT_F32, "the FP8 instructions are for 16-bit outputs");
+    const uint64_t xv = static_cast<uint64_t>(x[2 * H]) | (static_cast<uint64_t>(x[2 * H + 1]) << 32);
+    const uint64_t yv = static_cast<uint64_t>(y[2 * H]) | (static_cast<uint64_t>(y[2 * H + 1]) << 32);
+    return mfma_codes<AF, BF>(xv, yv, p);
+}
 
 // Map a workgroup to its 256 x 256 tile.  Workgroups are dealt to the 8 XCDs
 // round-robin; each XCD is given a contiguous range of tiles, walked in groups
@@ -164,16 +177,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     const int kend = K - dchunk * 16;
     // Load J (0..7) of a stage: A for even J, B for odd, rows 64 (J / 2) + ...
     // checked: the stage may be the partial last one; the select costs a few
-    // VALU instructions but keeps the stage one basic block.
-    auto dma_one = [&](auto J, int stage, int buf, bool checked) {
+    // VALU instructions but keeps the stage one basic block.  MC (compile
+    // time) false drops the select from the stages that never need it.
+    auto dma_one = [&](auto J, int stage, int buf, auto MC, bool checked) {
         constexpr int j = J;
         constexpr int i = j >> 1;
         const int so = min(stage, last) * 128;
-        // bit 31 set puts every chunk at or past K out of range; the empty asm
-        // keeps the compiler from turning the select into a branch per load
-        uint32_t oob = (!checked || so < kend) ? 0u : 0x80000000u;
-        asm volatile("" : "+v"(oob));
-        const uint32_t vo = (dma + i * row_step) | oob;
+        uint32_t vo = dma + i * row_step;
+        if constexpr (MC) {
+            // bit 31 set puts every chunk at or past K out of range; the empty
+            // asm keeps the compiler from turning the select into a branch per load
+            uint32_t oob = (!checked || so < kend) ? 0u : 0x80000000u;
+            asm volatile("" : "+v"(oob));
+            vo |= oob;
+        }
         lds_void* dst = (lds_void*)(lds + (j & 1) * kBOffset + buf * kOperand + (64 * i + 8 * wave) * kRow);
         __builtin_amdgcn_raw_ptr_buffer_load_lds((j & 1) ? rs_b : rs_a, dst, 16, vo, so, 0, 0);
     };
@@ -220,12 +237,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     // A full stage's four scales lie inside the tile row (stage offset in the
     // scalar offset); a partial last stage's would reach past it, so CHECKED
     // loads put the stage offset in the range-checked VGPR offset.
-    auto load_scales = [&](u32x4& ra, u32x4& rb, int stage, bool checked) {
+    auto load_scales = [&](u32x4& ra, u32x4& rb, int stage, bool chk) {
         const int so = min(stage, last) * 16;
         const int so_sa = a_tensor ? 0 : so;
         const int so_sb = b_tensor ? 0 : so;
-        const uint32_t va = so_a + (checked ? so_sa : 0), vb = so_b + (checked ? so_sb : 0);
-        const int sa_s = checked ? 0 : so_sa, sb_s = checked ? 0 : so_sb;
+        const uint32_t va = so_a + (chk ? so_sa : 0), vb = so_b + (chk ? so_sb : 0);
+        const int sa_s = chk ? 0 : so_sa, sb_s = chk ? 0 : so_sb;
         asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(ra) : "v"(va), "s"(rs_sa), "s"(sa_s) : "memory");
         asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(rb) : "v"(vb), "s"(rs_sb), "s"(sb_s) : "memory");
     };
@@ -247,7 +264,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     // stage 0 and its scales; stage s + 1 is loaded during stage s
-    static_for<8>([&](auto J) { dma_one(J, 0, 0, true); });
+    using MayCheck = std::true_type;
+    using NoCheck = std::false_type;
+    static_for<8>([&](auto J) { dma_one(J, 0, 0, MayCheck{}, true); });
     load_scales(nsa, nsb, 0, true);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -263,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     // stage (the only one that can load a partial stage).  Group g multiplies
     // B tile g with both A tiles, the tiles (g, 0) and (g, 1), while the VALU
     // promotes the tile before each.
-    auto run_stage = [&](int s, auto CB, bool checked) {
+    auto run_stage = [&](int s, auto CB, auto MC, bool checked) {
         constexpr int cb = CB;
         // this stage's scales were loaded during the last stage, whose barrier
         // waited for every load
@@ -274,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             sig[k] = (a_tensor ? sa0 : __uint_as_float(ca[k])) * (b_tensor ? sb0 : __uint_as_float(cbv[k]));
-        load_scales(nsa, nsb, s + 1, checked);
+        load_scales(nsa, nsb, s + 1, MC && checked);
         static_for<4>([&](auto KB) {
             constexpr int kb = KB;
             constexpr int as = kb & 1;          // this block's A set
@@ -303,20 +322,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
                     read_a(fa[as ^ 1][1], 0, std::integral_constant<int, cb ^ 1>{}, I1{});
                     read_b(fb[0], 0, std::integral_constant<int, cb ^ 1>{}, I0{});
                 }
-                if constexpr (kb < 2) dma_one(std::integral_constant<int, 4 * kb + g>{}, s + 1, cb ^ 1, checked);
+                if constexpr (kb < 2) dma_one(std::integral_constant<int, 4 * kb + g>{}, s + 1, cb ^ 1, MC, checked);
                 // tile (g, 0) while the previous tile is promoted, then tile
-                // (g, 1) while (g, 0) is
+                // (g, 1) while (g, 0) is: one MFMA, then 8 FMAs on a product
+                // that an earlier MFMA finished, four times.  The scheduling
+                // barriers fix that order: left free, the compiler placed
+                // FMAs right behind the MFMA whose result they read, so the
+                // wave waited there with its next MFMA held back (7-11%
+                // slower).  FP32 output keeps the looser order, which lets
+                // the compiler widen the fragments to bf16 ahead of their
+                // MFMAs (1% faster there).
                 v16f& prev = acc[g == 0 ? 3 : g - 1][1];
-                {
+                if constexpr (OUT == BSFP8_OUT_F32) {
                     const v16f p0 = tile_product<AF, BF, OUT>(bcur, fa[as][0]);
                     promote(prev, g == 0 ? pend_sig : sg, pend);
                     pend = tile_product<AF, BF, OUT>(bcur, fa[as][1]);
                     promote(acc[g][0], sg, p0);
-                }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);     // then 8 FMAs
+                    for (int i = 0; i < 4; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);     // then 8 FMAs
+                    }
+                } else {
+                    const float psg = g == 0 ? pend_sig : sg;
+                    __builtin_amdgcn_sched_barrier(0);
+                    v16f p0 = product_half<AF, BF, OUT, 0>(bcur, fa[as][0], v16f{});
+                    __builtin_amdgcn_sched_barrier(0);
+                    promote_half<0>(prev, psg, pend);
+                    __builtin_amdgcn_sched_barrier(0);
+                    p0 = product_half<AF, BF, OUT, 1>(bcur, fa[as][0], p0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    promote_half<1>(prev, psg, pend);
+                    __builtin_amdgcn_sched_barrier(0);
+                    v16f pn = product_half<AF, BF, OUT, 0>(bcur, fa[as][1], v16f{});
+                    __builtin_amdgcn_sched_barrier(0);
+                    promote_half<0>(acc[g][0], sg, p0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    pn = product_half<AF, BF, OUT, 1>(bcur, fa[as][1], pn);
+                    __builtin_amdgcn_sched_barrier(0);
+                    promote_half<1>(acc[g][0], sg, p0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    pend = pn;
                 }
                 // the group's promotions finish before the next group starts,
                 // so that at most two products are live (the MFMA builtins
@@ -326,13 +372,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
             pend_sig = sg;
         });
     };
+    // stages before nfast load a full next stage: their loads need no check
     const int nfast = nfull < nst ? nfull - 1 : nfull;
     int s0 = 0;
-    for (; s0 + 1 < nfull; s0 += 2) {
-        run_stage(s0, std::integral_constant<int, 0>{}, s0 >= nfast);
-        run_stage(s0 + 1, std::integral_constant<int, 1>{}, s0 + 1 >= nfast);
+    for (; s0 + 1 < nfast; s0 += 2) {
+        run_stage(s0, I0{}, NoCheck{}, false);
+        run_stage(s0 + 1, I1{}, NoCheck{}, false);
     }
-    if (s0 < nfull) run_stage(s0, std::integral_constant<int, 0>{}, s0 >= nfast);
+    // the one or two full stages left, the last of which may load a partial one
+    if (s0 < nfull) {
+        run_stage(s0, I0{}, MayCheck{}, s0 >= nfast);
+        ++s0;
+    }
+    if (s0 < nfull) run_stage(s0, I1{}, MayCheck{}, s0 >= nfast);
     promote(acc[3][1], pend_sig, pend);
 
     if (nfull < nst) {
