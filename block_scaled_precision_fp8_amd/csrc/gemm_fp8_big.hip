@@ -261,6 +261,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     // block's (read during the current block's last group), and two slots for
     // the B fragments, each read one group (two 32 x 32 tiles) ahead.
     u32x4 fa[2][2], fb[2];      // fa[set][t]
+    // FP32 output: this block's A fragments widened to bf16 once, [t][half]
+    // (widening them for every group cost 3 VALU instructions per MFMA)
+    v8bf wa[2][2];
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     // stage 0 and its scales; stage s + 1 is loaded during stage s
@@ -329,36 +332,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
                 // barriers fix that order: left free, the compiler placed
                 // FMAs right behind the MFMA whose result they read, so the
                 // wave waited there with its next MFMA held back (7-11%
-                // slower).  FP32 output keeps the looser order, which lets
-                // the compiler widen the fragments to bf16 ahead of their
-                // MFMAs (1% faster there).
+                // slower; 2.5% on FP32 output).
                 v16f& prev = acc[g == 0 ? 3 : g - 1][1];
+                const float psg = g == 0 ? pend_sig : sg;
+                v8bf xb[2];
                 if constexpr (OUT == BSFP8_OUT_F32) {
-                    const v16f p0 = tile_product<AF, BF, OUT>(bcur, fa[as][0]);
-                    promote(prev, g == 0 ? pend_sig : sg, pend);
-                    pend = tile_product<AF, BF, OUT>(bcur, fa[as][1]);
-                    promote(acc[g][0], sg, p0);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);     // then 8 FMAs
+                    if constexpr (g == 0) {
+                        wa[0][0] = widen8<AF>(fa[as][0][0], fa[as][0][1]);
+                        wa[0][1] = widen8<AF>(fa[as][0][2], fa[as][0][3]);
+                        wa[1][0] = widen8<AF>(fa[as][1][0], fa[as][1][1]);
+                        wa[1][1] = widen8<AF>(fa[as][1][2], fa[as][1][3]);
                     }
-                } else {
-                    const float psg = g == 0 ? pend_sig : sg;
+                    xb[0] = widen8<BF>(bcur[0], bcur[1]);
+                    xb[1] = widen8<BF>(bcur[2], bcur[3]);
+                }
+                // half H of the product of B tile g and A tile T
+                auto mf = [&](auto T, auto H, const v16f& c) -> v16f {
+                    if constexpr (OUT == BSFP8_OUT_F32)
+                        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[H], wa[T][H], c, 0, 0, 0);
+                    else
+                        return product_half<AF, BF, OUT, H>(bcur, fa[as][T], c);
+                };
+                {
                     __builtin_amdgcn_sched_barrier(0);
-                    v16f p0 = product_half<AF, BF, OUT, 0>(bcur, fa[as][0], v16f{});
+                    v16f p0 = mf(I0{}, I0{}, v16f{});
                     __builtin_amdgcn_sched_barrier(0);
                     promote_half<0>(prev, psg, pend);
                     __builtin_amdgcn_sched_barrier(0);
-                    p0 = product_half<AF, BF, OUT, 1>(bcur, fa[as][0], p0);
+                    p0 = mf(I0{}, I1{}, p0);
                     __builtin_amdgcn_sched_barrier(0);
                     promote_half<1>(prev, psg, pend);
                     __builtin_amdgcn_sched_barrier(0);
-                    v16f pn = product_half<AF, BF, OUT, 0>(bcur, fa[as][1], v16f{});
+                    v16f pn = mf(I1{}, I0{}, v16f{});
                     __builtin_amdgcn_sched_barrier(0);
                     promote_half<0>(acc[g][0], sg, p0);
                     __builtin_amdgcn_sched_barrier(0);
-                    pn = product_half<AF, BF, OUT, 1>(bcur, fa[as][1], pn);
+                    pn = mf(I1{}, I1{}, pn);
                     __builtin_amdgcn_sched_barrier(0);
                     promote_half<1>(acc[g][0], sg, p0);
                     __builtin_amdgcn_sched_barrier(0);
