@@ -210,3 +210,78 @@ def test_big_tile_scale_loads_stay_inside_scale_array(rows, K):
 def test_big_tile_replay_finds_the_unchecked_overrun(K):
     rows = 1000
     assert max_code_byte_big(rows, K, fixed=False) >= rows * K
+
+
+# ------------------------------------------------- MXFP4 large tiles: scales
+# gemm_mxfp4_big_kernel (csrc/gemm_mxfp4.hip) stages the E8M0 scales through
+# LDS: a period of 4 stages (256 K values each, 8 scale bytes per row and
+# stage) is 32 bytes of each of the tile's 256 A rows and 256 B rows.  Wave w
+# (0..3) issues load q (0..3) of a period as one 16-byte-per-lane direct load:
+# lane l brings bytes 16 (l / 32) .. + 15 of the period's 32 bytes of row
+# 128 (w % 2) + 32 q + l % 32 of A (w < 2) or B, range-checked against the
+# scale array (rows * K / 32 bytes), into LDS buffer (period % 2) at
+# (4 w + q) * 1024 + 16 l.  A lane (frag_row r, half h) of wave (wm, wn)
+# reads the 8 bytes of stage s of A tile t at
+# (s / 4 % 2) * 16384 + (4 wm + t) * 1024 + (s / 2 % 2) * 512 + 16 r + (s % 2) * 8,
+# and of B tile t at the same place with load index 8 + 4 wn + t.
+def _mx_scale_dma(scales, rows, nkb, r0, wave, q, period, lastp):
+    """The 1 KB one direct load writes: {lds offset in its buffer: byte}."""
+    records = rows * nkb
+    out = {}
+    for lane in range(64):
+        row = r0 + 128 * (wave & 1) + 32 * q + (lane & 31)
+        vo = row * nkb + (lane >> 5) * 16 + min(period, lastp) * 32
+        for j in range(16):
+            v = vo + j
+            # per-dword range check: a dword wholly inside reads, else zero
+            d0 = v - (v % 4)
+            out[(4 * wave + q) * 1024 + 16 * lane + j] = scales[v] if d0 + 4 <= records else 0
+    return out
+
+
+def _mx_scale_replay(M, N, K, tm, tn, read_off=lambda s: ((s >> 1) & 1) * 512 + (s & 1) * 8):
+    """Replay the staging and the reads of tile (tm, tn); return the number of
+    (lane, stage, tile) reads whose 8 bytes differ from the rows' scales."""
+    import numpy as np
+    rng = np.random.default_rng(M * 7 + N + K)
+    nkb = K // 32
+    nst = K // 256
+    lastp = (nst - 1) >> 2
+    sa = rng.integers(0, 256, size=M * nkb, dtype=np.int64)
+    sb = rng.integers(0, 256, size=N * nkb, dtype=np.int64)
+    m0, n0 = 256 * tm, 256 * tn
+    bad = 0
+    for period in range(lastp + 1):
+        buf = {}
+        for wave in range(4):
+            for q in range(4):
+                if wave < 2:
+                    buf.update(_mx_scale_dma(sa, M, nkb, m0, wave, q, period, lastp))
+                else:
+                    buf.update(_mx_scale_dma(sb, N, nkb, n0, wave, q, period, lastp))
+        for s in range(4 * period, min(4 * period + 4, nst)):
+            for wm_or_wn, side, base_j, arr, rows, r_base in ((0, "a", 0, sa, M, m0), (1, "a", 0, sa, M, m0),
+                                                               (0, "b", 8, sb, N, n0), (1, "b", 8, sb, N, n0)):
+                for t in range(4):
+                    for r in range(32):
+                        off = (base_j + 4 * wm_or_wn + t) * 1024 + 16 * r + read_off(s)
+                        got = [buf[off + i] for i in range(8)]
+                        row = r_base + 128 * wm_or_wn + 32 * t + r
+                        want = [int(arr[row * nkb + 8 * s + i]) if row < rows else 0 for i in range(8)]
+                        bad += got != want
+    return bad
+
+
+@pytest.mark.parametrize("M,N,K,tm,tn", [
+    (512, 512, 1024, 1, 1),      # one full period
+    (2088, 2072, 768, 8, 8),     # partial period, edge tile: rows past M and N read as zero
+    (600, 520, 1280, 2, 2),      # a second period of one stage; rows 8-byte aligned
+    (512, 520, 2304, 0, 2),      # two periods and one stage
+])
+def test_mxfp4_big_scale_staging_delivers_each_rows_bytes(M, N, K, tm, tn):
+    assert _mx_scale_replay(M, N, K, tm, tn) == 0
+
+
+def test_mxfp4_big_scale_replay_finds_a_wrong_read_offset():
+    # reading the other 8-byte word of the 16-byte piece must be caught
+    assert _mx_scale_replay(512, 512, 1024, 0, 0, read_off=lambda s: ((s >> 1) & 1) * 512 + ((s + 1) & 1) * 8) > 0
