@@ -740,13 +740,20 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_fp8_
     const bool a_tensor = (tensor_mask & 1) != 0, b_tensor = (tensor_mask & 2) != 0;
     const float* sa_row = sA + (a_tensor ? 0 : static_cast<int64_t>(m0 >> 7) * nkb);
     const float* sb_row = sB + (b_tensor ? 0 : static_cast<int64_t>(n0 >> 7) * nkb);
+    // (bit 2 / bit 3: that side's scales are per row and applied at
+    // write-back; bits 0 / 1 are then set as well, so index 0 is in range).
+    // Branch-free: both scales are loaded from a clamped index and selected,
+    // since conditional loads here compiled to a branch per block.
+    const bool a_unit = (tensor_mask & 4) != 0, b_unit = (tensor_mask & 8) != 0;
     auto sigma = [&](int kb) {
-        if (kb >= kb1) return 0.0f;
-        if constexpr (OUTER) return 1.0f;
-        // (bit 2 / bit 3: that side's scales are per row and applied at write-back)
-        const float sa = (tensor_mask & 4) ? 1.0f : a_tensor ? sa_row[0] : sa_row[kb];
-        const float sb = (tensor_mask & 8) ? 1.0f : b_tensor ? sb_row[0] : sb_row[kb];
-        return sa * sb;
+        if constexpr (OUTER) return kb < kb1 ? 1.0f : 0.0f;
+        const int kc = max(0, min(kb, nkb - 1));
+        float la = sa_row[a_tensor ? 0 : kc], lb = sb_row[b_tensor ? 0 : kc];
+        // the empty asm uses both loads, so that they are not moved into branches
+        asm volatile("" : "+s"(la), "+s"(lb));
+        const float sa = a_unit ? 1.0f : la;
+        const float sb = b_unit ? 1.0f : lb;
+        return kb < kb1 ? sa * sb : 0.0f;
     };
     // Loads read whole 128-byte row segments: lane l takes 16-byte piece l & 7
     // of row (l >> 3) + 8 i, so each instruction covers 8 rows x 128 bytes.
