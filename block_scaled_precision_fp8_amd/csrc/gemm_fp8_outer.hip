@@ -40,6 +40,17 @@ constexpr int kOperandBytes = 256 * kRowBytes;       // 16 KB
 constexpr int kStageBytes = 2 * kOperandBytes;       // 32 KB
 constexpr int kBuffers = 4;
 constexpr int kLdsBytes = kBuffers * kStageBytes;    // 128 KB
+// after the stage buffers: the tile's 256 row scales of A, then its 256
+// column scales of B (2 KB), staged once at the start so that the epilogue
+// reads them from LDS instead of waiting on global loads per row tile
+constexpr int kScaleLds = kLdsBytes;
+constexpr int kLdsTotal = kLdsBytes + 2 * 256 * 4;
+// stages loaded before the first wait; the rest of the first four follow it,
+// so that stage 0's loads do not queue behind three more stages' worth
+#ifndef BSFP8_OUTER_PROLOGUE_STAGES
+#define BSFP8_OUTER_PROLOGUE_STAGES 2
+#endif
+constexpr int kPrologueStages = BSFP8_OUTER_PROLOGUE_STAGES;
 
 template <int FMT>
 constexpr int mfma_fmt() { return FMT == BSFP8_E4M3 ? 0 : 1; }
@@ -55,31 +66,20 @@ __device__ __forceinline__ void mfma_fp8_k64(v16f& acc, const u32x8& x, const u3
 
 // The epilogue's per-element scale: sA of the element's row times sB of its
 // column (step 0 broadcasts one scale per tensor); zero outside the matrix.
-// Row-operand tile ti covers columns n_base + 32 ti + 8 q + e (q, e < 4) of
-// this lane; its 16 column scales are loaded when the epilogue reaches ti.
-// Indices past the edge are clamped and the value then replaced, so the loads
-// need no branches.
+// The tile's scales are in LDS (ss: 256 of A, then 256 of B, tile-relative).
+// Row-operand tile ti covers tile columns b_base + 32 ti + 8 q + e (q, e < 4)
+// of this lane; its 16 column scales are read when the epilogue reaches ti.
 struct OuterScale {
-    const float* sA;
-    const float* sB;
-    int sa_step, sb_step, N, n_base;
+    const float* ss;
+    int b_base;
     float sa[4], sb[16];
-    __device__ OuterScale(const float* a, int as, const float* b, int bs, int M, int N_, int m_base, int nb)
-        : sA(a), sB(b), sa_step(as), sb_step(bs), N(N_), n_base(nb) {
+    __device__ OuterScale(const float* s, int a_base, int bb) : ss(s), b_base(bb) {
 #pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
-            const int m = m_base + 32 * tj;
-            const float v = sA[static_cast<int64_t>(min(m, M - 1)) * sa_step];
-            sa[tj] = m < M ? v : 0.0f;
-        }
+        for (int tj = 0; tj < 4; ++tj) sa[tj] = ss[a_base + 32 * tj];
     }
     __device__ void load(int ti) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int n = n_base + 32 * ti + 8 * (r >> 2) + (r & 3);
-            const float v = sB[static_cast<int64_t>(min(n, N - 1)) * sb_step];
-            sb[r] = n < N ? v : 0.0f;
-        }
+        for (int r = 0; r < 16; ++r) sb[r] = ss[256 + b_base + 32 * ti + 8 * (r >> 2) + (r & 3)];
     }
     __device__ float operator()(int, int tj, int r, float v) const { return (sa[tj] * sb[r]) * v; }
 };
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_outer_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA, int sa_step,
     const uint8_t* __restrict__ B, const float* __restrict__ sB, int sb_step, void* __restrict__ D,
     int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsTotal];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -207,10 +207,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_outer_kernel(
     constexpr int CB = mfma_fmt<BF>();    // the row operand is B
     constexpr int BG = mfma_fmt<AF>();
 
-    // Prologue: stages 0-3 on their way into buffers 0-3; stage 0's fragments
-    // into registers once it has landed.
-    static_for<4>([&](auto S) { static_for<8>([&](auto J) { dma_one(J, S, S); }); });
-    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    // The tile's scales: thread t loads A row m0 + t and B column n0 + t
+    // (indices past the edge clamped, the value then replaced by zero); they
+    // are stored to LDS below, once the stage loads are on their way.
+    const float sc_a = sA[static_cast<int64_t>(min(m0 + tid, M - 1)) * sa_step];
+    const float sc_b = sB[static_cast<int64_t>(min(n0 + tid, N - 1)) * sb_step];
+    // Prologue: stages 0-3 on their way into buffers 0-3 (the first
+    // kPrologueStages before the wait for stage 0, the others after it);
+    // stage 0's fragments into registers once it has landed.
+    static_for<kPrologueStages>([&](auto S) { static_for<8>([&](auto J) { dma_one(J, S, S); }); });
+    {
+        float* ss = reinterpret_cast<float*>(lds + kScaleLds);
+        ss[tid] = m0 + tid < M ? sc_a : 0.0f;
+        ss[256 + tid] = n0 + tid < N ? sc_b : 0.0f;
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" :: "i"(8 * (kPrologueStages - 1)) : "memory");
+    static_for<4 - kPrologueStages>([&](auto S) {
+        constexpr auto st = std::integral_constant<int, kPrologueStages + S>{};
+        static_for<8>([&](auto J) { dma_one(J, st, st); });
+    });
     lds_wait_barrier();
     static_for<16>([&](auto R) { read_one(R, fr[0], std::integral_constant<int, 0>{}); });
 
@@ -291,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_outer_kernel(
                    "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
                    "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
 
-    OuterScale sc(sA, sa_step, sB, sb_step, M, N, m0 + wm * 128 + frag_row, n0 + wn * 128 + 4 * half);
+    OuterScale sc(reinterpret_cast<const float*>(lds + kScaleLds), wm * 128 + frag_row, wn * 128 + 4 * half);
     epilogue<OUT, STAGE16>(acc, lds, wave, lane, m0, n0, M, N, D, ldd, ep, vec_ok, sc);
 }
 
