@@ -138,7 +138,10 @@ __device__ __forceinline__ void map_big_tile(int pid, int tiles_m, int tiles_n, 
     map_tile(pid, tiles_m, tiles_n, 4, tm, tn);
 }
 
-template <int AF, int BF, int OUT>
+// TILE_ONLY: both operands have per-tile scales (tensor_mask == 0), so the
+// per-tensor selects drop out of the scale products at compile time (two
+// VALU instructions per K block; the common case gets its own instantiation).
+template <int AF, int BF, int OUT, bool TILE_ONLY>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const float* __restrict__ sA,
     const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ D, int64_t ldd,
@@ -221,8 +224,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     // A per-tensor side (bit 0 of tensor_mask: A, bit 1: B) has a one-float
     // array: its offset stays zero and the dwords past it read as zero (the
     // range check of a dwordx4 load is per dword); sa0 / sb0 stand in.
-    const bool a_tensor = (tensor_mask & 1) != 0;
-    const bool b_tensor = (tensor_mask & 2) != 0;
+    const bool a_tensor = !TILE_ONLY && (tensor_mask & 1) != 0;
+    const bool b_tensor = !TILE_ONLY && (tensor_mask & 2) != 0;
     const int st_m = (M + 127) >> 7, st_n = (N + 127) >> 7;
     const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(sA), 0, a_tensor ? 4 : st_m * nkb * 4, 0x00020000);
@@ -231,8 +234,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(
     const uint32_t so_a = a_tensor ? 0u : static_cast<uint32_t>(2 * tm + (wm >> 1)) * nkb * 4;
     const uint32_t so_b = b_tensor ? 0u : static_cast<uint32_t>(2 * tn + wn) * nkb * 4;
     // bit 2 (bit 3): that side's scales are per row, applied at write-back
-    const float sa0 = (tensor_mask & 4) ? 1.0f : sA[0];
-    const float sb0 = (tensor_mask & 8) ? 1.0f : sB[0];
+    const float sa0 = TILE_ONLY ? 0.0f : (tensor_mask & 4) ? 1.0f : sA[0];
+    const float sb0 = TILE_ONLY ? 0.0f : (tensor_mask & 8) ? 1.0f : sB[0];
     u32x4 nsa, nsb;
     // A full stage's four scales lie inside the tile row (stage offset in the
     // scalar offset); a partial last stage's would reach past it, so CHECKED
@@ -522,9 +525,14 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const f
     const int tiles_m = static_cast<int>((M + kTile - 1) / kTile);
     const int tiles_n = static_cast<int>((N + kTile - 1) / kTile);
     const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));
-    hipLaunchKernelGGL((gemm_fp8_big_kernel<AF, BF, OUT>), grid, dim3(kThreads), 0, stream,
-                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, sa, b, sb, d, ldd,
-                       ep, tiles_m, tiles_n, vec16_ok(OUT, d, ldd, ep), tensor_mask);
+    if (tensor_mask == 0)
+        hipLaunchKernelGGL((gemm_fp8_big_kernel<AF, BF, OUT, true>), grid, dim3(kThreads), 0, stream,
+                           static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, sa, b, sb, d, ldd,
+                           ep, tiles_m, tiles_n, vec16_ok(OUT, d, ldd, ep), tensor_mask);
+    else
+        hipLaunchKernelGGL((gemm_fp8_big_kernel<AF, BF, OUT, false>), grid, dim3(kThreads), 0, stream,
+                           static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, sa, b, sb, d, ldd,
+                           ep, tiles_m, tiles_n, vec16_ok(OUT, d, ldd, ep), tensor_mask);
     return hipGetLastError();
 }
 
