@@ -414,8 +414,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     });
     read_scales(0);
 
-    for (int s = 0; s < nst; ++s) {
-        const int cb = s & 1;
+    // Stage s uses buffer s % 2.  The loop runs pairs of stages so that the
+    // buffer, and with it every LDS address of the stage, is a compile-time
+    // choice (run-time selects had kept both buffers' read addresses live:
+    // 128 VGPRs instead of 212, and 2-4% faster).
+    auto run_stage = [&](int s, auto CB) {
+        constexpr int cb = CB;
         // this stage's scales and first fragments were read during the last
         // stage's step 3 (or the prologue)
         lds_wait();
@@ -477,7 +481,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_wait_barrier();
         kstep(std::integral_constant<int, 3>{});
+    };
+    int s0 = 0;
+    for (; s0 + 1 < nst; s0 += 2) {
+        run_stage(s0, std::integral_constant<int, 0>{});
+        run_stage(s0 + 1, std::integral_constant<int, 1>{});
     }
+    if (s0 < nst) run_stage(s0, std::integral_constant<int, 0>{});
     // no direct load may still be writing LDS when the workgroup ends, and no
     // register load may still be in flight when its register is reused: the
     // last stage's scale loads and fragment reads have no consumer, so they
