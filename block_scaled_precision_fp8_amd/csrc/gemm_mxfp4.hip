@@ -206,6 +206,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_kernel(
 // Codes go straight from global memory to LDS (direct loads, rows past the
 // matrix edge read as zero) one stage ahead of use; the E8M0 scales go the
 // same way a period of 4 stages ahead, into 32 KB of LDS beside the codes.
+//
+// The same kernel serves E2M1 blocks of 16 K values with E8M0 scales (SUB = 2
+// scale blocks per 32 K; "Rubin FP4 GEMM deep dive", section 5.3 for the
+// smaller blocks).  The instruction takes one scale per lane and 32 K values,
+// so each 32-K half of a lane is split in two: one MFMA multiplies the first
+// 16 values of the A operand (the other 16 zero) under both operands' scales
+// of the first block, a second one the last 16 under the second block's
+// scales.  Zero codes add nothing, so every block keeps its own exact
+// power-of-two scale, at two FP4 instructions per 64 K: half the FP4 rate,
+// twice that of the bf16 instruction the dequantising kernels use.
 // ---------------------------------------------------------------------------
 
 // E2M1 x E2M1 MFMA with E8M0 block scales; byte SEL of each scale register is used.
@@ -213,6 +223,20 @@ template <int SEL>
 __device__ __forceinline__ void mfma_fp4_sel(v16f& acc, const u32x4& x, const u32x4& y, uint32_t sx,
                                              uint32_t sy) {
     asm volatile(
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%5,0] "
+        "op_sel_hi:[%6,%6,0] cbsz:4 blgp:4"
+        : "+a"(acc)
+        : "v"(x), "v"(y), "v"(sx), "v"(sy), "i"(SEL & 1), "i"(SEL >> 1));
+}
+// The same for an operand with a zero half, whose zero registers the compiler
+// may rewrite with VALU moves just before: the two wait states in front cover
+// the VALU-write to MFMA-read dependency, which the compiler does not track
+// for inline assembly.
+template <int SEL>
+__device__ __forceinline__ void mfma_fp4_sel_w(v16f& acc, const u32x4& x, const u32x4& y, uint32_t sx,
+                                               uint32_t sy) {
+    asm volatile(
+        "s_nop 1\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%5,0] "
         "op_sel_hi:[%6,%6,0] cbsz:4 blgp:4"
         : "+a"(acc)
@@ -239,6 +263,21 @@ __device__ __forceinline__ void gather_scales(uint32_t& w0, uint32_t& w1, uint32
         : "v"(s0.x), "v"(s0.y), "v"(s1.x), "v"(s1.y), "v"(s2.x), "v"(s2.y), "v"(s3.x),
           "v"(s3.y), "v"(sel));
 }
+// Blocks of 16: a row's 16 scale bytes of a stage, byte 4 ks + 2 half + sub
+// for the block of K step ks, lane half and sub-block sub; gather byte
+// 2 half + sub of each of the four words into byte ks of lo (sub 0) and hi
+// (sub 1).  sel is 0x05010400 + 0x02020202 * half.
+__device__ __forceinline__ void gather_scales16(uint32_t& lo, uint32_t& hi, const u32x4& s, uint32_t sel) {
+    uint32_t p01, p23;
+    asm volatile(
+        "v_perm_b32 %2, %5, %4, %8\n\t"
+        "v_perm_b32 %3, %7, %6, %8\n\t"
+        "v_perm_b32 %0, %3, %2, %9\n\t"
+        "v_perm_b32 %1, %3, %2, %10\n\t"
+        "s_nop 4"
+        : "=&v"(lo), "=&v"(hi), "=&v"(p01), "=&v"(p23)
+        : "v"(s.x), "v"(s.y), "v"(s.z), "v"(s.w), "v"(sel), "v"(0x05040100u), "v"(0x07060302u));
+}
 
 // Large-tile LDS layout: per buffer, A then B, each 256 rows of 128 bytes
 // (unpadded, so that direct global-to-LDS loads can fill them).  Row R keeps
@@ -251,8 +290,9 @@ constexpr int kDmaStageBytes = 2 * kDmaOperandBytes;     // 64 KB
 constexpr int kDmaLdsBytes = 2 * kDmaStageBytes;         // 128 KB
 typedef __attribute__((address_space(3))) void lds_void;
 // The large-tile kernel's scales go through LDS as well, after the codes: a
-// period of 4 stages (1024 K) takes 32 scale bytes of each of the tile's 256
-// A rows and 256 B rows, 16 KB, in two buffers (160 KB of LDS in all).
+// period of 4 stages (1024 K; 2 stages with blocks of 16) takes 32 scale
+// bytes of each of the tile's 256 A rows and 256 B rows, 16 KB, in two
+// buffers (160 KB of LDS in all).
 constexpr int kScalePeriodBytes = 16 * 1024;
 constexpr int kScaleLdsOffset = kDmaLdsBytes;
 constexpr int kBigLdsBytes = kDmaLdsBytes + 2 * kScalePeriodBytes;
@@ -260,12 +300,14 @@ constexpr int kBigLdsBytes = kDmaLdsBytes + 2 * kScalePeriodBytes;
 // STAGE16: 16-bit output with beta == 0, converted while staged (one pass).
 // It is a template parameter rather than a branch on beta so that each
 // instantiation holds only one epilogue: with both, the 256 live accumulators
-// at the branch spilled to scratch.
-template <int OUT, bool STAGE16>
+// at the branch spilled to scratch.  SUB: E8M0 scale blocks per 32 K values
+// (1: MXFP4, 2: blocks of 16).
+template <int OUT, bool STAGE16, int SUB>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
     int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
+    static_assert(SUB == 1 || SUB == 2, "blocks of 32 or 16 K values");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigLdsBytes];
 
     const int tid = threadIdx.x;
@@ -279,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     const int m0 = tm * 256;
     const int n0 = tn * 256;
     const int kbytes = K >> 1;
-    const int nkb = K >> 5;
+    const int nsb = (K >> 5) * SUB;  // scale bytes per row
     const int nst = K >> 8;          // K is a multiple of 256
     const int last = nst - 1;
 
@@ -334,28 +376,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         }
 
     // Scales: this lane feeds rows wm*128 + 32 t + frag_row of A and
-    // wn*128 + 32 t + frag_row of B; a stage covers 8 scale blocks (bytes) per
-    // row.  A scale row of K / 32 bytes holds a whole 16-byte load only every
-    // few rows, and a load into registers of one lane's 8 bytes touches 32 rows
-    // (32 cache lines) per instruction, which holds the single wave per SIMD
-    // back for long.  So the scales are staged in LDS by direct loads of 32
-    // rows x 32 bytes (a period of 4 stages), one per wave and stage, a period
-    // ahead of use, and read with ds_read_b64.  Load j (0..15) of a period
-    // covers operand j / 8 (A, then B), rows 32 (j % 8) .. + 31 of the tile;
-    // lane l brings 16 bytes, half l / 32 of the period's 32 bytes of row
-    // l % 32, and lands at (l / 32) * 512 + (l % 32) * 16 of the load's 1 KB.
-    // Offsets are range-checked (VGPR offset only): rows past M or N and bytes
-    // past the scale array read as zero, bytes past a row's end read the next
-    // row and are never used.
+    // wn*128 + 32 t + frag_row of B; a stage covers 8 SUB scale blocks (bytes)
+    // per row.  A scale row of K / 32 SUB bytes holds a whole 16-byte load
+    // only every few rows, and a load into registers of one lane's bytes
+    // touches 32 rows (32 cache lines) per instruction, which holds the single
+    // wave per SIMD back for long.  So the scales are staged in LDS by direct
+    // loads of 32 rows x 32 bytes (a period of 4 / SUB stages), 4 per wave and
+    // period, a period ahead of use, and read with ds_read_b64 (ds_read_b128
+    // for blocks of 16).  Load j (0..15) of a period covers operand j / 8 (A,
+    // then B), rows 32 (j % 8) .. + 31 of the tile; lane l brings 16 bytes,
+    // half l / 32 of the period's 32 bytes of row l % 32, and lands at
+    // (l / 32) * 512 + (l % 32) * 16 of the load's 1 KB.  Offsets are
+    // range-checked (VGPR offset only): rows past M or N and bytes past the
+    // scale array read as zero, bytes past a row's end read the next row and
+    // are never used.
+    constexpr int kPeriod = 4 / SUB;     // stages per scale period
     const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(sA), 0, M * nkb, 0x00020000);
+        const_cast<uint8_t*>(sA), 0, M * nsb, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(sB), 0, N * nkb, 0x00020000);
-    const uint32_t srow_step = 32u * static_cast<uint32_t>(nkb);
-    const int lastp = (nst - 1) >> 2;
+        const_cast<uint8_t*>(sB), 0, N * nsb, 0x00020000);
+    const uint32_t srow_step = 32u * static_cast<uint32_t>(nsb);
+    const int lastp = (nst - 1) / kPeriod;
     // this wave's loads q = 0..3 of a period are j = 4 wave + q: operand
     // wave / 2, rows 128 (wave % 2) + 32 q + lane % 32
-    const uint32_t sdma = static_cast<uint32_t>((wave < 2 ? m0 : n0) + 128 * (wave & 1) + (lane & 31)) * nkb +
+    const uint32_t sdma = static_cast<uint32_t>((wave < 2 ? m0 : n0) + 128 * (wave & 1) + (lane & 31)) * nsb +
                           (lane >> 5) * 16;
     auto scale_dma = [&](int period, int q) {
         const uint32_t vo = sdma + q * srow_step + min(period, lastp) * 32;
@@ -363,29 +407,45 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
                                     (4 * wave + q) * 1024);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wave < 2 ? rs_sa : rs_sb, dst, 16, vo, 0, 0, 0);
     };
+    // a stage's scale bytes of a row within the period's buffers: 8 (16) bytes
+    // at the stage's byte offset 8 SUB (stage % period) of the row's 32
+    auto scale_stage_offset = [&](int stage) -> uint32_t {
+        if constexpr (SUB == 1)
+            return ((stage >> 2) & 1) * kScalePeriodBytes + ((stage >> 1) & 1) * 512 + (stage & 1) * 8;
+        else
+            return ((stage >> 1) & 1) * kScalePeriodBytes + (stage & 1) * 512;
+    };
     // reads of a stage's scales: A tile t is load j = 4 wm + t, B tile t is
-    // j = 8 + 4 wn + t; the stage's buffer, half and 8-byte word are added per
-    // stage, t is an immediate offset
+    // j = 8 + 4 wn + t; the stage's offset is added per stage, t is an
+    // immediate offset
     const uint32_t srd_a = lds0 + kScaleLdsOffset + (4 * wm) * 1024 + frag_row * 16;
     const uint32_t srd_b = lds0 + kScaleLdsOffset + (8 + 4 * wn) * 1024 + frag_row * 16;
-    const uint32_t perm_sel = 0x06040200u + 0x01010101u * static_cast<uint32_t>(half);
-    u32x2 nsa[4], nsb[4];
+    const uint32_t perm_sel = SUB == 1 ? 0x06040200u + 0x01010101u * static_cast<uint32_t>(half)
+                                       : 0x05010400u + 0x02020202u * static_cast<uint32_t>(half);
+    using SV = std::conditional_t<SUB == 1, u32x2, u32x4>;
+    SV nsa[4], nsb4[4];
+    auto read_sv = [&](SV& v, uint32_t addr, auto OFF) {
+        if constexpr (SUB == 1)
+            lds_read8<OFF>(v, addr);
+        else
+            lds_read16<OFF>(v, addr);
+    };
     auto read_scales = [&](int stage) {
-        const uint32_t so = ((stage >> 2) & 1) * kScalePeriodBytes + ((stage >> 1) & 1) * 512 + (stage & 1) * 8;
+        const uint32_t so = scale_stage_offset(stage);
         const uint32_t ra = srd_a + so, rb = srd_b + so;
         static_for<4>([&](auto T) {
             constexpr int t = T;
-            lds_read8<t * 1024>(nsa[t], ra);
-            lds_read8<t * 1024>(nsb[t], rb);
+            read_sv(nsa[t], ra, std::integral_constant<int, t * 1024>{});
+            read_sv(nsb4[t], rb, std::integral_constant<int, t * 1024>{});
         });
     };
     // scale read T (0..7: A tile T / 2 for even T, B tile T / 2 for odd T) of a stage
     auto read_scale_one = [&](uint32_t ra, uint32_t rb, auto T) {
         constexpr int t = T;
         if constexpr (t & 1)
-            lds_read8<(t >> 1) * 1024>(nsb[t >> 1], rb);
+            read_sv(nsb4[t >> 1], rb, std::integral_constant<int, (t >> 1) * 1024>{});
         else
-            lds_read8<(t >> 1) * 1024>(nsa[t >> 1], ra);
+            read_sv(nsa[t >> 1], ra, std::integral_constant<int, (t >> 1) * 1024>{});
     };
 
     v16f acc[4][4];
@@ -394,8 +454,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-    struct Frag { u32x4 x[4], y[4]; };
+    // Fragments of one K step: B (x) and A (y) 16-byte chunks; with blocks of
+    // 16 the A chunk is held twice, its first 8 bytes with zeros after them
+    // (y) and its last 8 after zeros (yh).
+    struct Frag { u32x4 x[4], y[4], yh[SUB == 2 ? 4 : 1]; };
     Frag fr[2];
+    if constexpr (SUB == 2) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                fr[b].y[t] = u32x4{0u, 0u, 0u, 0u};
+                fr[b].yh[t] = u32x4{0u, 0u, 0u, 0u};
+            }
+    }
+    // A fragment T of a K step into g from LDS address addr (+ the tile's offset)
+    auto read_y = [&](Frag& g, uint32_t addr, auto T) {
+        constexpr int t = T;
+        if constexpr (SUB == 1) {
+            lds_read16<t * 32 * kDmaRowBytes>(g.y[t], addr);
+        } else {
+            u32x2 lo, hi;
+            lds_read8<t * 32 * kDmaRowBytes>(lo, addr);
+            lds_read8<t * 32 * kDmaRowBytes + 8>(hi, addr);
+            g.y[t].x = lo.x;
+            g.y[t].y = lo.y;
+            g.yh[t].z = hi.x;
+            g.yh[t].w = hi.y;
+        }
+    };
 
     // Prologue: stage 0 into buffer 0, the first period's scales and the
     // first half of stage 1 (loads 0..7; stage 0's step 0 issues the rest)
@@ -410,7 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     lds_wait_barrier();
     static_for<4>([&](auto t) {
         lds_read16<t * 32 * kDmaRowBytes>(fr[0].x[t], rd_b[0][0]);
-        lds_read16<t * 32 * kDmaRowBytes>(fr[0].y[t], rd_a[0][0]);
+        read_y(fr[0], rd_a[0][0], t);
     });
     read_scales(0);
 
@@ -423,50 +510,70 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         // this stage's scales and first fragments were read during the last
         // stage's step 3 (or the prologue)
         lds_wait();
-        uint32_t wa[4], wb[4];
-        gather_scales(wa[0], wa[1], wa[2], wa[3], nsa[0], nsa[1], nsa[2], nsa[3], perm_sel);
-        gather_scales(wb[0], wb[1], wb[2], wb[3], nsb[0], nsb[1], nsb[2], nsb[3], perm_sel);
-        // stage s + 1's scale reads (step 3): its buffer, half and word
-        const int s1 = s + 1;
-        const uint32_t sso = ((s1 >> 2) & 1) * kScalePeriodBytes + ((s1 >> 1) & 1) * 512 + (s1 & 1) * 8;
+        uint32_t wa[4], wb[4], wah[SUB == 2 ? 4 : 1], wbh[SUB == 2 ? 4 : 1];
+        if constexpr (SUB == 1) {
+            gather_scales(wa[0], wa[1], wa[2], wa[3], nsa[0], nsa[1], nsa[2], nsa[3], perm_sel);
+            gather_scales(wb[0], wb[1], wb[2], wb[3], nsb4[0], nsb4[1], nsb4[2], nsb4[3], perm_sel);
+        } else {
+            static_for<4>([&](auto T) {
+                constexpr int t = T;
+                gather_scales16(wa[t], wah[t], nsa[t], perm_sel);
+                gather_scales16(wb[t], wbh[t], nsb4[t], perm_sel);
+            });
+        }
+        // stage s + 1's scale reads (step 3)
+        const uint32_t sso = scale_stage_offset(s + 1);
         const uint32_t sra = srd_a + sso, srb = srd_b + sso;
 
-        // One K step (64 K values): 16 MFMAs on fragment set KS & 1 with the 8
-        // fragment reads of the next step in their shadows.  Step 3 follows
-        // the barrier that publishes stage s + 1: it reads that stage's first
-        // fragments and scales and issues the first 8 direct loads of stage
-        // s + 2 into this stage's buffer, which no wave reads any more; step 0
-        // of the next stage issues the other 8, and this wave's share of the
-        // next period's scales.  With one wave per SIMD, a memory instruction
-        // between two MFMAs holds the matrix core until it issues, and the
-        // loads back up once they ask more of L2 than it delivers to a CU: one
-        // direct load after every second MFMA, over two steps, keeps a stage's
-        // 64 KB under that rate (16 loads in one step measured 5-7% slower).
+        // One K step (64 K values): 16 MFMAs (32 with blocks of 16) on
+        // fragment set KS & 1 with the fragment reads of the next step in
+        // their shadows.  Step 3 follows the barrier that publishes stage
+        // s + 1: it reads that stage's first fragments and scales and issues
+        // the first 8 direct loads of stage s + 2 into this stage's buffer,
+        // which no wave reads any more; step 0 of the next stage issues the
+        // other 8, and this wave's share of the next period's scales.  With
+        // one wave per SIMD, a memory instruction between two MFMAs holds the
+        // matrix core until it issues, and the loads back up once they ask
+        // more of L2 than it delivers to a CU: one direct load every 32
+        // MFMA-cycles, over two steps, keeps a stage's 64 KB under that rate
+        // (16 loads in one step measured 5-7% slower).
         auto kstep = [&](auto KS) {
             constexpr int ks = KS;
             constexpr int nks = (ks + 1) & 3;
+            constexpr int NM = 16 * SUB;          // MFMAs of the step
+            constexpr int LD = 2 * SUB;           // MFMAs per direct load
             const Frag& f = fr[ks & 1];
             Frag& g = fr[(ks + 1) & 1];
             const int rb = ks == 3 ? cb ^ 1 : cb;
             const uint32_t ra_addr = rb ? rd_a[1][nks] : rd_a[0][nks];
             const uint32_t rb_addr = rb ? rd_b[1][nks] : rd_b[0][nks];
-            static_for<16>([&](auto J) {
+            static_for<NM>([&](auto J) {
                 constexpr int j = J;
-                constexpr int ti = j >> 2, tj = j & 3;
-                mfma_fp4_sel<ks>(acc[ti][tj], f.x[ti], f.y[tj], wb[ti], wa[tj]);
+                constexpr int jj = j & 15;
+                constexpr int ti = jj >> 2, tj = jj & 3;
+                if constexpr (SUB == 1)
+                    mfma_fp4_sel<ks>(acc[ti][tj], f.x[ti], f.y[tj], wb[ti], wa[tj]);
+                else if constexpr (j < 16)
+                    mfma_fp4_sel_w<ks>(acc[ti][tj], f.x[ti], f.y[tj], wb[ti], wa[tj]);
+                else
+                    mfma_fp4_sel_w<ks>(acc[ti][tj], f.x[ti], f.yh[tj], wbh[ti], wah[tj]);
+                // the next step's fragment reads, then (step 3) the next
+                // stage's scale reads, one after each MFMA
                 if constexpr (j < 8) {
                     constexpr int t = j >> 1;
                     if constexpr (j & 1)
-                        lds_read16<t * 32 * kDmaRowBytes>(g.y[t], ra_addr);
+                        read_y(g, ra_addr, std::integral_constant<int, t>{});
                     else
                         lds_read16<t * 32 * kDmaRowBytes>(g.x[t], rb_addr);
-                } else if constexpr (ks == 3) {
+                } else if constexpr (ks == 3 && j < 16) {
                     read_scale_one(sra, srb, std::integral_constant<int, j - 8>{});
                 }
-                if constexpr (ks == 0 && j == 8) scale_dma((s >> 2) + 1, s & 3);
-                if constexpr (ks == 3 && (j & 1)) dma_one(std::integral_constant<int, (j >> 1)>{}, s + 2, cb);
-                if constexpr (ks == 0 && (j & 1))
-                    dma_one(std::integral_constant<int, (8 + (j >> 1))>{}, s + 1, cb ^ 1);
+                if constexpr (ks == 0 && j % 8 == 0 && j >= 8 && j < 8 + 8 * SUB)
+                    scale_dma((s / kPeriod) + 1, SUB * (s % kPeriod) + (j - 8) / 8);
+                if constexpr (ks == 3 && j % LD == LD - 1)
+                    dma_one(std::integral_constant<int, (j / LD)>{}, s + 2, cb);
+                if constexpr (ks == 0 && j % LD == LD - 1)
+                    dma_one(std::integral_constant<int, (8 + j / LD)>{}, s + 1, cb ^ 1);
             });
         };
         kstep(std::integral_constant<int, 0>{});
@@ -475,8 +582,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         lds_wait();
         kstep(std::integral_constant<int, 2>{});
         // stage s + 1 has landed (its second half was issued in step 0), and
-        // so has this stage's scale load: publish them (the last reads of the
-        // scale buffer that the next period's loads refill were waited for
+        // so have this stage's scale loads: publish them (the last reads of
+        // the scale buffer that the next period's loads refill were waited for
         // before an earlier barrier)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_wait_barrier();
@@ -497,8 +604,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
                        "v"(fr[0].y[0]), "v"(fr[0].y[1]), "v"(fr[0].y[2]), "v"(fr[0].y[3]));
     asm volatile("" :: "v"(fr[1].x[0]), "v"(fr[1].x[1]), "v"(fr[1].x[2]), "v"(fr[1].x[3]),
                        "v"(fr[1].y[0]), "v"(fr[1].y[1]), "v"(fr[1].y[2]), "v"(fr[1].y[3]));
+    if constexpr (SUB == 2) {
+        asm volatile("" :: "v"(fr[0].yh[0]), "v"(fr[0].yh[1]), "v"(fr[0].yh[2]), "v"(fr[0].yh[3]),
+                           "v"(fr[1].yh[0]), "v"(fr[1].yh[1]), "v"(fr[1].yh[2]), "v"(fr[1].yh[3]));
+    }
     asm volatile("" :: "v"(nsa[0]), "v"(nsa[1]), "v"(nsa[2]), "v"(nsa[3]),
-                       "v"(nsb[0]), "v"(nsb[1]), "v"(nsb[2]), "v"(nsb[3]));
+                       "v"(nsb4[0]), "v"(nsb4[1]), "v"(nsb4[2]), "v"(nsb4[3]));
     // MFMA results must settle before the accumulation registers are read.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
@@ -931,7 +1042,7 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const u
         if constexpr (OUT != BSFP8_OUT_F32) {
             if (ep.beta == 0.0f) {
                 if (two)
-                    hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, true>), g, dim3(kThreads), 0, stream,
+                    hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, true, 1>), g, dim3(kThreads), 0, stream,
                                        Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
                 else
                     hipLaunchKernelGGL((gemm_mxfp4_ring_kernel<OUT, true>), g, dim3(kThreads), 0, stream,
@@ -940,7 +1051,7 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const u
             }
         }
         if (two)
-            hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, false>), g, dim3(kThreads), 0, stream,
+            hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, false, 1>), g, dim3(kThreads), 0, stream,
                                Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
         else
             hipLaunchKernelGGL((gemm_mxfp4_ring_kernel<OUT, false>), g, dim3(kThreads), 0, stream,
@@ -956,7 +1067,43 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const u
     return hipGetLastError();
 }
 
+template <int OUT>
+hipError_t launch_out16(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* a_scales,
+                        const uint8_t* b, const uint8_t* b_scales, void* d, int64_t ldd,
+                        const Epilogue& ep, hipStream_t stream) {
+    const int vec = vec16_ok(OUT, d, ldd, ep);
+    const int tm = static_cast<int>((M + 255) / 256), tn = static_cast<int>((N + 255) / 256);
+    const dim3 g(static_cast<uint32_t>(tm) * static_cast<uint32_t>(tn));
+    const int Mi = static_cast<int>(M), Ni = static_cast<int>(N), Ki = static_cast<int>(K);
+    if constexpr (OUT != BSFP8_OUT_F32) {
+        if (ep.beta == 0.0f) {
+            hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, true, 2>), g, dim3(kThreads), 0, stream,
+                               Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, false, 2>), g, dim3(kThreads), 0, stream,
+                       Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool mx16_big_applies(int64_t M, int64_t N, int64_t K) {
+    const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    return K % 256 == 0 && M > kSkinnyMaxM && big_tiles >= kBigTileThreshold &&
+           M * (K / 2) < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31);
+}
+
+hipError_t launch_gemm_mx16_big(int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                                const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
+                                int out, void* d, int64_t ldd, const Epilogue& ep, hipStream_t stream) {
+    if (out == BSFP8_OUT_F32)
+        return launch_out16<BSFP8_OUT_F32>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+    if (out == BSFP8_OUT_BF16)
+        return launch_out16<BSFP8_OUT_BF16>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+    return launch_out16<BSFP8_OUT_F16>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+}
 
 hipError_t launch_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                              const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,

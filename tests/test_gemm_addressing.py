@@ -214,74 +214,95 @@ def test_big_tile_replay_finds_the_unchecked_overrun(K):
 
 # ------------------------------------------------- MXFP4 large tiles: scales
 # gemm_mxfp4_big_kernel (csrc/gemm_mxfp4.hip) stages the E8M0 scales through
-# LDS: a period of 4 stages (256 K values each, 8 scale bytes per row and
-# stage) is 32 bytes of each of the tile's 256 A rows and 256 B rows.  Wave w
-# (0..3) issues load q (0..3) of a period as one 16-byte-per-lane direct load:
-# lane l brings bytes 16 (l / 32) .. + 15 of the period's 32 bytes of row
+# LDS.  SUB scale blocks per 32 K values (1: MXFP4, 2: blocks of 16); a stage
+# is 256 K values, 8 SUB scale bytes per row, and a period of 4 / SUB stages
+# is 32 bytes of each of the tile's 256 A rows and 256 B rows.  Wave w (0..3)
+# issues load q (0..3) of a period as one 16-byte-per-lane direct load: lane
+# l brings bytes 16 (l / 32) .. + 15 of the period's 32 bytes of row
 # 128 (w % 2) + 32 q + l % 32 of A (w < 2) or B, range-checked against the
-# scale array (rows * K / 32 bytes), into LDS buffer (period % 2) at
-# (4 w + q) * 1024 + 16 l.  A lane (frag_row r, half h) of wave (wm, wn)
-# reads the 8 bytes of stage s of A tile t at
-# (s / 4 % 2) * 16384 + (4 wm + t) * 1024 + (s / 2 % 2) * 512 + 16 r + (s % 2) * 8,
-# and of B tile t at the same place with load index 8 + 4 wn + t.
-def _mx_scale_dma(scales, rows, nkb, r0, wave, q, period, lastp):
-    """The 1 KB one direct load writes: {lds offset in its buffer: byte}."""
-    records = rows * nkb
+# scale array (rows * K SUB / 32 bytes), into LDS buffer (period % 2) at
+# (period % 2) * 16384 + (4 w + q) * 1024 + 16 l.  A lane (frag_row r) of
+# wave (wm, wn) reads the 8 SUB bytes of stage s of A tile t at
+# stage_off(s) + (4 wm + t) * 1024 + 16 r, and of B tile t at the same place
+# with load index 8 + 4 wn + t, where stage_off(s) is
+# (s / 4 % 2) * 16384 + (s / 2 % 2) * 512 + (s % 2) * 8 (SUB 1) or
+# (s / 2 % 2) * 16384 + (s % 2) * 512 (SUB 2).
+def _mx_stage_off(s, sub):
+    if sub == 1:
+        return ((s >> 2) & 1) * 16384 + ((s >> 1) & 1) * 512 + (s & 1) * 8
+    return ((s >> 1) & 1) * 16384 + (s & 1) * 512
+
+
+def _mx_scale_dma(scales, rows, nsb, r0, wave, q, period, lastp):
+    """The 1 KB one direct load writes: {lds offset: byte}."""
+    records = rows * nsb
     out = {}
     for lane in range(64):
         row = r0 + 128 * (wave & 1) + 32 * q + (lane & 31)
-        vo = row * nkb + (lane >> 5) * 16 + min(period, lastp) * 32
+        vo = row * nsb + (lane >> 5) * 16 + min(period, lastp) * 32
         for j in range(16):
             v = vo + j
             # per-dword range check: a dword wholly inside reads, else zero
             d0 = v - (v % 4)
-            out[(4 * wave + q) * 1024 + 16 * lane + j] = scales[v] if d0 + 4 <= records else 0
+            out[(period & 1) * 16384 + (4 * wave + q) * 1024 + 16 * lane + j] = \
+                scales[v] if d0 + 4 <= records else 0
     return out
 
 
-def _mx_scale_replay(M, N, K, tm, tn, read_off=lambda s: ((s >> 1) & 1) * 512 + (s & 1) * 8):
+def _mx_scale_replay(M, N, K, tm, tn, sub=1, read_off=_mx_stage_off):
     """Replay the staging and the reads of tile (tm, tn); return the number of
-    (lane, stage, tile) reads whose 8 bytes differ from the rows' scales."""
+    (lane, stage, tile) reads whose 8 SUB bytes differ from the rows' scales."""
     import numpy as np
     rng = np.random.default_rng(M * 7 + N + K)
-    nkb = K // 32
+    nsb = K // 32 * sub
     nst = K // 256
-    lastp = (nst - 1) >> 2
-    sa = rng.integers(0, 256, size=M * nkb, dtype=np.int64)
-    sb = rng.integers(0, 256, size=N * nkb, dtype=np.int64)
+    per = 4 // sub
+    lastp = (nst - 1) // per
+    sa = rng.integers(0, 256, size=M * nsb, dtype=np.int64)
+    sb = rng.integers(0, 256, size=N * nsb, dtype=np.int64)
     m0, n0 = 256 * tm, 256 * tn
     bad = 0
+    lds = {}
     for period in range(lastp + 1):
-        buf = {}
+        # a period's loads land in its buffer before its first stage reads
+        # them; the next period's go to the other buffer
         for wave in range(4):
             for q in range(4):
                 if wave < 2:
-                    buf.update(_mx_scale_dma(sa, M, nkb, m0, wave, q, period, lastp))
+                    lds.update(_mx_scale_dma(sa, M, nsb, m0, wave, q, period, lastp))
                 else:
-                    buf.update(_mx_scale_dma(sb, N, nkb, n0, wave, q, period, lastp))
-        for s in range(4 * period, min(4 * period + 4, nst)):
-            for wm_or_wn, side, base_j, arr, rows, r_base in ((0, "a", 0, sa, M, m0), (1, "a", 0, sa, M, m0),
-                                                               (0, "b", 8, sb, N, n0), (1, "b", 8, sb, N, n0)):
+                    lds.update(_mx_scale_dma(sb, N, nsb, n0, wave, q, period, lastp))
+        for s in range(per * period, min(per * period + per, nst)):
+            for wm_or_wn, base_j, arr, rows, r_base in ((0, 0, sa, M, m0), (1, 0, sa, M, m0),
+                                                        (0, 8, sb, N, n0), (1, 8, sb, N, n0)):
                 for t in range(4):
                     for r in range(32):
-                        off = (base_j + 4 * wm_or_wn + t) * 1024 + 16 * r + read_off(s)
-                        got = [buf[off + i] for i in range(8)]
+                        off = read_off(s, sub) + (base_j + 4 * wm_or_wn + t) * 1024 + 16 * r
+                        got = [lds.get(off + i) for i in range(8 * sub)]   # None: never written
                         row = r_base + 128 * wm_or_wn + 32 * t + r
-                        want = [int(arr[row * nkb + 8 * s + i]) if row < rows else 0 for i in range(8)]
+                        want = [int(arr[row * nsb + 8 * sub * s + i]) if row < rows else 0
+                                for i in range(8 * sub)]
                         bad += got != want
     return bad
 
 
+@pytest.mark.parametrize("sub", [1, 2])
 @pytest.mark.parametrize("M,N,K,tm,tn", [
-    (512, 512, 1024, 1, 1),      # one full period
+    (512, 512, 1024, 1, 1),      # one full period (two with blocks of 16)
     (2088, 2072, 768, 8, 8),     # partial period, edge tile: rows past M and N read as zero
-    (600, 520, 1280, 2, 2),      # a second period of one stage; rows 8-byte aligned
-    (512, 520, 2304, 0, 2),      # two periods and one stage
+    (600, 520, 1280, 2, 2),      # a last period of one stage
+    (512, 520, 2304, 0, 2),      # several periods and one stage
 ])
-def test_mxfp4_big_scale_staging_delivers_each_rows_bytes(M, N, K, tm, tn):
-    assert _mx_scale_replay(M, N, K, tm, tn) == 0
+def test_mxfp4_big_scale_staging_delivers_each_rows_bytes(M, N, K, tm, tn, sub):
+    assert _mx_scale_replay(M, N, K, tm, tn, sub) == 0
 
 
 def test_mxfp4_big_scale_replay_finds_a_wrong_read_offset():
     # reading the other 8-byte word of the 16-byte piece must be caught
-    assert _mx_scale_replay(512, 512, 1024, 0, 0, read_off=lambda s: ((s >> 1) & 1) * 512 + ((s + 1) & 1) * 8) > 0
+    assert _mx_scale_replay(512, 512, 1024, 0, 0, 1,
+                            lambda s, sub: _mx_stage_off(s, 1) ^ 8) > 0
+    # blocks of 16: the other stage's half of the period, or the other buffer
+    assert _mx_scale_replay(512, 512, 1024, 0, 0, 2,
+                            lambda s, sub: _mx_stage_off(s, 2) ^ 512) > 0
+    assert _mx_scale_replay(512, 512, 1024, 0, 0, 2,
+                            lambda s, sub: _mx_stage_off(s, 2) ^ 16384) > 0
