@@ -295,11 +295,17 @@ bsfp8_status mx_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, in
  * 32, below 2^23 unless block == 32 with E8M0 scales (BSFP8_ERR_UNSUPPORTED).
  * alpha, c, ldc, beta, out, d, ldd: as for scaled_gemm_ex.
  * block = 32 with E8M0 scales runs the block-scaled MXFP4 GEMM of
- * scaled_gemm.  Every other combination is beyond the matrix instructions'
- * block scaling (one E8M0 scale per 32 K values): its operands are
- * dequantised exactly to bf16 (a wide scale as an exact bf16 pair hi + lo) and
- * multiplied with FP32 accumulation; 16-bit outputs leave out the lo * lo
- * products (below 2^-16 of hi * hi).  Accuracy as for scaled_gemm_ex.
+ * scaled_gemm.  block = 16 with E8M0 scales runs, where K is a multiple of 256
+ * and the output has at least 64 tiles of 256 x 256 (and 32-bit offsets
+ * suffice, as for MXFP4), on the same block-scaled instruction: each
+ * 32-value K block of an operand lane is multiplied in two passes, one per
+ * 16-value half with the other half zeroed, each under its own block's scale,
+ * so every block keeps its exact scale.  Every other combination is beyond
+ * the matrix instructions' block scaling (one E8M0 scale per 32 K values): its
+ * operands are dequantised exactly to bf16 (a wide scale as an exact bf16
+ * pair hi + lo) and multiplied with FP32 accumulation; 16-bit outputs leave
+ * out the lo * lo products (below 2^-16 of hi * hi).  Accuracy as for
+ * scaled_gemm_ex.
  */
 bsfp8_status scaled_gemm_mx(int64_t M, int64_t N, int64_t K, int block, bsfp8_mx_scale sfmt,
                             const void* a, const void* a_scales, const void* b,
