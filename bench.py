@@ -123,9 +123,9 @@ def committed_counters(workload, source_file):
     return out
 
 
-def mx16_fp4_kernel(w):
-    """E8M0 blocks of 16 run on the large MXFP4 kernel when its tiling applies
-    (mirrors mx16_big_applies in the library)."""
+def mx_fp4_kernel(w):
+    """E8M0 blocks of 16 or 8 run on the large MXFP4 kernel when its tiling
+    applies (mirrors mx_fp4_big_applies in the library)."""
     big_tiles = ((w.M + 255) // 256) * ((w.N + 255) // 256)
     return (w.K % 256 == 0 and w.M > 64 and big_tiles >= 64 and
             w.M * (w.K // 2) < 2**31 and w.N * (w.K // 2) < 2**31)
@@ -138,7 +138,7 @@ def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False):
     if mx_variant:
         if skinny:
             return "gemm_mx_skinny_kernel"
-        if mx_variant == "e8m0_16":
+        if mx_variant == "e8m0_fp4":
             return "gemm_mxfp4_big_kernel"
         if ((w.M + 255) // 256) * ((w.N + 255) // 256) >= 128:
             return "gemm_mx_split_big_kernel" if mx_variant == "wide" else "gemm_mx_big_kernel"
@@ -386,8 +386,8 @@ def main():
         sys.exit(2)
     mxv = mx and (args.mx_block != 32 or args.mx_scale != "e8m0")
     mx_kind = ("wide" if args.mx_scale != "e8m0" else "e8m0") if mxv else False
-    if mx_kind == "e8m0" and args.mx_block == 16 and mx16_fp4_kernel(w):
-        mx_kind = "e8m0_16"     # blocks of 16 on the large MXFP4 kernel (FP4 instruction)
+    if mx_kind == "e8m0" and mx_fp4_kernel(w):
+        mx_kind = "e8m0_fp4"    # blocks of 16 or 8 on the large MXFP4 kernel (FP4 instruction)
     if not mx and (args.mx_block != 32 or args.mx_scale != "e8m0"):
         print("bench.py: --mx-block / --mx-scale apply to the MXFP4 workload", file=sys.stderr)
         sys.exit(2)
@@ -508,11 +508,11 @@ def main():
 
     gpu_info = {"compute_units": torch.cuda.get_device_properties(dev).multi_processor_count}
 
-    in_type = "bf16" if mxv and mx_kind != "e8m0_16" else ("fp4" if mx else "fp8")
+    in_type = "bf16" if mxv and mx_kind != "e8m0_fp4" else ("fp4" if mx else "fp8")
     gemm_tflops = w.flops / (gemm_ms * 1e-3) / 1e12
     kname = gemm_kernel_name(w, gran, online, mx_kind)
     src = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc",
-                       "gemm_mx.hip" if mxv and mx_kind != "e8m0_16" else "gemm_mxfp4.hip" if mx else
+                       "gemm_mx.hip" if mxv and mx_kind != "e8m0_fp4" else "gemm_mxfp4.hip" if mx else
                        "gemm_fp8_big.hip" if kname == "gemm_fp8_big_kernel" else
                        ("gemm_fp8.hip" if gran == "tile" else "gemm_fp8_outer.hip"))
     profile_tag = (f"{w.name}_b{args.mx_block}_{args.mx_scale}" if mxv else f"{w.name}_online" if online
@@ -572,7 +572,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4e2m1 (dequantised to bf16)" if mxv and mx_kind != "e8m0_16" else "fp4e2m1" if mx else ("fp8e4m3" if w.a_fmt == w.b_fmt == "e4m3" else "fp8e5m2xe4m3"),
+        "dtype": "fp4e2m1 (dequantised to bf16)" if mxv and mx_kind != "e8m0_fp4" else "fp4e2m1" if mx else ("fp8e4m3" if w.a_fmt == w.b_fmt == "e4m3" else "fp8e5m2xe4m3"),
         "data": "synthetic (seeded numpy, distributions of the workload table)",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "a_fmt": w.a_fmt,
                    "b_fmt": w.b_fmt, "out": w.out,

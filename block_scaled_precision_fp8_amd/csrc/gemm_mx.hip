@@ -1008,12 +1008,14 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const v
             return hipGetLastError();
         }
     }
-    if constexpr (SFMT == BSFP8_MX_E8M0 && BLOCK == 16) {
-        // the block-scaled FP4 instruction, two per 64 K (half the FP4 rate,
-        // twice the bf16 one), where the large MXFP4 kernel's tiling applies
-        if (mx16_big_applies(M, N, K))
-            return launch_gemm_mx16_big(M, N, K, a, static_cast<const uint8_t*>(sa), b,
-                                        static_cast<const uint8_t*>(sb), OUT, d, ldd, ep, stream);
+    if constexpr (SFMT == BSFP8_MX_E8M0 && BLOCK != 32) {
+        // the block-scaled FP4 instruction, 32 / BLOCK per 64 K, where the
+        // large MXFP4 kernel's tiling applies: blocks of 16 at half the FP4
+        // rate (twice the bf16 one), blocks of 8 at the bf16 rate without the
+        // dequantisation
+        if (mx_fp4_big_applies(M, N, K))
+            return launch_gemm_mx_fp4_big(M, N, K, BLOCK, a, static_cast<const uint8_t*>(sa), b,
+                                          static_cast<const uint8_t*>(sb), OUT, d, ldd, ep, stream);
     }
     if constexpr (SFMT == BSFP8_MX_E8M0 && BLOCK != 32) {
         // the large tile wherever it still gives the chip enough workgroups

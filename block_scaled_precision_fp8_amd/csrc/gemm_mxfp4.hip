@@ -250,6 +250,10 @@ template <int OFF>
 __device__ __forceinline__ void lds_read8(u32x2& v, uint32_t addr) {
     asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
 }
+template <int OFF>
+__device__ __forceinline__ void lds_read4(uint32_t& v, uint32_t addr) {
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
 __device__ __forceinline__ void gather_scales(uint32_t& w0, uint32_t& w1, uint32_t& w2, uint32_t& w3,
                                               const u32x2& s0, const u32x2& s1, const u32x2& s2,
                                               const u32x2& s3, uint32_t sel) {
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
     int64_t ldd, Epilogue ep, int tiles_m, int tiles_n, int vec_ok) {
-    static_assert(SUB == 1 || SUB == 2, "blocks of 32 or 16 K values");
+    static_assert(SUB == 1 || SUB == 2 || SUB == 4, "blocks of 32, 16 or 8 K values");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kBigLdsBytes];
 
     const int tid = threadIdx.x;
@@ -422,6 +426,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     const uint32_t srd_b = lds0 + kScaleLdsOffset + (8 + 4 * wn) * 1024 + frag_row * 16;
     const uint32_t perm_sel = SUB == 1 ? 0x06040200u + 0x01010101u * static_cast<uint32_t>(half)
                                        : 0x05010400u + 0x02020202u * static_cast<uint32_t>(half);
+    // Blocks of 8: a stage is one period, and K step ks of lane half h needs
+    // the 4 scale bytes of blocks 8 ks + 4 h .. + 3, which are dword 2 ks + h of
+    // the row's 32 bytes: one ds_read_b32 per tile and step, byte q selected
+    // by the MFMA's op_sel for block q of the lane's 32 values.  Offsets: the
+    // stage's buffer (s % 2) 16384, (ks / 2) 512 + (ks % 2) 8, tile t 1024.
+    const uint32_t srd4_a = srd_a + 4 * half, srd4_b = srd_b + 4 * half;
+    uint32_t ssa[2][4], ssb[2][4];   // [set][tile]
+    auto read_step_scales = [&](auto BUF, auto KS, int set, auto T) {
+        constexpr int off = BUF * kScalePeriodBytes + (KS >> 1) * 512 + (KS & 1) * 8 + T * 1024;
+        lds_read4<off>(ssa[set][T], srd4_a);
+        lds_read4<off>(ssb[set][T], srd4_b);
+    };
     using SV = std::conditional_t<SUB == 1, u32x2, u32x4>;
     SV nsa[4], nsb4[4];
     auto read_sv = [&](SV& v, uint32_t addr, auto OFF) {
@@ -456,7 +472,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
 
     // Fragments of one K step: B (x) and A (y) 16-byte chunks; with blocks of
     // 16 the A chunk is held twice, its first 8 bytes with zeros after them
-    // (y) and its last 8 after zeros (yh).
+    // (y) and its last 8 after zeros (yh); with blocks of 8 it is held whole
+    // and each MFMA gets a copy with one dword kept and three zeroed.
     struct Frag { u32x4 x[4], y[4], yh[SUB == 2 ? 4 : 1]; };
     Frag fr[2];
     if constexpr (SUB == 2) {
@@ -471,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
     // A fragment T of a K step into g from LDS address addr (+ the tile's offset)
     auto read_y = [&](Frag& g, uint32_t addr, auto T) {
         constexpr int t = T;
-        if constexpr (SUB == 1) {
+        if constexpr (SUB != 2) {
             lds_read16<t * 32 * kDmaRowBytes>(g.y[t], addr);
         } else {
             u32x2 lo, hi;
@@ -499,7 +516,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         lds_read16<t * 32 * kDmaRowBytes>(fr[0].x[t], rd_b[0][0]);
         read_y(fr[0], rd_a[0][0], t);
     });
-    read_scales(0);
+    if constexpr (SUB == 4)
+        static_for<4>([&](auto t) {
+            read_step_scales(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, 0, t);
+        });
+    else
+        read_scales(0);
 
     // Stage s uses buffer s % 2.  The loop runs pairs of stages so that the
     // buffer, and with it every LDS address of the stage, is a compile-time
@@ -511,7 +533,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         // stage's step 3 (or the prologue)
         lds_wait();
         uint32_t wa[4], wb[4], wah[SUB == 2 ? 4 : 1], wbh[SUB == 2 ? 4 : 1];
-        if constexpr (SUB == 1) {
+        if constexpr (SUB == 4) {
+            // read one K step ahead instead
+        } else if constexpr (SUB == 1) {
             gather_scales(wa[0], wa[1], wa[2], wa[3], nsa[0], nsa[1], nsa[2], nsa[3], perm_sel);
             gather_scales(wb[0], wb[1], wb[2], wb[3], nsb4[0], nsb4[1], nsb4[2], nsb4[3], perm_sel);
         } else {
@@ -525,9 +549,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         const uint32_t sso = scale_stage_offset(s + 1);
         const uint32_t sra = srd_a + sso, srb = srd_b + sso;
 
-        // One K step (64 K values): 16 MFMAs (32 with blocks of 16) on
-        // fragment set KS & 1 with the fragment reads of the next step in
-        // their shadows.  Step 3 follows the barrier that publishes stage
+        // One K step (64 K values): 16 MFMAs (32 with blocks of 16, 64 with
+        // blocks of 8) on fragment set KS & 1 with the fragment reads (and,
+        // for blocks of 8, the scale reads) of the next step in their shadows.  Step 3 follows the barrier that publishes stage
         // s + 1: it reads that stage's first fragments and scales and issues
         // the first 8 direct loads of stage s + 2 into this stage's buffer,
         // which no wave reads any more; step 0 of the next stage issues the
@@ -551,9 +575,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
                 constexpr int j = J;
                 constexpr int jj = j & 15;
                 constexpr int ti = jj >> 2, tj = jj & 3;
-                if constexpr (SUB == 1)
+                if constexpr (SUB == 1) {
                     mfma_fp4_sel<ks>(acc[ti][tj], f.x[ti], f.y[tj], wb[ti], wa[tj]);
-                else if constexpr (j < 16)
+                } else if constexpr (SUB == 4) {
+                    // block q = j / 16 of each lane's 32 values: dword q of A kept
+                    constexpr int q = j >> 4;
+                    u32x4 yq = {0u, 0u, 0u, 0u};
+                    yq[q] = f.y[tj][q];
+                    mfma_fp4_sel_w<q>(acc[ti][tj], f.x[ti], yq, ssb[ks & 1][ti], ssa[ks & 1][tj]);
+                } else if constexpr (j < 16)
                     mfma_fp4_sel_w<ks>(acc[ti][tj], f.x[ti], f.y[tj], wb[ti], wa[tj]);
                 else
                     mfma_fp4_sel_w<ks>(acc[ti][tj], f.x[ti], f.yh[tj], wbh[ti], wah[tj]);
@@ -565,7 +595,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
                         read_y(g, ra_addr, std::integral_constant<int, t>{});
                     else
                         lds_read16<t * 32 * kDmaRowBytes>(g.x[t], rb_addr);
-                } else if constexpr (ks == 3 && j < 16) {
+                } else if constexpr (SUB == 4 && j < 12) {
+                    // the next step's scales: its stage's buffer
+                    read_step_scales(std::integral_constant<int, (ks == 3 ? cb ^ 1 : cb)>{},
+                                     std::integral_constant<int, nks>{}, (ks + 1) & 1,
+                                     std::integral_constant<int, j - 8>{});
+                } else if constexpr (SUB != 4 && ks == 3 && j < 16) {
                     read_scale_one(sra, srb, std::integral_constant<int, j - 8>{});
                 }
                 if constexpr (ks == 0 && j % 8 == 0 && j >= 8 && j < 8 + 8 * SUB)
@@ -608,8 +643,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
         asm volatile("" :: "v"(fr[0].yh[0]), "v"(fr[0].yh[1]), "v"(fr[0].yh[2]), "v"(fr[0].yh[3]),
                            "v"(fr[1].yh[0]), "v"(fr[1].yh[1]), "v"(fr[1].yh[2]), "v"(fr[1].yh[3]));
     }
-    asm volatile("" :: "v"(nsa[0]), "v"(nsa[1]), "v"(nsa[2]), "v"(nsa[3]),
-                       "v"(nsb4[0]), "v"(nsb4[1]), "v"(nsb4[2]), "v"(nsb4[3]));
+    if constexpr (SUB == 4)
+        asm volatile("" :: "v"(ssa[0][0]), "v"(ssa[0][1]), "v"(ssa[0][2]), "v"(ssa[0][3]),
+                           "v"(ssb[0][0]), "v"(ssb[0][1]), "v"(ssb[0][2]), "v"(ssb[0][3]));
+    else
+        asm volatile("" :: "v"(nsa[0]), "v"(nsa[1]), "v"(nsa[2]), "v"(nsa[3]),
+                           "v"(nsb4[0]), "v"(nsb4[1]), "v"(nsb4[2]), "v"(nsb4[3]));
     // MFMA results must settle before the accumulation registers are read.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
@@ -1067,42 +1106,50 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const u
     return hipGetLastError();
 }
 
-template <int OUT>
-hipError_t launch_out16(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* a_scales,
-                        const uint8_t* b, const uint8_t* b_scales, void* d, int64_t ldd,
-                        const Epilogue& ep, hipStream_t stream) {
+template <int OUT, int SUB>
+hipError_t launch_out_sub(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* a_scales,
+                          const uint8_t* b, const uint8_t* b_scales, void* d, int64_t ldd,
+                          const Epilogue& ep, hipStream_t stream) {
     const int vec = vec16_ok(OUT, d, ldd, ep);
     const int tm = static_cast<int>((M + 255) / 256), tn = static_cast<int>((N + 255) / 256);
     const dim3 g(static_cast<uint32_t>(tm) * static_cast<uint32_t>(tn));
     const int Mi = static_cast<int>(M), Ni = static_cast<int>(N), Ki = static_cast<int>(K);
     if constexpr (OUT != BSFP8_OUT_F32) {
         if (ep.beta == 0.0f) {
-            hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, true, 2>), g, dim3(kThreads), 0, stream,
+            hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, true, SUB>), g, dim3(kThreads), 0, stream,
                                Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, false, 2>), g, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((gemm_mxfp4_big_kernel<OUT, false, SUB>), g, dim3(kThreads), 0, stream,
                        Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
     return hipGetLastError();
 }
 
+template <int SUB>
+hipError_t launch_sub(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* a_scales,
+                      const uint8_t* b, const uint8_t* b_scales, int out, void* d, int64_t ldd,
+                      const Epilogue& ep, hipStream_t stream) {
+    if (out == BSFP8_OUT_F32)
+        return launch_out_sub<BSFP8_OUT_F32, SUB>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+    if (out == BSFP8_OUT_BF16)
+        return launch_out_sub<BSFP8_OUT_BF16, SUB>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+    return launch_out_sub<BSFP8_OUT_F16, SUB>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+}
+
 }  // namespace
 
-bool mx16_big_applies(int64_t M, int64_t N, int64_t K) {
+bool mx_fp4_big_applies(int64_t M, int64_t N, int64_t K) {
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
     return K % 256 == 0 && M > kSkinnyMaxM && big_tiles >= kBigTileThreshold &&
            M * (K / 2) < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31);
 }
 
-hipError_t launch_gemm_mx16_big(int64_t M, int64_t N, int64_t K, const uint8_t* a,
-                                const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
-                                int out, void* d, int64_t ldd, const Epilogue& ep, hipStream_t stream) {
-    if (out == BSFP8_OUT_F32)
-        return launch_out16<BSFP8_OUT_F32>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
-    if (out == BSFP8_OUT_BF16)
-        return launch_out16<BSFP8_OUT_BF16>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
-    return launch_out16<BSFP8_OUT_F16>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+hipError_t launch_gemm_mx_fp4_big(int64_t M, int64_t N, int64_t K, int block, const uint8_t* a,
+                                  const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
+                                  int out, void* d, int64_t ldd, const Epilogue& ep, hipStream_t stream) {
+    if (block == 16) return launch_sub<2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, stream);
+    return launch_sub<4>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, stream);
 }
 
 hipError_t launch_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* a,

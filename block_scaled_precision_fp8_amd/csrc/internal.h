@@ -87,14 +87,14 @@ hipError_t launch_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                              const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
                              int out, void* d, int64_t ldd, const Epilogue& ep,
                              hipStream_t stream);
-// E2M1 operands with blocks of 16 K values and E8M0 scales on the large-tile
-// MXFP4 kernel (two MFMAs per 64 K, each on one half of every lane's 32
-// values): for K a multiple of 256 and enough 256 x 256 tiles, which
-// mx16_big_applies tells.
-bool mx16_big_applies(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_mx16_big(int64_t M, int64_t N, int64_t K, const uint8_t* a,
-                                const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
-                                int out, void* d, int64_t ldd, const Epilogue& ep, hipStream_t stream);
+// E2M1 operands with blocks of 16 or 8 K values and E8M0 scales on the
+// large-tile MXFP4 kernel (two or four MFMAs per 64 K, each on one block of
+// every lane's 32 values, the others zero): for K a multiple of 256 and enough
+// 256 x 256 tiles, which mx_fp4_big_applies tells.
+bool mx_fp4_big_applies(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_mx_fp4_big(int64_t M, int64_t N, int64_t K, int block, const uint8_t* a,
+                                  const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
+                                  int out, void* d, int64_t ldd, const Epilogue& ep, hipStream_t stream);
 // E2M1 operands with blocks of `block` K values and sfmt block scales
 // (not the hardware-scaled block = 32 / E8M0 case), dequantised to bf16.
 hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, int block, int sfmt, const uint8_t* a,

@@ -226,11 +226,18 @@ def test_big_tile_replay_finds_the_unchecked_overrun(K):
 # stage_off(s) + (4 wm + t) * 1024 + 16 r, and of B tile t at the same place
 # with load index 8 + 4 wn + t, where stage_off(s) is
 # (s / 4 % 2) * 16384 + (s / 2 % 2) * 512 + (s % 2) * 8 (SUB 1) or
-# (s / 2 % 2) * 16384 + (s % 2) * 512 (SUB 2).
+# (s / 2 % 2) * 16384 + (s % 2) * 512 (SUB 2).  With SUB 4 (blocks of 8) a
+# stage is a period and each K step ks reads only the 4 bytes of the lane's
+# half h (blocks 8 ks + 4 h .. + 3): at
+# (s % 2) * 16384 + (ks / 2) * 512 + (ks % 2) * 8 + 4 h + tile offset + 16 r.
 def _mx_stage_off(s, sub):
     if sub == 1:
         return ((s >> 2) & 1) * 16384 + ((s >> 1) & 1) * 512 + (s & 1) * 8
     return ((s >> 1) & 1) * 16384 + (s & 1) * 512
+
+
+def _mx_step_off(s, ks, h):
+    return (s & 1) * 16384 + (ks >> 1) * 512 + (ks & 1) * 8 + 4 * h
 
 
 def _mx_scale_dma(scales, rows, nsb, r0, wave, q, period, lastp):
@@ -249,9 +256,10 @@ def _mx_scale_dma(scales, rows, nsb, r0, wave, q, period, lastp):
     return out
 
 
-def _mx_scale_replay(M, N, K, tm, tn, sub=1, read_off=_mx_stage_off):
+def _mx_scale_replay(M, N, K, tm, tn, sub=1, read_off=_mx_stage_off, step_off=_mx_step_off):
     """Replay the staging and the reads of tile (tm, tn); return the number of
-    (lane, stage, tile) reads whose 8 SUB bytes differ from the rows' scales."""
+    (lane, stage, tile) reads (SUB 4: lane, K step, tile) whose bytes differ
+    from the rows' scales."""
     import numpy as np
     rng = np.random.default_rng(M * 7 + N + K)
     nsb = K // 32 * sub
@@ -277,16 +285,25 @@ def _mx_scale_replay(M, N, K, tm, tn, sub=1, read_off=_mx_stage_off):
                                                         (0, 8, sb, N, n0), (1, 8, sb, N, n0)):
                 for t in range(4):
                     for r in range(32):
+                        row = r_base + 128 * wm_or_wn + 32 * t + r
+                        if sub == 4:
+                            for ks in range(4):
+                                for h in range(2):
+                                    off = step_off(s, ks, h) + (base_j + 4 * wm_or_wn + t) * 1024 + 16 * r
+                                    got = [lds.get(off + i) for i in range(4)]
+                                    want = [int(arr[row * nsb + 32 * s + 8 * ks + 4 * h + i])
+                                            if row < rows else 0 for i in range(4)]
+                                    bad += got != want
+                            continue
                         off = read_off(s, sub) + (base_j + 4 * wm_or_wn + t) * 1024 + 16 * r
                         got = [lds.get(off + i) for i in range(8 * sub)]   # None: never written
-                        row = r_base + 128 * wm_or_wn + 32 * t + r
                         want = [int(arr[row * nsb + 8 * sub * s + i]) if row < rows else 0
                                 for i in range(8 * sub)]
                         bad += got != want
     return bad
 
 
-@pytest.mark.parametrize("sub", [1, 2])
+@pytest.mark.parametrize("sub", [1, 2, 4])
 @pytest.mark.parametrize("M,N,K,tm,tn", [
     (512, 512, 1024, 1, 1),      # one full period (two with blocks of 16)
     (2088, 2072, 768, 8, 8),     # partial period, edge tile: rows past M and N read as zero
@@ -306,3 +323,8 @@ def test_mxfp4_big_scale_replay_finds_a_wrong_read_offset():
                             lambda s, sub: _mx_stage_off(s, 2) ^ 512) > 0
     assert _mx_scale_replay(512, 512, 1024, 0, 0, 2,
                             lambda s, sub: _mx_stage_off(s, 2) ^ 16384) > 0
+    # blocks of 8: the other half's dword, or the other buffer
+    assert _mx_scale_replay(512, 512, 1024, 0, 0, 4,
+                            step_off=lambda s, ks, h: _mx_step_off(s, ks, 1 - h)) > 0
+    assert _mx_scale_replay(512, 512, 1024, 0, 0, 4,
+                            step_off=lambda s, ks, h: _mx_step_off(s, ks, h) ^ 16384) > 0

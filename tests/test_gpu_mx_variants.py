@@ -10,9 +10,9 @@ elements, section 5.3; FP16 or BF16 block scales, section 3.2) on the GPU.
   block size and scale format, FP32 / bf16 / FP16 output, alpha / beta and
   ragged M, N, K, on the skinny kernel (up to 64 rows or few tiles), the
   128 x 128 kernel and both 256 x 256 kernels (E8M0; FP16 / BF16 scales),
-  the large MXFP4 kernel's form for E8M0 blocks of 16 (two FP4 instructions
-  per 64 K, one per 16-block half); and the 8192^3 shape of the MXFP4
-  workload on sampled outputs.
+  the large MXFP4 kernel's form for E8M0 blocks of 16 and 8 (two or four FP4
+  instructions per 64 K, one per block of each lane's 32 values); and the
+  8192^3 shape of the MXFP4 workload on sampled outputs.
 """
 import numpy as np
 import pytest
@@ -39,11 +39,12 @@ def inputs(seed, rows, k, kind="normal"):
     if kind == "rows":      # each row at its own magnitude, some all-zero rows
         x = x * np.exp2(rng.integers(-24, 24, size=(rows, 1)))
         x[rng.random(rows) < 0.1] = 0.0
-    if kind.startswith("blocks16"):  # each 16-element block at its own magnitude, some all zero
-        nb = k // 16
-        span = 8 if kind == "blocks16_narrow" else 30   # narrow: products stay in FP16's range
-        x = x * np.repeat(np.exp2(rng.integers(-span, span, size=(rows, nb))), 16, axis=1)
-        x.reshape(rows, nb, 16)[rng.random((rows, nb)) < 0.05] = 0.0
+    if kind.startswith("blocks"):  # "blocks<B>[_narrow]": each B-element block at its own magnitude
+        bl = int(kind[6:].split("_")[0])
+        nb = k // bl
+        span = 8 if kind.endswith("_narrow") else 30   # narrow: products stay in FP16's range
+        x = x * np.repeat(np.exp2(rng.integers(-span, span, size=(rows, nb))), bl, axis=1)
+        x.reshape(rows, nb, bl)[rng.random((rows, nb)) < 0.05] = 0.0   # some all zero
     return x.astype(np.float32)
 
 
@@ -217,32 +218,35 @@ def test_mx_gemm_large_tile_parity(M, N, K, block, scale, out):
 @pytest.mark.parametrize("out", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("M,N,K", [(2048, 2048, 256), (2056, 2048, 768), (2048, 2064, 1280),
                                    (2304, 3840, 512)])
-def test_mx16_fp4_kernel_parity(M, N, K, out):
-    """E8M0 blocks of 16 with K a multiple of 256 and at least 64 tiles of
-    256 x 256 run on the block-scaled FP4 instruction, one per 16-block half
-    of each lane's 32 K values.  A's blocks each sit at their own power of
-    two (some all zero; within 2^±8 for FP16 output, whose range the wider
-    spread would overflow), so a half paired with its neighbour's scale fails;
-    K = 256, 768 and 1280 give one stage, an odd number of stages and a
-    partial last scale period; M and N are ragged."""
-    say(f"scaled_gemm_mx blocks of 16 on the FP4 kernel M={M} N={N} K={K} -> {out}")
-    a = inputs(M + 3 * K, M, K, "blocks16_narrow" if out == "f16" else "blocks16")
+@pytest.mark.parametrize("block", [16, 8])
+def test_mx_fp4_form_parity(block, M, N, K, out):
+    """E8M0 blocks of 16 or 8 with K a multiple of 256 and at least 64 tiles of
+    256 x 256 run on the block-scaled FP4 instruction, one per block of each
+    lane's 32 K values (the others zero).  A's blocks each sit at their own
+    power of two (some all zero; within 2^±8 for FP16 output, whose range the
+    wider spread would overflow), so a block paired with a neighbour's scale
+    fails; K = 256, 768 and 1280 give one stage, an odd number of stages and
+    (blocks of 16) a partial last scale period; M and N are ragged."""
+    say(f"scaled_gemm_mx blocks of {block} on the FP4 kernel M={M} N={N} K={K} -> {out}")
+    kind = f"blocks{block}" + ("_narrow" if out == "f16" else "")
+    a = inputs(M + 3 * K + block, M, K, kind)
     b = inputs(N + 5 * K, N, K, "laplace")
-    qa, sa = oracle.mx_quantize(a, 16, "e8m0")
-    qb, sb = oracle.mx_quantize(b, 16, "e8m0")
-    d = run_gemm(qa, sa, qb, sb, 16, "e8m0", out, K)
-    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, 16, "e8m0")
-    check_gemm(d, dr, sr, out, f"mx16 fp4 kernel {M}x{N}x{K} {out}")
+    qa, sa = oracle.mx_quantize(a, block, "e8m0")
+    qb, sb = oracle.mx_quantize(b, block, "e8m0")
+    d = run_gemm(qa, sa, qb, sb, block, "e8m0", out, K)
+    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, block, "e8m0")
+    check_gemm(d, dr, sr, out, f"mx{block} fp4 kernel {M}x{N}x{K} {out}")
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
-def test_mx16_fp4_kernel_alpha_beta(out):
+@pytest.mark.parametrize("block", [16, 8])
+def test_mx_fp4_form_alpha_beta(block, out):
     import torch
     M, N, K = 2304, 3840, 512
-    a = inputs(91, M, K, "blocks16")
-    b = inputs(92, N, K, "blocks16")
-    qa, sa = oracle.mx_quantize(a, 16, "e8m0")
-    qb, sb = oracle.mx_quantize(b, 16, "e8m0")
+    a = inputs(91, M, K, f"blocks{block}")
+    b = inputs(92, N, K, f"blocks{block}")
+    qa, sa = oracle.mx_quantize(a, block, "e8m0")
+    qb, sb = oracle.mx_quantize(b, block, "e8m0")
     c32 = np.random.default_rng(93).standard_normal((M, N)).astype(np.float32) * 20
     if out == "bf16":
         c = torch.from_numpy(c32).to(torch.bfloat16)
@@ -250,10 +254,10 @@ def test_mx16_fp4_kernel_alpha_beta(out):
     else:
         c = torch.from_numpy(c32)
         cref = c32.astype(np.float64)
-    say(f"scaled_gemm_mx blocks of 16 on the FP4 kernel alpha/beta -> {out}")
-    d = run_gemm(qa, sa, qb, sb, 16, "e8m0", out, K, 0.75, c.cuda(), -1.5)
-    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, 16, "e8m0")
-    check_gemm_ex(d, dr, sr, 0.75, -1.5, cref, out, f"mx16 fp4 kernel alpha/beta {out}")
+    say(f"scaled_gemm_mx blocks of {block} on the FP4 kernel alpha/beta -> {out}")
+    d = run_gemm(qa, sa, qb, sb, block, "e8m0", out, K, 0.75, c.cuda(), -1.5)
+    dr, sr = oracle.gemm_mx(qa, sa, qb, sb, block, "e8m0")
+    check_gemm_ex(d, dr, sr, 0.75, -1.5, cref, out, f"mx{block} fp4 kernel alpha/beta {out}")
 
 
 @pytest.mark.parametrize("block,scale", [(16, "e8m0"), (8, "e8m0"), (16, "f16"), (8, "bf16")])
@@ -298,7 +302,7 @@ def test_mx_end_to_end(block, scale):
     check_gemm(from_dev(d), dr, sr, "bf16", f"mx end to end {block} {scale}")
 
 
-@pytest.mark.parametrize("block,scale", [(16, "e8m0"), (32, "bf16")])
+@pytest.mark.parametrize("block,scale", [(16, "e8m0"), (8, "e8m0"), (32, "bf16")])
 def test_mx_gemm_8192_sampled(block, scale):
     """The 8192^3 shape of the MXFP4 workload, checked on sampled outputs."""
     w = workloads.by_name("mxfp4_8192")
