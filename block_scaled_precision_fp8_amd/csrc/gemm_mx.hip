@@ -1009,13 +1009,16 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const v
         }
     }
     if constexpr (SFMT == BSFP8_MX_E8M0 && BLOCK != 32) {
-        // the block-scaled FP4 instruction, 32 / BLOCK per 64 K, where the
-        // large MXFP4 kernel's tiling applies: blocks of 16 at half the FP4
-        // rate (twice the bf16 one), blocks of 8 at the bf16 rate without the
-        // dequantisation
-        if (mx_fp4_big_applies(M, N, K))
-            return launch_gemm_mx_fp4_big(M, N, K, BLOCK, a, static_cast<const uint8_t*>(sa), b,
-                                          static_cast<const uint8_t*>(sb), OUT, d, ldd, ep, stream);
+        // the block-scaled FP4 instruction, 32 / BLOCK per 64 K (blocks of 16
+        // at half the FP4 rate, twice the bf16 one; blocks of 8 at the bf16
+        // rate without the dequantisation): on the large MXFP4 kernel where
+        // its tiling applies, on the 128 x 128 one below 128 large tiles; the
+        // remaining large shapes (K not a multiple of 256) stay on the large
+        // dequantising kernel
+        const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+        if (mx_fp4_big_applies(M, N, K) || big < 128)
+            return launch_gemm_mx_fp4(M, N, K, BLOCK, a, static_cast<const uint8_t*>(sa), b,
+                                      static_cast<const uint8_t*>(sb), OUT, d, ldd, ep, stream);
     }
     if constexpr (SFMT == BSFP8_MX_E8M0 && BLOCK != 32) {
         // the large tile wherever it still gives the chip enough workgroups

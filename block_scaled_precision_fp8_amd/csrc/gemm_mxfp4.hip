@@ -34,18 +34,22 @@ constexpr int KPS = 256;        // K elements per stage (128 packed bytes per ro
 // The 256 x 256 kernel is used once it has at least this many tiles.
 constexpr int64_t kBigTileThreshold = 64;
 
+// byte Q of each scale register
+template <int Q = 0>
 __device__ __forceinline__ v16f mfma_fp4(uint4 x, uint4 y, uint32_t sx, uint32_t sy, v16f c) {
     v8i a = {static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z),
              static_cast<int>(x.w), 0, 0, 0, 0};
     v8i b = {static_cast<int>(y.x), static_cast<int>(y.y), static_cast<int>(y.z),
              static_cast<int>(y.w), 0, 0, 0, 0};
-    // format 4 = E2M1 for both operands; scale byte 0 of each scale register.
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0,
-                                                           static_cast<int>(sx), 0,
+    // format 4 = E2M1 for both operands
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, Q, static_cast<int>(sx), Q,
                                                            static_cast<int>(sy));
 }
 
-template <int OUT>
+// SUB: E8M0 scale blocks per 32 K values (1: MXFP4; 2, 4: blocks of 16, 8,
+// one MFMA per block with the lane's other A values zeroed, as in the large
+// kernel below).
+template <int OUT, int SUB = 1>
 __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
@@ -63,7 +67,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_kernel(
     const int m0 = tm * BM;
     const int n0 = tn * BN;
     const int kbytes = K >> 1;       // packed bytes per row
-    const int nkb = K >> 5;          // scale blocks per row
+    const int nkb = K >> 5;          // 32-wide K blocks per row
+    const int nsb = nkb * SUB;       // scale bytes per row
     const int nst = (K + KPS - 1) / KPS;
 
     // staging: 128 rows x 128 bytes per operand = 1024 chunks, 4 per thread
@@ -108,9 +113,31 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_kernel(
     for (int t = 0; t < 2; ++t) {
         const int ra = min(m0 + wm * 64 + 32 * t + frag_row, M - 1);
         const int rb = min(n0 + wn * 64 + 32 * t + frag_row, N - 1);
-        sa_p[t] = sA + static_cast<int64_t>(ra) * nkb;
-        sb_p[t] = sB + static_cast<int64_t>(rb) * nkb;
+        sa_p[t] = sA + static_cast<int64_t>(ra) * nsb;
+        sb_p[t] = sB + static_cast<int64_t>(rb) * nsb;
     }
+    // the lane's SUB scale bytes of 32-wide block kb (one aligned load)
+    auto scale_word = [&](const uint8_t* p, int kb) -> uint32_t {
+        if constexpr (SUB == 1) return p[kb];
+        else if constexpr (SUB == 2) return *reinterpret_cast<const uint16_t*>(p + 2 * kb);
+        else return *reinterpret_cast<const uint32_t*>(p + 4 * kb);
+    };
+    // SUB MFMAs per tile pair: block q of the lane's 32 values (A's other
+    // values zero) under scale byte q of each operand
+    auto mfma_sub = [&](v16f& c, const uint4& xv, const uint4& yv, uint32_t sx, uint32_t sy) {
+        if constexpr (SUB == 1) {
+            c = mfma_fp4(xv, yv, sx, sy, c);
+        } else {
+            static_for<SUB>([&](auto Q) {
+                constexpr int q = Q;
+                const uint32_t w[4] = {yv.x, yv.y, yv.z, yv.w};
+                uint32_t z[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) z[i] = (i * SUB / 4 == q) ? w[i] : 0u;
+                c = mfma_fp4<q>(xv, make_uint4(z[0], z[1], z[2], z[3]), sx, sy, c);
+            });
+        }
+    };
 
     v16f acc[2][2];
 #pragma unroll
@@ -128,14 +155,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_kernel(
         for (int t = 0; t < 2; ++t) {
             x[t] = *reinterpret_cast<const uint4*>(lb + (wn * 64 + 32 * t + frag_row) * kStride + off);
             y[t] = *reinterpret_cast<const uint4*>(la + (wm * 64 + 32 * t + frag_row) * kStride + off);
-            sx[t] = sb_p[t][blk];
-            sy[t] = sa_p[t][blk];
+            sx[t] = scale_word(sb_p[t], blk);
+            sy[t] = scale_word(sa_p[t], blk);
         }
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
             for (int tj = 0; tj < 2; ++tj)
-                acc[ti][tj] = mfma_fp4(x[ti], y[tj], sx[ti], sy[tj], acc[ti][tj]);
+                mfma_sub(acc[ti][tj], x[ti], y[tj], sx[ti], sy[tj]);
     };
 
     const int nsteps = K >> 6;   // K / 64 (K is a multiple of 32; an odd block count is handled below)
@@ -167,14 +194,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mxfp4_kernel(
                     x[t] = *reinterpret_cast<const uint4*>(lb + (wn * 64 + 32 * t + frag_row) * kStride + off);
                     y[t] = *reinterpret_cast<const uint4*>(la + (wm * 64 + 32 * t + frag_row) * kStride + off);
                     if (half) { x[t] = make_uint4(0, 0, 0, 0); y[t] = make_uint4(0, 0, 0, 0); }
-                    sx[t] = sb_p[t][nkb - 1];
-                    sy[t] = sa_p[t][nkb - 1];
+                    sx[t] = scale_word(sb_p[t], nkb - 1);
+                    sy[t] = scale_word(sa_p[t], nkb - 1);
                 }
 #pragma unroll
                 for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                     for (int tj = 0; tj < 2; ++tj)
-                        acc[ti][tj] = mfma_fp4(x[ti], y[tj], sx[ti], sy[tj], acc[ti][tj]);
+                        mfma_sub(acc[ti][tj], x[ti], y[tj], sx[ti], sy[tj]);
             }
         }
         if (s + 1 < nst) lstore((s + 1) & 1);
@@ -1126,10 +1153,30 @@ hipError_t launch_out_sub(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
     return hipGetLastError();
 }
 
+template <int OUT, int SUB>
+hipError_t launch_tile_sub(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* a_scales,
+                           const uint8_t* b, const uint8_t* b_scales, void* d, int64_t ldd,
+                           const Epilogue& ep, hipStream_t stream) {
+    const int tiles_m = static_cast<int>((M + BM - 1) / BM);
+    const int tiles_n = static_cast<int>((N + BN - 1) / BN);
+    const dim3 grid(static_cast<uint32_t>(tiles_m) * static_cast<uint32_t>(tiles_n));
+    hipLaunchKernelGGL((gemm_mxfp4_kernel<OUT, SUB>), grid, dim3(kThreads), 0, stream,
+                       static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), a, a_scales,
+                       b, b_scales, d, ldd, ep, tiles_m, tiles_n, vec16_ok(OUT, d, ldd, ep));
+    return hipGetLastError();
+}
+
 template <int SUB>
 hipError_t launch_sub(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* a_scales,
                       const uint8_t* b, const uint8_t* b_scales, int out, void* d, int64_t ldd,
                       const Epilogue& ep, hipStream_t stream) {
+    if (!mx_fp4_big_applies(M, N, K)) {
+        if (out == BSFP8_OUT_F32)
+            return launch_tile_sub<BSFP8_OUT_F32, SUB>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+        if (out == BSFP8_OUT_BF16)
+            return launch_tile_sub<BSFP8_OUT_BF16, SUB>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+        return launch_tile_sub<BSFP8_OUT_F16, SUB>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
+    }
     if (out == BSFP8_OUT_F32)
         return launch_out_sub<BSFP8_OUT_F32, SUB>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);
     if (out == BSFP8_OUT_BF16)
@@ -1145,7 +1192,7 @@ bool mx_fp4_big_applies(int64_t M, int64_t N, int64_t K) {
            M * (K / 2) < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31);
 }
 
-hipError_t launch_gemm_mx_fp4_big(int64_t M, int64_t N, int64_t K, int block, const uint8_t* a,
+hipError_t launch_gemm_mx_fp4(int64_t M, int64_t N, int64_t K, int block, const uint8_t* a,
                                   const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
                                   int out, void* d, int64_t ldd, const Epilogue& ep, hipStream_t stream) {
     if (block == 16) return launch_sub<2>(M, N, K, a, a_scales, b, b_scales, out, d, ldd, ep, stream);

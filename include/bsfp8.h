@@ -295,12 +295,12 @@ bsfp8_status mx_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, in
  * 32, below 2^23 unless block == 32 with E8M0 scales (BSFP8_ERR_UNSUPPORTED).
  * alpha, c, ldc, beta, out, d, ldd: as for scaled_gemm_ex.
  * block = 32 with E8M0 scales runs the block-scaled MXFP4 GEMM of
- * scaled_gemm.  block = 16 or 8 with E8M0 scales runs, where K is a multiple
- * of 256 and the output has at least 64 tiles of 256 x 256 (and 32-bit offsets
- * suffice, as for MXFP4), on the same block-scaled instruction: each
- * 32-value K block of an operand lane is multiplied in 32 / block passes, one
- * per block with the other values zeroed, each under its own block's scale,
- * so every block keeps its exact scale.  Every other combination is beyond
+ * scaled_gemm.  block = 16 or 8 with E8M0 scales runs on the same
+ * block-scaled instruction (except on skinny shapes, and on shapes with at
+ * least 128 tiles of 256 x 256 that the large MXFP4 tiling does not take):
+ * each 32-value K block of an operand lane is multiplied in 32 / block
+ * passes, one per block with the other values zeroed, each under its own
+ * block's scale, so every block keeps its exact scale.  Every other combination is beyond
  * the matrix instructions' block scaling (one E8M0 scale per 32 K values): its
  * operands are dequantised exactly to bf16 (a wide scale as an exact bf16
  * pair hi + lo) and multiplied with FP32 accumulation; 16-bit outputs leave
