@@ -124,11 +124,16 @@ def committed_counters(workload, source_file):
 
 
 def mx_fp4_kernel(w):
-    """E8M0 blocks of 16 or 8 run on the large MXFP4 kernel when its tiling
-    applies (mirrors mx_fp4_big_applies in the library)."""
+    """The MXFP4 kernel that E8M0 blocks of 16 or 8 run on (one FP4 MFMA per
+    block), or None where they stay on a dequantising kernel (mirrors the
+    library's dispatch)."""
     big_tiles = ((w.M + 255) // 256) * ((w.N + 255) // 256)
-    return (w.K % 256 == 0 and w.M > 64 and big_tiles >= 64 and
-            w.M * (w.K // 2) < 2**31 and w.N * (w.K // 2) < 2**31)
+    if w.M <= 64 or ((w.M + 127) // 128) * ((w.N + 127) // 128) < 32:
+        return "gemm_mxfp4_skinny_kernel"
+    if (w.K % 256 == 0 and big_tiles >= 64 and
+            w.M * (w.K // 2) < 2**31 and w.N * (w.K // 2) < 2**31):
+        return "gemm_mxfp4_big_kernel"
+    return "gemm_mxfp4_kernel" if big_tiles < 128 else None
 
 
 def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False):
@@ -136,10 +141,10 @@ def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False):
     launchers' selection)."""
     skinny = w.M <= 64 or ((w.M + 127) // 128) * ((w.N + 127) // 128) < 32
     if mx_variant:
+        if mx_variant == "e8m0_fp4":
+            return mx_fp4_kernel(w)
         if skinny:
             return "gemm_mx_skinny_kernel"
-        if mx_variant == "e8m0_fp4":
-            return "gemm_mxfp4_big_kernel"
         if ((w.M + 255) // 256) * ((w.N + 255) // 256) >= 128:
             return "gemm_mx_split_big_kernel" if mx_variant == "wide" else "gemm_mx_big_kernel"
         return "gemm_mx_kernel"

@@ -979,6 +979,19 @@ template <int BLOCK, int SFMT, int OUT>
 hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const void* sa,
                       const uint8_t* b, const void* sb, void* d, int64_t ldd, const Epilogue& ep,
                       hipStream_t stream) {
+    if constexpr (SFMT == BSFP8_MX_E8M0 && BLOCK != 32) {
+        // the block-scaled FP4 instruction, 32 / BLOCK per 64 K (blocks of 16
+        // at half the FP4 rate, twice the bf16 one; blocks of 8 at the bf16
+        // rate without the dequantisation): on the MXFP4 kernels' skinny,
+        // large or 128 x 128 form; the remaining large shapes (at least 128
+        // tiles of 256 x 256 with K not a multiple of 256) stay on the large
+        // dequantising kernel
+        const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+        const bool skinny = M <= kMxSkinnyMaxM || ((M + 127) / 128) * ((N + 127) / 128) < kMxSkinnyMaxTiles;
+        if (skinny || mx_fp4_big_applies(M, N, K) || big < 128)
+            return launch_gemm_mx_fp4(M, N, K, BLOCK, a, static_cast<const uint8_t*>(sa), b,
+                                      static_cast<const uint8_t*>(sb), OUT, d, ldd, ep, stream);
+    }
     if (M <= kMxSkinnyMaxM || ((M + 127) / 128) * ((N + 127) / 128) < kMxSkinnyMaxTiles) {
         const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
         const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
@@ -1007,18 +1020,6 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const v
                                    sa8, b, sb8, d, ldd, ep, tm, tn, vec);
             return hipGetLastError();
         }
-    }
-    if constexpr (SFMT == BSFP8_MX_E8M0 && BLOCK != 32) {
-        // the block-scaled FP4 instruction, 32 / BLOCK per 64 K (blocks of 16
-        // at half the FP4 rate, twice the bf16 one; blocks of 8 at the bf16
-        // rate without the dequantisation): on the large MXFP4 kernel where
-        // its tiling applies, on the 128 x 128 one below 128 large tiles; the
-        // remaining large shapes (K not a multiple of 256) stay on the large
-        // dequantising kernel
-        const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-        if (mx_fp4_big_applies(M, N, K) || big < 128)
-            return launch_gemm_mx_fp4(M, N, K, BLOCK, a, static_cast<const uint8_t*>(sa), b,
-                                      static_cast<const uint8_t*>(sb), OUT, d, ldd, ep, stream);
     }
     if constexpr (SFMT == BSFP8_MX_E8M0 && BLOCK != 32) {
         // the large tile wherever it still gives the chip enough workgroups

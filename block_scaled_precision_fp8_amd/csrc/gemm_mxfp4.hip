@@ -967,13 +967,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_ring_kernel(
 // the E8M0 byte of block 2 s + h of row r for 64-K step s), and the partial
 // sums are added in a fixed order through LDS.  Blocks past K or past the
 // wave's range read as zero codes with a zero scale byte (2^-127), which
-// contribute nothing.
+// contribute nothing.  SUB as for the other kernels: blocks of 16 or 8 take
+// one MFMA per block, with the lane's other A values zeroed, and a 2- or
+// 4-byte scale load.
 constexpr int kSkinnyDepth = 2;              // chunks of 8 blocks in flight per wave
 constexpr int kSkinnyWaves = 4;              // waves per workgroup, splitting K
 constexpr int64_t kSkinnyMaxM = 64;
 constexpr int64_t kSkinnyMaxTiles = 32;      // 128 x 128 tiles below which the skinny form is used too
 
-template <int OUT>
+template <int OUT, int SUB = 1>
 __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_mxfp4_skinny_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, void* __restrict__ D,
@@ -991,7 +993,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_mxfp
     const int tm = rem >> 3, tn = grp * 8 + (rem & 7);
     if (tn >= tiles_n) return;
     const int m0 = tm * 32, n0 = tn * 32;
-    const int kbytes = K >> 1, nkb = K >> 5;
+    const int kbytes = K >> 1, nkb = K >> 5, nsb = nkb * SUB;   // 32-wide blocks, scale bytes per row
     // K is split into chunks of 8 blocks (128 bytes of each row); each wave
     // takes a contiguous range of chunks
     const int nch = (nkb + 7) >> 3;
@@ -1004,9 +1006,9 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_mxfp
     const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(B) + static_cast<int64_t>(n0) * kbytes, 0, rows_b * kbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_sa = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(sA) + static_cast<int64_t>(m0) * nkb, 0, rows_a * nkb, 0x00020000);
+        const_cast<uint8_t*>(sA) + static_cast<int64_t>(m0) * nsb, 0, rows_a * nsb, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_sb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(sB) + static_cast<int64_t>(n0) * nkb, 0, rows_b * nkb, 0x00020000);
+        const_cast<uint8_t*>(sB) + static_cast<int64_t>(n0) * nsb, 0, rows_b * nsb, 0x00020000);
     const int r = lane & 31, h = lane >> 5;
     constexpr uint32_t kOut = 0x80000000u;
     // Code loads read whole 128-byte row segments: lane l takes 16-byte piece
@@ -1034,9 +1036,17 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_mxfp
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int blk = 8 * c + 2 * st + h;
-            const uint32_t os = cok && blk < nkb ? static_cast<uint32_t>(r * nkb + blk) : kOut;
-            ea[j][st] = __builtin_amdgcn_raw_buffer_load_b8(rs_sa, static_cast<int>(os), 0, 0);
-            eb[j][st] = __builtin_amdgcn_raw_buffer_load_b8(rs_sb, static_cast<int>(os), 0, 0);
+            const uint32_t os = cok && blk < nkb ? static_cast<uint32_t>((r * nkb + blk) * SUB) : kOut;
+            if constexpr (SUB == 1) {
+                ea[j][st] = __builtin_amdgcn_raw_buffer_load_b8(rs_sa, static_cast<int>(os), 0, 0);
+                eb[j][st] = __builtin_amdgcn_raw_buffer_load_b8(rs_sb, static_cast<int>(os), 0, 0);
+            } else if constexpr (SUB == 2) {
+                ea[j][st] = __builtin_amdgcn_raw_buffer_load_b16(rs_sa, static_cast<int>(os), 0, 0);
+                eb[j][st] = __builtin_amdgcn_raw_buffer_load_b16(rs_sb, static_cast<int>(os), 0, 0);
+            } else {
+                ea[j][st] = __builtin_amdgcn_raw_buffer_load_b32(rs_sa, static_cast<int>(os), 0, 0);
+                eb[j][st] = __builtin_amdgcn_raw_buffer_load_b32(rs_sb, static_cast<int>(os), 0, 0);
+            }
         }
     };
     v16f acc = v16f{};
@@ -1063,7 +1073,19 @@ __global__ __launch_bounds__(64 * kSkinnyWaves, 8 / kSkinnyWaves) void gemm_mxfp
                 const int pos = r * 128 + 16 * ((2 * st + h) ^ (r & 7));
                 const uint4 xa = *reinterpret_cast<const uint4*>(st_a + pos);
                 const uint4 xb = *reinterpret_cast<const uint4*>(st_b + pos);
-                acc = mfma_fp4(xb, xa, sb4[st], sa4[st], acc);   // B rows are the row operand
+                // B rows are the row operand
+                if constexpr (SUB == 1) {
+                    acc = mfma_fp4(xb, xa, sb4[st], sa4[st], acc);
+                } else {
+                    static_for<SUB>([&](auto Q) {
+                        constexpr int q = Q;
+                        const uint32_t w[4] = {xa.x, xa.y, xa.z, xa.w};
+                        uint32_t z[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) z[i] = (i * SUB / 4 == q) ? w[i] : 0u;
+                        acc = mfma_fp4<q>(xb, make_uint4(z[0], z[1], z[2], z[3]), sb4[st], sa4[st], acc);
+                    });
+                }
             }
         });
     }
@@ -1170,6 +1192,22 @@ template <int SUB>
 hipError_t launch_sub(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* a_scales,
                       const uint8_t* b, const uint8_t* b_scales, int out, void* d, int64_t ldd,
                       const Epilogue& ep, hipStream_t stream) {
+    if (M <= kSkinnyMaxM || ((M + 127) / 128) * ((N + 127) / 128) < kSkinnyMaxTiles) {
+        const int tm = static_cast<int>((M + 31) / 32), tn = static_cast<int>((N + 31) / 32);
+        const uint32_t wgs = static_cast<uint32_t>((tn + 7) / 8) * 8u * static_cast<uint32_t>(tm);
+        const int vec = vec16_ok(out, d, ldd, ep);
+        const int Mi = static_cast<int>(M), Ni = static_cast<int>(N), Ki = static_cast<int>(K);
+        if (out == BSFP8_OUT_F32)
+            hipLaunchKernelGGL((gemm_mxfp4_skinny_kernel<BSFP8_OUT_F32, SUB>), dim3(wgs), dim3(64 * kSkinnyWaves),
+                               0, stream, Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
+        else if (out == BSFP8_OUT_BF16)
+            hipLaunchKernelGGL((gemm_mxfp4_skinny_kernel<BSFP8_OUT_BF16, SUB>), dim3(wgs), dim3(64 * kSkinnyWaves),
+                               0, stream, Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
+        else
+            hipLaunchKernelGGL((gemm_mxfp4_skinny_kernel<BSFP8_OUT_F16, SUB>), dim3(wgs), dim3(64 * kSkinnyWaves),
+                               0, stream, Mi, Ni, Ki, a, a_scales, b, b_scales, d, ldd, ep, tm, tn, vec);
+        return hipGetLastError();
+    }
     if (!mx_fp4_big_applies(M, N, K)) {
         if (out == BSFP8_OUT_F32)
             return launch_tile_sub<BSFP8_OUT_F32, SUB>(M, N, K, a, a_scales, b, b_scales, d, ldd, ep, stream);

@@ -89,9 +89,9 @@ hipError_t launch_gemm_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                              hipStream_t stream);
 // E2M1 operands with blocks of 16 or 8 K values and E8M0 scales on the
 // block-scaled FP4 instruction (two or four MFMAs per 64 K, each on one block
-// of every lane's 32 values, the others zero): the large-tile MXFP4 kernel
-// where mx_fp4_big_applies (K a multiple of 256, enough 256 x 256 tiles),
-// else the 128 x 128 one.
+// of every lane's 32 values, the others zero): the skinny MXFP4 kernel for
+// up to 64 rows or few tiles, the large-tile one where mx_fp4_big_applies (K
+// a multiple of 256, enough 256 x 256 tiles), else the 128 x 128 one.
 bool mx_fp4_big_applies(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_mx_fp4(int64_t M, int64_t N, int64_t K, int block, const uint8_t* a,
                               const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,

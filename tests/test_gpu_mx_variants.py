@@ -217,14 +217,16 @@ def test_mx_gemm_large_tile_parity(M, N, K, block, scale, out):
 
 @pytest.mark.parametrize("out", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("M,N,K", [(2048, 2048, 256), (2056, 2048, 768), (2048, 2064, 1280),
-                                   (2304, 3840, 512), (1000, 600, 96), (1536, 1032, 2080)])
+                                   (2304, 3840, 512), (1000, 600, 96), (1536, 1032, 2080),
+                                   (16, 1000, 4096), (64, 2100, 1568), (1, 520, 416)])
 @pytest.mark.parametrize("block", [16, 8])
 def test_mx_fp4_form_parity(block, M, N, K, out):
     """E8M0 blocks of 16 or 8 run on the block-scaled FP4 instruction, one per
     block of each lane's 32 K values (the others zero): on the large MXFP4
     kernel for K a multiple of 256 and at least 64 tiles of 256 x 256, on the
-    128 x 128 one below 128 such tiles (the last two shapes: K % 64 == 32 and
-    a partial last stage).  A's blocks each sit at their own
+    128 x 128 one below 128 such tiles (1000 x 600 x 96 and 1536 x 1032 x 2080:
+    K % 64 == 32 and a partial last stage), and on the skinny one for up to 64
+    rows (the last three, K split over the waves with a ragged last chunk).  A's blocks each sit at their own
     power of two (some all zero; within 2^±8 for FP16 output, whose range the
     wider spread would overflow), so a block paired with a neighbour's scale
     fails; K = 256, 768 and 1280 give one stage, an odd number of stages and
