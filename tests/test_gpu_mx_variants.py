@@ -244,9 +244,10 @@ def test_mx_fp4_form_parity(block, M, N, K, out):
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 @pytest.mark.parametrize("block", [16, 8])
-def test_mx_fp4_form_alpha_beta(block, out):
+@pytest.mark.parametrize("M,N,K", [(2304, 3840, 512), (1000, 600, 96), (40, 700, 640)])
+def test_mx_fp4_form_alpha_beta(M, N, K, block, out):
+    """alpha, beta * C on the large, 128 x 128 and skinny FP4 forms."""
     import torch
-    M, N, K = 2304, 3840, 512
     a = inputs(91, M, K, f"blocks{block}")
     b = inputs(92, N, K, f"blocks{block}")
     qa, sa = oracle.mx_quantize(a, block, "e8m0")
