@@ -97,7 +97,9 @@ hipError_t launch_gemm_mx_fp4(int64_t M, int64_t N, int64_t K, int block, const 
                               const uint8_t* a_scales, const uint8_t* b, const uint8_t* b_scales,
                               int out, void* d, int64_t ldd, const Epilogue& ep, hipStream_t stream);
 // E2M1 operands with blocks of `block` K values and sfmt block scales
-// (not the hardware-scaled block = 32 / E8M0 case), dequantised to bf16.
+// (not the hardware-scaled block = 32 / E8M0 case), dequantised to bf16;
+// E8M0 blocks of 16 and 8 go to launch_gemm_mx_fp4 wherever one of its
+// forms applies.
 hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, int block, int sfmt, const uint8_t* a,
                           const void* a_scales, const uint8_t* b, const void* b_scales, int out,
                           void* d, int64_t ldd, const Epilogue& ep, hipStream_t stream);
