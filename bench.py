@@ -123,7 +123,7 @@ def committed_counters(workload, source_file):
     return out
 
 
-def mx_fp4_kernel(w):
+def mx_fp4_kernel(w, block):
     """The MXFP4 kernel that E8M0 blocks of 16 or 8 run on (one FP4 MFMA per
     block), or None where they stay on a dequantising kernel (mirrors the
     library's dispatch)."""
@@ -133,16 +133,16 @@ def mx_fp4_kernel(w):
     if (w.K % 256 == 0 and big_tiles >= 64 and
             w.M * (w.K // 2) < 2**31 and w.N * (w.K // 2) < 2**31):
         return "gemm_mxfp4_big_kernel"
-    return "gemm_mxfp4_kernel" if big_tiles < 128 else None
+    return "gemm_mxfp4_kernel" if big_tiles < 128 or block == 16 else None
 
 
-def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False):
+def gemm_kernel_name(w, gran="tile", online=False, mx_variant=False, mx_block=32):
     """The kernel scaled_gemm dispatches for this workload (mirrors the
     launchers' selection)."""
     skinny = w.M <= 64 or ((w.M + 127) // 128) * ((w.N + 127) // 128) < 32
     if mx_variant:
         if mx_variant == "e8m0_fp4":
-            return mx_fp4_kernel(w)
+            return mx_fp4_kernel(w, mx_block)
         if skinny:
             return "gemm_mx_skinny_kernel"
         if ((w.M + 255) // 256) * ((w.N + 255) // 256) >= 128:
@@ -391,7 +391,7 @@ def main():
         sys.exit(2)
     mxv = mx and (args.mx_block != 32 or args.mx_scale != "e8m0")
     mx_kind = ("wide" if args.mx_scale != "e8m0" else "e8m0") if mxv else False
-    if mx_kind == "e8m0" and mx_fp4_kernel(w):
+    if mx_kind == "e8m0" and mx_fp4_kernel(w, args.mx_block):
         mx_kind = "e8m0_fp4"    # blocks of 16 or 8 on the large MXFP4 kernel (FP4 instruction)
     if not mx and (args.mx_block != 32 or args.mx_scale != "e8m0"):
         print("bench.py: --mx-block / --mx-scale apply to the MXFP4 workload", file=sys.stderr)
@@ -515,7 +515,7 @@ def main():
 
     in_type = "bf16" if mxv and mx_kind != "e8m0_fp4" else ("fp4" if mx else "fp8")
     gemm_tflops = w.flops / (gemm_ms * 1e-3) / 1e12
-    kname = gemm_kernel_name(w, gran, online, mx_kind)
+    kname = gemm_kernel_name(w, gran, online, mx_kind, args.mx_block)
     src = os.path.join(ROOT, "block_scaled_precision_fp8_amd", "csrc",
                        "gemm_mx.hip" if mxv and mx_kind != "e8m0_fp4" else "gemm_mxfp4.hip" if mx else
                        "gemm_fp8_big.hip" if kname == "gemm_fp8_big_kernel" else
@@ -539,11 +539,11 @@ def main():
     gbytes = gemm_bytes(w, gran, args.mx_block, args.mx_scale, mx)
     if w.flops / gbytes < PEAK_TFLOPS[in_type] * 1e12 / (HBM_GBPS * 1e9):
         gemm_gbps = gbytes / (gemm_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "kernel": gemm_kernel_name(w, gran, online, mx_kind),
+        roofline = {"bound": "hbm", "kernel": gemm_kernel_name(w, gran, online, mx_kind, args.mx_block),
                     "achieved": round(gemm_gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
                     "frac": round(gemm_gbps / HBM_GBPS, 4), "algorithmic_bytes": gbytes}
     else:
-        roofline = {"bound": "mfma", "kernel": gemm_kernel_name(w, gran, online, mx_kind),
+        roofline = {"bound": "mfma", "kernel": gemm_kernel_name(w, gran, online, mx_kind, args.mx_block),
                     "achieved": round(gemm_tflops, 1), "peak": PEAK_TFLOPS[in_type], "unit": "TFLOP/s",
                     "frac": round(gemm_tflops / PEAK_TFLOPS[in_type], 4),
                     "algorithmic_flops": w.flops}

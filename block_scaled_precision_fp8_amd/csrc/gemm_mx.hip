@@ -983,12 +983,13 @@ hipError_t launch_out(int64_t M, int64_t N, int64_t K, const uint8_t* a, const v
         // the block-scaled FP4 instruction, 32 / BLOCK per 64 K (blocks of 16
         // at half the FP4 rate, twice the bf16 one; blocks of 8 at the bf16
         // rate without the dequantisation): on the MXFP4 kernels' skinny,
-        // large or 128 x 128 form; the remaining large shapes (at least 128
-        // tiles of 256 x 256 with K not a multiple of 256) stay on the large
-        // dequantising kernel
+        // large or 128 x 128 form.  Blocks of 8 on large shapes that the large
+        // form does not take (at least 128 tiles of 256 x 256, K not a
+        // multiple of 256) stay on the large dequantising kernel, which the
+        // 128 x 128 form did not beat there; blocks of 16 did (by 29-32%).
         const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
         const bool skinny = M <= kMxSkinnyMaxM || ((M + 127) / 128) * ((N + 127) / 128) < kMxSkinnyMaxTiles;
-        if (skinny || mx_fp4_big_applies(M, N, K) || big < 128)
+        if (BLOCK == 16 || skinny || mx_fp4_big_applies(M, N, K) || big < 128)
             return launch_gemm_mx_fp4(M, N, K, BLOCK, a, static_cast<const uint8_t*>(sa), b,
                                       static_cast<const uint8_t*>(sb), OUT, d, ldd, ep, stream);
     }

@@ -296,8 +296,8 @@ bsfp8_status mx_quantize(const float* x, int64_t rows, int64_t k, int64_t ld, in
  * alpha, c, ldc, beta, out, d, ldd: as for scaled_gemm_ex.
  * block = 32 with E8M0 scales runs the block-scaled MXFP4 GEMM of
  * scaled_gemm.  block = 16 or 8 with E8M0 scales runs on the same
- * block-scaled instruction (except on skinny shapes, and on shapes with at
- * least 128 tiles of 256 x 256 that the large MXFP4 tiling does not take):
+ * block-scaled instruction (block = 8 except on shapes with at least 128
+ * tiles of 256 x 256 that the large MXFP4 tiling does not take):
  * each 32-value K block of an operand lane is multiplied in 32 / block
  * passes, one per block with the other values zeroed, each under its own
  * block's scale, so every block keeps its exact scale.  Every other combination is beyond
