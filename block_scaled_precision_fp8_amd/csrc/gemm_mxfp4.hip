@@ -255,10 +255,10 @@ __device__ __forceinline__ void mfma_fp4_sel(v16f& acc, const u32x4& x, const u3
         : "+a"(acc)
         : "v"(x), "v"(y), "v"(sx), "v"(sy), "i"(SEL & 1), "i"(SEL >> 1));
 }
-// The same for an operand with a zero half, whose zero registers the compiler
-// may rewrite with VALU moves just before: the two wait states in front cover
-// the VALU-write to MFMA-read dependency, which the compiler does not track
-// for inline assembly.
+// The same for an operand that the compiler assembles with VALU moves just
+// before (an A chunk with some dwords zeroed): the two wait states in front
+// cover the VALU-write to MFMA-read dependency, which the compiler does not
+// track for inline assembly.
 template <int SEL>
 __device__ __forceinline__ void mfma_fp4_sel_w(v16f& acc, const u32x4& x, const u32x4& y, uint32_t sx,
                                                uint32_t sy) {
@@ -497,35 +497,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-    // Fragments of one K step: B (x) and A (y) 16-byte chunks; with blocks of
-    // 16 the A chunk is held twice, its first 8 bytes with zeros after them
-    // (y) and its last 8 after zeros (yh); with blocks of 8 it is held whole
-    // and each MFMA gets a copy with one dword kept and three zeroed.
-    struct Frag { u32x4 x[4], y[4], yh[SUB == 2 ? 4 : 1]; };
+    // Fragments of one K step: B (x) and A (y) 16-byte chunks.  With blocks
+    // of 16 or 8 each MFMA gets a copy of the A chunk with one block's dwords
+    // kept and the others zeroed (built by the compiler from the whole chunk;
+    // reading the halves separately into zero-padded registers measured 1%
+    // slower and conflicted in LDS).
+    struct Frag { u32x4 x[4], y[4]; };
     Frag fr[2];
-    if constexpr (SUB == 2) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                fr[b].y[t] = u32x4{0u, 0u, 0u, 0u};
-                fr[b].yh[t] = u32x4{0u, 0u, 0u, 0u};
-            }
-    }
     // A fragment T of a K step into g from LDS address addr (+ the tile's offset)
     auto read_y = [&](Frag& g, uint32_t addr, auto T) {
         constexpr int t = T;
-        if constexpr (SUB != 2) {
-            lds_read16<t * 32 * kDmaRowBytes>(g.y[t], addr);
-        } else {
-            u32x2 lo, hi;
-            lds_read8<t * 32 * kDmaRowBytes>(lo, addr);
-            lds_read8<t * 32 * kDmaRowBytes + 8>(hi, addr);
-            g.y[t].x = lo.x;
-            g.y[t].y = lo.y;
-            g.yh[t].z = hi.x;
-            g.yh[t].w = hi.y;
-        }
+        lds_read16<t * 32 * kDmaRowBytes>(g.y[t], addr);
     };
 
     // Prologue: stage 0 into buffer 0, the first period's scales and the
@@ -610,10 +592,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
                     u32x4 yq = {0u, 0u, 0u, 0u};
                     yq[q] = f.y[tj][q];
                     mfma_fp4_sel_w<q>(acc[ti][tj], f.x[ti], yq, ssb[ks & 1][ti], ssa[ks & 1][tj]);
-                } else if constexpr (j < 16)
-                    mfma_fp4_sel_w<ks>(acc[ti][tj], f.x[ti], f.y[tj], wb[ti], wa[tj]);
-                else
-                    mfma_fp4_sel_w<ks>(acc[ti][tj], f.x[ti], f.yh[tj], wbh[ti], wah[tj]);
+                } else {
+                    // block j / 16 of each lane's 32 values: dwords 2 (j / 16), + 1 of A kept
+                    constexpr int q = j >> 4;
+                    u32x4 yq = {0u, 0u, 0u, 0u};
+                    yq[2 * q] = f.y[tj][2 * q];
+                    yq[2 * q + 1] = f.y[tj][2 * q + 1];
+                    if constexpr (q == 0)
+                        mfma_fp4_sel_w<ks>(acc[ti][tj], f.x[ti], yq, wb[ti], wa[tj]);
+                    else
+                        mfma_fp4_sel_w<ks>(acc[ti][tj], f.x[ti], yq, wbh[ti], wah[tj]);
+                }
                 // the next step's fragment reads, then (step 3) the next
                 // stage's scale reads, one after each MFMA
                 if constexpr (j < 8) {
@@ -666,10 +655,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_big_kernel(
                        "v"(fr[0].y[0]), "v"(fr[0].y[1]), "v"(fr[0].y[2]), "v"(fr[0].y[3]));
     asm volatile("" :: "v"(fr[1].x[0]), "v"(fr[1].x[1]), "v"(fr[1].x[2]), "v"(fr[1].x[3]),
                        "v"(fr[1].y[0]), "v"(fr[1].y[1]), "v"(fr[1].y[2]), "v"(fr[1].y[3]));
-    if constexpr (SUB == 2) {
-        asm volatile("" :: "v"(fr[0].yh[0]), "v"(fr[0].yh[1]), "v"(fr[0].yh[2]), "v"(fr[0].yh[3]),
-                           "v"(fr[1].yh[0]), "v"(fr[1].yh[1]), "v"(fr[1].yh[2]), "v"(fr[1].yh[3]));
-    }
     if constexpr (SUB == 4)
         asm volatile("" :: "v"(ssa[0][0]), "v"(ssa[0][1]), "v"(ssa[0][2]), "v"(ssa[0][3]),
                            "v"(ssb[0][0]), "v"(ssb[0][1]), "v"(ssb[0][2]), "v"(ssb[0][3]));
